@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark: fused codebook-GEMV decompressed-weight GB/s at batch 1, and % of HBM peak.
+
+One step = one batch-1 fused decode+GEMV pass (cbk_gemv) over every tensor of the workload, with
+the compressed tensors already resident in HBM.  Workloads (seeded synthetic BF16 weights):
+
+  attn4096     Llama-7B-shaped 4096x4096 attention projections, N(0, 0.02); 24 distinct tensors
+               (654 MB compressed, well above the 256 MB Infinity Cache) so every step reads HBM.
+  llama7b      full 7B-shaped decode step: 32 layers x {q,k,v,o 4096x4096, gate/up 11008x4096,
+               down 4096x11008}, N(0, 0.02), one codebook per tensor (224 tensors, 10.5 GB).
+
+The step is captured once in a HIP graph and replayed; the timed region is bracketed by
+torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the GEMV
+consumes) / step time.  The dominant kernel's roofline uses its algorithmic bytes per launch
+(packed indices ceil(n*b/8) + codebook 2U + x 2K + y 4M) over its average launch duration,
+measured with HIP events on the launch stream.  The CPU baseline times the oracle (decode + GEMV
+in float64) on a bounded sample with host threads.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload_tensors(name: str, count: int):
+    import synth
+    if name == "attn4096":
+        t = synth.WORKLOADS[2][0][0]
+        return [(2, layer, t) for layer in range(count)]
+    if name == "llama7b":
+        tensors, layers = synth.WORKLOADS[4]
+        return [(4, layer, t) for layer in range(layers) for t in tensors]
+    raise SystemExit(f"unknown workload {name}")
+
+
+def prepare(specs, threads):
+    """Generate and encode every tensor on the host (threads), upload to the GPU."""
+    import synth
+    import fly_decode_amd as cbk
+
+    def make(spec):
+        cfg, layer, t = spec
+        w = synth.workload_tensor(cfg, layer, t)
+        return cbk.encode(w)
+
+    out = []
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for i, c in enumerate(ex.map(make, specs)):
+            out.append(c.to("cuda"))
+            if (i + 1) % 16 == 0 or i + 1 == len(specs):
+                log(f"encoded + uploaded {i + 1}/{len(specs)} tensors")
+    return out
+
+
+def cpu_baseline(specs, seconds: float, threads: int):
+    """The oracle (decode + GEMV, float64) on whole tensors of the workload, rows split over host
+    threads, until about `seconds` of wall time have been spent."""
+    import oracle
+    import synth
+
+    oracle.build(force=False)
+    done_w, t_total, used = 0, 0.0, 0
+    cfg, layer, t = specs[0]
+    w = synth.workload_tensor(cfg, layer, t)
+    e = oracle.encode(w)
+    x = synth.workload_x(cfg, t.cols)[0]
+    y = np.zeros(t.rows, dtype=np.float64)
+    ab = np.zeros(t.rows, dtype=np.float64)
+    chunk = max(1, t.rows // (threads * 4))
+    spans = [(r, min(t.rows, r + chunk)) for r in range(0, t.rows, chunk)]
+    while t_total < seconds and used < 64:
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda s: oracle.gemv_rows_into(e, x, s[0], s[1], y, ab), spans))
+        t_total += time.perf_counter() - t0
+        done_w += t.rows * t.cols
+        used += 1
+    return {
+        "value": round(2.0 * done_w / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{used} full passes of decode+GEMV (float64) over one {t.rows}x{t.cols} tensor "
+                  f"of the workload, rows split over {threads} host threads, {t_total:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b"])
+    ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the GEMV shards by output rows; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fly_decode_amd as cbk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cbk.load_library()
+    threads = min(16, os.cpu_count() or 1)
+    specs = workload_tensors(args.workload, args.tensors)
+    log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
+    t0 = time.perf_counter()
+    tensors = prepare(specs, threads)
+    log(f"setup {time.perf_counter() - t0:.1f} s")
+
+    import synth
+    xs = {}
+    for d in tensors:
+        if d.cols not in xs:
+            x = synth.workload_x(specs[0][0], d.cols)[0]
+            xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in tensors]
+
+    def step():
+        for d, y in zip(tensors, ys):
+            cbk.gemv(d, xs[d.cols], y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K steps
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (event), wall {wall:.3f} s")
+
+    # ---- per-launch durations of the GEMV kernel (HIP events on the launch stream)
+    per = []
+    pairs = []
+    reps = max(1, min(args.steps, 10))
+    for _ in range(reps):
+        for d, y in zip(tensors, ys):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cbk.gemv(d, xs[d.cols], y=y)
+            b.record(stream)
+            pairs.append((d, a, b))
+    torch.cuda.synchronize()
+    for d, a, b in pairs:
+        per.append((d, a.elapsed_time(b) * 1e-3))
+    avg_launch_s = float(np.mean([t for _, t in per]))
+
+    n_total = sum(d.n for d in tensors)
+    comp_total = sum(d.compressed_bytes + 2 * d.cols + 4 * d.rows for d in tensors)
+    step_s = ms_step * 1e-3
+    value = 2.0 * n_total / step_s / 1e9
+    comp_gbps = comp_total / step_s / 1e9
+    algo_per_launch = comp_total / len(tensors)
+    achieved = algo_per_launch / avg_launch_s / 1e9
+    bits = sorted({d.b for d in tensors})
+    layers = 32 if args.workload == "llama7b" else len(tensors)
+
+    result = {
+        "metric": "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "tensors": len(tensors),
+            "shapes": sorted({f"{d.rows}x{d.cols}" for d in tensors}),
+            "batch": 1,
+            "index_bits": bits,
+            "compressed_bytes_per_step": comp_total,
+            "raw_bf16_bytes_per_step": 2 * n_total,
+            "graph_replay": graph is not None,
+        },
+        "compressed_GBps": round(comp_gbps, 2),
+        "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),
+        "layer_time_us": round(ms_step * 1e3 / (32 if args.workload == "llama7b" else layers), 3),
+        "tokens_per_s_equiv": round(1.0 / step_s, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"k_gemv_fast<{bits[-1]}>",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(algo_per_launch),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("CPU baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

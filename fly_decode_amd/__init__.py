@@ -1,0 +1,202 @@
+"""fly_decode_amd -- lossless codebook-compressed BF16 weights decoded on MI355X (gfx950).
+
+A thin ctypes binding over ``libcbk.so`` (C ABI declared in ``include/cbk.h``).  Every step of the
+hot path runs in the library's HIP kernels; this module only marshals arguments.  PyTorch is used
+for device memory and streams: inputs and outputs are torch tensors whose ``data_ptr()`` is handed
+to the library, and GPU calls are enqueued on ``torch.cuda.current_stream()``.
+
+If the library has not been built, importing works but every call raises ``RuntimeError``: there
+is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
+           "Compressed", "decode_bf16", "gemv", "gemm_small", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcbk.so")
+_lib = None
+
+CBK_OK = 0
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+
+
+class CbkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {load_library().cbk_status_str(status).decode()} (status {status})")
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64), ("U", ctypes.c_uint32),
+                ("b", ctypes.c_uint32), ("codebook", ctypes.c_void_p), ("words", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libcbk.so (built in-tree by fly_decode_amd/build.py); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: run fly_decode_amd/build.py (or "
+                               "__graft_entry__.build()) first; there is no fallback path")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.cbk_bits_for.restype = ctypes.c_uint32
+        lib.cbk_bits_for.argtypes = [ctypes.c_uint32]
+        lib.cbk_words_for.restype = ctypes.c_uint64
+        lib.cbk_words_for.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        lib.cbk_compressed_bytes.restype = ctypes.c_uint64
+        lib.cbk_compressed_bytes.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        lib.cbk_status_str.restype = ctypes.c_char_p
+        lib.cbk_status_str.argtypes = [ctypes.c_int]
+        lib.cbk_encode.restype = ctypes.c_int
+        lib.cbk_encode.argtypes = [_u16p, ctypes.c_uint64, _u16p, _u32p, _u32p, _u32p,
+                                   ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+        tp = ctypes.POINTER(_Tensor)
+        lib.cbk_decode_bf16.restype = ctypes.c_int
+        lib.cbk_decode_bf16.argtypes = [tp, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_gemv.restype = ctypes.c_int
+        lib.cbk_gemv.argtypes = [tp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_gemm_small.restype = ctypes.c_int
+        lib.cbk_gemm_small.argtypes = [tp, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
+                                       ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def bits_for(U: int) -> int:
+    return int(load_library().cbk_bits_for(U))
+
+
+def words_for(n: int, b: int) -> int:
+    return int(load_library().cbk_words_for(n, b))
+
+
+def compressed_bytes(n: int, U: int) -> int:
+    return int(load_library().cbk_compressed_bytes(n, U))
+
+
+class Compressed:
+    """A compressed tensor: codebook (uint16[U]) and words (uint32[words_for(n, b)]).
+
+    Host arrays after ``encode``; ``to(device)`` returns a copy whose arrays are torch tensors on
+    that device, ready for the GPU calls."""
+
+    def __init__(self, rows, cols, U, b, codebook, words):
+        self.rows, self.cols, self.U, self.b = int(rows), int(cols), int(U), int(b)
+        self.codebook, self.words = codebook, words
+
+    @property
+    def n(self) -> int:
+        return self.rows * self.cols
+
+    @property
+    def compressed_bytes(self) -> int:
+        return compressed_bytes(self.n, self.U)
+
+    def to(self, device) -> "Compressed":
+        import torch
+        def put(a, view):
+            if isinstance(a, np.ndarray):
+                return torch.from_numpy(np.ascontiguousarray(a).view(view)).to(device)
+            return a.to(device)
+        cb = put(self.codebook, np.int16)
+        wd = put(self.words, np.int32)
+        return Compressed(self.rows, self.cols, self.U, self.b, cb, wd)
+
+    def _struct(self) -> _Tensor:
+        cb = self.codebook.data_ptr() if self.U and self.codebook.numel() else None
+        wd = self.words.data_ptr() if self.words.numel() else None
+        return _Tensor(self.rows, self.cols, self.U, self.b, cb, wd)
+
+
+def encode(w, rows: int | None = None, cols: int | None = None) -> Compressed:
+    """Compress a host array of BF16 bit patterns (numpy uint16/int16, or a CPU torch tensor of
+    bfloat16/int16/uint16), shape [rows][cols] (or 1-D with rows/cols given)."""
+    if hasattr(w, "detach"):
+        w = w.detach().contiguous().cpu()
+        w = w.view(__import__("torch").int16).numpy()
+    w = np.ascontiguousarray(w)
+    if w.dtype not in (np.uint16, np.int16):
+        raise TypeError("encode expects 16-bit patterns")
+    if rows is None:
+        rows, cols = (w.shape if w.ndim == 2 else (1, w.size))
+    flat = w.reshape(-1).view(np.uint16)
+    if flat.size != rows * cols:
+        raise ValueError("rows * cols does not match the array size")
+    lib = load_library()
+    cb = np.zeros(65536, dtype=np.uint16)
+    U, b, need = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint64()
+    src = flat.ctypes.data_as(_u16p) if flat.size else None
+    st = lib.cbk_encode(src, flat.size, cb.ctypes.data_as(_u16p), ctypes.byref(U), ctypes.byref(b),
+                        None, 0, ctypes.byref(need))
+    if st not in (CBK_OK, 2):
+        raise CbkError(st, "cbk_encode")
+    words = np.zeros(need.value, dtype=np.uint32)
+    st = lib.cbk_encode(src, flat.size, cb.ctypes.data_as(_u16p), ctypes.byref(U), ctypes.byref(b),
+                        words.ctypes.data_as(_u32p) if words.size else None, words.size,
+                        ctypes.byref(need))
+    if st != CBK_OK:
+        raise CbkError(st, "cbk_encode")
+    return Compressed(rows, cols, U.value, b.value, cb[:U.value].copy(), words)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(st, what):
+    if st != CBK_OK:
+        raise CbkError(st, what)
+
+
+def decode_bf16(t: Compressed, out=None, stream=None):
+    """Standalone decode into a [rows][cols] torch.bfloat16 tensor (exact original bits)."""
+    import torch
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device=t.words.device)
+    ts = t._struct()
+    _check(load_library().cbk_decode_bf16(ctypes.byref(ts), ctypes.c_void_p(out.data_ptr() or None),
+                                          _stream(stream)), "cbk_decode_bf16")
+    return out
+
+
+def gemv(t: Compressed, x, y=None, stream=None):
+    """y[rows] (float32) = W . x for a torch.bfloat16 vector x[cols] on the device."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.numel() != t.cols or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 vector of length cols")
+    if y is None:
+        y = torch.empty(t.rows, dtype=torch.float32, device=x.device)
+    ts = t._struct()
+    _check(load_library().cbk_gemv(ctypes.byref(ts), ctypes.c_void_p(x.data_ptr() or None),
+                                   ctypes.c_void_p(y.data_ptr() or None), _stream(stream)),
+           "cbk_gemv")
+    return y
+
+
+def gemm_small(t: Compressed, X, Y=None, stream=None):
+    """Y[batch][rows] (float32) = X . W^T for a torch.bfloat16 X[batch][cols] (row stride may
+    exceed cols but must be a multiple of 8)."""
+    import torch
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or X.shape[1] != t.cols or X.stride(1) != 1:
+        raise ValueError("X must be a [batch][cols] bfloat16 matrix with unit column stride")
+    batch = X.shape[0]
+    if Y is None:
+        Y = torch.empty((batch, t.rows), dtype=torch.float32, device=X.device)
+    ts = t._struct()
+    _check(load_library().cbk_gemm_small(ctypes.byref(ts), ctypes.c_void_p(X.data_ptr() or None),
+                                         X.stride(0), batch, ctypes.c_void_p(Y.data_ptr() or None),
+                                         Y.stride(0), _stream(stream)), "cbk_gemm_small")
+    return Y

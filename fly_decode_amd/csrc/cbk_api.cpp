@@ -1,0 +1,178 @@
+// Host half of libcbk: size helpers, the encoder, and argument validation in front of the HIP
+// launchers.  Nothing here touches the GPU until every argument has been checked.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "cbk_internal.h"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Presence of every 16-bit pattern in w[begin, end).
+void mark_present(const uint16_t *w, uint64_t begin, uint64_t end, uint8_t *seen) {
+    for (uint64_t i = begin; i < end; ++i) seen[w[i]] = 1;
+}
+
+// Pack fields [f0, f1) (f0 a multiple of 32, so it starts on word f0*b/32) into words.
+void pack_range(const uint16_t *w, uint64_t f0, uint64_t f1, const uint16_t *index_of, uint32_t b,
+                uint32_t *words) {
+    uint64_t acc = 0;
+    uint32_t nbits = 0;
+    uint32_t *dst = words + (f0 * b) / 32;
+    for (uint64_t i = f0; i < f1; ++i) {
+        acc |= static_cast<uint64_t>(index_of[w[i]]) << nbits;
+        nbits += b;
+        if (nbits >= 32) {
+            *dst++ = static_cast<uint32_t>(acc);
+            acc >>= 32;
+            nbits -= 32;
+        }
+    }
+    if (nbits) *dst = static_cast<uint32_t>(acc);
+}
+
+unsigned worker_count(uint64_t n) {
+    if (n < (uint64_t(1) << 22)) return 1;
+    unsigned hw = std::thread::hardware_concurrency();
+    return std::max(1u, std::min(hw ? hw : 1u, 16u));
+}
+
+cbk_status check_tensor(const cbk_tensor *t) {
+    if (!t) return CBK_E_INVALID;
+    if (t->rows && t->cols > UINT64_MAX / t->rows) return CBK_E_INVALID;
+    const uint64_t n = t->rows * t->cols;
+    if (t->U > 65536u) return CBK_E_INVALID;
+    if (t->b != cbk_bits_for(t->U)) return CBK_E_INVALID;
+    if (n > 0 && t->U == 0) return CBK_E_INVALID;
+    if (t->U > 0 && !t->codebook) return CBK_E_INVALID;
+    if (n > 0 && t->b > 0 && !t->words) return CBK_E_INVALID;
+    if (t->words && !aligned(t->words, 16)) return CBK_E_ALIGN;
+    if (t->codebook && !aligned(t->codebook, 2)) return CBK_E_ALIGN;
+    // Field offsets are computed in 64-bit; the kernels index 16-byte chunks in 32-bit.
+    if (n > (uint64_t(1) << 36)) return CBK_E_UNSUPPORTED;
+    if (t->rows > 0xFFFFFFFFull || t->cols > 0xFFFFFFFFull) return CBK_E_UNSUPPORTED;
+    return CBK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t cbk_bits_for(uint32_t U) {
+    uint32_t b = 0;
+    while ((uint64_t(1) << b) < U) ++b;
+    return b;
+}
+
+uint64_t cbk_words_for(uint64_t n, uint32_t b) {
+    const uint64_t words = (n * b + 31) / 32;
+    return (words + 3) & ~uint64_t(3);
+}
+
+uint64_t cbk_compressed_bytes(uint64_t n, uint32_t U) {
+    return 2ull * U + (n * cbk_bits_for(U) + 7) / 8;
+}
+
+const char *cbk_status_str(int status) {
+    switch (status) {
+        case CBK_OK: return "ok";
+        case CBK_E_INVALID: return "invalid argument";
+        case CBK_E_CAPACITY: return "output buffer too small";
+        case CBK_E_ALIGN: return "misaligned pointer or leading dimension";
+        case CBK_E_UNSUPPORTED: return "unsupported shape";
+        case CBK_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+cbk_status cbk_encode(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_t *U_out,
+                      uint32_t *b_out, uint32_t *words, uint64_t words_cap, uint64_t *words_needed) {
+    if ((n > 0 && !w) || !codebook || !U_out || !b_out) return CBK_E_INVALID;
+    if (n > (uint64_t(1) << 40)) return CBK_E_UNSUPPORTED;
+
+    // 1. which of the 65,536 patterns occur (threads mark private tables, then merge)
+    const unsigned nt = worker_count(n);
+    std::vector<std::vector<uint8_t>> seen(nt, std::vector<uint8_t>(65536, 0));
+    if (nt == 1) {
+        mark_present(w, 0, n, seen[0].data());
+    } else {
+        std::vector<std::thread> pool;
+        for (unsigned k = 0; k < nt; ++k)
+            pool.emplace_back(mark_present, w, n * k / nt, n * (k + 1) / nt, seen[k].data());
+        for (auto &th : pool) th.join();
+        for (unsigned k = 1; k < nt; ++k)
+            for (uint32_t v = 0; v < 65536; ++v) seen[0][v] |= seen[k][v];
+    }
+    // 2. ascending scan gives the sorted codebook and every pattern's index
+    std::vector<uint16_t> index_of(65536, 0);
+    uint32_t U = 0;
+    for (uint32_t v = 0; v < 65536; ++v) {
+        if (seen[0][v]) {
+            index_of[v] = static_cast<uint16_t>(U);
+            codebook[U++] = static_cast<uint16_t>(v);
+        }
+    }
+    const uint32_t b = cbk_bits_for(U);
+    const uint64_t need = cbk_words_for(n, b);
+    *U_out = U;
+    *b_out = b;
+    if (words_needed) *words_needed = need;
+    if (need > words_cap || (need > 0 && !words)) return CBK_E_CAPACITY;
+    if (need == 0) return CBK_OK;
+    memset(words, 0, need * sizeof(uint32_t));
+    if (b == 0) return CBK_OK;
+
+    // 3. pack, LSB first; chunks start on multiples of 32 fields so they own whole words
+    if (nt == 1) {
+        pack_range(w, 0, n, index_of.data(), b, words);
+    } else {
+        const uint64_t groups = (n + 31) / 32;
+        std::vector<std::thread> pool;
+        for (unsigned k = 0; k < nt; ++k) {
+            const uint64_t f0 = std::min(n, 32 * (groups * k / nt));
+            const uint64_t f1 = std::min(n, 32 * (groups * (k + 1) / nt));
+            if (f1 > f0) pool.emplace_back(pack_range, w, f0, f1, index_of.data(), b, words);
+        }
+        for (auto &th : pool) th.join();
+    }
+    return CBK_OK;
+}
+
+cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream) {
+    cbk_status st = check_tensor(t);
+    if (st != CBK_OK) return st;
+    const uint64_t n = t->rows * t->cols;
+    if (n == 0) return CBK_OK;
+    if (!out) return CBK_E_INVALID;
+    if (!aligned(out, 2)) return CBK_E_ALIGN;
+    return cbk::launch_decode(*t, out, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_gemv(const cbk_tensor *t, const uint16_t *x, float *y, void *stream) {
+    cbk_status st = check_tensor(t);
+    if (st != CBK_OK) return st;
+    if (t->rows == 0) return CBK_OK;
+    if (!y || (t->cols > 0 && !x)) return CBK_E_INVALID;
+    if (!aligned(y, 4) || (x && !aligned(x, 2))) return CBK_E_ALIGN;
+    return cbk::launch_gemv(*t, x, y, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_gemm_small(const cbk_tensor *t, const uint16_t *X, uint64_t ldx, uint32_t batch,
+                          float *Y, uint64_t ldy, void *stream) {
+    cbk_status st = check_tensor(t);
+    if (st != CBK_OK) return st;
+    if (batch < 1 || batch > 16) return CBK_E_INVALID;
+    if (t->rows == 0) return CBK_OK;
+    if (!Y || (t->cols > 0 && !X)) return CBK_E_INVALID;
+    if (ldx < t->cols || ldy < t->rows) return CBK_E_INVALID;
+    if (!aligned(Y, 4) || (X && !aligned(X, 2))) return CBK_E_ALIGN;
+    if (ldx > 0xFFFFFFFFull || ldy > 0xFFFFFFFFull) return CBK_E_UNSUPPORTED;
+    return cbk::launch_gemm(*t, X, ldx, batch, Y, ldy, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,644 @@
+// HIP kernels for gfx950 (CDNA4): decode of codebook-compressed BF16 tensors, standalone and
+// fused into GEMV (batch 1) and skinny GEMM (batch 2..16).
+//
+// What is computed follows the codebook lossless compression overview ("How it works": the
+// stored index is replaced by its dictionary value, exactly) and the Codebook-Quantization
+// digest ("Key points": bit-packed indices of the unique weights).  Fields are b bits wide,
+// packed LSB first into little-endian uint32 words, row-major with no row padding.
+//
+// Layout of the work (fast paths, templated on b so every shift is a compile-time constant):
+//  * A "unit" is C = odd_part(b) 16-byte chunks = F = 128 / 2^v2(b) whole fields.  Units start
+//    on 16-byte boundaries and no field crosses a unit boundary.
+//  * A wave loads 64 units with C fully coalesced 128-bit loads per lane (lane l takes chunk
+//    j*64 + l), writes them to a wave-private LDS stage, and reads back its own unit as C
+//    128-bit LDS reads (odd stride C chunks: no bank conflicts).  For C == 1 the lane already
+//    holds its unit and the stage is skipped.
+//  * Fields are unpacked in registers (one shift/and, or alignbit + and when a field straddles
+//    two words) and gathered from the codebook staged in LDS, padded to 2^b entries with 0x7FC0
+//    so a corrupt index can never leave the table.
+//  * GEMV (batch 1): units run along rows; x sits in LDS, padded 16 bytes per unit so the
+//    lanes' 128-bit reads are conflict-free; BF16 pairs are multiplied with v_dot2c_f32_bf16
+//    into fp32; a segmented wave reduction (rows are contiguous runs of lanes) produces y.
+//  * Skinny GEMM: a wave owns a 16-row tile and walks K in steps of 4 units per row; lane
+//    (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded tile to
+//    v_mfma_f32_16x16x32_bf16; batches up to 8 use v_dot2c on the vector ALUs.  When K is split
+//    across waves the partial sums are added into a zero-filled Y with fp32 atomics.
+//
+// Generic kernels (any b and shape, runtime field extraction straight from global memory) cover
+// b == 0, rows whose length is not a whole number of units, and shapes beyond the LDS budget.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+#include <utility>
+
+#include "cbk_internal.h"
+
+namespace cbk {
+namespace {
+
+constexpr uint16_t kCorrupt = 0x7FC0;
+constexpr int kWaves = 4;                 // waves per workgroup, decode and GEMV
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGemmWaves = 4;             // waves per workgroup, skinny GEMM
+constexpr uint32_t kLdsLimit = 160 * 1024;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t h) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
+}
+
+template <int B>
+struct Geo {
+    static constexpr int C = B >> __builtin_ctz(B);   // 16-byte chunks per unit
+    static constexpr int F = 128 >> __builtin_ctz(B); // fields per unit
+    static constexpr int D = 4 * C;                   // dwords per unit
+    static constexpr uint32_t NE = 1u << B;           // codebook entries in LDS
+    static constexpr uint32_t mask = (1u << B) - 1u;
+};
+
+// Field f of a unit held in registers; f is a constant once the caller's loop is unrolled.
+template <int B>
+__device__ __forceinline__ uint32_t unit_field(const uint32_t *d, int f) {
+    const int bit = f * B, w = bit >> 5, s = bit & 31;
+    if (s + B <= 32) return (d[w] >> s) & Geo<B>::mask;
+    return __builtin_amdgcn_alignbit(d[w + 1], d[w], s) & Geo<B>::mask;
+}
+
+// Field i of a stream, runtime width (generic kernels).
+__device__ __forceinline__ uint32_t stream_field(const uint32_t *__restrict__ words, uint32_t b,
+                                                 uint64_t i) {
+    if (b == 0) return 0;
+    const uint64_t bit = i * b;
+    const uint64_t w = bit >> 5;
+    const uint32_t s = static_cast<uint32_t>(bit) & 31u;
+    const uint32_t lo = words[w];
+    const uint32_t hi = (s + b > 32) ? words[w + 1] : 0u;
+    return __builtin_amdgcn_alignbit(hi, lo, s) & ((1u << b) - 1u);
+}
+
+// q = n / P, r = n % P with m = floor(2^32 / P) (m = 2^32 - 1 for P = 1): the estimate is exact or
+// one short for every 32-bit n, so a single correction suffices.
+__device__ __forceinline__ void divmod(uint32_t n, uint32_t P, uint32_t m, uint32_t &q, uint32_t &r) {
+    q = __umulhi(n, m);
+    r = n - q * P;
+    if (r >= P) { ++q; r -= P; }
+}
+
+template <int B>
+__device__ __forceinline__ void stage_codebook(uint16_t *cbl, const uint16_t *__restrict__ cb,
+                                               uint32_t U, int tid, int nthreads) {
+    for (uint32_t i = tid; i < Geo<B>::NE; i += nthreads) cbl[i] = i < U ? cb[i] : kCorrupt;
+}
+
+constexpr uint32_t round16(uint32_t v) { return (v + 15u) & ~15u; }
+
+// ------------------------------------------------------------------------------ fast decode
+// Flat: unit u decodes weights [u*F, u*F + F).  Waves own contiguous unit ranges.
+template <int B>
+__global__ __launch_bounds__(kThreads) void k_decode_fast(const uint4 *__restrict__ w4,
+                                                          uint32_t nchunks,
+                                                          const uint16_t *__restrict__ cb,
+                                                          uint32_t U, uint16_t *__restrict__ out,
+                                                          uint64_t n, uint32_t T) {
+    using G = Geo<B>;
+    constexpr int C = G::C, F = G::F;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *cbl = reinterpret_cast<uint16_t *>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint4 *stage = reinterpret_cast<uint4 *>(smem + round16(G::NE * 2)) + wave * 64 * C;
+    stage_codebook<B>(cbl, cb, U, tid, kThreads);
+    __syncthreads();
+
+    const uint32_t NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
+    const uint32_t u0 = static_cast<uint64_t>(T) * gw / NW;
+    const uint32_t u1 = static_cast<uint64_t>(T) * (gw + 1) / NW;
+    if (u0 >= u1) return;
+    const uint32_t ch_lim = min(u1 * C, nchunks);
+
+    uint4 nxt[C];
+    auto load = [&](uint32_t us) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const uint32_t ch = us * C + j * 64 + lane;
+            nxt[j] = ch < ch_lim ? w4[ch] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    load(u0);
+    for (uint32_t us = u0; us < u1; us += 64) {
+        uint32_t d[G::D];
+        if constexpr (C == 1) {
+            d[0] = nxt[0].x; d[1] = nxt[0].y; d[2] = nxt[0].z; d[3] = nxt[0].w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < C; ++j) stage[j * 64 + lane] = nxt[j];
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const uint4 v = stage[lane * C + j];
+                d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
+            }
+        }
+        if (us + 64 < u1) load(us + 64);
+
+        const uint32_t gu = us + lane;
+        if (gu < u1) {
+            const uint64_t base = static_cast<uint64_t>(gu) * F;
+            if (base + F <= n) {
+                uint4 *o = reinterpret_cast<uint4 *>(out + base);
+#pragma unroll
+                for (int t = 0; t < F / 8; ++t) {
+                    uint32_t p[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t i0 = unit_field<B>(d, 8 * t + 2 * q);
+                        const uint32_t i1 = unit_field<B>(d, 8 * t + 2 * q + 1);
+                        p[q] = static_cast<uint32_t>(cbl[i0]) | (static_cast<uint32_t>(cbl[i1]) << 16);
+                    }
+                    o[t] = make_uint4(p[0], p[1], p[2], p[3]);
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+                    if (base + f < n) out[base + f] = cbl[unit_field<B>(d, f)];
+            }
+        }
+    }
+}
+
+// -------------------------------------------------------------------------------- fast GEMV
+template <int B>
+__global__ __launch_bounds__(kThreads) void k_gemv_fast(const uint4 *__restrict__ w4,
+                                                        const uint16_t *__restrict__ cb, uint32_t U,
+                                                        const uint16_t *__restrict__ x,
+                                                        float *__restrict__ y, uint32_t M,
+                                                        uint32_t P, uint32_t Pm) {
+    using G = Geo<B>;
+    constexpr int C = G::C, F = G::F;
+    constexpr uint32_t XU = 2 * F + 16;  // LDS bytes per unit of x (16 bytes of padding)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *cbl = reinterpret_cast<uint16_t *>(smem);
+    unsigned char *xl = smem + round16(G::NE * 2);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint4 *stage = reinterpret_cast<uint4 *>(xl + P * XU) + wave * 64 * C;
+
+    stage_codebook<B>(cbl, cb, U, tid, kThreads);
+    {
+        const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
+        const uint32_t xchunks = P * (F / 8);
+        for (uint32_t q = tid; q < xchunks; q += kThreads) {
+            const uint32_t unit = q / (F / 8), off = q % (F / 8);
+            *reinterpret_cast<uint4 *>(xl + unit * XU + off * 16) = x4[q];
+        }
+    }
+    __syncthreads();
+
+    const uint32_t NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
+    const uint32_t r0 = static_cast<uint64_t>(M) * gw / NW;
+    const uint32_t r1 = static_cast<uint64_t>(M) * (gw + 1) / NW;
+    const uint32_t u0 = r0 * P, u1 = r1 * P;
+    if (u0 >= u1) return;
+    const uint32_t ch_lim = u1 * C;
+
+    uint4 nxt[C];
+    auto load = [&](uint32_t us) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const uint32_t ch = us * C + j * 64 + lane;
+            nxt[j] = ch < ch_lim ? w4[ch] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    load(u0);
+    float carry = 0.f;
+    for (uint32_t us = u0; us < u1; us += 64) {
+        uint32_t d[G::D];
+        if constexpr (C == 1) {
+            d[0] = nxt[0].x; d[1] = nxt[0].y; d[2] = nxt[0].z; d[3] = nxt[0].w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < C; ++j) stage[j * 64 + lane] = nxt[j];
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const uint4 v = stage[lane * C + j];
+                d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
+            }
+        }
+        if (us + 64 < u1) load(us + 64);
+
+        const uint32_t gu = us + lane;
+        const bool act = gu < u1;
+        uint32_t row, cu;
+        divmod(gu, P, Pm, row, cu);
+        const unsigned char *xb = xl + cu * XU;
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < F / 8; ++t) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xb + 16 * t);
+            const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i0 = unit_field<B>(d, 8 * t + 2 * q);
+                const uint32_t i1 = unit_field<B>(d, 8 * t + 2 * q + 1);
+                const uint32_t wp = static_cast<uint32_t>(cbl[i0]) | (static_cast<uint32_t>(cbl[i1]) << 16);
+                a[q] = dot2(wp, xs[q], a[q]);
+            }
+        }
+        float acc = act ? (a[0] + a[1]) + (a[2] + a[3]) : 0.f;
+
+        // Segmented suffix sums: lanes of one row form a contiguous run (units are consecutive).
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_down(acc, off, 64);
+            if (lane + off < 64 && cu + off < P) acc += o;
+        }
+        const uint32_t last_lane = min(u1 - 1u - us, 63u);
+        const uint32_t last_cu = __builtin_amdgcn_readlane(cu, last_lane);
+        const bool open = last_cu != P - 1;                       // last row continues next step
+        const uint32_t head_last = last_lane - min(last_lane, last_cu);
+        if (lane == 0) acc += carry;
+        const bool head = lane == 0 || cu == 0;
+        if (act && head && !(open && static_cast<uint32_t>(lane) == head_last)) y[row] = acc;
+        carry = open ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, acc), head_last))
+                     : 0.f;
+    }
+}
+
+// ------------------------------------------------------------------------- fast skinny GEMM
+// A wave owns a 16-row tile and a range of k-steps (4 units of every row per step).
+template <int B, int NB, bool MFMA>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_fast(
+    const uint4 *__restrict__ w4, const uint16_t *__restrict__ cb, uint32_t U,
+    const uint16_t *__restrict__ X, uint32_t ldx, uint32_t batch, float *__restrict__ Y,
+    uint32_t ldy, uint32_t M, uint32_t P, uint32_t ksteps, uint32_t splits, uint32_t items,
+    int atomic) {
+    using G = Geo<B>;
+    constexpr int C = G::C, F = G::F;
+    constexpr int RS = 4 * C + 1;  // padded stage row stride in chunks (odd: conflict-free)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *cbl = reinterpret_cast<uint16_t *>(smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint4 *stage = reinterpret_cast<uint4 *>(smem + round16(G::NE * 2)) + wave * 16 * RS;
+    stage_codebook<B>(cbl, cb, U, tid, 64 * kGemmWaves);
+    __syncthreads();
+
+    const int li = lane & 15, lg = lane >> 4;
+    const uint32_t NW = gridDim.x * kGemmWaves;
+    for (uint32_t item = blockIdx.x * kGemmWaves + wave; item < items; item += NW) {
+        const uint32_t tile = item / splits, split = item % splits;
+        const uint32_t ks0 = static_cast<uint64_t>(ksteps) * split / splits;
+        const uint32_t ks1 = static_cast<uint64_t>(ksteps) * (split + 1) / splits;
+        const uint32_t row0 = tile * 16;
+
+        f32x4_t cm = {0.f, 0.f, 0.f, 0.f};
+        float acc[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] = 0.f;
+
+        for (uint32_t ks = ks0; ks < ks1; ++ks) {
+            // Cooperative load of 16 rows x 4 units (4C chunks per row), coalesced per row.
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const uint32_t q = j * 64 + lane;       // 0 .. 64C-1
+                const uint32_t i = q / (4 * C), off = q % (4 * C);
+                const uint32_t unit = ks * 4 + off / C;
+                const uint32_t row = row0 + i;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (row < M && unit < P) v = w4[(static_cast<uint64_t>(row) * P + ks * 4) * C + off];
+                stage[i * RS + off] = v;
+            }
+            uint32_t d[G::D];
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const uint4 v = stage[li * RS + lg * C + j];
+                d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
+            }
+            const uint32_t unit = ks * 4 + lg;
+            const bool valid = unit < P && row0 + li < M;
+            const uint32_t kbase = unit * F;
+#pragma unroll
+            for (int t = 0; t < F / 8; ++t) {
+                uint32_t wp[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t i0 = unit_field<B>(d, 8 * t + 2 * q);
+                    const uint32_t i1 = unit_field<B>(d, 8 * t + 2 * q + 1);
+                    wp[q] = valid ? (static_cast<uint32_t>(cbl[i0]) | (static_cast<uint32_t>(cbl[i1]) << 16)) : 0u;
+                }
+                if constexpr (MFMA) {
+                    // A: row li, k = 8 consecutive of unit lg.  B: batch column li, same k.
+                    uint4 xv = make_uint4(0, 0, 0, 0);
+                    if (static_cast<uint32_t>(li) < batch && unit < P)
+                        xv = *reinterpret_cast<const uint4 *>(X + static_cast<uint64_t>(li) * ldx + kbase + 8 * t);
+                    const uint4 wv = make_uint4(wp[0], wp[1], wp[2], wp[3]);
+                    cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
+                                                                 __builtin_bit_cast(bf16x8_t, xv),
+                                                                 cm, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) {
+                        uint4 xv = make_uint4(0, 0, 0, 0);
+                        if (unit < P)
+                            xv = *reinterpret_cast<const uint4 *>(X + static_cast<uint64_t>(n) * ldx + kbase + 8 * t);
+                        acc[n] = dot2(wp[0], xv.x, acc[n]);
+                        acc[n] = dot2(wp[1], xv.y, acc[n]);
+                        acc[n] = dot2(wp[2], xv.z, acc[n]);
+                        acc[n] = dot2(wp[3], xv.w, acc[n]);
+                    }
+                }
+            }
+        }
+
+        if constexpr (MFMA) {
+            // Lane l holds C[i = 4*(l/16) + r][n = l % 16], r = 0..3.
+            const int n = li;
+            if (static_cast<uint32_t>(n) < batch) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t row = row0 + 4 * lg + r;
+                    if (row < M) {
+                        float *dst = Y + static_cast<uint64_t>(n) * ldy + row;
+                        if (atomic) atomicAdd(dst, cm[r]); else *dst = cm[r];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                float v = acc[n];
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                acc[n] = v;
+            }
+            const uint32_t row = row0 + li;
+            if (lg == 0 && row < M) {
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    float *dst = Y + static_cast<uint64_t>(n) * ldy + row;
+                    if (atomic) atomicAdd(dst, acc[n]); else *dst = acc[n];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------ generic kernels
+__global__ __launch_bounds__(256) void k_decode_generic(const uint32_t *__restrict__ words,
+                                                        uint32_t b, const uint16_t *__restrict__ cb,
+                                                        uint32_t U, uint16_t *__restrict__ out,
+                                                        uint64_t n) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint32_t idx = stream_field(words, b, i);
+        out[i] = idx < U ? cb[idx] : kCorrupt;
+    }
+}
+
+// One wave per row, grid-stride over rows; NB batch columns (NB <= 16).
+template <int NB>
+__global__ __launch_bounds__(256) void k_gemm_generic(const uint32_t *__restrict__ words, uint32_t b,
+                                                      const uint16_t *__restrict__ cb, uint32_t U,
+                                                      const uint16_t *__restrict__ X, uint64_t ldx,
+                                                      uint32_t batch, float *__restrict__ Y,
+                                                      uint64_t ldy, uint32_t M, uint32_t K) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t wpb = blockDim.x >> 6;
+    for (uint32_t row = blockIdx.x * wpb + (threadIdx.x >> 6); row < M; row += gridDim.x * wpb) {
+        float acc[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] = 0.f;
+        for (uint32_t k = lane; k < K; k += 64) {
+            const uint32_t idx = stream_field(words, b, static_cast<uint64_t>(row) * K + k);
+            const float w = bf16_value(idx < U ? cb[idx] : kCorrupt);
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                if (n < static_cast<int>(batch)) acc[n] = fmaf(w, bf16_value(X[n * ldx + k]), acc[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            float v = acc[n];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            if (lane == 0 && n < static_cast<int>(batch)) Y[n * ldy + row] = v;
+        }
+    }
+}
+
+__global__ void k_fill_zero(float *__restrict__ Y, uint64_t ldy, uint32_t rows, uint32_t batch) {
+    const uint64_t total = static_cast<uint64_t>(rows) * batch;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride)
+        Y[(i / rows) * ldy + (i % rows)] = 0.f;
+}
+
+// ------------------------------------------------------------------------------ host side
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+cbk_status launched() { return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP; }
+
+uint32_t magic_for(uint32_t P) {
+    return P == 1 ? 0xFFFFFFFFu : static_cast<uint32_t>((uint64_t(1) << 32) / P);
+}
+
+// Workgroups that fit on one CU given the LDS footprint (capped at 2: register-limited).
+uint32_t groups_per_cu(uint32_t lds) {
+    return lds == 0 ? 2u : std::max(1u, std::min(2u, kLdsLimit / lds));
+}
+
+// Kernels above 64 KiB of dynamic LDS must raise their limit first.
+template <typename K>
+bool allow_lds(K kernel, uint32_t lds) {
+    if (lds <= 65536) return true;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(lds)) == hipSuccess;
+}
+
+// Runs Fn<b>::run(args) for the b in Bs that matches; false when none does or run declines.
+template <template <int> class Fn, typename Args, int... Bs>
+bool dispatch_b(int b, Args &args, std::integer_sequence<int, Bs...>) {
+    bool ok = false;
+    (void)((b == Bs ? (ok = Fn<Bs>::run(args), true) : false) || ...);
+    return ok;
+}
+using AllB = std::integer_sequence<int, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>;
+
+struct DecodeArgs {
+    const cbk_tensor &t; uint16_t *out; hipStream_t s; cbk_status st;
+};
+
+template <int B>
+struct DecodeRun {
+    static bool run(DecodeArgs &a) {
+        using G = Geo<B>;
+        const cbk_tensor &t = a.t;
+        const uint64_t n = t.rows * t.cols;
+        const uint64_t T64 = (n + G::F - 1) / G::F;
+        const uint64_t nchunks = cbk_words_for(n, B) / 4;
+        if (T64 * G::C >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
+        const uint32_t lds = round16(G::NE * 2) + (G::C == 1 ? 0u : kWaves * 64u * G::C * 16u);
+        if (!allow_lds(k_decode_fast<B>, lds)) return false;
+        const uint32_t max_groups = cu_count() * groups_per_cu(lds);
+        const uint64_t want = std::min<uint64_t>((T64 + 63) / 64, uint64_t(max_groups) * kWaves);
+        const uint32_t grid = std::max<uint32_t>(1, static_cast<uint32_t>((want + kWaves - 1) / kWaves));
+        hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(kThreads), lds, a.s,
+                           reinterpret_cast<const uint4 *>(t.words), static_cast<uint32_t>(nchunks),
+                           t.codebook, t.U, a.out, n, static_cast<uint32_t>(T64));
+        a.st = launched();
+        return true;
+    }
+};
+
+struct GemvArgs {
+    const cbk_tensor &t; const uint16_t *x; float *y; hipStream_t s; cbk_status st;
+};
+
+template <int B>
+struct GemvRun {
+    static bool run(GemvArgs &a) {
+        using G = Geo<B>;
+        const cbk_tensor &t = a.t;
+        if (t.cols == 0 || t.cols % G::F != 0) return false;
+        const uint64_t P = t.cols / G::F;
+        if (t.rows * P * G::C >= (uint64_t(1) << 32)) return false;
+        if (t.rows * P * P >= (uint64_t(1) << 32)) return false;
+        const uint64_t lds64 = round16(G::NE * 2) + P * (2 * G::F + 16) +
+                               (G::C == 1 ? 0u : kWaves * 64u * G::C * 16u);
+        if (lds64 > kLdsLimit) return false;
+        const uint32_t lds = static_cast<uint32_t>(lds64);
+        if (!allow_lds(k_gemv_fast<B>, lds)) return false;
+        const uint32_t M = static_cast<uint32_t>(t.rows);
+        const uint64_t steps = (uint64_t(M) * P + 63) / 64;
+        const uint64_t max_waves = uint64_t(cu_count()) * groups_per_cu(lds) * kWaves;
+        const uint64_t want = std::min<uint64_t>(std::min<uint64_t>(steps, max_waves), M);
+        const uint32_t grid = std::max<uint32_t>(1, static_cast<uint32_t>((want + kWaves - 1) / kWaves));
+        hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(kThreads), lds, a.s,
+                           reinterpret_cast<const uint4 *>(t.words), t.codebook, t.U, a.x, a.y, M,
+                           static_cast<uint32_t>(P), magic_for(static_cast<uint32_t>(P)));
+        a.st = launched();
+        return true;
+    }
+};
+
+struct GemmArgs {
+    const cbk_tensor &t; const uint16_t *X; uint64_t ldx; uint32_t batch; float *Y; uint64_t ldy;
+    hipStream_t s; cbk_status st;
+};
+
+template <int B, int NB, bool MFMA>
+bool gemm_launch(GemmArgs &a, uint32_t lds) {
+    using G = Geo<B>;
+    const cbk_tensor &t = a.t;
+    if (!allow_lds(k_gemm_fast<B, NB, MFMA>, lds)) return false;
+    const uint64_t P = t.cols / G::F;
+    const uint32_t M = static_cast<uint32_t>(t.rows);
+    const uint32_t ksteps = static_cast<uint32_t>((P + 3) / 4);
+    const uint32_t tiles = (M + 15) / 16;
+    const uint32_t resident = cu_count() * groups_per_cu(lds) * kGemmWaves;
+    uint32_t splits = 1;
+    while (uint64_t(tiles) * splits < resident && splits * 2 <= ksteps) splits *= 2;
+    const uint32_t items = tiles * splits;
+    const int atomic = splits > 1;
+    if (atomic) {
+        const uint64_t total = uint64_t(M) * a.batch;
+        hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<uint32_t>(std::min<uint64_t>(1024, (total + 255) / 256))),
+                           dim3(256), 0, a.s, a.Y, a.ldy, M, a.batch);
+    }
+    const uint32_t waves = std::min(items, resident);
+    const uint32_t grid = std::max(1u, (waves + kGemmWaves - 1) / kGemmWaves);
+    hipLaunchKernelGGL((k_gemm_fast<B, NB, MFMA>), dim3(grid), dim3(64 * kGemmWaves), lds, a.s,
+                       reinterpret_cast<const uint4 *>(t.words), t.codebook, t.U, a.X,
+                       static_cast<uint32_t>(a.ldx), a.batch, a.Y, static_cast<uint32_t>(a.ldy), M,
+                       static_cast<uint32_t>(P), ksteps, splits, items, atomic);
+    return true;
+}
+
+template <int B>
+struct GemmRun {
+    static bool run(GemmArgs &a) {
+        using G = Geo<B>;
+        const cbk_tensor &t = a.t;
+        if (t.cols == 0 || t.cols % G::F != 0) return false;
+        const uint64_t P = t.cols / G::F;
+        if (t.rows * P * G::C >= (uint64_t(1) << 32)) return false;
+        const uint32_t lds = round16(G::NE * 2) + kGemmWaves * 16u * (4 * G::C + 1) * 16u;
+        if (lds > kLdsLimit) return false;
+        bool ok;
+        switch (a.batch) {
+            case 1: ok = gemm_launch<B, 1, false>(a, lds); break;
+            case 2: ok = gemm_launch<B, 2, false>(a, lds); break;
+            case 3: ok = gemm_launch<B, 3, false>(a, lds); break;
+            case 4: ok = gemm_launch<B, 4, false>(a, lds); break;
+            case 5: ok = gemm_launch<B, 5, false>(a, lds); break;
+            case 6: ok = gemm_launch<B, 6, false>(a, lds); break;
+            case 7: ok = gemm_launch<B, 7, false>(a, lds); break;
+            case 8: ok = gemm_launch<B, 8, false>(a, lds); break;
+            default: ok = gemm_launch<B, 16, true>(a, lds); break;
+        }
+        if (ok) a.st = launched();
+        return ok;
+    }
+};
+
+}  // namespace
+
+cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s) {
+    const uint64_t n = t.rows * t.cols;
+    if (t.b > 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+        DecodeArgs a{t, out, s, CBK_OK};
+        if (dispatch_b<DecodeRun>(static_cast<int>(t.b), a, AllB{})) return a.st;
+    }
+    const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>((n + 255) / 256, 65536));
+    hipLaunchKernelGGL(k_decode_generic, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook, t.U,
+                       out, n);
+    return launched();
+}
+
+cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
+                       float *Y, uint64_t ldy, hipStream_t s) {
+    const uint32_t M = static_cast<uint32_t>(t.rows), K = static_cast<uint32_t>(t.cols);
+    if (t.b > 0 && K > 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && ldx % 8 == 0) {
+        GemmArgs a{t, X, ldx, batch, Y, ldy, s, CBK_OK};
+        if (dispatch_b<GemmRun>(static_cast<int>(t.b), a, AllB{})) return a.st;
+    }
+    const uint32_t grid = std::max(1u, std::min<uint32_t>((M + 3) / 4, 4096));
+    if (batch <= 8)
+        hipLaunchKernelGGL(k_gemm_generic<8>, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook,
+                           t.U, X, ldx, batch, Y, ldy, M, K);
+    else
+        hipLaunchKernelGGL(k_gemm_generic<16>, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook,
+                           t.U, X, ldx, batch, Y, ldy, M, K);
+    return launched();
+}
+
+cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s) {
+    const uint32_t M = static_cast<uint32_t>(t.rows), K = static_cast<uint32_t>(t.cols);
+    if (t.b > 0 && K > 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        GemvArgs a{t, x, y, s, CBK_OK};
+        if (dispatch_b<GemvRun>(static_cast<int>(t.b), a, AllB{})) return a.st;
+    }
+    const uint32_t grid = std::max(1u, std::min<uint32_t>((M + 3) / 4, 4096));
+    hipLaunchKernelGGL(k_gemm_generic<1>, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook,
+                       t.U, x, uint64_t(0), 1u, y, uint64_t(0), M, K);
+    return launched();
+}
+
+}  // namespace cbk

@@ -1,0 +1,126 @@
+/*
+ * cbk.h -- C ABI of libcbk: lossless codebook compression of BF16 weight tensors, decoded on
+ * an MI355X (gfx950) GPU standalone or fused into the decode-step GEMV / skinny GEMM.
+ *
+ * The operation (codebook lossless compression overview, section "How it works"; and the
+ * Codebook-Quantization digest, "Key points" and competitor table): a weight tensor is stored
+ * as a dictionary of its distinct values plus, for every weight, the index of its value in that
+ * dictionary, the indices bit-packed at a fixed width of about 12-13 bits; at inference the
+ * original values are substituted back exactly.  The format fixed here:
+ *
+ *   codebook  U distinct 16-bit patterns of the tensor, strictly ascending as unsigned
+ *             integers (+0 and -0 differ; every NaN payload is its own entry), 0 <= U <= 65536;
+ *   b         the smallest width with 2^b >= U (0 when U <= 1);
+ *   words     index i occupies bits [i*b, i*b + b) of a little-endian uint32 stream, least
+ *             significant bit first; bits at positions >= n*b are zero.  Buffers handed to the
+ *             GPU calls hold cbk_words_for(n, b) words (the stream rounded up to 16 bytes).
+ *
+ * Tensors are row-major [rows][cols] (rows = output features, cols = input features) and the
+ * stream runs through them in that order with no per-row padding.
+ *
+ * Conventions for every call:
+ *  - Every call returns a cbk_status; nothing throws across the ABI.
+ *  - Arguments are validated on the host before any HIP call; on error nothing is enqueued.
+ *  - GPU calls take device pointers (in the arguments and inside cbk_tensor, which itself lives
+ *    in host memory), enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ *    return without waiting.  Buffers must stay alive until that work completes.
+ *  - The caller owns every buffer.  The library allocates no memory and keeps no per-call state,
+ *    so calls are safe from several host threads and streams at once.
+ *  - Outputs must not alias inputs.
+ *  - An index >= U in a (corrupt) stream never causes an out-of-bounds access; the weight it
+ *    names reads as 0x7FC0 (a quiet NaN).
+ */
+#ifndef CBK_H
+#define CBK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CBK_OK = 0,
+    CBK_E_INVALID = 1,      /* null pointer, bad size, U/b mismatch, batch out of range      */
+    CBK_E_CAPACITY = 2,     /* cbk_encode: output word buffer too small (see words_needed)  */
+    CBK_E_ALIGN = 3,        /* a device pointer or leading dimension breaks an alignment rule */
+    CBK_E_UNSUPPORTED = 4,  /* shape beyond what the kernels accept (see each call)          */
+    CBK_E_HIP = 5           /* the HIP runtime reported an error at launch                   */
+} cbk_status;
+
+/* A compressed tensor as the GPU calls see it.  Host struct, device pointers. */
+typedef struct {
+    uint64_t rows;             /* output features; rows * cols must not overflow              */
+    uint64_t cols;             /* input features                                              */
+    uint32_t U;                /* codebook entries, 0..65536 (0 only when rows * cols == 0)   */
+    uint32_t b;                /* index width; must equal cbk_bits_for(U)                     */
+    const uint16_t *codebook;  /* device, U entries (may be NULL when U == 0)                 */
+    const uint32_t *words;     /* device, cbk_words_for(rows*cols, b) words, 16-byte aligned
+                                  (may be NULL when b == 0)                                   */
+} cbk_tensor;
+
+/* Smallest b with 2^b >= U; 0 for U <= 1. */
+uint32_t cbk_bits_for(uint32_t U);
+
+/* Words a GPU call reads for n fields of b bits: ceil(n*b/32) rounded up to a multiple of 4. */
+uint64_t cbk_words_for(uint64_t n, uint32_t b);
+
+/* Accounting size of a compressed tensor in bytes: 2*U + ceil(n*b/8) (the padding of the word
+ * buffer is not counted).  This is the size the compression ratio and GB/s figures use. */
+uint64_t cbk_compressed_bytes(uint64_t n, uint32_t U);
+
+/* Static, NUL-terminated description of a status code. */
+const char *cbk_status_str(int status);
+
+/*
+ * cbk_encode -- host, synchronous, re-entrant.  Compresses n 16-bit patterns w[0..n).
+ *   codebook   out, capacity 65536 entries (host); receives the U sorted distinct patterns.
+ *   U, b       out (host).
+ *   words      out (host), capacity words_cap words; receives cbk_words_for(n, b) words, the
+ *              padding words zero.  May be NULL with words_cap == 0 to query the size.
+ *   words_needed  out (host, may be NULL): cbk_words_for(n, b).
+ * Returns CBK_E_CAPACITY (after filling codebook, U, b and words_needed) when words_cap is too
+ * small, CBK_E_INVALID for a NULL w with n > 0 or a NULL codebook/U/b.
+ */
+cbk_status cbk_encode(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_t *U, uint32_t *b,
+                      uint32_t *words, uint64_t words_cap, uint64_t *words_needed);
+
+/*
+ * Kernel choice (all calls): a width b >= 1 whose rows hold a whole number of lane units
+ * (cols % (128 >> ctz(b)) == 0) takes the fast kernels, which stage the codebook (and x) in LDS;
+ * b == 0, ragged rows, misaligned operands and shapes beyond the LDS budget take generic kernels
+ * that give the same results.
+ */
+
+/*
+ * cbk_decode_bf16 -- GPU.  Standalone decode: out[i] = codebook[index i] for i < rows*cols,
+ * the exact original bit patterns (no float conversion anywhere).
+ *   out   device, rows*cols uint16, 2-byte aligned.
+ */
+cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream);
+
+/*
+ * cbk_gemv -- GPU.  Fused decode + GEMV at batch 1: y[r] = sum_k W[r][k] * x[k], products and
+ * sums in fp32 (the summation order is unspecified; each BF16 x BF16 product is exact in fp32).
+ *   x   device, cols BF16 patterns, 2-byte aligned (16-byte aligned for the fast kernels).
+ *   y   device, rows fp32, 4-byte aligned.  Fully overwritten (zeros when cols == 0).
+ */
+cbk_status cbk_gemv(const cbk_tensor *t, const uint16_t *x, float *y, void *stream);
+
+/*
+ * cbk_gemm_small -- GPU.  Fused decode + skinny GEMM: Y[j][r] = sum_k W[r][k] * X[j][k] for
+ * j < batch, fp32 products and sums.
+ *   X     device, [batch][ldx] BF16, 2-byte aligned, ldx >= cols.  The fast kernels need X
+ *         16-byte aligned and ldx % 8 == 0; other layouts take the generic kernel.
+ *   batch 1..16.  Batches up to 8 run on the vector ALUs; 9..16 run on the matrix cores.
+ *   Y     device, [batch][ldy] fp32, 4-byte aligned; ldy >= rows.  Y[j][0..rows) overwritten.
+ */
+cbk_status cbk_gemm_small(const cbk_tensor *t, const uint16_t *X, uint64_t ldx, uint32_t batch,
+                          float *Y, uint64_t ldy, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBK_H */

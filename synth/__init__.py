@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16", "bf16_to_f32", "gaussian_bf16", "student_t_bf16", "activation_bf16",
-    "activations_bf16", "from_alphabet", "with_distinct_count", "WORKLOADS", "Workload",
+    "activations_bf16", "from_alphabet", "with_distinct_count", "finite_exponents", "WORKLOADS", "Workload",
     "workload_tensor", "workload_x",
 ]
 
@@ -74,29 +74,38 @@ def from_alphabet(n: int, alphabet, seed) -> np.ndarray:
     return alphabet[rng.integers(0, len(alphabet), size=n)]
 
 
-def with_distinct_count(n: int, distinct: int, seed, finite_bf16: bool = False) -> np.ndarray:
+def with_distinct_count(n: int, distinct: int, seed, exponents=None) -> np.ndarray:
     """n patterns holding exactly ``distinct`` different 16-bit values (needs n >= distinct).
 
-    The distinct values are a random subset of all 65,536 patterns (or of the finite,
-    non-subnormal-free BF16 patterns of magnitude in [2^-8, 2^8) when ``finite_bf16``), every one
-    appears at least once, and the order is shuffled.
+    The distinct values are a random subset of all 65,536 patterns, or, with
+    ``exponents=(lo, hi)``, of the finite normal BF16 patterns whose biased exponent lies in
+    [lo, hi) (2 * (hi - lo) * 128 candidates, both signs).  Every value appears at least once and
+    the order is shuffled.
     """
     if distinct > n or distinct > 65536:
         raise ValueError("need n >= distinct and distinct <= 65536")
     rng = np.random.default_rng(seed)
-    if finite_bf16:
-        # sign x exponent in [119, 135) x mantissa: 2 * 16 * 128 = 4096 candidates
-        exps = np.arange(127 - 8, 127 + 8, dtype=np.uint32)
+    if exponents is not None:
+        lo, hi = exponents
+        if not 1 <= lo < hi <= 255:
+            raise ValueError("exponents must lie in [1, 255)")
+        exps = np.arange(lo, hi, dtype=np.uint32)
         mags = (exps[:, None] << 7 | np.arange(128, dtype=np.uint32)[None, :]).ravel()
         pool = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
         if distinct > len(pool):
-            raise ValueError("finite_bf16 pool holds 4096 patterns")
+            raise ValueError(f"the exponent range holds only {len(pool)} patterns")
     else:
         pool = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     values = rng.choice(pool, size=distinct, replace=False)
     picks = np.concatenate([np.arange(distinct), rng.integers(0, distinct, size=n - distinct)])
     rng.shuffle(picks)
     return values[picks].astype(np.uint16)
+
+
+def finite_exponents(distinct: int):
+    """An exponent range around 1.0 wide enough for ``distinct`` finite normal BF16 values."""
+    half = max(8, -(-distinct // 512))  # 256 patterns per exponent (two signs x 128 mantissas)
+    return (127 - half, 127 + half)
 
 
 class Workload:

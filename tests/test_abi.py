@@ -1,0 +1,143 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, its host encoder is
+byte-identical to the oracle's encoding, and argument validation rejects bad calls before any
+HIP call is made (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def cbk():
+    import fly_decode_amd
+    if not os.path.exists(fly_decode_amd.library_path()):
+        from fly_decode_amd import build
+        build.build()
+    fly_decode_amd.load_library()
+    return fly_decode_amd
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "cbk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cbk_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemm_small", "cbk_bits_for",
+              "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(cbk):
+    lib = ctypes.CDLL(cbk.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_library_does_not_link_the_oracle(cbk):
+    data = open(cbk.library_path(), "rb").read()
+    assert b"oracle_" not in data
+
+
+def test_size_helpers_match_oracle(cbk, oracle_mod):
+    for U in [0, 1, 2, 3, 4, 5, 255, 256, 257, 4673, 8192, 8193, 65535, 65536]:
+        assert cbk.bits_for(U) == oracle_mod.bits_for(U)
+    for n in [0, 1, 7, 31, 32, 33, 1000, 1 << 20]:
+        for b in range(17):
+            w = oracle_mod.stream_words(n, b)
+            assert cbk.words_for(n, b) == (w + 3) // 4 * 4
+    assert cbk.compressed_bytes(5, 4) == 10 and cbk.compressed_bytes(12, 6) == 17
+    assert cbk.compressed_bytes(7, 1) == 2 and cbk.compressed_bytes(0, 0) == 0
+
+
+def _check_encode(cbk, oracle_mod, w):
+    c = cbk.encode(w.reshape(1, -1) if w.ndim == 1 else w)
+    e = oracle_mod.encode(w)
+    assert c.U == e.U and c.b == e.b
+    assert np.array_equal(c.codebook, e.codebook)
+    assert np.array_equal(c.words[:e.words.size], e.words)
+    assert not c.words[e.words.size:].any()
+    assert c.words.size == cbk.words_for(w.size, e.b)
+    assert c.compressed_bytes == e.compressed_bytes
+
+
+@pytest.mark.parametrize("U", [1, 2, 3, 5, 8, 100, 257, 4097, 8193, 32769, 65536])
+def test_encoder_byte_parity_distinct_counts(cbk, oracle_mod, U):
+    _check_encode(cbk, oracle_mod, synth.with_distinct_count(max(U, 5003), U, seed=[21, U]))
+
+
+def test_encoder_empty_and_constant(cbk):
+    c = cbk.encode(np.zeros((0, 5), dtype=np.uint16))
+    assert (c.U, c.b, c.words.size, c.compressed_bytes) == (0, 0, 0, 0)
+    c = cbk.encode(np.full((3, 7), 0x3C00, dtype=np.uint16))
+    assert (c.U, c.b, c.words.size, c.compressed_bytes) == (1, 0, 0, 2)
+
+
+def test_encoder_byte_parity_cfg1(cbk, oracle_mod):
+    w = synth.workload_tensor(1, 0, synth.WORKLOADS[1][0][0])
+    _check_encode(cbk, oracle_mod, w)
+
+
+def test_encoder_multithreaded_path(cbk, oracle_mod):
+    # > 4M fields takes the threaded presence and pack passes
+    w = synth.student_t_bf16((1031, 4099), 4.0, 0.02, seed=[22])
+    _check_encode(cbk, oracle_mod, w)
+
+
+def test_encode_capacity_and_invalid(cbk):
+    lib = cbk.load_library()
+    w = np.array([1, 2, 3, 4, 5], dtype=np.uint16)
+    cb = np.zeros(65536, dtype=np.uint16)
+    U, b, need = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint64()
+    p16 = ctypes.POINTER(ctypes.c_uint16)
+    p32 = ctypes.POINTER(ctypes.c_uint32)
+    words = np.zeros(2, dtype=np.uint32)
+    st = lib.cbk_encode(w.ctypes.data_as(p16), 5, cb.ctypes.data_as(p16), ctypes.byref(U),
+                        ctypes.byref(b), words.ctypes.data_as(p32), 2, ctypes.byref(need))
+    assert st == 2 and need.value == 4 and U.value == 5 and b.value == 3
+    st = lib.cbk_encode(None, 5, cb.ctypes.data_as(p16), ctypes.byref(U), ctypes.byref(b), None, 0,
+                        None)
+    assert st == 1
+    st = lib.cbk_encode(w.ctypes.data_as(p16), 5, None, ctypes.byref(U), ctypes.byref(b), None, 0,
+                        None)
+    assert st == 1
+
+
+def _tensor(cbk, rows, cols, U, b, cb=0x1000, words=0x2000):
+    return cbk._Tensor(rows, cols, U, b, cb, words)
+
+
+def test_gpu_calls_validate_before_any_hip_call(cbk):
+    """Every invalid argument is rejected on the host (no device is present here)."""
+    lib = cbk.load_library()
+    T = lambda **kw: ctypes.byref(_tensor(cbk, **{**dict(rows=4, cols=8, U=5, b=3), **kw}))
+    X, Y = ctypes.c_void_p(0x4000), ctypes.c_void_p(0x8000)
+    assert lib.cbk_gemv(None, X, Y, None) == 1
+    assert lib.cbk_gemv(T(b=4), X, Y, None) == 1             # b != bits_for(U)
+    assert lib.cbk_gemv(T(U=70000, b=17), X, Y, None) == 1   # U > 65536
+    assert lib.cbk_gemv(T(U=0, b=0), X, Y, None) == 1        # empty codebook, non-empty tensor
+    assert lib.cbk_gemv(T(cb=0), X, Y, None) == 1            # null codebook
+    assert lib.cbk_gemv(T(words=0), X, Y, None) == 1         # null words with b > 0
+    assert lib.cbk_gemv(T(words=0x2004), X, Y, None) == 3    # words not 16-byte aligned
+    assert lib.cbk_gemv(T(), ctypes.c_void_p(0x4001), Y, None) == 3
+    assert lib.cbk_gemv(T(), X, ctypes.c_void_p(0x8002), None) == 3
+    assert lib.cbk_gemv(T(), None, Y, None) == 1
+    assert lib.cbk_gemv(T(rows=1 << 40, cols=1 << 40), X, Y, None) == 1  # rows*cols overflow
+    assert lib.cbk_decode_bf16(T(), None, None) == 1
+    assert lib.cbk_decode_bf16(T(), ctypes.c_void_p(0x4001), None) == 3
+    assert lib.cbk_gemm_small(T(), X, 8, 0, Y, 4, None) == 1      # batch 0
+    assert lib.cbk_gemm_small(T(), X, 8, 17, Y, 4, None) == 1     # batch 17
+    assert lib.cbk_gemm_small(T(), X, 4, 2, Y, 4, None) == 1      # ldx < cols
+    assert lib.cbk_gemm_small(T(), X, 8, 2, Y, 3, None) == 1      # ldy < rows
+    assert lib.cbk_gemm_small(T(), ctypes.c_void_p(0x4001), 8, 2, Y, 4, None) == 3
+    # zero-size tensors are accepted without work (no HIP call either)
+    assert lib.cbk_gemv(T(rows=0, cols=0, U=0, b=0, cb=0, words=0), None, None, None) == 0
+    assert lib.cbk_decode_bf16(T(rows=0, cols=9, U=0, b=0, cb=0, words=0), None, None) == 0

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bar: standalone decode bit-exact; fused GEMV / GEMM within |y - y_ref| <= 1e-3 * sum_k |W x| per
+element (y_ref and the bound from the oracle, float64); exact equality where the result is exact
+whatever the summation order (integer-valued data, one-hot x, constant tensors).
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import fly_decode_amd as cbk
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cbk.load_library()
+    return torch, cbk
+
+
+def _up(torch, a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(dtype)
+
+
+def _decode_check(env, w, oracle_mod=None):
+    torch, cbk = env
+    c = cbk.encode(w)
+    d = c.to("cuda")
+    out = cbk.decode_bf16(d)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape)
+    assert np.array_equal(got, w), f"decode mismatch U={c.U} b={c.b} shape={w.shape}"
+    return c, d
+
+
+def _gemv_check(env, oracle_mod, w, x, rows=None, exact=False):
+    torch, cbk = env
+    c = cbk.encode(w)
+    d = c.to("cuda")
+    y = cbk.gemv(d, _up(torch, x, torch.bfloat16))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    e = oracle_mod.encode(w)
+    ref, absb = oracle_mod.gemv(e, x, rows=rows)
+    got = y if rows is None else y[np.asarray(rows)]
+    if exact:
+        assert np.array_equal(got, ref)
+    else:
+        err = np.abs(got - ref)
+        assert np.all(err <= TOL * absb), f"max err/bound {np.max(err / np.maximum(absb, 1e-300))}"
+    return got, ref
+
+
+def _gemm_check(env, oracle_mod, w, X, rows=None, exact=False, ldx=None):
+    torch, cbk = env
+    c = cbk.encode(w)
+    d = c.to("cuda")
+    batch, K = X.shape
+    if ldx is None:
+        Xd = _up(torch, X, torch.bfloat16)
+    else:
+        buf = torch.zeros((batch, ldx), dtype=torch.bfloat16, device="cuda")
+        buf[:, :K] = _up(torch, X, torch.bfloat16)
+        Xd = buf[:, :K]
+    Y = cbk.gemm_small(d, Xd)
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy().astype(np.float64)
+    e = oracle_mod.encode(w)
+    ref, absb = oracle_mod.gemm(e, X, rows=rows)
+    got = Y if rows is None else Y[:, np.asarray(rows)]
+    if exact:
+        assert np.array_equal(got, ref)
+    else:
+        err = np.abs(got - ref)
+        assert np.all(err <= TOL * absb), f"max err/bound {np.max(err / np.maximum(absb, 1e-300))}"
+    return got
+
+
+# --------------------------------------------------------------------------------- decode
+UNIT_FIELDS = {b: 128 >> ((b & -b).bit_length() - 1) for b in range(1, 17)}
+
+
+@pytest.mark.parametrize("b", list(range(0, 17)))
+def test_decode_every_width(env, b):
+    """Every width b = 0..16, U at both ends of the width, ragged and unit-aligned lengths."""
+    for U in sorted({max(1, 2 ** (b - 1) + 1) if b else 1, 2 ** b}):
+        for rows, cols in [(37, 111), (3, 2 * 128 * 7 + 5), (64, 256)]:
+            n = rows * cols
+            if n < U:
+                rows = (U + cols - 1) // cols
+                n = rows * cols
+            w = synth.with_distinct_count(n, U, seed=[31, b, U, cols]).reshape(rows, cols)
+            c, _ = _decode_check(env, w)
+            assert c.U == U and c.b == b
+
+
+def test_decode_tail_and_misaligned_output(env):
+    torch, cbk = env
+    w = synth.with_distinct_count(12345, 6000, seed=[32]).reshape(1, -1)
+    c = cbk.encode(w)
+    d = c.to("cuda")
+    buf = torch.zeros(12345 + 8, dtype=torch.bfloat16, device="cuda")
+    out = buf[1:1 + 12345].view(1, -1)  # 2-byte aligned only: generic path
+    cbk.decode_bf16(d, out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), w)
+    assert int(buf[0].view(torch.int16)) == 0 and not buf[1 + 12345:].view(torch.int16).any()
+
+
+def test_decode_corrupt_index_is_memory_safe(env, oracle_mod):
+    torch, cbk = env
+    w = synth.with_distinct_count(4096, 5000 // 2, seed=[33]).reshape(32, 128)
+    c = cbk.encode(w)
+    assert c.b == 12 and c.U < 4096
+    words = c.words.copy()
+    bad_fields = [0, 77, 1000, 4095]
+    for f in bad_fields:  # force index 4095 >= U into these fields
+        for j in range(12):
+            p = f * 12 + j
+            words[p >> 5] |= np.uint32(1 << (p & 31))
+    bad = c.__class__(c.rows, c.cols, c.U, c.b, c.codebook, words).to("cuda")
+    out = cbk.decode_bf16(bad)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    e = oracle_mod.Encoded(c.codebook, c.U, c.b, words[:oracle_mod.stream_words(4096, 12)], 4096, (32, 128))
+    assert np.array_equal(got, oracle_mod.decode(e))
+    assert all(got[f] == 0x7FC0 for f in bad_fields)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_decode_workload_full_size(env, cfg):
+    w = synth.workload_tensor(cfg, 0, synth.WORKLOADS[cfg][0][0])
+    c, _ = _decode_check(env, w)
+    assert c.b in (12, 13)
+
+
+def test_decode_heavy_tailed_mlp_full_size(env):
+    for t in synth.WORKLOADS[3][0]:
+        if t.name in ("gate", "down"):
+            _decode_check(env, synth.workload_tensor(3, 0, t))
+
+
+# ----------------------------------------------------------------------------------- GEMV
+def _int_bf16(vals):
+    return synth.f32_to_bf16(np.asarray(vals, dtype=np.float32))
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16])
+def test_gemv_every_width(env, oracle_mod, b):
+    F = UNIT_FIELDS[b]
+    U = 2 ** b if b <= 12 else 2 ** (b - 1) + 3
+    for rows, cols in [(67, 3 * F), (5, 64 * F + F), (33, 2 * F + 1)]:
+        n = rows * cols
+        if n < U:
+            rows = (U + cols - 1) // cols
+        w = synth.with_distinct_count(rows * cols, U, seed=[41, b, cols],
+                                      exponents=synth.finite_exponents(U)).reshape(rows, cols)
+        x = synth.activation_bf16(cols, seed=[42, cols])
+        _gemv_check(env, oracle_mod, w, x)
+
+
+def test_gemv_integer_exact(env, oracle_mod):
+    rng = np.random.default_rng(43)
+    for rows, cols in [(129, 4096), (70, 1000), (1024, 1024)]:
+        Wi = rng.integers(-8, 8, size=(rows, cols))
+        xi = rng.integers(-4, 5, size=cols)
+        _gemv_check(env, oracle_mod, _int_bf16(Wi), _int_bf16(xi), exact=True)
+
+
+def test_gemv_one_hot_returns_column(env, oracle_mod):
+    w = synth.gaussian_bf16((300, 4096), 0.02, seed=[44])
+    for k in (0, 129, 4095):
+        x = np.zeros(4096, dtype=np.float32)
+        x[k] = 1.0
+        got, _ = _gemv_check(env, oracle_mod, w, _int_bf16(x), exact=True)
+        assert np.array_equal(got, synth.bf16_to_f32(w[:, k]).astype(np.float64))
+
+
+def test_gemv_constant_tensor(env, oracle_mod):
+    w = np.full((50, 640), 0x4040, dtype=np.uint16)
+    xi = np.random.default_rng(45).integers(-3, 4, size=640)
+    _gemv_check(env, oracle_mod, w, _int_bf16(xi), exact=True)
+
+
+def test_gemv_zero_cols(env):
+    torch, cbk = env
+    c = cbk.encode(np.zeros((8, 0), dtype=np.uint16), rows=8, cols=0).to("cuda")
+    y = torch.full((8,), 5.0, device="cuda")
+    x = torch.zeros(8, dtype=torch.bfloat16, device="cuda")[:0]
+    cbk.gemv(c, x, y=y)
+    torch.cuda.synchronize()
+    assert not y.any()
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_gemv_workload_full_size(env, oracle_mod, cfg):
+    t = synth.WORKLOADS[cfg][0][0]
+    w = synth.workload_tensor(cfg, 0, t)
+    x = synth.workload_x(cfg, t.cols)[0]
+    _gemv_check(env, oracle_mod, w, x)
+
+
+def test_gemv_mlp_full_size(env, oracle_mod):
+    for t in synth.WORKLOADS[3][0]:
+        if t.name in ("gate", "down"):
+            w = synth.workload_tensor(3, 0, t)
+            x = synth.workload_x(3, t.cols)[0]
+            rows = np.random.default_rng(46).choice(t.rows, 512, replace=False)
+            _gemv_check(env, oracle_mod, w, x, rows=rows)
+
+
+def test_gemv_70b_shapes_sampled(env, oracle_mod):
+    """70B-shaped tensors at full size (one of each shape), 128 sampled rows each."""
+    for t in synth.WORKLOADS[5][0]:
+        if t.name in ("q", "k", "gate", "down"):
+            w = synth.workload_tensor(5, 0, t)
+            x = synth.workload_x(5, t.cols)[0]
+            rows = np.random.default_rng(47).choice(t.rows, 128, replace=False)
+            _gemv_check(env, oracle_mod, w, x, rows=rows)
+
+
+# ----------------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("batch", [1, 2, 3, 5, 8, 9, 12, 16])
+def test_gemm_batches(env, oracle_mod, batch):
+    for b, U in [(13, 5000), (12, 3000), (8, 200), (16, 40000)]:
+        F = UNIT_FIELDS[b]
+        for rows, cols in [(50, 5 * F), (16, 16 * F), (23, 3 * F + 9)]:
+            n = rows * cols
+            if n < U:
+                rows = (U + cols - 1) // cols
+            w = synth.with_distinct_count(rows * cols, U, seed=[51, b, cols],
+                                          exponents=synth.finite_exponents(U)).reshape(rows, cols)
+            X = synth.activations_bf16(batch, cols, 52)
+            _gemm_check(env, oracle_mod, w, X)
+
+
+def test_gemm_integer_exact_and_column_equals_gemv(env, oracle_mod):
+    torch, cbk = env
+    rng = np.random.default_rng(53)
+    for batch in (4, 8, 16):
+        Wi = rng.integers(-8, 8, size=(200, 2048))
+        Xi = rng.integers(-4, 5, size=(batch, 2048))
+        w, X = _int_bf16(Wi), _int_bf16(Xi)
+        Y = _gemm_check(env, oracle_mod, w, X, exact=True)
+        d = cbk.encode(w).to("cuda")
+        for j in range(batch):
+            y = cbk.gemv(d, _up(torch, X[j], torch.bfloat16)).cpu().numpy()
+            assert np.array_equal(y.astype(np.float64), Y[j])
+
+
+def test_gemm_padded_leading_dimension(env, oracle_mod):
+    w = synth.gaussian_bf16((96, 1024), 0.02, seed=[54])
+    X = synth.activations_bf16(10, 1024, 54)
+    _gemm_check(env, oracle_mod, w, X, ldx=1024 + 24)
+    _gemm_check(env, oracle_mod, w, X[:4], ldx=1024 + 3)  # ldx % 8 != 0: generic kernel
+
+
+def test_gemv_misaligned_x_takes_generic_path(env, oracle_mod):
+    torch, cbk = env
+    w = synth.gaussian_bf16((64, 512), 0.02, seed=[59])
+    x = synth.activation_bf16(512, seed=[60])
+    d = cbk.encode(w).to("cuda")
+    buf = torch.zeros(520, dtype=torch.bfloat16, device="cuda")
+    buf[1:513] = _up(torch, x, torch.bfloat16)
+    y = cbk.gemv(d, buf[1:513]).cpu().numpy()
+    ref, absb = oracle_mod.gemv(oracle_mod.encode(w), x)
+    assert np.all(np.abs(y - ref) <= TOL * absb)
+
+
+def test_gemm_mlp_batch8_sampled(env, oracle_mod):
+    for t in synth.WORKLOADS[3][0]:
+        if t.name in ("up", "down"):
+            w = synth.workload_tensor(3, 0, t)
+            X = synth.workload_x(3, t.cols, batch=8)
+            rows = np.random.default_rng(55).choice(t.rows, 96, replace=False)
+            _gemm_check(env, oracle_mod, w, X, rows=rows)
+
+
+def test_gemm_70b_batch16_sampled(env, oracle_mod):
+    for t in synth.WORKLOADS[5][0]:
+        if t.name in ("v", "o", "up", "down"):
+            w = synth.workload_tensor(5, 0, t)
+            X = synth.workload_x(5, t.cols, batch=16)
+            rows = np.random.default_rng(56).choice(t.rows, 32, replace=False)
+            _gemm_check(env, oracle_mod, w, X, rows=rows)
+
+
+def test_repeated_launches_are_identical(env):
+    torch, cbk = env
+    w = synth.gaussian_bf16((4096, 4096), 0.02, seed=[57])
+    d = cbk.encode(w).to("cuda")
+    x = _up(torch, synth.activation_bf16(4096, seed=[58]), torch.bfloat16)
+    y0 = cbk.gemv(d, x).clone()
+    for _ in range(5):
+        assert torch.equal(cbk.gemv(d, x), y0)
