@@ -6,26 +6,30 @@
 // digest ("Key points": bit-packed indices of the unique weights).  Fields are b bits wide,
 // packed LSB first into little-endian uint32 words, row-major with no row padding.
 //
-// Layout of the work (fast paths, templated on b so every shift is a compile-time constant):
-//  * A "unit" is C = odd_part(b) 16-byte chunks = F = 128 / 2^v2(b) whole fields.  Units start
-//    on 16-byte boundaries and no field crosses a unit boundary.
-//  * A wave loads 64 units with C fully coalesced 128-bit loads per lane (lane l takes chunk
-//    j*64 + l), writes them to a wave-private LDS stage, and reads back its own unit as C
-//    128-bit LDS reads (odd stride C chunks: no bank conflicts).  For C == 1 the lane already
-//    holds its unit and the stage is skipped.
-//  * Fields are unpacked in registers (one shift/and, or alignbit + and when a field straddles
-//    two words) and gathered from the codebook staged in LDS, padded to 2^b entries with 0x7FC0
-//    so a corrupt index can never leave the table.
-//  * GEMV (batch 1): units run along rows; x sits in LDS, padded 16 bytes per unit so the
-//    lanes' 128-bit reads are conflict-free; BF16 pairs are multiplied with v_dot2c_f32_bf16
-//    into fp32; a segmented wave reduction (rows are contiguous runs of lanes) produces y.
-//  * Skinny GEMM: a wave owns a 16-row tile and walks K in steps of 4 units per row; lane
-//    (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded tile to
-//    v_mfma_f32_16x16x32_bf16; batches up to 8 use v_dot2c on the vector ALUs.  When K is split
-//    across waves the partial sums are added into a zero-filled Y with fp32 atomics.
+// Decode and GEMV (templated on b so every shift and mask is a compile-time constant):
+//  * A lane "unit" is 64 consecutive fields = 2b dwords; a wave step covers 64 units.  The wave
+//    loads the step's bytes with fully coalesced 128-bit loads (lane l takes chunk j*64 + l),
+//    writes them to a wave-private LDS stage and reads back its own unit: 64-bit LDS reads at an
+//    odd qword stride (odd b) or 128-bit reads at an odd chunk stride (even b; b % 4 == 0 pads
+//    one chunk per unit), so the transposition has no bank conflicts.  The next step's loads
+//    are issued before the current step is decoded.
+//  * Fields are unpacked in registers (shift/and, or alignbit + and across a word boundary)
+//    and gathered from the codebook held in static LDS, padded to 2^b entries with 0x7FC0 so a
+//    corrupt index cannot leave the table.  Gathers are issued one 8-field group ahead of use.
+//  * GEMV: units run along rows; x sits in LDS, 16 bytes of padding per unit so the lanes'
+//    128-bit reads are conflict-free; BF16 pairs are multiplied with v_dot2c_f32_bf16 into fp32;
+//    a segmented wave reduction (a row is a contiguous run of lanes) produces y.
+//  * Workgroups hold as many waves as the LDS budget allows (up to 16), sharing one codebook and
+//    one copy of x; the grid is persistent and rows are split evenly over its waves.
+//
+// Skinny GEMM: a wave owns a 16-row tile and walks K in steps of 4 units (128 fields) per row;
+// lane (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded tile to
+// v_mfma_f32_16x16x32_bf16; batches up to 8 use v_dot2c on the vector ALUs.  When K is split
+// across waves the partial sums are added into a zero-filled Y with fp32 atomics.
 //
 // Generic kernels (any b and shape, runtime field extraction straight from global memory) cover
-// b == 0, rows whose length is not a whole number of units, and shapes beyond the LDS budget.
+// b == 0, rows whose length is not a multiple of 64, misaligned operands and shapes beyond the
+// LDS budget.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,14 +43,15 @@ namespace cbk {
 namespace {
 
 constexpr uint16_t kCorrupt = 0x7FC0;
-constexpr int kWaves = 4;                 // waves per workgroup, decode and GEMV
-constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxWaves = 16;             // waves per workgroup, decode and GEMV
 constexpr int kGemmWaves = 4;             // waves per workgroup, skinny GEMM
 constexpr uint32_t kLdsLimit = 160 * 1024;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
@@ -57,12 +62,19 @@ __device__ __forceinline__ float bf16_value(uint16_t h) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
 }
 
+constexpr uint32_t round16(uint32_t v) { return (v + 15u) & ~15u; }
+
+// Geometry of the 64-field lane unit for width B (decode and GEMV).
 template <int B>
-struct Geo {
-    static constexpr int C = B >> __builtin_ctz(B);   // 16-byte chunks per unit
-    static constexpr int F = 128 >> __builtin_ctz(B); // fields per unit
-    static constexpr int D = 4 * C;                   // dwords per unit
-    static constexpr uint32_t NE = 1u << B;           // codebook entries in LDS
+struct U64 {
+    static constexpr int UD = 2 * B;                            // dwords per unit
+    static constexpr int G = (UD % 4 == 0) ? 4 : 2;             // LDS read width (dwords)
+    static constexpr int NG = UD / G;                           // reads per unit
+    static constexpr bool PAD = (G == 4) && (NG % 2 == 0);      // pad to an odd chunk stride
+    static constexpr int SG = PAD ? NG + 1 : NG;                // unit stride in reads
+    static constexpr int LPL = (16 * UD + 1 + 63) / 64;         // 16-byte loads per lane per step
+    static constexpr int STAGE_CHUNKS = 64 * LPL + (PAD ? 64 * LPL / NG + 1 : 0);
+    static constexpr uint32_t NE = 1u << B;                     // codebook entries in LDS
     static constexpr uint32_t mask = (1u << B) - 1u;
 };
 
@@ -70,8 +82,8 @@ struct Geo {
 template <int B>
 __device__ __forceinline__ uint32_t unit_field(const uint32_t *d, int f) {
     const int bit = f * B, w = bit >> 5, s = bit & 31;
-    if (s + B <= 32) return (d[w] >> s) & Geo<B>::mask;
-    return __builtin_amdgcn_alignbit(d[w + 1], d[w], s) & Geo<B>::mask;
+    if (s + B <= 32) return (d[w] >> s) & U64<B>::mask;
+    return __builtin_amdgcn_alignbit(d[w + 1], d[w], s) & U64<B>::mask;
 }
 
 // Field i of a stream, runtime width (generic kernels).
@@ -97,141 +109,143 @@ __device__ __forceinline__ void divmod(uint32_t n, uint32_t P, uint32_t m, uint3
 template <int B>
 __device__ __forceinline__ void stage_codebook(uint16_t *cbl, const uint16_t *__restrict__ cb,
                                                uint32_t U, int tid, int nthreads) {
-    for (uint32_t i = tid; i < Geo<B>::NE; i += nthreads) cbl[i] = i < U ? cb[i] : kCorrupt;
+    for (uint32_t i = tid; i < U64<B>::NE; i += nthreads) cbl[i] = i < U ? cb[i] : kCorrupt;
 }
 
-constexpr uint32_t round16(uint32_t v) { return (v + 15u) & ~15u; }
+// Step loads: the chunks covering units [us, us + 64) start at chunk (us * UD) / 4; an odd-b
+// step may start half-way into a chunk (the stage read then skips one qword).  Addresses past
+// the stream are clamped to its last chunk: those lanes feed only inactive units.
+template <int B>
+__device__ __forceinline__ void load_step(u32x4 (&v)[U64<B>::LPL], const u32x4 *__restrict__ w4,
+                                          uint32_t us, uint32_t nchunks, int lane) {
+    const uint32_t c0 = static_cast<uint32_t>((static_cast<uint64_t>(us) * U64<B>::UD) >> 2);
+#pragma unroll
+    for (int j = 0; j < U64<B>::LPL; ++j) v[j] = w4[min(c0 + j * 64 + lane, nchunks - 1)];
+}
+
+// Write a step to the wave's stage and read back this lane's unit (UD dwords).
+template <int B>
+__device__ __forceinline__ void transpose_step(uint32_t (&d)[U64<B>::UD], const u32x4 (&v)[U64<B>::LPL],
+                                               u32x4 *stage, uint32_t us, int lane) {
+    using G = U64<B>;
+    // The stage is written as 16-byte vectors and, for odd b, read as 8-byte vectors; the
+    // compiler barriers keep type-based alias analysis from moving the reads above the writes
+    // (or the next step's writes above these reads).  LDS executes one wave's accesses in order.
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < G::LPL; ++j) {
+        const uint32_t q = j * 64 + lane;
+        stage[G::PAD ? q + q / G::NG : q] = v[j];
+    }
+    asm volatile("" ::: "memory");
+    if constexpr (G::G == 4) {
+#pragma unroll
+        for (int j = 0; j < G::NG; ++j) {
+            const u32x4 t = stage[lane * G::SG + j];
+            d[4 * j] = t.x; d[4 * j + 1] = t.y; d[4 * j + 2] = t.z; d[4 * j + 3] = t.w;
+        }
+    } else {
+        // odd b: the step starts (us * UD) % 4 dwords into its first chunk (0 or 2)
+        const u32x2 *st2 = reinterpret_cast<const u32x2 *>(stage) + ((us * G::UD) & 2u) / 2;
+#pragma unroll
+        for (int j = 0; j < G::NG; ++j) {
+            const u32x2 t = st2[lane * G::SG + j];
+            d[2 * j] = t.x; d[2 * j + 1] = t.y;
+        }
+    }
+    asm volatile("" ::: "memory");
+}
 
 // ------------------------------------------------------------------------------ fast decode
-// Flat: unit u decodes weights [u*F, u*F + F).  Waves own contiguous unit ranges.
+// Flat: unit u decodes weights [64u, 64u + 64).  Waves own contiguous ranges of whole steps.
 template <int B>
-__global__ __launch_bounds__(kThreads) void k_decode_fast(const uint4 *__restrict__ w4,
-                                                          uint32_t nchunks,
-                                                          const uint16_t *__restrict__ cb,
-                                                          uint32_t U, uint16_t *__restrict__ out,
-                                                          uint64_t n, uint32_t T) {
-    using G = Geo<B>;
-    constexpr int C = G::C, F = G::F;
+__global__ __launch_bounds__(64 * kMaxWaves) void k_decode_fast(const u32x4 *__restrict__ w4,
+                                                                uint32_t nchunks,
+                                                                const uint16_t *__restrict__ cb,
+                                                                uint32_t U, uint16_t *__restrict__ out,
+                                                                uint64_t n, uint32_t T) {
+    using G = U64<B>;
+    __shared__ uint16_t cbl[G::NE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t *cbl = reinterpret_cast<uint16_t *>(smem);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint4 *stage = reinterpret_cast<uint4 *>(smem + round16(G::NE * 2)) + wave * 64 * C;
-    stage_codebook<B>(cbl, cb, U, tid, kThreads);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+    u32x4 *stage = reinterpret_cast<u32x4 *>(smem) + wave * G::STAGE_CHUNKS;
+
+    const uint32_t NW = gridDim.x * waves, gw = blockIdx.x * waves + wave;
+    const uint32_t steps = (T + 63) / 64;
+    const uint32_t s0 = static_cast<uint64_t>(steps) * gw / NW;
+    const uint32_t s1 = static_cast<uint64_t>(steps) * (gw + 1) / NW;
+    u32x4 nxt[G::LPL];
+    if (s0 < s1) load_step<B>(nxt, w4, s0 * 64, nchunks, lane);
+    stage_codebook<B>(cbl, cb, U, tid, blockDim.x);
     __syncthreads();
+    if (s0 >= s1) return;
 
-    const uint32_t NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
-    const uint32_t u0 = static_cast<uint64_t>(T) * gw / NW;
-    const uint32_t u1 = static_cast<uint64_t>(T) * (gw + 1) / NW;
-    if (u0 >= u1) return;
-    const uint32_t ch_lim = min(u1 * C, nchunks);
-
-    uint4 nxt[C];
-    auto load = [&](uint32_t us) {
+    for (uint32_t st = s0; st < s1; ++st) {
+        const uint32_t us = st * 64;
+        uint32_t d[G::UD];
+        transpose_step<B>(d, nxt, stage, us, lane);
+        if (st + 1 < s1) load_step<B>(nxt, w4, us + 64, nchunks, lane);
+        const uint32_t gu = us + lane;
+        if (gu >= T) continue;
+        const uint64_t base = static_cast<uint64_t>(gu) * 64;
+        uint32_t wv[2][8];
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-            const uint32_t ch = us * C + j * 64 + lane;
-            nxt[j] = ch < ch_lim ? w4[ch] : make_uint4(0, 0, 0, 0);
-        }
-    };
-    load(u0);
-    for (uint32_t us = u0; us < u1; us += 64) {
-        uint32_t d[G::D];
-        if constexpr (C == 1) {
-            d[0] = nxt[0].x; d[1] = nxt[0].y; d[2] = nxt[0].z; d[3] = nxt[0].w;
+        for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+        if (base + 64 <= n) {
+            u32x4 *o = reinterpret_cast<u32x4 *>(out + base);
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                if (g + 1 < 8) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
+                }
+                const uint32_t *w = wv[g & 1];
+                o[g] = (u32x4){w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
+            }
         } else {
 #pragma unroll
-            for (int j = 0; j < C; ++j) stage[j * 64 + lane] = nxt[j];
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const uint4 v = stage[lane * C + j];
-                d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
-            }
-        }
-        if (us + 64 < u1) load(us + 64);
-
-        const uint32_t gu = us + lane;
-        if (gu < u1) {
-            const uint64_t base = static_cast<uint64_t>(gu) * F;
-            if (base + F <= n) {
-                uint4 *o = reinterpret_cast<uint4 *>(out + base);
-#pragma unroll
-                for (int t = 0; t < F / 8; ++t) {
-                    uint32_t p[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t i0 = unit_field<B>(d, 8 * t + 2 * q);
-                        const uint32_t i1 = unit_field<B>(d, 8 * t + 2 * q + 1);
-                        p[q] = static_cast<uint32_t>(cbl[i0]) | (static_cast<uint32_t>(cbl[i1]) << 16);
-                    }
-                    o[t] = make_uint4(p[0], p[1], p[2], p[3]);
-                }
-            } else {
-#pragma unroll
-                for (int f = 0; f < F; ++f)
-                    if (base + f < n) out[base + f] = cbl[unit_field<B>(d, f)];
-            }
+            for (int f = 0; f < 64; ++f)
+                if (base + f < n) out[base + f] = cbl[unit_field<B>(d, f)];
         }
     }
 }
 
 // -------------------------------------------------------------------------------- fast GEMV
 template <int B>
-__global__ __launch_bounds__(kThreads) void k_gemv_fast(const uint4 *__restrict__ w4,
-                                                        const uint16_t *__restrict__ cb, uint32_t U,
-                                                        const uint16_t *__restrict__ x,
-                                                        float *__restrict__ y, uint32_t M,
-                                                        uint32_t P, uint32_t Pm) {
-    using G = Geo<B>;
-    constexpr int C = G::C, F = G::F;
-    constexpr uint32_t XU = 2 * F + 16;  // LDS bytes per unit of x (16 bytes of padding)
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_fast(const u32x4 *__restrict__ w4,
+                                                              uint32_t nchunks,
+                                                              const uint16_t *__restrict__ cb,
+                                                              uint32_t U, const uint16_t *__restrict__ x,
+                                                              float *__restrict__ y, uint32_t M,
+                                                              uint32_t P, uint32_t Pm) {
+    using G = U64<B>;
+    constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
+    __shared__ uint16_t cbl[G::NE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t *cbl = reinterpret_cast<uint16_t *>(smem);
-    unsigned char *xl = smem + round16(G::NE * 2);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint4 *stage = reinterpret_cast<uint4 *>(xl + P * XU) + wave * 64 * C;
+    unsigned char *xl = smem;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+    u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
 
-    stage_codebook<B>(cbl, cb, U, tid, kThreads);
-    {
-        const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
-        const uint32_t xchunks = P * (F / 8);
-        for (uint32_t q = tid; q < xchunks; q += kThreads) {
-            const uint32_t unit = q / (F / 8), off = q % (F / 8);
-            *reinterpret_cast<uint4 *>(xl + unit * XU + off * 16) = x4[q];
-        }
-    }
-    __syncthreads();
-
-    const uint32_t NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
+    const uint32_t NW = gridDim.x * waves, gw = blockIdx.x * waves + wave;
     const uint32_t r0 = static_cast<uint64_t>(M) * gw / NW;
     const uint32_t r1 = static_cast<uint64_t>(M) * (gw + 1) / NW;
     const uint32_t u0 = r0 * P, u1 = r1 * P;
+    u32x4 nxt[G::LPL];
+    if (u0 < u1) load_step<B>(nxt, w4, u0, nchunks, lane);  // in flight during the staging below
+    stage_codebook<B>(cbl, cb, U, tid, blockDim.x);
+    {
+        const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
+        for (uint32_t q = tid; q < P * 8; q += blockDim.x)
+            *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = x4[q];
+    }
+    __syncthreads();
     if (u0 >= u1) return;
-    const uint32_t ch_lim = u1 * C;
 
-    uint4 nxt[C];
-    auto load = [&](uint32_t us) {
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-            const uint32_t ch = us * C + j * 64 + lane;
-            nxt[j] = ch < ch_lim ? w4[ch] : make_uint4(0, 0, 0, 0);
-        }
-    };
-    load(u0);
     float carry = 0.f;
     for (uint32_t us = u0; us < u1; us += 64) {
-        uint32_t d[G::D];
-        if constexpr (C == 1) {
-            d[0] = nxt[0].x; d[1] = nxt[0].y; d[2] = nxt[0].z; d[3] = nxt[0].w;
-        } else {
-#pragma unroll
-            for (int j = 0; j < C; ++j) stage[j * 64 + lane] = nxt[j];
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const uint4 v = stage[lane * C + j];
-                d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
-            }
-        }
-        if (us + 64 < u1) load(us + 64);
+        uint32_t d[G::UD];
+        transpose_step<B>(d, nxt, stage, us, lane);
+        if (us + 64 < u1) load_step<B>(nxt, w4, us + 64, nchunks, lane);
 
         const uint32_t gu = us + lane;
         const bool act = gu < u1;
@@ -239,17 +253,21 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fast(const uint4 *__restrict_
         divmod(gu, P, Pm, row, cu);
         const unsigned char *xb = xl + cu * XU;
         float a[4] = {0.f, 0.f, 0.f, 0.f};
+        uint32_t wv[2][8];
 #pragma unroll
-        for (int t = 0; t < F / 8; ++t) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(xb + 16 * t);
-            const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t i0 = unit_field<B>(d, 8 * t + 2 * q);
-                const uint32_t i1 = unit_field<B>(d, 8 * t + 2 * q + 1);
-                const uint32_t wp = static_cast<uint32_t>(cbl[i0]) | (static_cast<uint32_t>(cbl[i1]) << 16);
-                a[q] = dot2(wp, xs[q], a[q]);
+        for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
             }
+            const u32x4 xv = *reinterpret_cast<const u32x4 *>(xb + 16 * g);
+            const uint32_t *w = wv[g & 1];
+            a[0] = dot2(w[0] | (w[1] << 16), xv.x, a[0]);
+            a[1] = dot2(w[2] | (w[3] << 16), xv.y, a[1]);
+            a[2] = dot2(w[4] | (w[5] << 16), xv.z, a[2]);
+            a[3] = dot2(w[6] | (w[7] << 16), xv.w, a[3]);
         }
         float acc = act ? (a[0] + a[1]) + (a[2] + a[3]) : 0.f;
 
@@ -271,6 +289,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fast(const uint4 *__restrict_
                      : 0.f;
     }
 }
+
+// Geometry of the 128-field lane unit used by the skinny GEMM (C = odd part of b chunks).
+template <int B>
+struct Geo {
+    static constexpr int C = B >> __builtin_ctz(B);   // 16-byte chunks per unit
+    static constexpr int F = 128 >> __builtin_ctz(B); // fields per unit
+    static constexpr int D = 4 * C;                   // dwords per unit
+    static constexpr uint32_t NE = 1u << B;           // codebook entries in LDS
+};
 
 // ------------------------------------------------------------------------- fast skinny GEMM
 // A wave owns a 16-row tile and a range of k-steps (4 units of every row per step).
@@ -481,6 +508,16 @@ bool dispatch_b(int b, Args &args, std::integer_sequence<int, Bs...>) {
 }
 using AllB = std::integer_sequence<int, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>;
 
+// Waves per workgroup and grid for a persistent wave loop over `steps` 64-unit steps, when at
+// most `wfit` waves fit in one workgroup's LDS: one workgroup per CU for large problems, and for
+// small ones fewer waves per workgroup spread over all CUs.
+void shape_grid(uint64_t steps, uint32_t wfit, uint32_t &waves, uint32_t &grid) {
+    const uint64_t cus = static_cast<uint64_t>(cu_count());
+    const uint64_t total = std::max<uint64_t>(1, std::min<uint64_t>(steps, cus * wfit));
+    waves = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(wfit, (total + cus - 1) / cus)));
+    grid = static_cast<uint32_t>((total + waves - 1) / waves);
+}
+
 struct DecodeArgs {
     const cbk_tensor &t; uint16_t *out; hipStream_t s; cbk_status st;
 };
@@ -488,19 +525,22 @@ struct DecodeArgs {
 template <int B>
 struct DecodeRun {
     static bool run(DecodeArgs &a) {
-        using G = Geo<B>;
+        using G = U64<B>;
         const cbk_tensor &t = a.t;
         const uint64_t n = t.rows * t.cols;
-        const uint64_t T64 = (n + G::F - 1) / G::F;
+        const uint64_t T64 = (n + 63) / 64;
         const uint64_t nchunks = cbk_words_for(n, B) / 4;
-        if (T64 * G::C >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
-        const uint32_t lds = round16(G::NE * 2) + (G::C == 1 ? 0u : kWaves * 64u * G::C * 16u);
+        if (T64 * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
+        const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
+        const uint32_t budget = kLdsLimit - G::NE * 2;
+        const uint32_t wfit = std::min<uint32_t>(kMaxWaves, budget / stage_bytes);
+        if (wfit == 0) return false;
+        uint32_t waves, grid;
+        shape_grid((T64 + 63) / 64, wfit, waves, grid);
+        const uint32_t lds = waves * stage_bytes;
         if (!allow_lds(k_decode_fast<B>, lds)) return false;
-        const uint32_t max_groups = cu_count() * groups_per_cu(lds);
-        const uint64_t want = std::min<uint64_t>((T64 + 63) / 64, uint64_t(max_groups) * kWaves);
-        const uint32_t grid = std::max<uint32_t>(1, static_cast<uint32_t>((want + kWaves - 1) / kWaves));
-        hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(kThreads), lds, a.s,
-                           reinterpret_cast<const uint4 *>(t.words), static_cast<uint32_t>(nchunks),
+        hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s,
+                           reinterpret_cast<const u32x4 *>(t.words), static_cast<uint32_t>(nchunks),
                            t.codebook, t.U, a.out, n, static_cast<uint32_t>(T64));
         a.st = launched();
         return true;
@@ -514,25 +554,28 @@ struct GemvArgs {
 template <int B>
 struct GemvRun {
     static bool run(GemvArgs &a) {
-        using G = Geo<B>;
+        using G = U64<B>;
         const cbk_tensor &t = a.t;
-        if (t.cols == 0 || t.cols % G::F != 0) return false;
-        const uint64_t P = t.cols / G::F;
-        if (t.rows * P * G::C >= (uint64_t(1) << 32)) return false;
+        if (t.cols == 0 || t.cols % 64 != 0) return false;
+        const uint64_t P = t.cols / 64;
+        const uint64_t n = t.rows * t.cols;
+        const uint64_t nchunks = cbk_words_for(n, B) / 4;
+        if (t.rows * P * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32)) return false;
         if (t.rows * P * P >= (uint64_t(1) << 32)) return false;
-        const uint64_t lds64 = round16(G::NE * 2) + P * (2 * G::F + 16) +
-                               (G::C == 1 ? 0u : kWaves * 64u * G::C * 16u);
-        if (lds64 > kLdsLimit) return false;
-        const uint32_t lds = static_cast<uint32_t>(lds64);
-        if (!allow_lds(k_gemv_fast<B>, lds)) return false;
+        const uint64_t xbytes = P * (2 * 64 + 16);
+        const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
+        const uint64_t fixed = uint64_t(G::NE) * 2 + xbytes;
+        if (fixed + stage_bytes > kLdsLimit) return false;
+        const uint32_t wfit = std::min<uint32_t>(kMaxWaves, static_cast<uint32_t>((kLdsLimit - fixed) / stage_bytes));
         const uint32_t M = static_cast<uint32_t>(t.rows);
-        const uint64_t steps = (uint64_t(M) * P + 63) / 64;
-        const uint64_t max_waves = uint64_t(cu_count()) * groups_per_cu(lds) * kWaves;
-        const uint64_t want = std::min<uint64_t>(std::min<uint64_t>(steps, max_waves), M);
-        const uint32_t grid = std::max<uint32_t>(1, static_cast<uint32_t>((want + kWaves - 1) / kWaves));
-        hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(kThreads), lds, a.s,
-                           reinterpret_cast<const uint4 *>(t.words), t.codebook, t.U, a.x, a.y, M,
-                           static_cast<uint32_t>(P), magic_for(static_cast<uint32_t>(P)));
+        uint32_t waves, grid;
+        shape_grid(std::min<uint64_t>((uint64_t(M) * P + 63) / 64, M), wfit, waves, grid);
+        const uint32_t lds = static_cast<uint32_t>(xbytes) + waves * stage_bytes;
+        if (!allow_lds(k_gemv_fast<B>, lds)) return false;
+        hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s,
+                           reinterpret_cast<const u32x4 *>(t.words), static_cast<uint32_t>(nchunks),
+                           t.codebook, t.U, a.x, a.y, M, static_cast<uint32_t>(P),
+                           magic_for(static_cast<uint32_t>(P)));
         a.st = launched();
         return true;
     }
