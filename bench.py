@@ -5,9 +5,12 @@ One step = one batch-1 fused decode+GEMV pass (cbk_gemv) over every tensor of th
 the compressed tensors already resident in HBM.  Workloads (seeded synthetic BF16 weights):
 
   attn4096     Llama-7B-shaped 4096x4096 attention projections, N(0, 0.02); 24 distinct tensors
-               (654 MB compressed, well above the 256 MB Infinity Cache) so every step reads HBM.
+               (654 MB compressed, well above the 256 MB Infinity Cache) so every step reads HBM;
+               one cbk_gemv launch per tensor.
   llama7b      full 7B-shaped decode step: 32 layers x {q,k,v,o 4096x4096, gate/up 11008x4096,
                down 4096x11008}, N(0, 0.02), one codebook per tensor (224 tensors, 10.5 GB).
+               Per layer four dependent phases: [q,k,v] and [gate,up] each one cbk_gemv_group
+               launch (they share their input), o and down one cbk_gemv launch each.
 
 The step is captured once in a HIP graph and replayed; the timed region is bracketed by
 torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the GEMV
@@ -41,13 +44,23 @@ def log(msg):
 
 
 def workload_tensors(name: str, count: int):
+    """(specs, phases): specs are (cfg, layer, tensor) triples; phases are lists of spec indices
+    launched together (one launch per phase, phases run in order)."""
     import synth
     if name == "attn4096":
         t = synth.WORKLOADS[2][0][0]
-        return [(2, layer, t) for layer in range(count)]
+        specs = [(2, layer, t) for layer in range(count)]
+        return specs, [[i] for i in range(len(specs))]
     if name == "llama7b":
         tensors, layers = synth.WORKLOADS[4]
-        return [(4, layer, t) for layer in range(layers) for t in tensors]
+        specs, phases = [], []
+        for layer in range(layers):
+            base = len(specs)
+            specs += [(4, layer, t) for t in tensors]
+            names = [t.name for t in tensors]
+            for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+                phases.append([base + names.index(g) for g in group])
+        return specs, phases
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -113,6 +126,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -126,7 +140,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cbk.load_library()
     threads = min(16, os.cpu_count() or 1)
-    specs = workload_tensors(args.workload, args.tensors)
+    specs, phases = workload_tensors(args.workload, args.tensors)
+    if args.no_group:
+        phases = [[i] for ph in phases for i in ph]
     log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
     t0 = time.perf_counter()
     tensors = prepare(specs, threads)
@@ -141,8 +157,11 @@ def main():
     ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in tensors]
 
     def step():
-        for d, y in zip(tensors, ys):
-            cbk.gemv(d, xs[d.cols], y=y)
+        for ph in phases:
+            if len(ph) == 1:
+                cbk.gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
+            else:
+                cbk.gemv_group([tensors[i] for i in ph], xs[tensors[ph[0]].cols], ys=[ys[i] for i in ph])
 
     for _ in range(args.warmup):
         step()
@@ -178,14 +197,17 @@ def main():
     # The step is one graph of back-to-back GEMV launches on `stream`, so the event-timed step
     # divided by its launch count is the kernels' average launch duration (inter-kernel gaps
     # included, which makes it a slight overestimate; rocprofv3 kernel traces agree to ~2 %).
-    avg_launch_s = ms_step * 1e-3 / len(tensors)
+    launches = len(phases)
+    avg_launch_s = ms_step * 1e-3 / launches
 
     n_total = sum(d.n for d in tensors)
-    comp_total = sum(d.compressed_bytes + 2 * d.cols + 4 * d.rows for d in tensors)
+    # algorithmic bytes: packed indices + codebook + y for every tensor, x once per launch
+    comp_total = sum(d.compressed_bytes + 4 * d.rows for d in tensors) + \
+        sum(2 * tensors[ph[0]].cols for ph in phases)
     step_s = ms_step * 1e-3
     value = 2.0 * n_total / step_s / 1e9
     comp_gbps = comp_total / step_s / 1e9
-    algo_per_launch = comp_total / len(tensors)
+    algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors})
     layers = 32 if args.workload == "llama7b" else len(tensors)
@@ -212,6 +234,7 @@ def main():
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
+            "launches_per_step": launches,
         },
         "compressed_GBps": round(comp_gbps, 2),
         "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),

@@ -16,7 +16,8 @@ import os
 import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
-           "Compressed", "decode_bf16", "gemv", "gemm_small", "library_path", "load_library"]
+           "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
+           "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcbk.so")
@@ -66,6 +67,9 @@ def load_library():
         lib.cbk_decode_bf16.argtypes = [tp, ctypes.c_void_p, ctypes.c_void_p]
         lib.cbk_gemv.restype = ctypes.c_int
         lib.cbk_gemv.argtypes = [tp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_gemv_group.restype = ctypes.c_int
+        lib.cbk_gemv_group.argtypes = [tp, ctypes.c_uint32, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]
         lib.cbk_gemm_small.restype = ctypes.c_int
         lib.cbk_gemm_small.argtypes = [tp, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
@@ -184,6 +188,24 @@ def gemv(t: Compressed, x, y=None, stream=None):
                                    ctypes.c_void_p(y.data_ptr() or None), _stream(stream)),
            "cbk_gemv")
     return y
+
+
+def gemv_group(ts, x, ys=None, stream=None):
+    """ys[i] (float32, rows_i) = W_i . x for tensors that share one bfloat16 vector x."""
+    import torch
+    ts = list(ts)
+    if not ts:
+        return []
+    K = ts[0].cols
+    if x.dtype != torch.bfloat16 or x.numel() != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 vector of length cols")
+    if ys is None:
+        ys = [torch.empty(t.rows, dtype=torch.float32, device=x.device) for t in ts]
+    arr = (_Tensor * len(ts))(*[t._struct() for t in ts])
+    yp = (ctypes.c_void_p * len(ts))(*[y.data_ptr() or None for y in ys])
+    _check(load_library().cbk_gemv_group(arr, len(ts), ctypes.c_void_p(x.data_ptr() or None), yp,
+                                         _stream(stream)), "cbk_gemv_group")
+    return ys
 
 
 def gemm_small(t: Compressed, X, Y=None, stream=None):

@@ -162,6 +162,23 @@ cbk_status cbk_gemv(const cbk_tensor *t, const uint16_t *x, float *y, void *stre
     return cbk::launch_gemv(*t, x, y, static_cast<hipStream_t>(stream));
 }
 
+cbk_status cbk_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x, float *const *ys,
+                          void *stream) {
+    if (count == 0) return CBK_OK;
+    if (!ts || !ys || count > 4096) return CBK_E_INVALID;
+    const uint64_t K = ts[0].cols;
+    for (uint32_t i = 0; i < count; ++i) {
+        cbk_status st = check_tensor(&ts[i]);
+        if (st != CBK_OK) return st;
+        if (ts[i].cols != K) return CBK_E_INVALID;
+        if (ts[i].rows > 0 && !ys[i]) return CBK_E_INVALID;
+        if (ys[i] && !aligned(ys[i], 4)) return CBK_E_ALIGN;
+    }
+    if (K > 0 && !x) return CBK_E_INVALID;
+    if (x && !aligned(x, 2)) return CBK_E_ALIGN;
+    return cbk::launch_gemv_group(ts, count, x, ys, static_cast<hipStream_t>(stream));
+}
+
 cbk_status cbk_gemm_small(const cbk_tensor *t, const uint16_t *X, uint64_t ldx, uint32_t batch,
                           float *Y, uint64_t ldy, void *stream) {
     cbk_status st = check_tensor(t);

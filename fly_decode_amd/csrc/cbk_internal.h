@@ -18,6 +18,8 @@ inline constexpr uint32_t unit_chunks(uint32_t b) { return b >> __builtin_ctz(b)
 
 cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s);
 cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s);
+cbk_status launch_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x,
+                             float *const *ys, hipStream_t s);
 cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
                        float *Y, uint64_t ldy, hipStream_t s);
 

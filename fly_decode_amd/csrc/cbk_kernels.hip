@@ -211,22 +211,49 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_decode_fast(const u32x4 *__r
 }
 
 // -------------------------------------------------------------------------------- fast GEMV
+// Up to kMaxGroup tensors that share x (same cols and width b) run in one launch: workgroups
+// [first_block[t], first_block[t + 1]) belong to tensor t, so the launch's ramp-up and tail are
+// paid once for the group (the same idea as decompressing a whole transformer block at once).
+constexpr int kMaxGroup = 8;
+struct GemvTensor {
+    const u32x4 *w4;
+    const uint16_t *cb;
+    float *y;
+    uint32_t nchunks, U, M, first_block;
+};
+struct GemvGroup {
+    GemvTensor t[kMaxGroup];
+    uint32_t count, P, Pm;
+};
+
 template <int B>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_fast(const u32x4 *__restrict__ w4,
-                                                              uint32_t nchunks,
-                                                              const uint16_t *__restrict__ cb,
-                                                              uint32_t U, const uint16_t *__restrict__ x,
-                                                              float *__restrict__ y, uint32_t M,
-                                                              uint32_t P, uint32_t Pm) {
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_fast(const GemvGroup grp,
+                                                              const uint16_t *__restrict__ x) {
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
     __shared__ uint16_t cbl[G::NE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
+    const uint32_t P = grp.P, Pm = grp.Pm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
     u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
 
-    const uint32_t NW = gridDim.x * waves, gw = blockIdx.x * waves + wave;
+    // This workgroup's tensor (uniform selects over the descriptor table).
+    const u32x4 *w4 = grp.t[0].w4;
+    const uint16_t *cb = grp.t[0].cb;
+    float *y = grp.t[0].y;
+    uint32_t nchunks = grp.t[0].nchunks, U = grp.t[0].U, M = grp.t[0].M, b0 = 0;
+    uint32_t b1 = grp.count > 1 ? grp.t[1].first_block : gridDim.x;
+#pragma unroll
+    for (int k = 1; k < kMaxGroup; ++k) {
+        if (k < static_cast<int>(grp.count) && blockIdx.x >= grp.t[k].first_block) {
+            w4 = grp.t[k].w4; cb = grp.t[k].cb; y = grp.t[k].y;
+            nchunks = grp.t[k].nchunks; U = grp.t[k].U; M = grp.t[k].M;
+            b0 = grp.t[k].first_block;
+            b1 = k + 1 < static_cast<int>(grp.count) ? grp.t[k + 1].first_block : gridDim.x;
+        }
+    }
+    const uint32_t NW = (b1 - b0) * waves, gw = (blockIdx.x - b0) * waves + wave;
     const uint32_t r0 = static_cast<uint64_t>(M) * gw / NW;
     const uint32_t r1 = static_cast<uint64_t>(M) * (gw + 1) / NW;
     const uint32_t u0 = r0 * P, u1 = r1 * P;
@@ -548,34 +575,56 @@ struct DecodeRun {
 };
 
 struct GemvArgs {
-    const cbk_tensor &t; const uint16_t *x; float *y; hipStream_t s; cbk_status st;
+    const cbk_tensor *ts; uint32_t count; const uint16_t *x; float *const *ys; hipStream_t s; cbk_status st;
 };
 
+// One launch for up to kMaxGroup tensors of width B that share x (all have the same cols).
 template <int B>
 struct GemvRun {
     static bool run(GemvArgs &a) {
         using G = U64<B>;
-        const cbk_tensor &t = a.t;
-        if (t.cols == 0 || t.cols % 64 != 0) return false;
-        const uint64_t P = t.cols / 64;
-        const uint64_t n = t.rows * t.cols;
-        const uint64_t nchunks = cbk_words_for(n, B) / 4;
-        if (t.rows * P * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32)) return false;
-        if (t.rows * P * P >= (uint64_t(1) << 32)) return false;
+        const uint64_t K = a.ts[0].cols;
+        if (K == 0 || K % 64 != 0 || a.count == 0 || a.count > kMaxGroup) return false;
+        const uint64_t P = K / 64;
+        uint64_t steps = 0, rows = 0;
+        for (uint32_t i = 0; i < a.count; ++i) {
+            const cbk_tensor &t = a.ts[i];
+            if (t.b != B || t.cols != K || t.rows == 0) return false;
+            if (t.rows * P * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32)) return false;
+            if (t.rows * P * P >= (uint64_t(1) << 32)) return false;
+            steps += std::min<uint64_t>((t.rows * P + 63) / 64, t.rows);
+            rows += t.rows;
+        }
         const uint64_t xbytes = P * (2 * 64 + 16);
         const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
         const uint64_t fixed = uint64_t(G::NE) * 2 + xbytes;
         if (fixed + stage_bytes > kLdsLimit) return false;
         const uint32_t wfit = std::min<uint32_t>(kMaxWaves, static_cast<uint32_t>((kLdsLimit - fixed) / stage_bytes));
-        const uint32_t M = static_cast<uint32_t>(t.rows);
         uint32_t waves, grid;
-        shape_grid(std::min<uint64_t>((uint64_t(M) * P + 63) / 64, M), wfit, waves, grid);
+        shape_grid(steps, wfit, waves, grid);
+        grid = std::max(grid, a.count);
         const uint32_t lds = static_cast<uint32_t>(xbytes) + waves * stage_bytes;
         if (!allow_lds(k_gemv_fast<B>, lds)) return false;
-        hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s,
-                           reinterpret_cast<const u32x4 *>(t.words), static_cast<uint32_t>(nchunks),
-                           t.codebook, t.U, a.x, a.y, M, static_cast<uint32_t>(P),
-                           magic_for(static_cast<uint32_t>(P)));
+
+        GemvGroup grp{};
+        grp.count = a.count;
+        grp.P = static_cast<uint32_t>(P);
+        grp.Pm = magic_for(static_cast<uint32_t>(P));
+        // Workgroups per tensor in proportion to its rows, at least one each.
+        uint32_t first = 0;
+        uint64_t rows_before = 0;
+        for (uint32_t i = 0; i < a.count; ++i) {
+            const cbk_tensor &t = a.ts[i];
+            const uint32_t end = (i + 1 == a.count)
+                ? grid
+                : std::max<uint32_t>(first + 1, static_cast<uint32_t>(((rows_before + t.rows) * grid + rows / 2) / rows));
+            grp.t[i] = GemvTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.ys[i],
+                                  static_cast<uint32_t>(cbk_words_for(t.rows * t.cols, B) / 4), t.U,
+                                  static_cast<uint32_t>(t.rows), first};
+            rows_before += t.rows;
+            first = std::min(end, grid - (a.count - 1 - i));
+        }
+        hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s, grp, a.x);
         a.st = launched();
         return true;
     }
@@ -672,16 +721,46 @@ cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uin
     return launched();
 }
 
-cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s) {
+cbk_status launch_gemv_generic(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s) {
     const uint32_t M = static_cast<uint32_t>(t.rows), K = static_cast<uint32_t>(t.cols);
-    if (t.b > 0 && K > 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-        GemvArgs a{t, x, y, s, CBK_OK};
-        if (dispatch_b<GemvRun>(static_cast<int>(t.b), a, AllB{})) return a.st;
-    }
     const uint32_t grid = std::max(1u, std::min<uint32_t>((M + 3) / 4, 4096));
     hipLaunchKernelGGL(k_gemm_generic<1>, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook,
                        t.U, x, uint64_t(0), 1u, y, uint64_t(0), M, K);
     return launched();
+}
+
+cbk_status launch_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x, float *const *ys,
+                             hipStream_t s) {
+    // Consecutive runs of tensors with the same width take one fast launch each (at most
+    // kMaxGroup tensors); anything the fast kernel declines runs the generic kernel.
+    const bool x_aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    uint32_t i = 0;
+    while (i < count) {
+        uint32_t j = i + 1;
+        while (j < count && j - i < static_cast<uint32_t>(kMaxGroup) && ts[j].b == ts[i].b) ++j;
+        bool done = false;
+        if (ts[i].b > 0 && ts[i].cols > 0 && x_aligned) {
+            GemvArgs a{ts + i, j - i, x, ys + i, s, CBK_OK};
+            if (dispatch_b<GemvRun>(static_cast<int>(ts[i].b), a, AllB{})) {
+                if (a.st != CBK_OK) return a.st;
+                done = true;
+            }
+        }
+        if (!done) {
+            for (uint32_t k = i; k < j; ++k) {
+                if (ts[k].rows == 0) continue;
+                cbk_status st = launch_gemv_generic(ts[k], x, ys[k], s);
+                if (st != CBK_OK) return st;
+            }
+        }
+        i = j;
+    }
+    return CBK_OK;
+}
+
+cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s) {
+    float *ys[1] = {y};
+    return launch_gemv_group(&t, 1, x, ys, s);
 }
 
 }  // namespace cbk

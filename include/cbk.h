@@ -109,6 +109,22 @@ cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream);
 cbk_status cbk_gemv(const cbk_tensor *t, const uint16_t *x, float *y, void *stream);
 
 /*
+ * cbk_gemv_group -- GPU.  The same GEMV for `count` tensors that share one input vector x (for
+ * example the query/key/value projections of a layer, or its gate and up projections):
+ * ys[i][r] = sum_k W_i[r][k] * x[k].  Tensors of equal width b are decoded together in one launch
+ * (up to 8 per launch), so the launch's ramp-up and tail are paid once for the group.  This
+ * follows the DFloat11 page ("No more compromises! DFloat11 ...", section "How it works in
+ * practice"): decompressing all matrices of a transformer block together keeps the GPU busy
+ * and hides latency.
+ *   ts     host array of count tensors (device pointers inside), all with the same cols.
+ *   x      device, cols BF16 patterns (alignment as for cbk_gemv).
+ *   ys     host array of count device pointers; ys[i] receives ts[i].rows fp32 values.
+ * count == 0 is a no-op; count > 4096 or differing cols give CBK_E_INVALID.
+ */
+cbk_status cbk_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x, float *const *ys,
+                          void *stream);
+
+/*
  * cbk_gemm_small -- GPU.  Fused decode + skinny GEMM: Y[j][r] = sum_k W[r][k] * X[j][k] for
  * j < batch, fp32 products and sums.
  *   X     device, [batch][ldx] BF16, 2-byte aligned, ldx >= cols.  The fast kernels need X

@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemm_small", "cbk_bits_for",
+    for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemv_group", "cbk_gemm_small", "cbk_bits_for",
               "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str"]:
         assert n in names
 
@@ -138,6 +138,17 @@ def test_gpu_calls_validate_before_any_hip_call(cbk):
     assert lib.cbk_gemm_small(T(), X, 4, 2, Y, 4, None) == 1      # ldx < cols
     assert lib.cbk_gemm_small(T(), X, 8, 2, Y, 3, None) == 1      # ldy < rows
     assert lib.cbk_gemm_small(T(), ctypes.c_void_p(0x4001), 8, 2, Y, 4, None) == 3
+    # grouped GEMV: all tensors share cols; count 0 is a no-op
+    arr = (cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 4, 16, 5, 3))
+    ys = (ctypes.c_void_p * 2)(0x8000, 0x9000)
+    assert lib.cbk_gemv_group(arr, 2, X, ys, None) == 1            # differing cols
+    assert lib.cbk_gemv_group(arr, 0, X, ys, None) == 0
+    assert lib.cbk_gemv_group(None, 2, X, ys, None) == 1
+    arr2 = (cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 4, 8, 5, 4))
+    assert lib.cbk_gemv_group(arr2, 2, X, ys, None) == 1           # bad b in the second tensor
+    ys_bad = (ctypes.c_void_p * 2)(0x8000, 0x9002)
+    assert lib.cbk_gemv_group((cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 4, 8, 5, 3)),
+                              2, X, ys_bad, None) == 3
     # zero-size tensors are accepted without work (no HIP call either)
     assert lib.cbk_gemv(T(rows=0, cols=0, U=0, b=0, cb=0, words=0), None, None, None) == 0
     assert lib.cbk_decode_bf16(T(rows=0, cols=9, U=0, b=0, cb=0, words=0), None, None) == 0

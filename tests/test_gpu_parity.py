@@ -297,3 +297,44 @@ def test_repeated_launches_are_identical(env):
     y0 = cbk.gemv(d, x).clone()
     for _ in range(5):
         assert torch.equal(cbk.gemv(d, x), y0)
+
+
+# ----------------------------------------------------------------------------- grouped GEMV
+def test_gemv_group_matches_oracle_and_single_calls(env, oracle_mod):
+    """Tensors sharing x: different row counts and codebooks, a width change mid-list (two
+    launches), more than eight tensors (several launches) and one generic-path (b = 0) tensor."""
+    torch, cbk = env
+    K = 1024
+    ws = [synth.gaussian_bf16((r, K), 0.02, seed=[61, i]) for i, r in enumerate([300, 64, 1000, 7, 513])]
+    ws.append(synth.with_distinct_count(200 * K, 200, seed=[62], exponents=(120, 130)).reshape(200, K))
+    ws += [synth.gaussian_bf16((96, K), 0.02, seed=[63, i]) for i in range(5)]
+    ws.append(np.full((33, K), 0x3F80, dtype=np.uint16))
+    x = synth.activation_bf16(K, seed=[64])
+    xd = _up(torch, x, torch.bfloat16)
+    ds = [cbk.encode(w).to("cuda") for w in ws]
+    assert len({d.b for d in ds}) >= 3
+    ys = cbk.gemv_group(ds, xd)
+    torch.cuda.synchronize()
+    for w, d, y in zip(ws, ds, ys):
+        ref, absb = oracle_mod.gemv(oracle_mod.encode(w), x)
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - ref) <= TOL * absb)
+        assert torch.equal(cbk.gemv(d, xd), y)
+
+
+def test_gemv_group_7b_layer_phases(env, oracle_mod):
+    """The q/k/v and gate/up phases of a 7B-shaped layer as grouped launches, sampled rows."""
+    torch, cbk = env
+    tensors, _ = synth.WORKLOADS[4]
+    for names in (("q", "k", "v"), ("gate", "up")):
+        group = [t for t in tensors if t.name in names]
+        ws = [synth.workload_tensor(4, 0, t) for t in group]
+        x = synth.workload_x(4, group[0].cols)[0]
+        ds = [cbk.encode(w).to("cuda") for w in ws]
+        ys = cbk.gemv_group(ds, _up(torch, x, torch.bfloat16))
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(65).choice(group[0].rows, 256, replace=False)
+        for w, y in zip(ws, ys):
+            ref, absb = oracle_mod.gemv(oracle_mod.encode(w), x, rows=rows)
+            got = y.cpu().numpy().astype(np.float64)[rows]
+            assert np.all(np.abs(got - ref) <= TOL * absb)
