@@ -106,10 +106,103 @@ __device__ __forceinline__ void divmod(uint32_t n, uint32_t P, uint32_t m, uint3
     if (r >= P) { ++q; r -= P; }
 }
 
+// Codebook table in LDS: 2^b entries (at least 8) so any b-bit index stays inside it.
+template <int B>
+struct Table {
+    static constexpr uint32_t NCH = (U64<B>::NE + 7) / 8;  // 16-byte chunks
+    static constexpr uint32_t SIZE = NCH * 8;               // entries
+};
+
+// Stage the codebook into LDS, entries >= U set to 0x7FC0, in batches of four 16-byte chunks per
+// thread: chunks wholly inside the codebook are 16-byte loads when it is 16-byte aligned, the
+// rest guarded 2-byte loads.  A batch's loads are all issued before any is used, and the first
+// batch is loaded before the kernel's first weight loads are issued, so storing it waits only for
+// these (older) loads: vector-memory counters retire in order.
+// One 16-byte chunk (entries 8c .. 8c+7) of the padded table.
+__device__ __forceinline__ u32x4 cb_chunk(const uint16_t *__restrict__ cb, uint32_t U, uint32_t c,
+                                          uint32_t full) {
+    if (c < full) return reinterpret_cast<const u32x4 *>(cb)[c];
+    const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
+    if (8 * c >= U) return (u32x4){fill, fill, fill, fill};
+    uint32_t e[8];  // the chunk straddling U (every used chunk when cb is not 16-byte aligned)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = cb[min(8 * c + j, U - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = 8 * c + j < U ? e[j] : kCorrupt;
+    return (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
+template <int B>
+__device__ __forceinline__ void cb_load(u32x4 (&v)[4], const uint16_t *__restrict__ cb, uint32_t U,
+                                        uint32_t base, int tid, int nthreads) {
+    const uint32_t full = (reinterpret_cast<uintptr_t>(cb) & 15) == 0 ? U / 8 : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t c = base + k * nthreads + tid;
+        if (c < Table<B>::NCH) v[k] = cb_chunk(cb, U, c, full);
+    }
+}
+
+// Branch-free first batch (chunk c = tid), split into issue and finish so that a kernel can issue
+// its first weight loads in between: with no branches the compiler waits for exactly these loads
+// (vmcnt counts in issue order) rather than for everything in flight.  Issued: one 16-byte load
+// (clamped into the codebook's whole chunks, or from `dummy`, any readable 16-byte-aligned
+// address, when there are none) and the eight entries of the chunk straddling U, read by every
+// thread from the same addresses.  Needs a 16-byte-aligned codebook.
+struct CbFirst {
+    u32x4 whole;
+    uint32_t e[8];
+};
+
+__device__ __forceinline__ void cb_first_issue(CbFirst &f, const uint16_t *__restrict__ cb, uint32_t U,
+                                               const void *dummy, int tid) {
+    const uint32_t full = U / 8;
+    const u32x4 *src = full ? reinterpret_cast<const u32x4 *>(cb) + min(static_cast<uint32_t>(tid), full - 1)
+                            : reinterpret_cast<const u32x4 *>(dummy);
+    f.whole = *src;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.e[j] = cb[min(8 * full + j, U - 1)];
+}
+
+__device__ __forceinline__ u32x4 cb_first_finish(const CbFirst &f, uint32_t U, int tid) {
+    const uint32_t full = U / 8, c = static_cast<uint32_t>(tid);
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? f.e[j] : kCorrupt;
+    const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
+    const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    const u32x4 pad = {fill, fill, fill, fill};
+    return c < full ? f.whole : (c == full ? tail : pad);
+}
+
+template <int B>
+__device__ __forceinline__ void cb_store(uint16_t *cbl, const u32x4 (&v)[4], uint32_t base, int tid,
+                                         int nthreads) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t c = base + k * nthreads + tid;
+        if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = v[k];
+    }
+}
+
+// Remaining batches (after the first), for tables larger than 4 chunks per thread.
+template <int B>
+__device__ __forceinline__ void cb_stage_rest(uint16_t *cbl, const uint16_t *__restrict__ cb,
+                                              uint32_t U, int tid, int nthreads) {
+    for (uint32_t base = 4 * nthreads; base < Table<B>::NCH; base += 4 * nthreads) {
+        u32x4 v[4];
+        cb_load<B>(v, cb, U, base, tid, nthreads);
+        cb_store<B>(cbl, v, base, tid, nthreads);
+    }
+}
+
 template <int B>
 __device__ __forceinline__ void stage_codebook(uint16_t *cbl, const uint16_t *__restrict__ cb,
                                                uint32_t U, int tid, int nthreads) {
-    for (uint32_t i = tid; i < U64<B>::NE; i += nthreads) cbl[i] = i < U ? cb[i] : kCorrupt;
+    u32x4 v[4];
+    cb_load<B>(v, cb, U, 0, tid, nthreads);
+    cb_store<B>(cbl, v, 0, tid, nthreads);
+    cb_stage_rest<B>(cbl, cb, U, tid, nthreads);
 }
 
 // Step loads: the chunks covering units [us, us + 64) start at chunk (us * UD) / 4; an odd-b
@@ -165,7 +258,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_decode_fast(const u32x4 *__r
                                                                 uint32_t U, uint16_t *__restrict__ out,
                                                                 uint64_t n, uint32_t T) {
     using G = U64<B>;
-    __shared__ uint16_t cbl[G::NE];
+    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
     u32x4 *stage = reinterpret_cast<u32x4 *>(smem) + wave * G::STAGE_CHUNKS;
@@ -174,9 +267,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_decode_fast(const u32x4 *__r
     const uint32_t steps = (T + 63) / 64;
     const uint32_t s0 = static_cast<uint64_t>(steps) * gw / NW;
     const uint32_t s1 = static_cast<uint64_t>(steps) * (gw + 1) / NW;
-    u32x4 nxt[G::LPL];
-    if (s0 < s1) load_step<B>(nxt, w4, s0 * 64, nchunks, lane);
     stage_codebook<B>(cbl, cb, U, tid, blockDim.x);
+    u32x4 nxt[G::LPL];  // issued after the staging loads have been waited for (see k_gemv_fast)
+    if (s0 < s1) load_step<B>(nxt, w4, s0 * 64, nchunks, lane);
     __syncthreads();
     if (s0 >= s1) return;
 
@@ -219,11 +312,12 @@ struct GemvTensor {
     const u32x4 *w4;
     const uint16_t *cb;
     float *y;
-    uint32_t nchunks, U, M, first_block;
+    uint32_t nchunks, U, M, pad;
 };
 struct GemvGroup {
-    GemvTensor t[kMaxGroup];
+    uint32_t first_block[kMaxGroup + 1];  // first_block[count] = grid size
     uint32_t count, P, Pm;
+    GemvTensor t[kMaxGroup];
 };
 
 template <int B>
@@ -231,42 +325,56 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_fast(const GemvGroup gr
                                                               const uint16_t *__restrict__ x) {
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
-    __shared__ uint16_t cbl[G::NE];
+    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
     const uint32_t P = grp.P, Pm = grp.Pm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
     u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
 
-    // This workgroup's tensor (uniform selects over the descriptor table).
-    const u32x4 *w4 = grp.t[0].w4;
-    const uint16_t *cb = grp.t[0].cb;
-    float *y = grp.t[0].y;
-    uint32_t nchunks = grp.t[0].nchunks, U = grp.t[0].U, M = grp.t[0].M, b0 = 0;
-    uint32_t b1 = grp.count > 1 ? grp.t[1].first_block : gridDim.x;
+    // This workgroup's tensor: count the group boundaries at or below blockIdx.x (uniform).
+    uint32_t k = 0;
 #pragma unroll
-    for (int k = 1; k < kMaxGroup; ++k) {
-        if (k < static_cast<int>(grp.count) && blockIdx.x >= grp.t[k].first_block) {
-            w4 = grp.t[k].w4; cb = grp.t[k].cb; y = grp.t[k].y;
-            nchunks = grp.t[k].nchunks; U = grp.t[k].U; M = grp.t[k].M;
-            b0 = grp.t[k].first_block;
-            b1 = k + 1 < static_cast<int>(grp.count) ? grp.t[k + 1].first_block : gridDim.x;
-        }
-    }
+    for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
+    const GemvTensor T = grp.t[k];
+    const u32x4 *w4 = T.w4;
+    const uint16_t *cb = T.cb;
+    float *y = T.y;
+    const uint32_t nchunks = T.nchunks, U = T.U, M = T.M;
+    const uint32_t b0 = grp.first_block[k], b1 = grp.first_block[k + 1];
     const uint32_t NW = (b1 - b0) * waves, gw = (blockIdx.x - b0) * waves + wave;
     const uint32_t r0 = static_cast<uint64_t>(M) * gw / NW;
     const uint32_t r1 = static_cast<uint64_t>(M) * (gw + 1) / NW;
     const uint32_t u0 = r0 * P, u1 = r1 * P;
-    u32x4 nxt[G::LPL];
-    if (u0 < u1) load_step<B>(nxt, w4, u0, nchunks, lane);  // in flight during the staging below
-    stage_codebook<B>(cbl, cb, U, tid, blockDim.x);
-    {
-        const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
-        for (uint32_t q = tid; q < P * 8; q += blockDim.x)
-            *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = x4[q];
+    // Staging: the first codebook batch and the x chunks are loaded (branch-free, all in flight
+    // together) and stored to LDS.
+    const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
+    const uint32_t xch = P * 8;
+    CbFirst cf;
+    cb_first_issue(cf, cb, U, x4, tid);
+    u32x4 xv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xv[k] = x4[min(k * blockDim.x + tid, xch - 1)];
+
+    if (static_cast<uint32_t>(tid) < Table<B>::NCH)
+        reinterpret_cast<u32x4 *>(cbl)[tid] = cb_first_finish(cf, U, tid);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t q = k * blockDim.x + tid;
+        if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[k];
     }
+    // rare remainders: tables or x larger than one (four) chunk(s) per thread
+    for (uint32_t c = blockDim.x + tid; c < Table<B>::NCH; c += blockDim.x)
+        reinterpret_cast<u32x4 *>(cbl)[c] = cb_chunk(cb, U, c, U / 8);
+    for (uint32_t q = 4 * blockDim.x + tid; q < xch; q += blockDim.x)
+        *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = x4[q];
     __syncthreads();
     if (u0 >= u1) return;
+    // The first weight step is issued only after the staging: issued earlier, the whole grid's
+    // first-step burst (tens of MB) queues ahead of the small codebook and x reads in the memory
+    // system and the staging barrier then waits for most of it.
+    u32x4 nxt[G::LPL];
+    load_step<B>(nxt, w4, u0, nchunks, lane);
 
     float carry = 0.f;
     for (uint32_t us = u0; us < u1; us += 64) {
@@ -559,7 +667,7 @@ struct DecodeRun {
         const uint64_t nchunks = cbk_words_for(n, B) / 4;
         if (T64 * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
         const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
-        const uint32_t budget = kLdsLimit - G::NE * 2;
+        const uint32_t budget = kLdsLimit - Table<B>::SIZE * 2;
         const uint32_t wfit = std::min<uint32_t>(kMaxWaves, budget / stage_bytes);
         if (wfit == 0) return false;
         uint32_t waves, grid;
@@ -590,6 +698,7 @@ struct GemvRun {
         for (uint32_t i = 0; i < a.count; ++i) {
             const cbk_tensor &t = a.ts[i];
             if (t.b != B || t.cols != K || t.rows == 0) return false;
+            if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
             if (t.rows * P * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32)) return false;
             if (t.rows * P * P >= (uint64_t(1) << 32)) return false;
             steps += std::min<uint64_t>((t.rows * P + 63) / 64, t.rows);
@@ -597,7 +706,7 @@ struct GemvRun {
         }
         const uint64_t xbytes = P * (2 * 64 + 16);
         const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
-        const uint64_t fixed = uint64_t(G::NE) * 2 + xbytes;
+        const uint64_t fixed = uint64_t(Table<B>::SIZE) * 2 + xbytes;
         if (fixed + stage_bytes > kLdsLimit) return false;
         const uint32_t wfit = std::min<uint32_t>(kMaxWaves, static_cast<uint32_t>((kLdsLimit - fixed) / stage_bytes));
         uint32_t waves, grid;
@@ -620,10 +729,12 @@ struct GemvRun {
                 : std::max<uint32_t>(first + 1, static_cast<uint32_t>(((rows_before + t.rows) * grid + rows / 2) / rows));
             grp.t[i] = GemvTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.ys[i],
                                   static_cast<uint32_t>(cbk_words_for(t.rows * t.cols, B) / 4), t.U,
-                                  static_cast<uint32_t>(t.rows), first};
+                                  static_cast<uint32_t>(t.rows), 0};
+            grp.first_block[i] = first;
             rows_before += t.rows;
             first = std::min(end, grid - (a.count - 1 - i));
         }
+        grp.first_block[a.count] = grid;
         hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s, grp, a.x);
         a.st = launched();
         return true;
