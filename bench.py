@@ -242,7 +242,7 @@ def main():
         "tokens_per_s_equiv": round(1.0 / step_s, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"k_gemv_fast<{bits[-1]}>",
+            "kernel": f"k_gemv_rows<{bits[-1]}>",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

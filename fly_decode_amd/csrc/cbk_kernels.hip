@@ -16,11 +16,13 @@
 //  * Fields are unpacked in registers (shift/and, or alignbit + and across a word boundary)
 //    and gathered from the codebook held in static LDS, padded to 2^b entries with 0x7FC0 so a
 //    corrupt index cannot leave the table.  Gathers are issued one 8-field group ahead of use.
-//  * GEMV: units run along rows; x sits in LDS, 16 bytes of padding per unit so the lanes'
-//    128-bit reads are conflict-free; BF16 pairs are multiplied with v_dot2c_f32_bf16 into fp32;
-//    a segmented wave reduction (a row is a contiguous run of lanes) produces y.
-//  * Workgroups hold as many waves as the LDS budget allows (up to 16), sharing one codebook and
-//    one copy of x; the grid is persistent and rows are split evenly over its waves.
+//  * GEMV: rows are dealt round-robin to the waves (the grid sweeps the stream front to back);
+//    a row is ceil(K / 4096) wave steps, lane l of step j taking unit 64j + l of the row.  x sits
+//    in LDS, 16 bytes of padding per unit so the lanes' 128-bit reads are conflict-free; BF16
+//    pairs are multiplied with v_dot2c_f32_bf16 into fp32; lanes accumulate across the row's
+//    steps and one wave reduction per row produces y.  The codebook and x staging loads are all
+//    issued before any weight load (vector-memory data returns in issue order).
+//  * One workgroup of 8 waves per CU shares one codebook table and one copy of x.
 //
 // Skinny GEMM: a wave owns a 16-row tile and walks K in steps of 4 units (128 fields) per row;
 // lane (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded tile to
@@ -29,7 +31,7 @@
 //
 // Generic kernels (any b and shape, runtime field extraction straight from global memory) cover
 // b == 0, rows whose length is not a multiple of 64, misaligned operands and shapes beyond the
-// LDS budget.
+// LDS budget (including the b = 16 GEMV).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -98,14 +100,6 @@ __device__ __forceinline__ uint32_t stream_field(const uint32_t *__restrict__ wo
     return __builtin_amdgcn_alignbit(hi, lo, s) & ((1u << b) - 1u);
 }
 
-// q = n / P, r = n % P with m = floor(2^32 / P) (m = 2^32 - 1 for P = 1): the estimate is exact or
-// one short for every 32-bit n, so a single correction suffices.
-__device__ __forceinline__ void divmod(uint32_t n, uint32_t P, uint32_t m, uint32_t &q, uint32_t &r) {
-    q = __umulhi(n, m);
-    r = n - q * P;
-    if (r >= P) { ++q; r -= P; }
-}
-
 // Codebook table in LDS: 2^b entries (at least 8) so any b-bit index stays inside it.
 template <int B>
 struct Table {
@@ -115,9 +109,7 @@ struct Table {
 
 // Stage the codebook into LDS, entries >= U set to 0x7FC0, in batches of four 16-byte chunks per
 // thread: chunks wholly inside the codebook are 16-byte loads when it is 16-byte aligned, the
-// rest guarded 2-byte loads.  A batch's loads are all issued before any is used, and the first
-// batch is loaded before the kernel's first weight loads are issued, so storing it waits only for
-// these (older) loads: vector-memory counters retire in order.
+// rest guarded 2-byte loads.  A batch's loads are all issued before any is used.
 // One 16-byte chunk (entries 8c .. 8c+7) of the padded table.
 __device__ __forceinline__ u32x4 cb_chunk(const uint16_t *__restrict__ cb, uint32_t U, uint32_t c,
                                           uint32_t full) {
@@ -141,38 +133,6 @@ __device__ __forceinline__ void cb_load(u32x4 (&v)[4], const uint16_t *__restric
         const uint32_t c = base + k * nthreads + tid;
         if (c < Table<B>::NCH) v[k] = cb_chunk(cb, U, c, full);
     }
-}
-
-// Branch-free first batch (chunk c = tid), split into issue and finish so that a kernel can issue
-// its first weight loads in between: with no branches the compiler waits for exactly these loads
-// (vmcnt counts in issue order) rather than for everything in flight.  Issued: one 16-byte load
-// (clamped into the codebook's whole chunks, or from `dummy`, any readable 16-byte-aligned
-// address, when there are none) and the eight entries of the chunk straddling U, read by every
-// thread from the same addresses.  Needs a 16-byte-aligned codebook.
-struct CbFirst {
-    u32x4 whole;
-    uint32_t e[8];
-};
-
-__device__ __forceinline__ void cb_first_issue(CbFirst &f, const uint16_t *__restrict__ cb, uint32_t U,
-                                               const void *dummy, int tid) {
-    const uint32_t full = U / 8;
-    const u32x4 *src = full ? reinterpret_cast<const u32x4 *>(cb) + min(static_cast<uint32_t>(tid), full - 1)
-                            : reinterpret_cast<const u32x4 *>(dummy);
-    f.whole = *src;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.e[j] = cb[min(8 * full + j, U - 1)];
-}
-
-__device__ __forceinline__ u32x4 cb_first_finish(const CbFirst &f, uint32_t U, int tid) {
-    const uint32_t full = U / 8, c = static_cast<uint32_t>(tid);
-    uint32_t e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? f.e[j] : kCorrupt;
-    const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
-    const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-    const u32x4 pad = {fill, fill, fill, fill};
-    return c < full ? f.whole : (c == full ? tail : pad);
 }
 
 template <int B>
@@ -304,32 +264,55 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_decode_fast(const u32x4 *__r
 }
 
 // -------------------------------------------------------------------------------- fast GEMV
+// Rows are dealt round-robin to the waves of the tensor's workgroups (row gw, gw + NW, ...), so at
+// any moment the grid reads one contiguous window of the stream, front to back.  A row of P units
+// is S = ceil(P / 64) wave steps; lane l of step j decodes unit 64j + l of the row (the last step
+// is partial when P % 64 != 0), accumulates in registers across the row's steps, and one wave
+// reduction per row produces y.
+//
 // Up to kMaxGroup tensors that share x (same cols and width b) run in one launch: workgroups
 // [first_block[t], first_block[t + 1]) belong to tensor t, so the launch's ramp-up and tail are
 // paid once for the group (the same idea as decompressing a whole transformer block at once).
+constexpr int kGemvWaves = 8;   // waves per workgroup, one workgroup per CU
 constexpr int kMaxGroup = 8;
+constexpr int kXPerThread = 8;  // x staging: 16-byte chunks per thread (K <= 8 * 8 * 512)
 struct GemvTensor {
     const u32x4 *w4;
     const uint16_t *cb;
     float *y;
-    uint32_t nchunks, U, M, pad;
+    uint32_t M, U;
 };
 struct GemvGroup {
     uint32_t first_block[kMaxGroup + 1];  // first_block[count] = grid size
-    uint32_t count, P, Pm;
+    uint32_t count, P, S;
     GemvTensor t[kMaxGroup];
 };
 
+// Loads of the wave step (row r, step j): the chunks holding units [rP + 64j, rP + 64j + nl).
+// Loads past the step's last chunk are clamped to it (same cache line, no extra traffic).
 template <int B>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_fast(const GemvGroup grp,
-                                                              const uint16_t *__restrict__ x) {
+__device__ __forceinline__ void load_row_step(u32x4 (&v)[U64<B>::LPL], const u32x4 *__restrict__ w4,
+                                              uint32_t us, uint32_t nl, int lane) {
+    const uint64_t c0 = (static_cast<uint64_t>(us) * U64<B>::UD) >> 2;
+    const uint64_t c1 = (static_cast<uint64_t>(us + nl) * U64<B>::UD + 3) >> 2;
+    const uint32_t last = static_cast<uint32_t>(c1 - 1 - c0);
+#pragma unroll
+    for (int j = 0; j < U64<B>::LPL; ++j)
+        v[j] = w4[c0 + min(static_cast<uint32_t>(j * 64 + lane), last)];
+}
+
+template <int B>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup grp,
+                                                               const uint16_t *__restrict__ x) {
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
+    constexpr int NT = 64 * kGemvWaves;
+    constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;  // codebook chunks per thread
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
-    const uint32_t P = grp.P, Pm = grp.Pm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+    const uint32_t P = grp.P, S = grp.S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
 
     // This workgroup's tensor: count the group boundaries at or below blockIdx.x (uniform).
@@ -339,89 +322,104 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemv_fast(const GemvGroup gr
     const GemvTensor T = grp.t[k];
     const u32x4 *w4 = T.w4;
     const uint16_t *cb = T.cb;
-    float *y = T.y;
-    const uint32_t nchunks = T.nchunks, U = T.U, M = T.M;
-    const uint32_t b0 = grp.first_block[k], b1 = grp.first_block[k + 1];
-    const uint32_t NW = (b1 - b0) * waves, gw = (blockIdx.x - b0) * waves + wave;
-    const uint32_t r0 = static_cast<uint64_t>(M) * gw / NW;
-    const uint32_t r1 = static_cast<uint64_t>(M) * (gw + 1) / NW;
-    const uint32_t u0 = r0 * P, u1 = r1 * P;
-    // Staging: the first codebook batch and the x chunks are loaded (branch-free, all in flight
-    // together) and stored to LDS.
+    const uint32_t M = T.M, U = T.U;
+    const uint32_t b0 = grp.first_block[k];
+    const uint32_t NW = (grp.first_block[k + 1] - b0) * kGemvWaves;
+    const uint32_t gw = (blockIdx.x - b0) * kGemvWaves + wave;
+
+    // Staging loads, branch-free: codebook chunks c = tid + NT * i (whole 16-byte loads clamped into
+    // the codebook, or from x when it has no whole chunk), the eight entries of the chunk that
+    // straddles U, and this thread's x chunks.  They are all issued, in every wave, before the
+    // barrier below; the weight loads come after it, so vector-memory data (returned in issue
+    // order) for the staging never waits behind the grid's first burst of weight loads.
     const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
-    const uint32_t xch = P * 8;
-    CbFirst cf;
-    cb_first_issue(cf, cb, U, x4, tid);
-    u32x4 xv[4];
+    const uint32_t full = U / 8, xch = P * 8;
+    u32x4 cw[CPT], xv[kXPerThread];
+    uint32_t te[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xv[k] = x4[min(k * blockDim.x + tid, xch - 1)];
+    for (int i = 0; i < CPT; ++i)
+        cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : x4[0];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i)
+        if (static_cast<uint32_t>(i * NT + tid) < xch) xv[i] = x4[i * NT + tid];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    if (static_cast<uint32_t>(tid) < Table<B>::NCH)
-        reinterpret_cast<u32x4 *>(cbl)[tid] = cb_first_finish(cf, U, tid);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t q = k * blockDim.x + tid;
-        if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[k];
-    }
-    // rare remainders: tables or x larger than one (four) chunk(s) per thread
-    for (uint32_t c = blockDim.x + tid; c < Table<B>::NCH; c += blockDim.x)
-        reinterpret_cast<u32x4 *>(cbl)[c] = cb_chunk(cb, U, c, U / 8);
-    for (uint32_t q = 4 * blockDim.x + tid; q < xch; q += blockDim.x)
-        *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = x4[q];
-    __syncthreads();
-    if (u0 >= u1) return;
-    // The first weight step is issued only after the staging: issued earlier, the whole grid's
-    // first-step burst (tens of MB) queues ahead of the small codebook and x reads in the memory
-    // system and the staging barrier then waits for most of it.
+    // First weight step (clamped to the last row for a wave without rows, so the load is harmless).
     u32x4 nxt[G::LPL];
-    load_step<B>(nxt, w4, u0, nchunks, lane);
+    const uint32_t r_first = min(gw, M - 1);
+    load_row_step<B>(nxt, w4, r_first * P, min(64u, P), lane);
 
-    float carry = 0.f;
-    for (uint32_t us = u0; us < u1; us += 64) {
+    // Staging stores: entries >= U of the table read 0x7FC0.
+    {
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? te[j] : kCorrupt;
+        const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
+        const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        const u32x4 pad = {fill, fill, fill, fill};
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const uint32_t c = i * NT + tid;
+            if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = c < full ? cw[i] : (c == full ? tail : pad);
+        }
+#pragma unroll
+        for (int i = 0; i < kXPerThread; ++i) {
+            const uint32_t q = i * NT + tid;
+            if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[i];
+        }
+    }
+    // LDS-only barrier: the weight loads stay in flight.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters unconstrained
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (gw >= M) return;
+
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t r = gw, j = 0;
+    while (true) {
+        const uint32_t us = r * P + 64 * j;
         uint32_t d[G::UD];
         transpose_step<B>(d, nxt, stage, us, lane);
-        if (us + 64 < u1) load_step<B>(nxt, w4, us + 64, nchunks, lane);
+        // next step of this wave: the rest of the row, then row r + NW
+        const bool row_end = j + 1 == S;
+        const uint32_t rn = row_end ? r + NW : r, jn = row_end ? 0 : j + 1;
+        if (rn < M) load_row_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), lane);
 
-        const uint32_t gu = us + lane;
-        const bool act = gu < u1;
-        uint32_t row, cu;
-        divmod(gu, P, Pm, row, cu);
-        const unsigned char *xb = xl + cu * XU;
-        float a[4] = {0.f, 0.f, 0.f, 0.f};
-        uint32_t wv[2][8];
+        const uint32_t cu = 64 * j + lane;  // this lane's unit within the row
+        if (cu < P) {
+            const unsigned char *xb = xl + cu * XU;
+            uint32_t wv[2][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+            for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            if (g + 1 < 8) {
+            for (int g = 0; g < 8; ++g) {
+                if (g + 1 < 8) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
+                    for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
+                }
+                const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + 16 * g);
+                const uint32_t *w = wv[g & 1];
+                a[0] = dot2(w[0] | (w[1] << 16), xq.x, a[0]);
+                a[1] = dot2(w[2] | (w[3] << 16), xq.y, a[1]);
+                a[2] = dot2(w[4] | (w[5] << 16), xq.z, a[2]);
+                a[3] = dot2(w[6] | (w[7] << 16), xq.w, a[3]);
             }
-            const u32x4 xv = *reinterpret_cast<const u32x4 *>(xb + 16 * g);
-            const uint32_t *w = wv[g & 1];
-            a[0] = dot2(w[0] | (w[1] << 16), xv.x, a[0]);
-            a[1] = dot2(w[2] | (w[3] << 16), xv.y, a[1]);
-            a[2] = dot2(w[4] | (w[5] << 16), xv.z, a[2]);
-            a[3] = dot2(w[6] | (w[7] << 16), xv.w, a[3]);
         }
-        float acc = act ? (a[0] + a[1]) + (a[2] + a[3]) : 0.f;
-
-        // Segmented suffix sums: lanes of one row form a contiguous run (units are consecutive).
+        if (row_end) {
+            float acc = (a[0] + a[1]) + (a[2] + a[3]);
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_down(acc, off, 64);
-            if (lane + off < 64 && cu + off < P) acc += o;
+            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+            if (lane == 0) T.y[r] = acc;
+            a[0] = a[1] = a[2] = a[3] = 0.f;
         }
-        const uint32_t last_lane = min(u1 - 1u - us, 63u);
-        const uint32_t last_cu = __builtin_amdgcn_readlane(cu, last_lane);
-        const bool open = last_cu != P - 1;                       // last row continues next step
-        const uint32_t head_last = last_lane - min(last_lane, last_cu);
-        if (lane == 0) acc += carry;
-        const bool head = lane == 0 || cu == 0;
-        if (act && head && !(open && static_cast<uint32_t>(lane) == head_last)) y[row] = acc;
-        carry = open ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                     __builtin_bit_cast(int, acc), head_last))
-                     : 0.f;
+        if (rn >= M) break;
+        r = rn;
+        j = jn;
     }
 }
 
@@ -616,10 +614,6 @@ int cu_count() {
 
 cbk_status launched() { return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP; }
 
-uint32_t magic_for(uint32_t P) {
-    return P == 1 ? 0xFFFFFFFFu : static_cast<uint32_t>((uint64_t(1) << 32) / P);
-}
-
 // Workgroups that fit on one CU given the LDS footprint (capped at 2: register-limited).
 uint32_t groups_per_cu(uint32_t lds) {
     return lds == 0 ? 2u : std::max(1u, std::min(2u, kLdsLimit / lds));
@@ -694,31 +688,27 @@ struct GemvRun {
         const uint64_t K = a.ts[0].cols;
         if (K == 0 || K % 64 != 0 || a.count == 0 || a.count > kMaxGroup) return false;
         const uint64_t P = K / 64;
-        uint64_t steps = 0, rows = 0;
+        if (P * 8 > static_cast<uint64_t>(kXPerThread) * 64 * kGemvWaves) return false;
+        uint64_t rows = 0;
         for (uint32_t i = 0; i < a.count; ++i) {
             const cbk_tensor &t = a.ts[i];
             if (t.b != B || t.cols != K || t.rows == 0) return false;
             if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
-            if (t.rows * P * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32)) return false;
-            if (t.rows * P * P >= (uint64_t(1) << 32)) return false;
-            steps += std::min<uint64_t>((t.rows * P + 63) / 64, t.rows);
+            if (t.rows * P >= (uint64_t(1) << 32)) return false;
             rows += t.rows;
         }
-        const uint64_t xbytes = P * (2 * 64 + 16);
-        const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
-        const uint64_t fixed = uint64_t(Table<B>::SIZE) * 2 + xbytes;
-        if (fixed + stage_bytes > kLdsLimit) return false;
-        const uint32_t wfit = std::min<uint32_t>(kMaxWaves, static_cast<uint32_t>((kLdsLimit - fixed) / stage_bytes));
-        uint32_t waves, grid;
-        shape_grid(steps, wfit, waves, grid);
-        grid = std::max(grid, a.count);
-        const uint32_t lds = static_cast<uint32_t>(xbytes) + waves * stage_bytes;
-        if (!allow_lds(k_gemv_fast<B>, lds)) return false;
+        const uint64_t lds = P * (2 * 64 + 16) + uint64_t(kGemvWaves) * G::STAGE_CHUNKS * 16;
+        if (lds + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
+        if (!allow_lds(k_gemv_rows<B>, static_cast<uint32_t>(lds))) return false;
+        // One workgroup per CU (fewer when there are not enough rows for every wave), at least one
+        // per tensor.
+        const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(
+            a.count, std::min<uint64_t>(cu_count(), (rows + kGemvWaves - 1) / kGemvWaves)));
 
         GemvGroup grp{};
         grp.count = a.count;
         grp.P = static_cast<uint32_t>(P);
-        grp.Pm = magic_for(static_cast<uint32_t>(P));
+        grp.S = static_cast<uint32_t>((P + 63) / 64);
         // Workgroups per tensor in proportion to its rows, at least one each.
         uint32_t first = 0;
         uint64_t rows_before = 0;
@@ -728,14 +718,13 @@ struct GemvRun {
                 ? grid
                 : std::max<uint32_t>(first + 1, static_cast<uint32_t>(((rows_before + t.rows) * grid + rows / 2) / rows));
             grp.t[i] = GemvTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.ys[i],
-                                  static_cast<uint32_t>(cbk_words_for(t.rows * t.cols, B) / 4), t.U,
-                                  static_cast<uint32_t>(t.rows), 0};
+                                  static_cast<uint32_t>(t.rows), t.U};
             grp.first_block[i] = first;
             rows_before += t.rows;
             first = std::min(end, grid - (a.count - 1 - i));
         }
         grp.first_block[a.count] = grid;
-        hipLaunchKernelGGL(k_gemv_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s, grp, a.x);
+        hipLaunchKernelGGL(k_gemv_rows<B>, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds), a.s, grp, a.x);
         a.st = launched();
         return true;
     }
