@@ -127,6 +127,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 3 device-to-device copies of BYTES (counter calibration for the "
+                         "traffic figure) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -136,8 +139,17 @@ def main():
 
     import torch
     import fly_decode_amd as cbk
+    from fly_decode_amd import profiling
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 3}), flush=True)
+        return
     cbk.load_library()
     threads = min(16, os.cpu_count() or 1)
     specs, phases = workload_tensors(args.workload, args.tensors)
@@ -211,6 +223,8 @@ def main():
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors})
     layers = 32 if args.workload == "llama7b" else len(tensors)
+    kernel_key = f"k_gemv_rows_b{bits[-1]}"
+    traffic = profiling.traffic_for(kernel_key, args.workload)
 
     result = {
         "metric": "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak",
@@ -247,9 +261,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": round(traffic["traffic_bytes_per_launch"]) if traffic else None,
             "bytes_per_launch": int(algo_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, args.workload), ROOT) if traffic else None,
         },
     }
     if not args.no_cpu_baseline:
