@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
-"""Benchmark: fused codebook-GEMV decompressed-weight GB/s at batch 1, and % of HBM peak.
+"""Benchmark: fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak.
 
-One step = one batch-1 fused decode+GEMV pass (cbk_gemv) over every tensor of the workload, with
-the compressed tensors already resident in HBM.  Workloads (seeded synthetic BF16 weights):
+One step = one pass of the fused decode + GEMV (or skinny GEMM) over every tensor of the workload,
+with the compressed tensors already resident in HBM.  Workloads (seeded synthetic BF16 weights,
+each tensor with its own codebook):
 
-  attn4096     Llama-7B-shaped 4096x4096 attention projections, N(0, 0.02); 24 distinct tensors
-               (654 MB compressed, well above the 256 MB Infinity Cache) so every step reads HBM;
-               one cbk_gemv launch per tensor.
-  llama7b      full 7B-shaped decode step: 32 layers x {q,k,v,o 4096x4096, gate/up 11008x4096,
-               down 4096x11008}, N(0, 0.02), one codebook per tensor (224 tensors, 10.5 GB).
-               Per layer four dependent phases: [q,k,v] and [gate,up] each one cbk_gemv_group
-               launch (they share their input), o and down one cbk_gemv launch each.
+  attn4096   (default) Llama-7B-shaped 4096x4096 attention projections, N(0, 0.02); 24 distinct
+             tensors (654 MB compressed, well above the 256 MB Infinity Cache) so every step reads
+             HBM; one cbk_gemv launch per tensor.
+  llama7b    full 7B-shaped decode step: 32 layers x {q,k,v,o 4096x4096, gate/up 11008x4096,
+             down 4096x11008}, N(0, 0.02) (224 tensors, 10.5 GB).  Per layer four dependent phases:
+             [q,k,v] and [gate,up] each one cbk_gemv_group launch (they share their input), o and
+             down one cbk_gemv launch each.
+  mlp_b8     Llama-7B MLP at batch 8: gate/up 11008x4096 and down 4096x11008, 0.02 * Student-t(4);
+             --layers distinct copies (default 8, 1.76 GB); one cbk_gemm_small launch per tensor.
+  l70b_b16   70B-shaped layer at batch 16: q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192,
+             down 8192x28672, N(0, 0.015); --layers distinct layers (default 2, 2.8 GB); one
+             cbk_gemm_small launch per tensor.
+  l70b_b1    the same tensors at batch 1, phases grouped as in llama7b.
 
 The step is captured once in a HIP graph and replayed; the timed region is bracketed by
-torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the GEMV
-consumes) / step time.  The dominant kernel's roofline uses its algorithmic bytes per launch
-(packed indices ceil(n*b/8) + codebook 2U + x 2K + y 4M) over its average launch duration,
-measured with HIP events on the launch stream.  The CPU baseline times the oracle (decode + GEMV
-in float64) on a bounded sample with host threads.
+torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
+feeds the multiply) / step time.  The dominant kernel's roofline uses its algorithmic bytes per
+launch (packed indices ceil(n*b/8) + codebook 2U + X 2*batch*K + Y 4*batch*M) over its average launch
+duration, measured with HIP events on the launch stream.  The CPU baseline times the oracle (decode
++ GEMV in float64) on a bounded sample with host threads.
 
 Prints one JSON line.
 """
@@ -43,24 +50,33 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def workload_tensors(name: str, count: int):
-    """(specs, phases): specs are (cfg, layer, tensor) triples; phases are lists of spec indices
-    launched together (one launch per phase, phases run in order)."""
+def workload_tensors(name: str, count: int, layers: int):
+    """(specs, phases, batch, layer_count): specs are (cfg, layer, tensor) triples; phases are lists
+    of spec indices launched together (one launch per phase, phases run in order)."""
     import synth
     if name == "attn4096":
         t = synth.WORKLOADS[2][0][0]
         specs = [(2, layer, t) for layer in range(count)]
-        return specs, [[i] for i in range(len(specs))]
-    if name == "llama7b":
-        tensors, layers = synth.WORKLOADS[4]
+        return specs, [[i] for i in range(len(specs))], 1, len(specs)
+    if name in ("llama7b", "l70b_b1", "l70b_b16"):
+        cfg = 4 if name == "llama7b" else 5
+        tensors, n_layers = synth.WORKLOADS[cfg]
+        n_layers = n_layers if name == "llama7b" else layers
         specs, phases = [], []
-        for layer in range(layers):
+        for layer in range(n_layers):
             base = len(specs)
-            specs += [(4, layer, t) for t in tensors]
+            specs += [(cfg, layer, t) for t in tensors]
+            if name == "l70b_b16":
+                phases += [[base + i] for i in range(len(tensors))]
+                continue
             names = [t.name for t in tensors]
             for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
                 phases.append([base + names.index(g) for g in group])
-        return specs, phases
+        return specs, phases, (16 if name == "l70b_b16" else 1), n_layers
+    if name == "mlp_b8":
+        tensors, _ = synth.WORKLOADS[3]
+        specs = [(3, layer, t) for layer in range(layers) for t in tensors]
+        return specs, [[i] for i in range(len(specs))], 8, layers
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -121,8 +137,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b"])
+    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1"])
     ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
+    ap.add_argument("--layers", type=int, default=0, help="distinct layers for mlp_b8 (8) and l70b_* (2)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
@@ -152,7 +169,8 @@ def main():
         return
     cbk.load_library()
     threads = min(16, os.cpu_count() or 1)
-    specs, phases = workload_tensors(args.workload, args.tensors)
+    layers_arg = args.layers or (8 if args.workload == "mlp_b8" else 2)
+    specs, phases, batch, n_layers = workload_tensors(args.workload, args.tensors, layers_arg)
     if args.no_group:
         phases = [[i] for ph in phases for i in ph]
     log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
@@ -164,13 +182,19 @@ def main():
     xs = {}
     for d in tensors:
         if d.cols not in xs:
-            x = synth.workload_x(specs[0][0], d.cols)[0]
+            x = synth.workload_x(specs[0][0], d.cols, batch)
             xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
-    ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in tensors]
+    if batch == 1:
+        xs = {k: v[0] for k, v in xs.items()}
+        ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in tensors]
+    else:
+        ys = [torch.empty((batch, d.rows), dtype=torch.float32, device="cuda") for d in tensors]
 
     def step():
         for ph in phases:
-            if len(ph) == 1:
+            if batch > 1:
+                cbk.gemm_small(tensors[ph[0]], xs[tensors[ph[0]].cols], Y=ys[ph[0]])
+            elif len(ph) == 1:
                 cbk.gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
             else:
                 cbk.gemv_group([tensors[i] for i in ph], xs[tensors[ph[0]].cols], ys=[ys[i] for i in ph])
@@ -213,21 +237,22 @@ def main():
     avg_launch_s = ms_step * 1e-3 / launches
 
     n_total = sum(d.n for d in tensors)
-    # algorithmic bytes: packed indices + codebook + y for every tensor, x once per launch
-    comp_total = sum(d.compressed_bytes + 4 * d.rows for d in tensors) + \
-        sum(2 * tensors[ph[0]].cols for ph in phases)
+    # algorithmic bytes: packed indices + codebook + Y for every tensor, X once per launch
+    comp_total = sum(d.compressed_bytes + 4 * batch * d.rows for d in tensors) + \
+        sum(2 * batch * tensors[ph[0]].cols for ph in phases)
     step_s = ms_step * 1e-3
     value = 2.0 * n_total / step_s / 1e9
     comp_gbps = comp_total / step_s / 1e9
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors})
-    layers = 32 if args.workload == "llama7b" else len(tensors)
-    kernel_key = f"k_gemv_rows_b{bits[-1]}"
+    kernel = "k_gemv_rows" if batch == 1 else ("k_gemm_tile" if batch <= 8 else "k_gemm_tile_mfma")
+    kernel_key = f"{kernel}_b{bits[-1]}"
     traffic = profiling.traffic_for(kernel_key, args.workload)
 
     result = {
-        "metric": "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak",
+        "metric": "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
+                  else f"fused codebook skinny-GEMM decompressed-weight GB/s at batch {batch}; % of HBM peak",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -243,7 +268,8 @@ def main():
             "workload": args.workload,
             "tensors": len(tensors),
             "shapes": sorted({f"{d.rows}x{d.cols}" for d in tensors}),
-            "batch": 1,
+            "batch": batch,
+            "layers": n_layers,
             "index_bits": bits,
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
@@ -252,11 +278,11 @@ def main():
         },
         "compressed_GBps": round(comp_gbps, 2),
         "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),
-        "layer_time_us": round(ms_step * 1e3 / (32 if args.workload == "llama7b" else layers), 3),
+        "layer_time_us": round(ms_step * 1e3 / n_layers, 3),
         "tokens_per_s_equiv": round(1.0 / step_s, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"k_gemv_rows<{bits[-1]}>",
+            "kernel": f"{kernel}<{bits[-1]}>",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -267,7 +293,10 @@ def main():
             "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, args.workload), ROOT) if traffic else None,
         },
     }
-    if not args.no_cpu_baseline:
+    if batch > 1:
+        flops = 2.0 * batch * n_total / step_s
+        result["effective_TFLOPs"] = round(flops / 1e12, 3)
+    if not args.no_cpu_baseline and batch == 1:
         log("CPU baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
     print(json.dumps(result), flush=True)

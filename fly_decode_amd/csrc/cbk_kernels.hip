@@ -46,7 +46,6 @@ namespace {
 
 constexpr uint16_t kCorrupt = 0x7FC0;
 constexpr int kMaxWaves = 16;             // waves per workgroup, decode and GEMV
-constexpr int kGemmWaves = 4;             // waves per workgroup, skinny GEMM
 constexpr uint32_t kLdsLimit = 160 * 1024;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -63,8 +62,6 @@ __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
 __device__ __forceinline__ float bf16_value(uint16_t h) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
 }
-
-constexpr uint32_t round16(uint32_t v) { return (v + 15u) & ~15u; }
 
 // Geometry of the 64-field lane unit for width B (decode and GEMV).
 template <int B>
@@ -423,127 +420,228 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
     }
 }
 
-// Geometry of the 128-field lane unit used by the skinny GEMM (C = odd part of b chunks).
+// ------------------------------------------------------------------------- fast skinny GEMM
+// Y[n][M] = X[n][K] . W^T for n = batch <= 16.  A wave owns a 16-row tile and one K slice; a wave
+// step covers 256 columns (4 units of 64 fields) of the tile's 16 rows, and lane (i = l % 16,
+// g = l / 16) decodes unit g of row i.  The workgroup's 8 waves (8 tiles) share one copy of the
+// K slice of X in LDS: the 16 lanes with the same g read the same X addresses (broadcast) on the
+// VALU path (batch <= 8, v_dot2c per column), and on the MFMA path (batch 9..16) the decoded
+// 8-field groups are exactly the A operand of v_mfma_f32_16x16x32_bf16 and X supplies B.  When K
+// is split over several workgroups, partial sums are added into a zero-filled Y with fp32 atomics.
+constexpr int kGemmWaves = 8;
+
 template <int B>
-struct Geo {
-    static constexpr int C = B >> __builtin_ctz(B);   // 16-byte chunks per unit
-    static constexpr int F = 128 >> __builtin_ctz(B); // fields per unit
-    static constexpr int D = 4 * C;                   // dwords per unit
-    static constexpr uint32_t NE = 1u << B;           // codebook entries in LDS
+struct GemmGeo {
+    static constexpr int UD = 2 * B;                         // dwords per 64-field unit
+    static constexpr int RCH = 2 * B + 1;                    // chunks of one row's 4-unit segment (+1: half-chunk start)
+    static constexpr int SRC = RCH + ((1 - RCH) % 16 + 16) % 16;  // stage row stride, = 1 mod 16 chunks
+    static constexpr int STEP_CH = 16 * RCH;                 // chunk slots loaded per step
+    static constexpr int LPL = (STEP_CH + 63) / 64;          // 16-byte loads per lane per step
+    static constexpr int STAGE = 16 * SRC;                   // stage chunks per wave
+};
+static_assert(GemmGeo<13>::SRC == 33 && GemmGeo<16>::SRC == 33 && GemmGeo<1>::SRC == 17, "stage stride");
+
+constexpr uint32_t kXUnit = 2 * 64 + 16;  // LDS bytes per 64-column unit of one X row (16 B padding)
+
+struct GemmShape {
+    uint32_t M, P;          // rows, units per row (K / 64)
+    uint32_t ks_units;      // K slice, in units (multiple of 4)
+    uint32_t tiles, kslices;
+    uint32_t batch, ldx, ldy;
+    uint32_t xrow;          // LDS bytes per X row
+    int atomic;
 };
 
-// ------------------------------------------------------------------------- fast skinny GEMM
-// A wave owns a 16-row tile and a range of k-steps (4 units of every row per step).
+// Loads of one step: row i of the tile, units [u0, u0 + nu); slot q = i * RCH + c.  Slots past the
+// row's last chunk are clamped to it, rows past M to row M - 1 (their lanes are inactive).
+template <int B>
+__device__ __forceinline__ void gemm_load(u32x4 (&v)[GemmGeo<B>::LPL], const u32x4 *__restrict__ w4,
+                                          uint32_t row0, uint32_t u0, uint32_t nu, const GemmShape &s,
+                                          int lane) {
+    using G = GemmGeo<B>;
+#pragma unroll
+    for (int j = 0; j < G::LPL; ++j) {
+        const uint32_t q = min(static_cast<uint32_t>(j * 64 + lane), static_cast<uint32_t>(G::STEP_CH - 1));
+        const uint32_t i = q / G::RCH, c = q - i * G::RCH;
+        const uint64_t r = min(row0 + i, s.M - 1);
+        const uint64_t d0 = (r * s.P + u0) * G::UD, d1 = d0 + static_cast<uint64_t>(nu) * G::UD;
+        const uint64_t c0 = d0 >> 2, c1 = (d1 + 3) >> 2;
+        v[j] = w4[c0 + min(static_cast<uint64_t>(c), c1 - c0 - 1)];
+    }
+}
+
 template <int B, int NB, bool MFMA>
-__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_fast(
-    const uint4 *__restrict__ w4, const uint16_t *__restrict__ cb, uint32_t U,
-    const uint16_t *__restrict__ X, uint32_t ldx, uint32_t batch, float *__restrict__ Y,
-    uint32_t ldy, uint32_t M, uint32_t P, uint32_t ksteps, uint32_t splits, uint32_t items,
-    int atomic) {
-    using G = Geo<B>;
-    constexpr int C = G::C, F = G::F;
-    constexpr int RS = 4 * C + 1;  // padded stage row stride in chunks (odd: conflict-free)
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
+    const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb, uint32_t U,
+    const uint16_t *__restrict__ X, float *__restrict__ Y, const GemmShape s) {
+    using G = GemmGeo<B>;
+    constexpr int NT = 64 * kGemmWaves;
+    constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t *cbl = reinterpret_cast<uint16_t *>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint4 *stage = reinterpret_cast<uint4 *>(smem + round16(G::NE * 2)) + wave * 16 * RS;
-    stage_codebook<B>(cbl, cb, U, tid, 64 * kGemmWaves);
-    __syncthreads();
+    const uint32_t kslice = blockIdx.x % s.kslices, group = blockIdx.x / s.kslices;
+    const uint32_t tile = group * kGemmWaves + wave;
+    const uint32_t su0 = kslice * s.ks_units;                 // first unit of the slice
+    const uint32_t su1 = min(su0 + s.ks_units, s.P);
+    unsigned char *xl = smem;                                  // [NB][slice units][144 B] (+16 B per row)
+    u32x4 *stage = reinterpret_cast<u32x4 *>(smem + NB * s.xrow) + wave * G::STAGE;
+
+    // Staging loads (branch-free codebook chunks; X chunks of the slice).  The whole slice width is
+    // staged for all NB rows, zeros past the last column and for rows >= batch, so the lanes of a
+    // partial step (whose weights are zero) never read uninitialised LDS: 0 * NaN would be NaN.
+    const uint32_t full = U / 8;
+    const uint32_t xu = su1 - su0, xw = s.ks_units, xch = NB * xw * 8;
+    const u32x4 *X4 = reinterpret_cast<const u32x4 *>(X);
+    u32x4 cw[CPT];
+    uint32_t te[8];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+        cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : X4[0];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
+    constexpr int XPT = 8;
+    u32x4 xv[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const uint32_t q = i * NT + tid;  // q = (n * xw + u) * 8 + c
+        const uint32_t n = q / (xw * 8), rem = q - n * xw * 8;
+        if (q < xch && n < s.batch && rem < xu * 8) xv[i] = X4[(static_cast<uint64_t>(n) * s.ldx) / 8 + su0 * 8 + rem];
+        else xv[i] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    const uint32_t row0 = min(tile, s.tiles - 1) * 16;
+    const uint32_t nsteps = (xu + 3) / 4;
+    u32x4 nxt[G::LPL];
+    gemm_load<B>(nxt, w4, row0, su0, min(4u, xu), s, lane);
+
+    {
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? te[j] : kCorrupt;
+        const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
+        const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        const u32x4 pad = {fill, fill, fill, fill};
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const uint32_t c = i * NT + tid;
+            if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = c < full ? cw[i] : (c == full ? tail : pad);
+        }
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const uint32_t q = i * NT + tid;
+            const uint32_t n = q / (xw * 8), rem = q - n * xw * 8;
+            if (q < xch)
+                *reinterpret_cast<u32x4 *>(xl + n * s.xrow + (rem >> 3) * kXUnit + (rem & 7) * 16) = xv[i];
+        }
+        // slices wider than the first batch of X chunks (not reached by the shapes the host picks)
+        for (uint32_t q = XPT * NT + tid; q < xch; q += NT) {
+            const uint32_t n = q / (xw * 8), rem = q - n * xw * 8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (n < s.batch && rem < xu * 8) v = X4[(static_cast<uint64_t>(n) * s.ldx) / 8 + su0 * 8 + rem];
+            *reinterpret_cast<u32x4 *>(xl + n * s.xrow + (rem >> 3) * kXUnit + (rem & 7) * 16) = v;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (tile >= s.tiles) return;
 
     const int li = lane & 15, lg = lane >> 4;
-    const uint32_t NW = gridDim.x * kGemmWaves;
-    for (uint32_t item = blockIdx.x * kGemmWaves + wave; item < items; item += NW) {
-        const uint32_t tile = item / splits, split = item % splits;
-        const uint32_t ks0 = static_cast<uint64_t>(ksteps) * split / splits;
-        const uint32_t ks1 = static_cast<uint64_t>(ksteps) * (split + 1) / splits;
-        const uint32_t row0 = tile * 16;
+    const bool row_ok = row0 + li < s.M;
+    f32x4_t cm = {0.f, 0.f, 0.f, 0.f};
+    float acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = 0.f;
 
-        f32x4_t cm = {0.f, 0.f, 0.f, 0.f};
-        float acc[NB];
+    for (uint32_t st = 0; st < nsteps; ++st) {
+        const uint32_t u0 = su0 + 4 * st;
+        // stage: row i's chunks at i * SRC; read back unit g of row li (qword offsets)
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int n = 0; n < NB; ++n) acc[n] = 0.f;
+        for (int j = 0; j < G::LPL; ++j) {
+            const uint32_t q = j * 64 + lane;
+            if (q < G::STEP_CH) {
+                const uint32_t i = q / G::RCH, c = q - i * G::RCH;
+                stage[i * G::SRC + c] = nxt[j];
+            }
+        }
+        asm volatile("" ::: "memory");
+        const uint64_t rr = min(row0 + li, s.M - 1);
+        const uint32_t off = static_cast<uint32_t>(((rr * s.P + u0) * G::UD) & 3u);  // 0 or 2 dwords
+        const u32x2 *st2 = reinterpret_cast<const u32x2 *>(stage + li * G::SRC) + off / 2 + lg * B;
+        uint32_t d[G::UD];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const u32x2 t = st2[j];
+            d[2 * j] = t.x; d[2 * j + 1] = t.y;
+        }
+        asm volatile("" ::: "memory");
+        if (st + 1 < nsteps) gemm_load<B>(nxt, w4, row0, u0 + 4, min(4u, su1 - u0 - 4), s, lane);
 
-        for (uint32_t ks = ks0; ks < ks1; ++ks) {
-            // Cooperative load of 16 rows x 4 units (4C chunks per row), coalesced per row.
+        const uint32_t unit = u0 + lg;
+        const bool valid = row_ok && unit < su1;
+        const unsigned char *xb = xl + (unit - su0) * kXUnit;  // + n * xrow + 16 * f
+        uint32_t wv[2][8];
 #pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const uint32_t q = j * 64 + lane;       // 0 .. 64C-1
-                const uint32_t i = q / (4 * C), off = q % (4 * C);
-                const uint32_t unit = ks * 4 + off / C;
-                const uint32_t row = row0 + i;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (row < M && unit < P) v = w4[(static_cast<uint64_t>(row) * P + ks * 4) * C + off];
-                stage[i * RS + off] = v;
+        for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            if (f + 1 < 8) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wv[(f + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (f + 1) + i)];
             }
-            uint32_t d[G::D];
+            const uint32_t *w = wv[f & 1];
+            u32x4 wp = {w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
+            if (!valid) wp = (u32x4){0u, 0u, 0u, 0u};
+            if constexpr (MFMA) {
+                // B operand: lane (n = l % 16, g) holds X[n][unit g, fields 8f .. 8f + 7]
+                const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + li * s.xrow + 16 * f);
+                cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wp),
+                                                             __builtin_bit_cast(bf16x8_t, xq), cm, 0, 0, 0);
+            } else {
 #pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const uint4 v = stage[li * RS + lg * C + j];
-                d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
-            }
-            const uint32_t unit = ks * 4 + lg;
-            const bool valid = unit < P && row0 + li < M;
-            const uint32_t kbase = unit * F;
-#pragma unroll
-            for (int t = 0; t < F / 8; ++t) {
-                uint32_t wp[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t i0 = unit_field<B>(d, 8 * t + 2 * q);
-                    const uint32_t i1 = unit_field<B>(d, 8 * t + 2 * q + 1);
-                    wp[q] = valid ? (static_cast<uint32_t>(cbl[i0]) | (static_cast<uint32_t>(cbl[i1]) << 16)) : 0u;
-                }
-                if constexpr (MFMA) {
-                    // A: row li, k = 8 consecutive of unit lg.  B: batch column li, same k.
-                    uint4 xv = make_uint4(0, 0, 0, 0);
-                    if (static_cast<uint32_t>(li) < batch && unit < P)
-                        xv = *reinterpret_cast<const uint4 *>(X + static_cast<uint64_t>(li) * ldx + kbase + 8 * t);
-                    const uint4 wv = make_uint4(wp[0], wp[1], wp[2], wp[3]);
-                    cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
-                                                                 __builtin_bit_cast(bf16x8_t, xv),
-                                                                 cm, 0, 0, 0);
-                } else {
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) {
-                        uint4 xv = make_uint4(0, 0, 0, 0);
-                        if (unit < P)
-                            xv = *reinterpret_cast<const uint4 *>(X + static_cast<uint64_t>(n) * ldx + kbase + 8 * t);
-                        acc[n] = dot2(wp[0], xv.x, acc[n]);
-                        acc[n] = dot2(wp[1], xv.y, acc[n]);
-                        acc[n] = dot2(wp[2], xv.z, acc[n]);
-                        acc[n] = dot2(wp[3], xv.w, acc[n]);
-                    }
+                for (int n = 0; n < NB; ++n) {
+                    const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + n * s.xrow + 16 * f);
+                    acc[n] = dot2(wp.x, xq.x, acc[n]);
+                    acc[n] = dot2(wp.y, xq.y, acc[n]);
+                    acc[n] = dot2(wp.z, xq.z, acc[n]);
+                    acc[n] = dot2(wp.w, xq.w, acc[n]);
                 }
             }
         }
+    }
 
-        if constexpr (MFMA) {
-            // Lane l holds C[i = 4*(l/16) + r][n = l % 16], r = 0..3.
-            const int n = li;
-            if (static_cast<uint32_t>(n) < batch) {
+    if constexpr (MFMA) {
+        // Lane l holds C[row 4 * (l / 16) + r][column l % 16], r = 0..3.
+        if (static_cast<uint32_t>(li) < s.batch) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t row = row0 + 4 * lg + r;
-                    if (row < M) {
-                        float *dst = Y + static_cast<uint64_t>(n) * ldy + row;
-                        if (atomic) atomicAdd(dst, cm[r]); else *dst = cm[r];
-                    }
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t row = row0 + 4 * lg + r;
+                if (row < s.M) {
+                    float *dst = Y + static_cast<uint64_t>(li) * s.ldy + row;
+                    if (s.atomic) atomicAdd(dst, cm[r]); else *dst = cm[r];
                 }
             }
-        } else {
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            float v = acc[n];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[n] = v;
+        }
+        if (lg == 0 && row_ok) {
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
-                float v = acc[n];
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                acc[n] = v;
-            }
-            const uint32_t row = row0 + li;
-            if (lg == 0 && row < M) {
-#pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    float *dst = Y + static_cast<uint64_t>(n) * ldy + row;
-                    if (atomic) atomicAdd(dst, acc[n]); else *dst = acc[n];
+                if (static_cast<uint32_t>(n) < s.batch) {
+                    float *dst = Y + static_cast<uint64_t>(n) * s.ldy + row0 + li;
+                    if (s.atomic) atomicAdd(dst, acc[n]); else *dst = acc[n];
                 }
             }
         }
@@ -613,11 +711,6 @@ int cu_count() {
 }
 
 cbk_status launched() { return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP; }
-
-// Workgroups that fit on one CU given the LDS footprint (capped at 2: register-limited).
-uint32_t groups_per_cu(uint32_t lds) {
-    return lds == 0 ? 2u : std::max(1u, std::min(2u, kLdsLimit / lds));
-}
 
 // Kernels above 64 KiB of dynamic LDS must raise their limit first.
 template <typename K>
@@ -736,54 +829,60 @@ struct GemmArgs {
 };
 
 template <int B, int NB, bool MFMA>
-bool gemm_launch(GemmArgs &a, uint32_t lds) {
-    using G = Geo<B>;
+bool gemm_launch(GemmArgs &a) {
+    using G = GemmGeo<B>;
     const cbk_tensor &t = a.t;
-    if (!allow_lds(k_gemm_fast<B, NB, MFMA>, lds)) return false;
-    const uint64_t P = t.cols / G::F;
-    const uint32_t M = static_cast<uint32_t>(t.rows);
-    const uint32_t ksteps = static_cast<uint32_t>((P + 3) / 4);
-    const uint32_t tiles = (M + 15) / 16;
-    const uint32_t resident = cu_count() * groups_per_cu(lds) * kGemmWaves;
-    uint32_t splits = 1;
-    while (uint64_t(tiles) * splits < resident && splits * 2 <= ksteps) splits *= 2;
-    const uint32_t items = tiles * splits;
-    const int atomic = splits > 1;
-    if (atomic) {
-        const uint64_t total = uint64_t(M) * a.batch;
+    const uint64_t P = t.cols / 64;
+    GemmShape s{};
+    s.M = static_cast<uint32_t>(t.rows);
+    s.P = static_cast<uint32_t>(P);
+    s.tiles = (s.M + 15) / 16;
+    s.batch = a.batch;
+    s.ldx = static_cast<uint32_t>(a.ldx);
+    s.ldy = static_cast<uint32_t>(a.ldy);
+    // LDS: codebook table (static) + X slice + 8 stages.  The widest slice that fits, narrowed so
+    // that the grid has at least one workgroup per CU when the tile count allows.
+    const uint64_t fixed = uint64_t(Table<B>::SIZE) * 2 + uint64_t(kGemmWaves) * G::STAGE * 16;
+    if (fixed + uint64_t(NB) * (4 * kXUnit + 16) > kLdsLimit) return false;
+    const uint64_t max_units = ((kLdsLimit - fixed) / NB - 16) / kXUnit / 4 * 4;
+    const uint64_t groups = (s.tiles + kGemmWaves - 1) / kGemmWaves;
+    const uint64_t want_slices = std::max<uint64_t>(1, (static_cast<uint64_t>(cu_count()) + groups - 1) / groups);
+    uint64_t units = std::min<uint64_t>(max_units, std::max<uint64_t>(4, ((P + want_slices - 1) / want_slices + 3) / 4 * 4));
+    // the X slice is staged with at most 8 chunks per thread in the first batch
+    units = std::min<uint64_t>(units, std::max<uint64_t>(4, uint64_t(8) * 64 * kGemmWaves / (8 * NB) / 4 * 4));
+    s.ks_units = static_cast<uint32_t>(units);
+    s.kslices = static_cast<uint32_t>((P + units - 1) / units);
+    s.xrow = static_cast<uint32_t>(units * kXUnit + 16);
+    s.atomic = s.kslices > 1;
+    const uint32_t lds = NB * s.xrow + kGemmWaves * G::STAGE * 16;
+    if (!allow_lds(k_gemm_tile<B, NB, MFMA>, lds)) return false;
+    const uint64_t grid = groups * s.kslices;
+    if (grid >= (uint64_t(1) << 31)) return false;
+    if (s.atomic) {
+        const uint64_t total = uint64_t(s.M) * a.batch;
         hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<uint32_t>(std::min<uint64_t>(1024, (total + 255) / 256))),
-                           dim3(256), 0, a.s, a.Y, a.ldy, M, a.batch);
+                           dim3(256), 0, a.s, a.Y, a.ldy, s.M, a.batch);
     }
-    const uint32_t waves = std::min(items, resident);
-    const uint32_t grid = std::max(1u, (waves + kGemmWaves - 1) / kGemmWaves);
-    hipLaunchKernelGGL((k_gemm_fast<B, NB, MFMA>), dim3(grid), dim3(64 * kGemmWaves), lds, a.s,
-                       reinterpret_cast<const uint4 *>(t.words), t.codebook, t.U, a.X,
-                       static_cast<uint32_t>(a.ldx), a.batch, a.Y, static_cast<uint32_t>(a.ldy), M,
-                       static_cast<uint32_t>(P), ksteps, splits, items, atomic);
+    hipLaunchKernelGGL((k_gemm_tile<B, NB, MFMA>), dim3(static_cast<uint32_t>(grid)), dim3(64 * kGemmWaves), lds,
+                       a.s, reinterpret_cast<const u32x4 *>(t.words), t.codebook, t.U, a.X, a.Y, s);
     return true;
 }
 
 template <int B>
 struct GemmRun {
     static bool run(GemmArgs &a) {
-        using G = Geo<B>;
         const cbk_tensor &t = a.t;
-        if (t.cols == 0 || t.cols % G::F != 0) return false;
-        const uint64_t P = t.cols / G::F;
-        if (t.rows * P * G::C >= (uint64_t(1) << 32)) return false;
-        const uint32_t lds = round16(G::NE * 2) + kGemmWaves * 16u * (4 * G::C + 1) * 16u;
-        if (lds > kLdsLimit) return false;
+        if (t.cols == 0 || t.cols % 64 != 0 || t.rows == 0) return false;
+        if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
+        if (t.rows * (t.cols / 64) >= (uint64_t(1) << 32)) return false;
+        if (a.ldx >= (uint64_t(1) << 32) || a.ldy >= (uint64_t(1) << 32)) return false;
         bool ok;
         switch (a.batch) {
-            case 1: ok = gemm_launch<B, 1, false>(a, lds); break;
-            case 2: ok = gemm_launch<B, 2, false>(a, lds); break;
-            case 3: ok = gemm_launch<B, 3, false>(a, lds); break;
-            case 4: ok = gemm_launch<B, 4, false>(a, lds); break;
-            case 5: ok = gemm_launch<B, 5, false>(a, lds); break;
-            case 6: ok = gemm_launch<B, 6, false>(a, lds); break;
-            case 7: ok = gemm_launch<B, 7, false>(a, lds); break;
-            case 8: ok = gemm_launch<B, 8, false>(a, lds); break;
-            default: ok = gemm_launch<B, 16, true>(a, lds); break;
+            case 1: ok = gemm_launch<B, 1, false>(a); break;
+            case 2: ok = gemm_launch<B, 2, false>(a); break;
+            case 3: case 4: ok = gemm_launch<B, 4, false>(a); break;
+            case 5: case 6: case 7: case 8: ok = gemm_launch<B, 8, false>(a); break;
+            default: ok = gemm_launch<B, 16, true>(a); break;
         }
         if (ok) a.st = launched();
         return ok;

@@ -81,9 +81,6 @@ def _gemm_check(env, oracle_mod, w, X, rows=None, exact=False, ldx=None):
 
 
 # --------------------------------------------------------------------------------- decode
-UNIT_FIELDS = {b: 128 >> ((b & -b).bit_length() - 1) for b in range(1, 17)}
-
-
 @pytest.mark.parametrize("b", list(range(0, 17)))
 def test_decode_every_width(env, b):
     """Every width b = 0..16, U at both ends of the width, ragged and unit-aligned lengths."""
@@ -149,11 +146,15 @@ def _int_bf16(vals):
     return synth.f32_to_bf16(np.asarray(vals, dtype=np.float32))
 
 
+# GEMV shapes: cols/64 = 3 (one partial wave step per row), 130 (three steps, the last partial),
+# 67 (odd: rows start half-way into a 16-byte chunk for odd b), and a ragged K (generic kernel).
+GEMV_SHAPES = [(67, 192), (5, 64 * 130), (9, 64 * 67), (33, 129)]
+
+
 @pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16])
 def test_gemv_every_width(env, oracle_mod, b):
-    F = UNIT_FIELDS[b]
     U = 2 ** b if b <= 12 else 2 ** (b - 1) + 3
-    for rows, cols in [(67, 3 * F), (5, 64 * F + F), (33, 2 * F + 1)]:
+    for rows, cols in GEMV_SHAPES:
         n = rows * cols
         if n < U:
             rows = (U + cols - 1) // cols
@@ -224,11 +225,16 @@ def test_gemv_70b_shapes_sampled(env, oracle_mod):
 
 
 # ----------------------------------------------------------------------------------- GEMM
-@pytest.mark.parametrize("batch", [1, 2, 3, 5, 8, 9, 12, 16])
+# GEMM shapes: cols/64 = 10 (steps of 4, 4, 2 units), 32, 13 (odd, M < 16: one partial row tile),
+# 64 with 40 rows (few tiles: K is split over workgroups and Y is accumulated with atomics), and a
+# ragged K (generic kernel).
+GEMM_SHAPES = [(50, 640), (16, 2048), (7, 832), (40, 4096), (23, 393)]
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8, 9, 12, 16])
 def test_gemm_batches(env, oracle_mod, batch):
-    for b, U in [(13, 5000), (12, 3000), (8, 200), (16, 40000)]:
-        F = UNIT_FIELDS[b]
-        for rows, cols in [(50, 5 * F), (16, 16 * F), (23, 3 * F + 9)]:
+    for b, U in [(13, 5000), (12, 3000), (8, 200), (3, 7), (16, 40000)]:
+        for rows, cols in GEMM_SHAPES:
             n = rows * cols
             if n < U:
                 rows = (U + cols - 1) // cols
