@@ -421,13 +421,16 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
 }
 
 // ------------------------------------------------------------------------- fast skinny GEMM
-// Y[n][M] = X[n][K] . W^T for n = batch <= 16.  A wave owns a 16-row tile and one K slice; a wave
+// Y[n][M] = X[n][K] . W^T for n = batch <= 16.  A wave owns a 16-row tile and a range of K; a wave
 // step covers 256 columns (4 units of 64 fields) of the tile's 16 rows, and lane (i = l % 16,
-// g = l / 16) decodes unit g of row i.  The workgroup's 8 waves (8 tiles) share one copy of the
-// K slice of X in LDS: the 16 lanes with the same g read the same X addresses (broadcast) on the
-// VALU path (batch <= 8, v_dot2c per column), and on the MFMA path (batch 9..16) the decoded
-// 8-field groups are exactly the A operand of v_mfma_f32_16x16x32_bf16 and X supplies B.  When K
-// is split over several workgroups, partial sums are added into a zero-filled Y with fp32 atomics.
+// g = l / 16) decodes unit g of row i.  With each step's weight chunks the wave loads the step's
+// columns of X (all batch rows) and passes both through its private LDS stage: the weights are
+// read back per lane, then X is written over them and read per 8-field group, one group ahead of
+// use.  VALU path (batch <= 8): the 16 lanes of a k-group read the same X addresses (broadcast)
+// and v_dot2c accumulates each column.  MFMA path (batch 9..16): the decoded 8-field groups are the
+// A operand of v_mfma_f32_16x16x32_bf16 and X supplies B.  When the tiles alone cannot fill the
+// CUs, the 8 waves of a workgroup take 8/TW parts of K for TW tiles and add their partial sums in
+// LDS, so every Y element is written once (no atomics; results do not depend on timing).
 constexpr int kGemmWaves = 8;
 
 template <int B>
@@ -437,27 +440,39 @@ struct GemmGeo {
     static constexpr int SRC = RCH + ((1 - RCH) % 16 + 16) % 16;  // stage row stride, = 1 mod 16 chunks
     static constexpr int STEP_CH = 16 * RCH;                 // chunk slots loaded per step
     static constexpr int LPL = (STEP_CH + 63) / 64;          // 16-byte loads per lane per step
-    static constexpr int STAGE = 16 * SRC;                   // stage chunks per wave
+    static constexpr int WSTAGE = 16 * SRC * 16;             // bytes of the weight stage
 };
 static_assert(GemmGeo<13>::SRC == 33 && GemmGeo<16>::SRC == 33 && GemmGeo<1>::SRC == 17, "stage stride");
 
-constexpr uint32_t kXUnit = 2 * 64 + 16;  // LDS bytes per 64-column unit of one X row (16 B padding)
+constexpr uint32_t kXUnit = 2 * 64 + 16;   // LDS bytes per 64-column unit of one X row (16 B padding)
+constexpr uint32_t kXRow = 4 * kXUnit + 16;  // LDS bytes per X row of one step
+
+template <int NB>
+struct GemmX {
+    static constexpr int CH = NB * 32;                       // X chunks per step (NB rows x 4 units x 8)
+    static constexpr int XL = (CH + 63) / 64;                // X loads per lane per step
+    static constexpr int BYTES = NB * kXRow;
+};
+
+template <int B, int NB>
+constexpr uint32_t gemm_stage_bytes() {
+    return static_cast<uint32_t>(GemmGeo<B>::WSTAGE > GemmX<NB>::BYTES ? GemmGeo<B>::WSTAGE : GemmX<NB>::BYTES);
+}
 
 struct GemmShape {
     uint32_t M, P;          // rows, units per row (K / 64)
-    uint32_t ks_units;      // K slice, in units (multiple of 4)
-    uint32_t tiles, kslices;
+    uint32_t tiles;         // ceil(M / 16)
+    uint32_t TW, KW;        // tiles per workgroup, parts of K per tile (TW * KW = 8)
+    uint32_t part_units;    // units per part of K (multiple of 4)
     uint32_t batch, ldx, ldy;
-    uint32_t xrow;          // LDS bytes per X row
-    int atomic;
 };
 
-// Loads of one step: row i of the tile, units [u0, u0 + nu); slot q = i * RCH + c.  Slots past the
-// row's last chunk are clamped to it, rows past M to row M - 1 (their lanes are inactive).
+// Weight loads of one step: row i of the tile, units [u0, u0 + nu); slot q = i * RCH + c.  Slots past
+// the row's last chunk are clamped to it, rows past M to row M - 1 (their lanes are inactive).
 template <int B>
-__device__ __forceinline__ void gemm_load(u32x4 (&v)[GemmGeo<B>::LPL], const u32x4 *__restrict__ w4,
-                                          uint32_t row0, uint32_t u0, uint32_t nu, const GemmShape &s,
-                                          int lane) {
+__device__ __forceinline__ void gemm_load_w(u32x4 (&v)[GemmGeo<B>::LPL], const u32x4 *__restrict__ w4,
+                                            uint32_t row0, uint32_t u0, uint32_t nu, const GemmShape &s,
+                                            int lane) {
     using G = GemmGeo<B>;
 #pragma unroll
     for (int j = 0; j < G::LPL; ++j) {
@@ -470,29 +485,48 @@ __device__ __forceinline__ void gemm_load(u32x4 (&v)[GemmGeo<B>::LPL], const u32
     }
 }
 
+// X loads of one step: chunk q = (n * 4 + u) * 8 + c.  Rows >= batch and units past the wave's range
+// read as zero, so the zero weights of inactive lanes never meet a non-finite X value.
+template <int NB>
+__device__ __forceinline__ void gemm_load_x(u32x4 (&v)[GemmX<NB>::XL], const u32x4 *__restrict__ X4,
+                                            uint32_t u0, uint32_t nu, const GemmShape &s, int lane) {
+#pragma unroll
+    for (int j = 0; j < GemmX<NB>::XL; ++j) {
+        const uint32_t q = j * 64 + lane;
+        const uint32_t n = q >> 5, u = (q >> 3) & 3, c = q & 7;
+        v[j] = (u32x4){0u, 0u, 0u, 0u};
+        if (q < static_cast<uint32_t>(GemmX<NB>::CH) && n < s.batch && u < nu)
+            v[j] = X4[(static_cast<uint64_t>(n) * s.ldx) / 8 + (u0 + u) * 8 + c];
+    }
+}
+
 template <int B, int NB, bool MFMA>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
     const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb, uint32_t U,
     const uint16_t *__restrict__ X, float *__restrict__ Y, const GemmShape s) {
     using G = GemmGeo<B>;
+    using XG = GemmX<NB>;
     constexpr int NT = 64 * kGemmWaves;
     constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;
+    constexpr uint32_t SB = gemm_stage_bytes<B, NB>();
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t kslice = blockIdx.x % s.kslices, group = blockIdx.x / s.kslices;
-    const uint32_t tile = group * kGemmWaves + wave;
-    const uint32_t su0 = kslice * s.ks_units;                 // first unit of the slice
-    const uint32_t su1 = min(su0 + s.ks_units, s.P);
-    unsigned char *xl = smem;                                  // [NB][slice units][144 B] (+16 B per row)
-    u32x4 *stage = reinterpret_cast<u32x4 *>(smem + NB * s.xrow) + wave * G::STAGE;
+    unsigned char *stb = smem + wave * SB;                    // this wave's stage (weights, then X)
+    u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
+    float *part = reinterpret_cast<float *>(smem + kGemmWaves * SB);  // [wave][16 rows][16 columns]
 
-    // Staging loads (branch-free codebook chunks; X chunks of the slice).  The whole slice width is
-    // staged for all NB rows, zeros past the last column and for rows >= batch, so the lanes of a
-    // partial step (whose weights are zero) never read uninitialised LDS: 0 * NaN would be NaN.
-    const uint32_t full = U / 8;
-    const uint32_t xu = su1 - su0, xw = s.ks_units, xch = NB * xw * 8;
+    const uint32_t tw = wave % s.TW, kr = wave / s.TW;
+    const uint32_t tile = blockIdx.x * s.TW + tw;
+    const bool has_tile = tile < s.tiles;
+    const uint32_t row0 = min(tile, s.tiles - 1) * 16;
+    const uint32_t ku0 = min(kr * s.part_units, s.P), ku1 = min(ku0 + s.part_units, s.P);
+    const uint32_t nsteps = has_tile ? (ku1 - ku0 + 3) / 4 : 0;
     const u32x4 *X4 = reinterpret_cast<const u32x4 *>(X);
+
+    // Codebook staging loads, branch-free, all issued before the barrier; the weight and X loads of
+    // the first step come after it (vector-memory data returns in issue order).
+    const uint32_t full = U / 8;
     u32x4 cw[CPT];
     uint32_t te[8];
 #pragma unroll
@@ -500,24 +534,13 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
         cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : X4[0];
 #pragma unroll
     for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
-    constexpr int XPT = 8;
-    u32x4 xv[XPT];
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const uint32_t q = i * NT + tid;  // q = (n * xw + u) * 8 + c
-        const uint32_t n = q / (xw * 8), rem = q - n * xw * 8;
-        if (q < xch && n < s.batch && rem < xu * 8) xv[i] = X4[(static_cast<uint64_t>(n) * s.ldx) / 8 + su0 * 8 + rem];
-        else xv[i] = (u32x4){0u, 0u, 0u, 0u};
-    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    const uint32_t row0 = min(tile, s.tiles - 1) * 16;
-    const uint32_t nsteps = (xu + 3) / 4;
-    u32x4 nxt[G::LPL];
-    gemm_load<B>(nxt, w4, row0, su0, min(4u, xu), s, lane);
-
+    u32x4 nw[G::LPL], nx[XG::XL];
+    gemm_load_w<B>(nw, w4, row0, ku0, min(4u, ku1 - ku0), s, lane);
+    gemm_load_x<NB>(nx, X4, ku0, min(4u, ku1 - ku0), s, lane);
     {
         uint32_t e[8];
 #pragma unroll
@@ -530,26 +553,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
             const uint32_t c = i * NT + tid;
             if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = c < full ? cw[i] : (c == full ? tail : pad);
         }
-#pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const uint32_t q = i * NT + tid;
-            const uint32_t n = q / (xw * 8), rem = q - n * xw * 8;
-            if (q < xch)
-                *reinterpret_cast<u32x4 *>(xl + n * s.xrow + (rem >> 3) * kXUnit + (rem & 7) * 16) = xv[i];
-        }
-        // slices wider than the first batch of X chunks (not reached by the shapes the host picks)
-        for (uint32_t q = XPT * NT + tid; q < xch; q += NT) {
-            const uint32_t n = q / (xw * 8), rem = q - n * xw * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (n < s.batch && rem < xu * 8) v = X4[(static_cast<uint64_t>(n) * s.ldx) / 8 + su0 * 8 + rem];
-            *reinterpret_cast<u32x4 *>(xl + n * s.xrow + (rem >> 3) * kXUnit + (rem & 7) * 16) = v;
-        }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (tile >= s.tiles) return;
 
     const int li = lane & 15, lg = lane >> 4;
     const bool row_ok = row0 + li < s.M;
@@ -559,15 +567,15 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
     for (int n = 0; n < NB; ++n) acc[n] = 0.f;
 
     for (uint32_t st = 0; st < nsteps; ++st) {
-        const uint32_t u0 = su0 + 4 * st;
-        // stage: row i's chunks at i * SRC; read back unit g of row li (qword offsets)
+        const uint32_t u0 = ku0 + 4 * st;
+        // weights: row i's chunks at i * SRC; read back unit g of row li (qword offsets)
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int j = 0; j < G::LPL; ++j) {
             const uint32_t q = j * 64 + lane;
             if (q < G::STEP_CH) {
                 const uint32_t i = q / G::RCH, c = q - i * G::RCH;
-                stage[i * G::SRC + c] = nxt[j];
+                stage[i * G::SRC + c] = nw[j];
             }
         }
         asm volatile("" ::: "memory");
@@ -581,54 +589,62 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
             d[2 * j] = t.x; d[2 * j + 1] = t.y;
         }
         asm volatile("" ::: "memory");
-        if (st + 1 < nsteps) gemm_load<B>(nxt, w4, row0, u0 + 4, min(4u, su1 - u0 - 4), s, lane);
+        // X over the same stage: row n at n * kXRow, unit u at u * kXUnit, chunk c at 16 c
+#pragma unroll
+        for (int j = 0; j < XG::XL; ++j) {
+            const uint32_t q = j * 64 + lane;
+            if (q < static_cast<uint32_t>(XG::CH))
+                *reinterpret_cast<u32x4 *>(stb + (q >> 5) * kXRow + ((q >> 3) & 3) * kXUnit + (q & 7) * 16) = nx[j];
+        }
+        asm volatile("" ::: "memory");
+        if (st + 1 < nsteps) {
+            const uint32_t nu = min(4u, ku1 - u0 - 4);
+            gemm_load_w<B>(nw, w4, row0, u0 + 4, nu, s, lane);
+            gemm_load_x<NB>(nx, X4, u0 + 4, nu, s, lane);
+        }
 
-        const uint32_t unit = u0 + lg;
-        const bool valid = row_ok && unit < su1;
-        const unsigned char *xb = xl + (unit - su0) * kXUnit;  // + n * xrow + 16 * f
+        const bool valid = row_ok && u0 + lg < ku1;
+        const unsigned char *xb = stb + lg * kXUnit;  // + n * kXRow + 16 * f
+        constexpr int XQ = MFMA ? 1 : NB;
         uint32_t wv[2][8];
+        u32x4 xq[2][XQ];
 #pragma unroll
         for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+#pragma unroll
+        for (int n = 0; n < XQ; ++n)
+            xq[0][n] = *reinterpret_cast<const u32x4 *>(xb + (MFMA ? li : n) * kXRow);
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
             if (f + 1 < 8) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) wv[(f + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (f + 1) + i)];
+#pragma unroll
+                for (int n = 0; n < XQ; ++n)
+                    xq[(f + 1) & 1][n] = *reinterpret_cast<const u32x4 *>(xb + (MFMA ? li : n) * kXRow + 16 * (f + 1));
             }
             const uint32_t *w = wv[f & 1];
             u32x4 wp = {w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
             if (!valid) wp = (u32x4){0u, 0u, 0u, 0u};
             if constexpr (MFMA) {
                 // B operand: lane (n = l % 16, g) holds X[n][unit g, fields 8f .. 8f + 7]
-                const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + li * s.xrow + 16 * f);
                 cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wp),
-                                                             __builtin_bit_cast(bf16x8_t, xq), cm, 0, 0, 0);
+                                                             __builtin_bit_cast(bf16x8_t, xq[f & 1][0]), cm, 0, 0, 0);
             } else {
 #pragma unroll
                 for (int n = 0; n < NB; ++n) {
-                    const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + n * s.xrow + 16 * f);
-                    acc[n] = dot2(wp.x, xq.x, acc[n]);
-                    acc[n] = dot2(wp.y, xq.y, acc[n]);
-                    acc[n] = dot2(wp.z, xq.z, acc[n]);
-                    acc[n] = dot2(wp.w, xq.w, acc[n]);
+                    const u32x4 x = xq[f & 1][n];
+                    acc[n] = dot2(wp.x, x.x, acc[n]);
+                    acc[n] = dot2(wp.y, x.y, acc[n]);
+                    acc[n] = dot2(wp.z, x.z, acc[n]);
+                    acc[n] = dot2(wp.w, x.w, acc[n]);
                 }
             }
         }
     }
 
-    if constexpr (MFMA) {
-        // Lane l holds C[row 4 * (l / 16) + r][column l % 16], r = 0..3.
-        if (static_cast<uint32_t>(li) < s.batch) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t row = row0 + 4 * lg + r;
-                if (row < s.M) {
-                    float *dst = Y + static_cast<uint64_t>(li) * s.ldy + row;
-                    if (s.atomic) atomicAdd(dst, cm[r]); else *dst = cm[r];
-                }
-            }
-        }
-    } else {
+    // This wave's partial tile P[row][column]: MFMA lane l holds rows 4 (l / 16) + r of column l % 16;
+    // VALU lanes with g = 0 hold row l % 16 of every column after summing the four k-groups.
+    if constexpr (!MFMA) {
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
             float v = acc[n];
@@ -636,15 +652,44 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
             v += __shfl_xor(v, 32, 64);
             acc[n] = v;
         }
-        if (lg == 0 && row_ok) {
+    }
+    if (s.KW == 1) {
+        if (!has_tile) return;
+        if constexpr (MFMA) {
+            if (static_cast<uint32_t>(li) < s.batch) {
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                if (static_cast<uint32_t>(n) < s.batch) {
-                    float *dst = Y + static_cast<uint64_t>(n) * s.ldy + row0 + li;
-                    if (s.atomic) atomicAdd(dst, acc[n]); else *dst = acc[n];
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t row = row0 + 4 * lg + r;
+                    if (row < s.M) Y[static_cast<uint64_t>(li) * s.ldy + row] = cm[r];
                 }
             }
+        } else if (lg == 0 && row_ok) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                if (static_cast<uint32_t>(n) < s.batch) Y[static_cast<uint64_t>(n) * s.ldy + row0 + li] = acc[n];
         }
+        return;
+    }
+    float *mine = part + wave * 256;
+    if constexpr (MFMA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mine[(4 * lg + r) * 16 + li] = cm[r];
+    } else if (lg == 0) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) mine[li * 16 + n] = acc[n];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kr != 0 || !has_tile) return;
+    // waves of part 0 sum the KW parts of their tile in a fixed order: lane l takes entries 4l .. 4l + 3
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t e = 4 * lane + k, row = e >> 4, n = e & 15;
+        float v = 0.f;
+        for (uint32_t p = 0; p < s.KW; ++p) v += part[(p * s.TW + tw) * 256 + e];
+        if (n < s.batch && n < static_cast<uint32_t>(NB) && row0 + row < s.M) Y[static_cast<uint64_t>(n) * s.ldy + row0 + row] = v;
     }
 }
 
@@ -688,13 +733,6 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const uint32_t *__restrict
             if (lane == 0 && n < static_cast<int>(batch)) Y[n * ldy + row] = v;
         }
     }
-}
-
-__global__ void k_fill_zero(float *__restrict__ Y, uint64_t ldy, uint32_t rows, uint32_t batch) {
-    const uint64_t total = static_cast<uint64_t>(rows) * batch;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride)
-        Y[(i / rows) * ldy + (i % rows)] = 0.f;
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -830,7 +868,6 @@ struct GemmArgs {
 
 template <int B, int NB, bool MFMA>
 bool gemm_launch(GemmArgs &a) {
-    using G = GemmGeo<B>;
     const cbk_tensor &t = a.t;
     const uint64_t P = t.cols / 64;
     GemmShape s{};
@@ -840,29 +877,17 @@ bool gemm_launch(GemmArgs &a) {
     s.batch = a.batch;
     s.ldx = static_cast<uint32_t>(a.ldx);
     s.ldy = static_cast<uint32_t>(a.ldy);
-    // LDS: codebook table (static) + X slice + 8 stages.  The widest slice that fits, narrowed so
-    // that the grid has at least one workgroup per CU when the tile count allows.
-    const uint64_t fixed = uint64_t(Table<B>::SIZE) * 2 + uint64_t(kGemmWaves) * G::STAGE * 16;
-    if (fixed + uint64_t(NB) * (4 * kXUnit + 16) > kLdsLimit) return false;
-    const uint64_t max_units = ((kLdsLimit - fixed) / NB - 16) / kXUnit / 4 * 4;
-    const uint64_t groups = (s.tiles + kGemmWaves - 1) / kGemmWaves;
-    const uint64_t want_slices = std::max<uint64_t>(1, (static_cast<uint64_t>(cu_count()) + groups - 1) / groups);
-    uint64_t units = std::min<uint64_t>(max_units, std::max<uint64_t>(4, ((P + want_slices - 1) / want_slices + 3) / 4 * 4));
-    // the X slice is staged with at most 8 chunks per thread in the first batch
-    units = std::min<uint64_t>(units, std::max<uint64_t>(4, uint64_t(8) * 64 * kGemmWaves / (8 * NB) / 4 * 4));
-    s.ks_units = static_cast<uint32_t>(units);
-    s.kslices = static_cast<uint32_t>((P + units - 1) / units);
-    s.xrow = static_cast<uint32_t>(units * kXUnit + 16);
-    s.atomic = s.kslices > 1;
-    const uint32_t lds = NB * s.xrow + kGemmWaves * G::STAGE * 16;
+    // Tiles per workgroup: the most (up to 8) that still leaves a workgroup for every CU; the rest
+    // of the 8 waves split K.
+    const uint64_t cus = static_cast<uint64_t>(cu_count());
+    s.TW = 1;
+    while (s.TW < kGemmWaves && (s.tiles + 2 * s.TW - 1) / (2 * s.TW) >= cus) s.TW *= 2;
+    s.KW = kGemmWaves / s.TW;
+    s.part_units = static_cast<uint32_t>(((P + s.KW - 1) / s.KW + 3) / 4 * 4);
+    const uint32_t lds = kGemmWaves * gemm_stage_bytes<B, NB>() + kGemmWaves * 256 * 4;
+    if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
     if (!allow_lds(k_gemm_tile<B, NB, MFMA>, lds)) return false;
-    const uint64_t grid = groups * s.kslices;
-    if (grid >= (uint64_t(1) << 31)) return false;
-    if (s.atomic) {
-        const uint64_t total = uint64_t(s.M) * a.batch;
-        hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<uint32_t>(std::min<uint64_t>(1024, (total + 255) / 256))),
-                           dim3(256), 0, a.s, a.Y, a.ldy, s.M, a.batch);
-    }
+    const uint64_t grid = (s.tiles + s.TW - 1) / s.TW;
     hipLaunchKernelGGL((k_gemm_tile<B, NB, MFMA>), dim3(static_cast<uint32_t>(grid)), dim3(64 * kGemmWaves), lds,
                        a.s, reinterpret_cast<const u32x4 *>(t.words), t.codebook, t.U, a.X, a.Y, s);
     return true;
