@@ -18,6 +18,8 @@ each tensor with its own codebook):
              down 8192x28672, N(0, 0.015); --layers distinct layers (default 2, 2.8 GB); one
              cbk_gemm_small launch per tensor.
   l70b_b1    the same tensors at batch 1, phases grouped as in llama7b.
+  decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors, one launch
+             per tensor; bytes = compressed reads + 2 bytes written per weight.
 
 The step is captured once in a HIP graph and replayed; the timed region is bracketed by
 torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
@@ -54,10 +56,10 @@ def workload_tensors(name: str, count: int, layers: int):
     """(specs, phases, batch, layer_count): specs are (cfg, layer, tensor) triples; phases are lists
     of spec indices launched together (one launch per phase, phases run in order)."""
     import synth
-    if name == "attn4096":
+    if name in ("attn4096", "decode4096"):
         t = synth.WORKLOADS[2][0][0]
         specs = [(2, layer, t) for layer in range(count)]
-        return specs, [[i] for i in range(len(specs))], 1, len(specs)
+        return specs, [[i] for i in range(len(specs))], (0 if name == "decode4096" else 1), len(specs)
     if name in ("llama7b", "l70b_b1", "l70b_b16"):
         cfg = 4 if name == "llama7b" else 5
         tensors, n_layers = synth.WORKLOADS[cfg]
@@ -137,7 +139,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1"])
+    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096"])
     ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers for mlp_b8 (8) and l70b_* (2)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -181,10 +183,12 @@ def main():
     import synth
     xs = {}
     for d in tensors:
-        if d.cols not in xs:
+        if d.cols not in xs and batch > 0:
             x = synth.workload_x(specs[0][0], d.cols, batch)
             xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
-    if batch == 1:
+    if batch == 0:
+        ys = [torch.empty((d.rows, d.cols), dtype=torch.bfloat16, device="cuda") for d in tensors]
+    elif batch == 1:
         xs = {k: v[0] for k, v in xs.items()}
         ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in tensors]
     else:
@@ -192,7 +196,9 @@ def main():
 
     def step():
         for ph in phases:
-            if batch > 1:
+            if batch == 0:
+                cbk.decode_bf16(tensors[ph[0]], out=ys[ph[0]])
+            elif batch > 1:
                 cbk.gemm_small(tensors[ph[0]], xs[tensors[ph[0]].cols], Y=ys[ph[0]])
             elif len(ph) == 1:
                 cbk.gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
@@ -240,19 +246,24 @@ def main():
     # algorithmic bytes: packed indices + codebook + Y for every tensor, X once per launch
     comp_total = sum(d.compressed_bytes + 4 * batch * d.rows for d in tensors) + \
         sum(2 * batch * tensors[ph[0]].cols for ph in phases)
+    if batch == 0:  # decode: compressed reads + the BF16 written
+        comp_total = sum(d.compressed_bytes + 2 * d.n for d in tensors)
     step_s = ms_step * 1e-3
     value = 2.0 * n_total / step_s / 1e9
     comp_gbps = comp_total / step_s / 1e9
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors})
-    kernel = "k_gemv_rows" if batch == 1 else ("k_gemm_tile" if batch <= 8 else "k_gemm_tile_mfma")
+    kernel = ("k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
+              else "k_gemm_tile" if batch <= 8 else "k_gemm_tile_mfma")
     kernel_key = f"{kernel}_b{bits[-1]}"
     traffic = profiling.traffic_for(kernel_key, args.workload)
 
     result = {
-        "metric": "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
-                  else f"fused codebook skinny-GEMM decompressed-weight GB/s at batch {batch}; % of HBM peak",
+        "metric": ("fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
+                   else "standalone codebook decode to BF16 in HBM, decompressed-weight GB/s; % of HBM peak"
+                   if batch == 0 else
+                   f"fused codebook skinny-GEMM decompressed-weight GB/s at batch {batch}; % of HBM peak"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

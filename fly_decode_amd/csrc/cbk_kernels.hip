@@ -45,7 +45,6 @@ namespace cbk {
 namespace {
 
 constexpr uint16_t kCorrupt = 0x7FC0;
-constexpr int kMaxWaves = 16;             // waves per workgroup, decode and GEMV
 constexpr uint32_t kLdsLimit = 160 * 1024;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -104,62 +103,58 @@ struct Table {
     static constexpr uint32_t SIZE = NCH * 8;               // entries
 };
 
-// Stage the codebook into LDS, entries >= U set to 0x7FC0, in batches of four 16-byte chunks per
-// thread: chunks wholly inside the codebook are 16-byte loads when it is 16-byte aligned, the
-// rest guarded 2-byte loads.  A batch's loads are all issued before any is used.
-// One 16-byte chunk (entries 8c .. 8c+7) of the padded table.
-__device__ __forceinline__ u32x4 cb_chunk(const uint16_t *__restrict__ cb, uint32_t U, uint32_t c,
-                                          uint32_t full) {
-    if (c < full) return reinterpret_cast<const u32x4 *>(cb)[c];
-    const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
-    if (8 * c >= U) return (u32x4){fill, fill, fill, fill};
-    uint32_t e[8];  // the chunk straddling U (every used chunk when cb is not 16-byte aligned)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = cb[min(8 * c + j, U - 1)];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = 8 * c + j < U ? e[j] : kCorrupt;
-    return (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-}
+// Codebook staging for the fast kernels: the table of Table<B>::NCH 16-byte chunks (entries >= U
+// read 0x7FC0) is loaded branch-free by NT threads, CPT chunks each: whole 16-byte loads clamped
+// into the codebook's whole chunks (from `dummy`, any readable 16-byte-aligned address, when it has
+// none) plus the eight entries of the chunk that straddles U, read by every thread from the same
+// addresses.  Kernels issue these loads in every wave before a barrier and their first weight loads
+// after it: vector-memory data returns in issue order, so the staging never waits behind the grid's
+// first burst of weight loads.  Needs a 16-byte-aligned codebook.
+template <int B, int NT>
+struct CbStage {
+    static constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;
+    u32x4 cw[CPT];
+    uint32_t te[8];
 
-template <int B>
-__device__ __forceinline__ void cb_load(u32x4 (&v)[4], const uint16_t *__restrict__ cb, uint32_t U,
-                                        uint32_t base, int tid, int nthreads) {
-    const uint32_t full = (reinterpret_cast<uintptr_t>(cb) & 15) == 0 ? U / 8 : 0;
+    __device__ __forceinline__ void issue(const uint16_t *__restrict__ cb, uint32_t U, const u32x4 *dummy, int tid) {
+        const uint32_t full = U / 8;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t c = base + k * nthreads + tid;
-        if (c < Table<B>::NCH) v[k] = cb_chunk(cb, U, c, full);
+        for (int i = 0; i < CPT; ++i)
+            cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : *dummy;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
     }
-}
 
-template <int B>
-__device__ __forceinline__ void cb_store(uint16_t *cbl, const u32x4 (&v)[4], uint32_t base, int tid,
-                                         int nthreads) {
+    __device__ __forceinline__ void store(uint16_t *cbl, uint32_t U, int tid) const {
+        const uint32_t full = U / 8;
+        uint32_t e[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t c = base + k * nthreads + tid;
-        if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = v[k];
+        for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? te[j] : kCorrupt;
+        const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
+        const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        const u32x4 pad = {fill, fill, fill, fill};
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const uint32_t c = i * NT + tid;
+            if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = c < full ? cw[i] : (c == full ? tail : pad);
+        }
     }
+};
+
+// Workgroup barrier on LDS only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-// Remaining batches (after the first), for tables larger than 4 chunks per thread.
-template <int B>
-__device__ __forceinline__ void cb_stage_rest(uint16_t *cbl, const uint16_t *__restrict__ cb,
-                                              uint32_t U, int tid, int nthreads) {
-    for (uint32_t base = 4 * nthreads; base < Table<B>::NCH; base += 4 * nthreads) {
-        u32x4 v[4];
-        cb_load<B>(v, cb, U, base, tid, nthreads);
-        cb_store<B>(cbl, v, base, tid, nthreads);
-    }
-}
-
-template <int B>
-__device__ __forceinline__ void stage_codebook(uint16_t *cbl, const uint16_t *__restrict__ cb,
-                                               uint32_t U, int tid, int nthreads) {
-    u32x4 v[4];
-    cb_load<B>(v, cb, U, 0, tid, nthreads);
-    cb_store<B>(cbl, v, 0, tid, nthreads);
-    cb_stage_rest<B>(cbl, cb, U, tid, nthreads);
+// Barrier that waits for nothing: orders the waves' instruction streams (used to put every wave's
+// staging loads ahead of any weight load in the CU's memory pipeline).
+__device__ __forceinline__ void issue_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Step loads: the chunks covering units [us, us + 64) start at chunk (us * UD) / 4; an odd-b
@@ -207,56 +202,77 @@ __device__ __forceinline__ void transpose_step(uint32_t (&d)[U64<B>::UD], const 
 }
 
 // ------------------------------------------------------------------------------ fast decode
-// Flat: unit u decodes weights [64u, 64u + 64).  Waves own contiguous ranges of whole steps.
+// Unit u decodes weights [64u, 64u + 64).  Wave steps (64 units) are dealt round-robin to the
+// waves, so the grid reads the stream front to back.  A step's decoded 8 KB go back through the
+// wave's stage (the weights have been read out of it by then) and leave as fully coalesced 16-byte
+// stores.  Staging as in the GEMV: codebook loads before a barrier, the first weight step after it.
+constexpr int kDecodeWaves = 8;
+constexpr uint32_t kOutUnit = 2 * 64 + 16;  // LDS bytes per decoded unit (16 bytes of padding)
+
 template <int B>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_decode_fast(const u32x4 *__restrict__ w4,
-                                                                uint32_t nchunks,
-                                                                const uint16_t *__restrict__ cb,
-                                                                uint32_t U, uint16_t *__restrict__ out,
-                                                                uint64_t n, uint32_t T) {
+constexpr uint32_t decode_stage_bytes() {
+    return U64<B>::STAGE_CHUNKS * 16 > 64 * kOutUnit ? U64<B>::STAGE_CHUNKS * 16 : 64 * kOutUnit;
+}
+
+template <int B>
+__global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *__restrict__ w4,
+                                                                   uint32_t nchunks,
+                                                                   const uint16_t *__restrict__ cb,
+                                                                   uint32_t U, uint16_t *__restrict__ out,
+                                                                   uint64_t n, uint32_t T) {
     using G = U64<B>;
+    constexpr int NT = 64 * kDecodeWaves;
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
-    u32x4 *stage = reinterpret_cast<u32x4 *>(smem) + wave * G::STAGE_CHUNKS;
-
-    const uint32_t NW = gridDim.x * waves, gw = blockIdx.x * waves + wave;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned char *stb = smem + wave * decode_stage_bytes<B>();
+    u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
+    const uint32_t NW = gridDim.x * kDecodeWaves, gw = blockIdx.x * kDecodeWaves + wave;
     const uint32_t steps = (T + 63) / 64;
-    const uint32_t s0 = static_cast<uint64_t>(steps) * gw / NW;
-    const uint32_t s1 = static_cast<uint64_t>(steps) * (gw + 1) / NW;
-    stage_codebook<B>(cbl, cb, U, tid, blockDim.x);
-    u32x4 nxt[G::LPL];  // issued after the staging loads have been waited for (see k_gemv_fast)
-    if (s0 < s1) load_step<B>(nxt, w4, s0 * 64, nchunks, lane);
-    __syncthreads();
-    if (s0 >= s1) return;
 
-    for (uint32_t st = s0; st < s1; ++st) {
+    CbStage<B, NT> cs;
+    cs.issue(cb, U, w4, tid);
+    issue_barrier();
+    u32x4 nxt[G::LPL];
+    load_step<B>(nxt, w4, min(gw, steps - 1) * 64, nchunks, lane);
+    cs.store(cbl, U, tid);
+    lds_barrier();
+
+    for (uint32_t st = gw; st < steps; st += NW) {
         const uint32_t us = st * 64;
         uint32_t d[G::UD];
         transpose_step<B>(d, nxt, stage, us, lane);
-        if (st + 1 < s1) load_step<B>(nxt, w4, us + 64, nchunks, lane);
-        const uint32_t gu = us + lane;
-        if (gu >= T) continue;
-        const uint64_t base = static_cast<uint64_t>(gu) * 64;
+        if (st + NW < steps) load_step<B>(nxt, w4, (st + NW) * 64, nchunks, lane);
+        // decode this lane's unit into the stage (unit stride kOutUnit bytes)
         uint32_t wv[2][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
-        if (base + 64 <= n) {
-            u32x4 *o = reinterpret_cast<u32x4 *>(out + base);
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                if (g + 1 < 8) {
+        for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
-                }
-                const uint32_t *w = wv[g & 1];
-                o[g] = (u32x4){w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
+                for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
             }
-        } else {
-#pragma unroll
-            for (int f = 0; f < 64; ++f)
-                if (base + f < n) out[base + f] = cbl[unit_field<B>(d, f)];
+            const uint32_t *w = wv[g & 1];
+            *reinterpret_cast<u32x4 *>(stb + lane * kOutUnit + 16 * g) =
+                (u32x4){w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
         }
+        asm volatile("" ::: "memory");
+        // coalesced stores: chunk q = j * 64 + lane of the step (unit q / 8, 8 weights at (q % 8) * 8)
+        const uint64_t base = static_cast<uint64_t>(us) * 64;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t q = j * 64 + lane;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stb + (q >> 3) * kOutUnit + (q & 7) * 16);
+            const uint64_t e0 = base + 8ull * q;
+            if (e0 + 8 <= n) {
+                *reinterpret_cast<u32x4 *>(out + e0) = v;
+            } else if (e0 < n) {
+                const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+                for (uint32_t k = 0; k < 8 && e0 + k < n; ++k) out[e0 + k] = static_cast<uint16_t>(h[k >> 1] >> (16 * (k & 1)));
+            }
+        }
+        asm volatile("" ::: "memory");
     }
 }
 
@@ -304,7 +320,6 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
     constexpr int NT = 64 * kGemvWaves;
-    constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;  // codebook chunks per thread
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
@@ -324,56 +339,30 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
     const uint32_t NW = (grp.first_block[k + 1] - b0) * kGemvWaves;
     const uint32_t gw = (blockIdx.x - b0) * kGemvWaves + wave;
 
-    // Staging loads, branch-free: codebook chunks c = tid + NT * i (whole 16-byte loads clamped into
-    // the codebook, or from x when it has no whole chunk), the eight entries of the chunk that
-    // straddles U, and this thread's x chunks.  They are all issued, in every wave, before the
-    // barrier below; the weight loads come after it, so vector-memory data (returned in issue
-    // order) for the staging never waits behind the grid's first burst of weight loads.
+    // Staging loads (codebook and this thread's x chunks), issued in every wave before the first
+    // weight load.
     const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
-    const uint32_t full = U / 8, xch = P * 8;
-    u32x4 cw[CPT], xv[kXPerThread];
-    uint32_t te[8];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-        cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : x4[0];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
+    const uint32_t xch = P * 8;
+    CbStage<B, NT> cs;
+    cs.issue(cb, U, x4, tid);
+    u32x4 xv[kXPerThread];
 #pragma unroll
     for (int i = 0; i < kXPerThread; ++i)
         if (static_cast<uint32_t>(i * NT + tid) < xch) xv[i] = x4[i * NT + tid];
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    issue_barrier();
 
     // First weight step (clamped to the last row for a wave without rows, so the load is harmless).
     u32x4 nxt[G::LPL];
     const uint32_t r_first = min(gw, M - 1);
     load_row_step<B>(nxt, w4, r_first * P, min(64u, P), lane);
 
-    // Staging stores: entries >= U of the table read 0x7FC0.
-    {
-        uint32_t e[8];
+    cs.store(cbl, U, tid);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? te[j] : kCorrupt;
-        const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
-        const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-        const u32x4 pad = {fill, fill, fill, fill};
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const uint32_t c = i * NT + tid;
-            if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = c < full ? cw[i] : (c == full ? tail : pad);
-        }
-#pragma unroll
-        for (int i = 0; i < kXPerThread; ++i) {
-            const uint32_t q = i * NT + tid;
-            if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[i];
-        }
+    for (int i = 0; i < kXPerThread; ++i) {
+        const uint32_t q = i * NT + tid;
+        if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[i];
     }
-    // LDS-only barrier: the weight loads stay in flight.
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters unconstrained
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    lds_barrier();
     if (gw >= M) return;
 
     float a[4] = {0.f, 0.f, 0.f, 0.f};
@@ -507,7 +496,6 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
     using G = GemmGeo<B>;
     using XG = GemmX<NB>;
     constexpr int NT = 64 * kGemmWaves;
-    constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;
     constexpr uint32_t SB = gemm_stage_bytes<B, NB>();
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -524,40 +512,15 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
     const uint32_t nsteps = has_tile ? (ku1 - ku0 + 3) / 4 : 0;
     const u32x4 *X4 = reinterpret_cast<const u32x4 *>(X);
 
-    // Codebook staging loads, branch-free, all issued before the barrier; the weight and X loads of
-    // the first step come after it (vector-memory data returns in issue order).
-    const uint32_t full = U / 8;
-    u32x4 cw[CPT];
-    uint32_t te[8];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-        cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : X4[0];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
+    // Codebook staging loads before the barrier, the first step's weight and X loads after it.
+    CbStage<B, NT> cs;
+    cs.issue(cb, U, X4, tid);
+    issue_barrier();
     u32x4 nw[G::LPL], nx[XG::XL];
     gemm_load_w<B>(nw, w4, row0, ku0, min(4u, ku1 - ku0), s, lane);
     gemm_load_x<NB>(nx, X4, ku0, min(4u, ku1 - ku0), s, lane);
-    {
-        uint32_t e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? te[j] : kCorrupt;
-        const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
-        const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-        const u32x4 pad = {fill, fill, fill, fill};
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const uint32_t c = i * NT + tid;
-            if (c < Table<B>::NCH) reinterpret_cast<u32x4 *>(cbl)[c] = c < full ? cw[i] : (c == full ? tail : pad);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    cs.store(cbl, U, tid);
+    lds_barrier();
 
     const int li = lane & 15, lg = lane >> 4;
     const bool row_ok = row0 + li < s.M;
@@ -678,10 +641,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
 #pragma unroll
         for (int n = 0; n < NB; ++n) mine[li * 16 + n] = acc[n];
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    lds_barrier();
     if (kr != 0 || !has_tile) return;
     // waves of part 0 sum the KW parts of their tile in a fixed order: lane l takes entries 4l .. 4l + 3
 #pragma unroll
@@ -768,16 +728,6 @@ bool dispatch_b(int b, Args &args, std::integer_sequence<int, Bs...>) {
 }
 using AllB = std::integer_sequence<int, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>;
 
-// Waves per workgroup and grid for a persistent wave loop over `steps` 64-unit steps, when at
-// most `wfit` waves fit in one workgroup's LDS: one workgroup per CU for large problems, and for
-// small ones fewer waves per workgroup spread over all CUs.
-void shape_grid(uint64_t steps, uint32_t wfit, uint32_t &waves, uint32_t &grid) {
-    const uint64_t cus = static_cast<uint64_t>(cu_count());
-    const uint64_t total = std::max<uint64_t>(1, std::min<uint64_t>(steps, cus * wfit));
-    waves = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(wfit, (total + cus - 1) / cus)));
-    grid = static_cast<uint32_t>((total + waves - 1) / waves);
-}
-
 struct DecodeArgs {
     const cbk_tensor &t; uint16_t *out; hipStream_t s; cbk_status st;
 };
@@ -785,21 +735,18 @@ struct DecodeArgs {
 template <int B>
 struct DecodeRun {
     static bool run(DecodeArgs &a) {
-        using G = U64<B>;
         const cbk_tensor &t = a.t;
         const uint64_t n = t.rows * t.cols;
         const uint64_t T64 = (n + 63) / 64;
         const uint64_t nchunks = cbk_words_for(n, B) / 4;
-        if (T64 * G::UD / 4 + 64 * G::LPL >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
-        const uint32_t stage_bytes = G::STAGE_CHUNKS * 16;
-        const uint32_t budget = kLdsLimit - Table<B>::SIZE * 2;
-        const uint32_t wfit = std::min<uint32_t>(kMaxWaves, budget / stage_bytes);
-        if (wfit == 0) return false;
-        uint32_t waves, grid;
-        shape_grid((T64 + 63) / 64, wfit, waves, grid);
-        const uint32_t lds = waves * stage_bytes;
+        if (T64 * U64<B>::UD / 4 + 64 * U64<B>::LPL >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
+        if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
+        const uint32_t lds = kDecodeWaves * decode_stage_bytes<B>();
+        if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
         if (!allow_lds(k_decode_fast<B>, lds)) return false;
-        hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(64 * waves), lds, a.s,
+        const uint64_t steps = (T64 + 63) / 64;
+        const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(cu_count(), (steps + kDecodeWaves - 1) / kDecodeWaves)));
+        hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(64 * kDecodeWaves), lds, a.s,
                            reinterpret_cast<const u32x4 *>(t.words), static_cast<uint32_t>(nchunks),
                            t.codebook, t.U, a.out, n, static_cast<uint32_t>(T64));
         a.st = launched();
