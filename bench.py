@@ -117,7 +117,7 @@ def cpu_baseline(specs, seconds: float, threads: int):
     ab = np.zeros(t.rows, dtype=np.float64)
     chunk = max(1, t.rows // (threads * 4))
     spans = [(r, min(t.rows, r + chunk)) for r in range(0, t.rows, chunk)]
-    while t_total < seconds and used < 64:
+    while t_total < seconds and used < 4096:
         t0 = time.perf_counter()
         with cf.ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(lambda s: oracle.gemv_rows_into(e, x, s[0], s[1], y, ab), spans))
