@@ -106,30 +106,32 @@ struct Table {
 // Codebook staging for the fast kernels: the table of Table<B>::NCH 16-byte chunks (entries >= U
 // read 0x7FC0) is loaded branch-free by NT threads, CPT chunks each: whole 16-byte loads clamped
 // into the codebook's whole chunks (from `dummy`, any readable 16-byte-aligned address, when it has
-// none) plus the eight entries of the chunk that straddles U, read by every thread from the same
-// addresses.  Kernels issue these loads in every wave before a barrier and their first weight loads
+// none) plus the eight entries of the chunk that straddles U, one per lane in lanes 0..7 of every
+// wave and broadcast with readlane.  Kernels issue these loads in every wave before a barrier and their first weight loads
 // after it: vector-memory data returns in issue order, so the staging never waits behind the grid's
 // first burst of weight loads.  Needs a 16-byte-aligned codebook.
 template <int B, int NT>
 struct CbStage {
     static constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;
     u32x4 cw[CPT];
-    uint32_t te[8];
+    uint32_t te;  // lane j < 8: entry 8 * full + j (clamped into the codebook)
 
     __device__ __forceinline__ void issue(const uint16_t *__restrict__ cb, uint32_t U, const u32x4 *dummy, int tid) {
         const uint32_t full = U / 8;
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
             cw[i] = full ? reinterpret_cast<const u32x4 *>(cb)[min(static_cast<uint32_t>(i * NT + tid), full - 1)] : *dummy;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) te[e] = cb[min(8 * full + e, U - 1)];
+        te = cb[min(8 * full + (tid & 7), U - 1)];
     }
 
     __device__ __forceinline__ void store(uint16_t *cbl, uint32_t U, int tid) const {
         const uint32_t full = U / 8;
         uint32_t e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = 8 * full + j < U ? te[j] : kCorrupt;
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t v = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(te), j));
+            e[j] = 8 * full + j < U ? v : kCorrupt;
+        }
         const uint32_t fill = static_cast<uint32_t>(kCorrupt) * 0x10001u;
         const u32x4 tail = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
         const u32x4 pad = {fill, fill, fill, fill};
@@ -314,7 +316,7 @@ __device__ __forceinline__ void load_row_step(u32x4 (&v)[U64<B>::LPL], const u32
         v[j] = w4[c0 + min(static_cast<uint32_t>(j * 64 + lane), last)];
 }
 
-template <int B>
+template <int B, bool GROUP>
 __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup grp,
                                                                const uint16_t *__restrict__ x) {
     using G = U64<B>;
@@ -327,16 +329,22 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
 
-    // This workgroup's tensor: count the group boundaries at or below blockIdx.x (uniform).
+    // This workgroup's tensor (uniform).  A single-tensor launch reads only t[0]: one round of
+    // kernel-argument loads.  A grouped launch counts the group boundaries at or below blockIdx.x,
+    // then reads that tensor's fields.
     uint32_t k = 0;
+    if constexpr (GROUP) {
 #pragma unroll
-    for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
-    const GemvTensor T = grp.t[k];
+        for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
+    }
+    const GemvTensor &T = grp.t[k];
     const u32x4 *w4 = T.w4;
     const uint16_t *cb = T.cb;
+    float *yt = T.y;
     const uint32_t M = T.M, U = T.U;
-    const uint32_t b0 = grp.first_block[k];
-    const uint32_t NW = (grp.first_block[k + 1] - b0) * kGemvWaves;
+    const uint32_t b0 = GROUP ? grp.first_block[k] : 0;
+    const uint32_t b1 = GROUP ? grp.first_block[k + 1] : gridDim.x;
+    const uint32_t NW = (b1 - b0) * kGemvWaves;
     const uint32_t gw = (blockIdx.x - b0) * kGemvWaves + wave;
 
     // Staging loads (codebook and this thread's x chunks), issued in every wave before the first
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
             float acc = (a[0] + a[1]) + (a[2] + a[3]);
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-            if (lane == 0) T.y[r] = acc;
+            if (lane == 0) yt[r] = acc;
             a[0] = a[1] = a[2] = a[3] = 0.f;
         }
         if (rn >= M) break;
@@ -777,7 +785,8 @@ struct GemvRun {
         }
         const uint64_t lds = P * (2 * 64 + 16) + uint64_t(kGemvWaves) * G::STAGE_CHUNKS * 16;
         if (lds + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
-        if (!allow_lds(k_gemv_rows<B>, static_cast<uint32_t>(lds))) return false;
+        auto kernel = a.count > 1 ? k_gemv_rows<B, true> : k_gemv_rows<B, false>;
+        if (!allow_lds(kernel, static_cast<uint32_t>(lds))) return false;
         // One workgroup per CU (fewer when there are not enough rows for every wave), at least one
         // per tensor.
         const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(
@@ -802,7 +811,7 @@ struct GemvRun {
             first = std::min(end, grid - (a.count - 1 - i));
         }
         grp.first_block[a.count] = grid;
-        hipLaunchKernelGGL(k_gemv_rows<B>, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds), a.s, grp, a.x);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds), a.s, grp, a.x);
         a.st = launched();
         return true;
     }
