@@ -13,10 +13,11 @@ each tensor with its own codebook):
              [q,k,v] and [gate,up] each one cbk_gemv_group launch (they share their input), o and
              down one cbk_gemv launch each.
   mlp_b8     Llama-7B MLP at batch 8: gate/up 11008x4096 and down 4096x11008, 0.02 * Student-t(4);
-             --layers distinct copies (default 8, 1.76 GB); one cbk_gemm_small launch per tensor.
+             --layers distinct copies (default 8, 1.76 GB); per layer [gate, up] one cbk_gemm_group
+             launch (they share X), down one cbk_gemm_small launch.
   l70b_b16   70B-shaped layer at batch 16: q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192,
-             down 8192x28672, N(0, 0.015); --layers distinct layers (default 2, 2.8 GB); one
-             cbk_gemm_small launch per tensor.
+             down 8192x28672, N(0, 0.015); --layers distinct layers (default 2, 2.8 GB); phases
+             grouped as in llama7b (cbk_gemm_group for [q, k, v] and [gate, up]).
   l70b_b1    the same tensors at batch 1, phases grouped as in llama7b.
   decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors, one launch
              per tensor; bytes = compressed reads + 2 bytes written per weight.
@@ -68,9 +69,6 @@ def workload_tensors(name: str, count: int, layers: int):
         for layer in range(n_layers):
             base = len(specs)
             specs += [(cfg, layer, t) for t in tensors]
-            if name == "l70b_b16":
-                phases += [[base + i] for i in range(len(tensors))]
-                continue
             names = [t.name for t in tensors]
             for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
                 phases.append([base + names.index(g) for g in group])
@@ -78,7 +76,8 @@ def workload_tensors(name: str, count: int, layers: int):
     if name == "mlp_b8":
         tensors, _ = synth.WORKLOADS[3]
         specs = [(3, layer, t) for layer in range(layers) for t in tensors]
-        return specs, [[i] for i in range(len(specs))], 8, layers
+        # per layer: [gate, up] share X (one grouped launch), then down
+        return specs, [p for l in range(layers) for p in ([3 * l, 3 * l + 1], [3 * l + 2])], 8, layers
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -198,8 +197,10 @@ def main():
         for ph in phases:
             if batch == 0:
                 cbk.decode_bf16(tensors[ph[0]], out=ys[ph[0]])
-            elif batch > 1:
+            elif batch > 1 and len(ph) == 1:
                 cbk.gemm_small(tensors[ph[0]], xs[tensors[ph[0]].cols], Y=ys[ph[0]])
+            elif batch > 1:
+                cbk.gemm_group([tensors[i] for i in ph], xs[tensors[ph[0]].cols], Ys=[ys[i] for i in ph])
             elif len(ph) == 1:
                 cbk.gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
             else:

@@ -73,6 +73,10 @@ def load_library():
         lib.cbk_gemm_small.restype = ctypes.c_int
         lib.cbk_gemm_small.argtypes = [tp, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        lib.cbk_gemm_group.restype = ctypes.c_int
+        lib.cbk_gemm_group.argtypes = [tp, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.POINTER(ctypes.c_uint64), ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -222,3 +226,24 @@ def gemm_small(t: Compressed, X, Y=None, stream=None):
                                          X.stride(0), batch, ctypes.c_void_p(Y.data_ptr() or None),
                                          Y.stride(0), _stream(stream)), "cbk_gemm_small")
     return Y
+
+
+def gemm_group(ts, X, Ys=None, stream=None):
+    """Ys[i][batch][rows_i] (float32) = X . W_i^T for tensors that share one bfloat16 X[batch][cols]
+    (row stride of X may exceed cols but must be a multiple of 8 for the fast kernels)."""
+    import torch
+    ts = list(ts)
+    if not ts:
+        return []
+    K = ts[0].cols
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or X.shape[1] != K or X.stride(1) != 1:
+        raise ValueError("X must be a [batch][cols] bfloat16 matrix with unit column stride")
+    batch = X.shape[0]
+    if Ys is None:
+        Ys = [torch.empty((batch, t.rows), dtype=torch.float32, device=X.device) for t in ts]
+    arr = (_Tensor * len(ts))(*[t._struct() for t in ts])
+    yp = (ctypes.c_void_p * len(ts))(*[Y.data_ptr() or None for Y in Ys])
+    ld = (ctypes.c_uint64 * len(ts))(*[Y.stride(0) for Y in Ys])
+    _check(load_library().cbk_gemm_group(arr, len(ts), ctypes.c_void_p(X.data_ptr() or None), X.stride(0),
+                                         batch, yp, ld, _stream(stream)), "cbk_gemm_group")
+    return Ys

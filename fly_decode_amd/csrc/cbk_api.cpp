@@ -192,4 +192,25 @@ cbk_status cbk_gemm_small(const cbk_tensor *t, const uint16_t *X, uint64_t ldx, 
     return cbk::launch_gemm(*t, X, ldx, batch, Y, ldy, static_cast<hipStream_t>(stream));
 }
 
+cbk_status cbk_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_t *X, uint64_t ldx,
+                          uint32_t batch, float *const *Ys, const uint64_t *ldys, void *stream) {
+    if (count == 0) return CBK_OK;
+    if (!ts || !Ys || !ldys || count > 4096) return CBK_E_INVALID;
+    if (batch < 1 || batch > 16) return CBK_E_INVALID;
+    const uint64_t K = ts[0].cols;
+    for (uint32_t i = 0; i < count; ++i) {
+        cbk_status st = check_tensor(&ts[i]);
+        if (st != CBK_OK) return st;
+        if (ts[i].cols != K) return CBK_E_INVALID;
+        if (ts[i].rows > 0 && (!Ys[i] || ldys[i] < ts[i].rows)) return CBK_E_INVALID;
+        if (Ys[i] && !aligned(Ys[i], 4)) return CBK_E_ALIGN;
+        if (ldys[i] > 0xFFFFFFFFull) return CBK_E_UNSUPPORTED;
+    }
+    if (K > 0 && !X) return CBK_E_INVALID;
+    if (ldx < K) return CBK_E_INVALID;
+    if (X && !aligned(X, 2)) return CBK_E_ALIGN;
+    if (ldx > 0xFFFFFFFFull) return CBK_E_UNSUPPORTED;
+    return cbk::launch_gemm_group(ts, count, X, ldx, batch, Ys, ldys, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -14,5 +14,7 @@ cbk_status launch_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_
                              float *const *ys, hipStream_t s);
 cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
                        float *Y, uint64_t ldy, hipStream_t s);
+cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_t *X, uint64_t ldx,
+                             uint32_t batch, float *const *Ys, const uint64_t *ldys, hipStream_t s);
 
 }  // namespace cbk

@@ -464,6 +464,20 @@ struct GemmShape {
     uint32_t batch, ldx, ldy;
 };
 
+// Up to kMaxGroup tensors that share X (same cols and width b) in one launch: workgroups
+// [first_block[t], first_block[t + 1]) belong to tensor t.
+struct GemmTensor {
+    const u32x4 *w4;
+    const uint16_t *cb;
+    float *Y;
+    uint32_t M, U, ldy, pad;
+};
+struct GemmGroup {
+    uint32_t first_block[kMaxGroup + 1];
+    uint32_t count, P, TW, KW, part_units, batch, ldx;
+    GemmTensor t[kMaxGroup];
+};
+
 // Weight loads of one step: row i of the tile, units [u0, u0 + nu); slot q = i * RCH + c.  Slots past
 // the row's last chunk are clamped to it, rows past M to row M - 1 (their lanes are inactive).
 template <int B>
@@ -498,9 +512,8 @@ __device__ __forceinline__ void gemm_load_x(u32x4 (&v)[GemmX<NB>::XL], const u32
 }
 
 template <int B, int NB, bool MFMA>
-__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
-    const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb, uint32_t U,
-    const uint16_t *__restrict__ X, float *__restrict__ Y, const GemmShape s) {
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup grp,
+                                                               const uint16_t *__restrict__ X) {
     using G = GemmGeo<B>;
     using XG = GemmX<NB>;
     constexpr int NT = 64 * kGemmWaves;
@@ -512,8 +525,28 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(
     u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
     float *part = reinterpret_cast<float *>(smem + kGemmWaves * SB);  // [wave][16 rows][16 columns]
 
+    // This workgroup's tensor (uniform): count the group boundaries at or below blockIdx.x.
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
+    const GemmTensor &T = grp.t[k];
+    const u32x4 *w4 = T.w4;
+    const uint16_t *cb = T.cb;
+    float *Y = T.Y;
+    const uint32_t U = T.U;
+    GemmShape s;
+    s.M = T.M;
+    s.P = grp.P;
+    s.tiles = (T.M + 15) / 16;
+    s.TW = grp.TW;
+    s.KW = grp.KW;
+    s.part_units = grp.part_units;
+    s.batch = grp.batch;
+    s.ldx = grp.ldx;
+    s.ldy = T.ldy;
+
     const uint32_t tw = wave % s.TW, kr = wave / s.TW;
-    const uint32_t tile = blockIdx.x * s.TW + tw;
+    const uint32_t tile = (blockIdx.x - grp.first_block[k]) * s.TW + tw;
     const bool has_tile = tile < s.tiles;
     const uint32_t row0 = min(tile, s.tiles - 1) * 16;
     const uint32_t ku0 = min(kr * s.part_units, s.P), ku1 = min(ku0 + s.part_units, s.P);
@@ -818,45 +851,59 @@ struct GemvRun {
 };
 
 struct GemmArgs {
-    const cbk_tensor &t; const uint16_t *X; uint64_t ldx; uint32_t batch; float *Y; uint64_t ldy;
-    hipStream_t s; cbk_status st;
+    const cbk_tensor *ts; uint32_t count; const uint16_t *X; uint64_t ldx; uint32_t batch;
+    float *const *Ys; const uint64_t *ldys; hipStream_t s; cbk_status st;
 };
 
+// One launch for up to kMaxGroup tensors of width B that share X (all have the same cols).
 template <int B, int NB, bool MFMA>
 bool gemm_launch(GemmArgs &a) {
-    const cbk_tensor &t = a.t;
-    const uint64_t P = t.cols / 64;
-    GemmShape s{};
-    s.M = static_cast<uint32_t>(t.rows);
-    s.P = static_cast<uint32_t>(P);
-    s.tiles = (s.M + 15) / 16;
-    s.batch = a.batch;
-    s.ldx = static_cast<uint32_t>(a.ldx);
-    s.ldy = static_cast<uint32_t>(a.ldy);
+    const uint64_t P = a.ts[0].cols / 64;
+    GemmGroup grp{};
+    grp.count = a.count;
+    grp.P = static_cast<uint32_t>(P);
+    grp.batch = a.batch;
+    grp.ldx = static_cast<uint32_t>(a.ldx);
+    uint64_t tiles = 0;
+    for (uint32_t i = 0; i < a.count; ++i) tiles += (a.ts[i].rows + 15) / 16;
     // Tiles per workgroup: the most (up to 8) that still leaves a workgroup for every CU; the rest
     // of the 8 waves split K.
     const uint64_t cus = static_cast<uint64_t>(cu_count());
-    s.TW = 1;
-    while (s.TW < kGemmWaves && (s.tiles + 2 * s.TW - 1) / (2 * s.TW) >= cus) s.TW *= 2;
-    s.KW = kGemmWaves / s.TW;
-    s.part_units = static_cast<uint32_t>(((P + s.KW - 1) / s.KW + 3) / 4 * 4);
+    grp.TW = 1;
+    while (grp.TW < kGemmWaves && (tiles + 2 * grp.TW - 1) / (2 * grp.TW) >= cus) grp.TW *= 2;
+    grp.KW = kGemmWaves / grp.TW;
+    grp.part_units = static_cast<uint32_t>(((P + grp.KW - 1) / grp.KW + 3) / 4 * 4);
     const uint32_t lds = kGemmWaves * gemm_stage_bytes<B, NB>() + kGemmWaves * 256 * 4;
     if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
     if (!allow_lds(k_gemm_tile<B, NB, MFMA>, lds)) return false;
-    const uint64_t grid = (s.tiles + s.TW - 1) / s.TW;
-    hipLaunchKernelGGL((k_gemm_tile<B, NB, MFMA>), dim3(static_cast<uint32_t>(grid)), dim3(64 * kGemmWaves), lds,
-                       a.s, reinterpret_cast<const u32x4 *>(t.words), t.codebook, t.U, a.X, a.Y, s);
+    uint64_t first = 0;
+    for (uint32_t i = 0; i < a.count; ++i) {
+        const cbk_tensor &t = a.ts[i];
+        grp.t[i] = GemmTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.Ys[i],
+                              static_cast<uint32_t>(t.rows), t.U, static_cast<uint32_t>(a.ldys[i]), 0};
+        grp.first_block[i] = static_cast<uint32_t>(first);
+        first += ((t.rows + 15) / 16 + grp.TW - 1) / grp.TW;
+    }
+    grp.first_block[a.count] = static_cast<uint32_t>(first);
+    if (first >= (uint64_t(1) << 31)) return false;
+    hipLaunchKernelGGL((k_gemm_tile<B, NB, MFMA>), dim3(static_cast<uint32_t>(first)), dim3(64 * kGemmWaves), lds,
+                       a.s, grp, a.X);
     return true;
 }
 
 template <int B>
 struct GemmRun {
     static bool run(GemmArgs &a) {
-        const cbk_tensor &t = a.t;
-        if (t.cols == 0 || t.cols % 64 != 0 || t.rows == 0) return false;
-        if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
-        if (t.rows * (t.cols / 64) >= (uint64_t(1) << 32)) return false;
-        if (a.ldx >= (uint64_t(1) << 32) || a.ldy >= (uint64_t(1) << 32)) return false;
+        const uint64_t K = a.ts[0].cols;
+        if (K == 0 || K % 64 != 0 || a.count == 0 || a.count > kMaxGroup) return false;
+        if (a.ldx >= (uint64_t(1) << 32)) return false;
+        for (uint32_t i = 0; i < a.count; ++i) {
+            const cbk_tensor &t = a.ts[i];
+            if (t.b != B || t.cols != K || t.rows == 0) return false;
+            if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
+            if (t.rows * (K / 64) >= (uint64_t(1) << 32)) return false;
+            if (a.ldys[i] >= (uint64_t(1) << 32)) return false;
+        }
         bool ok;
         switch (a.batch) {
             case 1: ok = gemm_launch<B, 1, false>(a); break;
@@ -884,13 +931,9 @@ cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s) {
     return launched();
 }
 
-cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
-                       float *Y, uint64_t ldy, hipStream_t s) {
+cbk_status launch_gemm_generic(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
+                               float *Y, uint64_t ldy, hipStream_t s) {
     const uint32_t M = static_cast<uint32_t>(t.rows), K = static_cast<uint32_t>(t.cols);
-    if (t.b > 0 && K > 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && ldx % 8 == 0) {
-        GemmArgs a{t, X, ldx, batch, Y, ldy, s, CBK_OK};
-        if (dispatch_b<GemmRun>(static_cast<int>(t.b), a, AllB{})) return a.st;
-    }
     const uint32_t grid = std::max(1u, std::min<uint32_t>((M + 3) / 4, 4096));
     if (batch <= 8)
         hipLaunchKernelGGL(k_gemm_generic<8>, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook,
@@ -899,6 +942,42 @@ cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uin
         hipLaunchKernelGGL(k_gemm_generic<16>, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook,
                            t.U, X, ldx, batch, Y, ldy, M, K);
     return launched();
+}
+
+cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_t *X, uint64_t ldx,
+                             uint32_t batch, float *const *Ys, const uint64_t *ldys, hipStream_t s) {
+    // Consecutive runs of tensors with the same width take one fast launch each (at most
+    // kMaxGroup tensors); anything the fast kernel declines runs the generic kernel.
+    const bool x_ok = (reinterpret_cast<uintptr_t>(X) & 15) == 0 && ldx % 8 == 0;
+    uint32_t i = 0;
+    while (i < count) {
+        uint32_t j = i + 1;
+        while (j < count && j - i < static_cast<uint32_t>(kMaxGroup) && ts[j].b == ts[i].b) ++j;
+        bool done = false;
+        if (ts[i].b > 0 && ts[i].cols > 0 && x_ok) {
+            GemmArgs a{ts + i, j - i, X, ldx, batch, Ys + i, ldys + i, s, CBK_OK};
+            if (dispatch_b<GemmRun>(static_cast<int>(ts[i].b), a, AllB{})) {
+                if (a.st != CBK_OK) return a.st;
+                done = true;
+            }
+        }
+        if (!done) {
+            for (uint32_t k = i; k < j; ++k) {
+                if (ts[k].rows == 0) continue;
+                cbk_status st = launch_gemm_generic(ts[k], X, ldx, batch, Ys[k], ldys[k], s);
+                if (st != CBK_OK) return st;
+            }
+        }
+        i = j;
+    }
+    return CBK_OK;
+}
+
+cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
+                       float *Y, uint64_t ldy, hipStream_t s) {
+    float *Ys[1] = {Y};
+    const uint64_t ldys[1] = {ldy};
+    return launch_gemm_group(&t, 1, X, ldx, batch, Ys, ldys, s);
 }
 
 cbk_status launch_gemv_generic(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s) {

@@ -135,6 +135,24 @@ cbk_status cbk_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *
 cbk_status cbk_gemm_small(const cbk_tensor *t, const uint16_t *X, uint64_t ldx, uint32_t batch,
                           float *Y, uint64_t ldy, void *stream);
 
+/*
+ * cbk_gemm_group -- GPU.  cbk_gemm_small for `count` tensors that share one input X (the
+ * query/key/value projections, or gate and up, of a layer at batch > 1):
+ * Ys[i][j][r] = sum_k W_i[r][k] * X[j][k] for j < batch.  Tensors of equal width b run in one
+ * launch (up to 8 per launch), so a small tensor (a 1024-row key projection, say) shares the
+ * machine with its neighbours instead of occupying a few CUs on its own; same source as
+ * cbk_gemv_group (the DFloat11 page, "How it works in practice": decompress a block's
+ * matrices together).
+ *   ts       host array of count tensors (device pointers inside), all with the same cols.
+ *   X, ldx, batch   as for cbk_gemm_small (shared by all tensors).
+ *   Ys       host array of count device pointers; Ys[i] is [batch][ldys[i]] fp32, 4-byte aligned.
+ *   ldys     host array of count leading dimensions, ldys[i] >= ts[i].rows.
+ * count == 0 is a no-op.  count > 4096, differing cols, a null array, ldys[i] < rows or any
+ * argument cbk_gemm_small would reject give the same status codes (checked before any launch).
+ */
+cbk_status cbk_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_t *X, uint64_t ldx,
+                          uint32_t batch, float *const *Ys, const uint64_t *ldys, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemv_group", "cbk_gemm_small", "cbk_bits_for",
+    for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemv_group", "cbk_gemm_small", "cbk_gemm_group", "cbk_bits_for",
               "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str"]:
         assert n in names
 
@@ -149,6 +149,21 @@ def test_gpu_calls_validate_before_any_hip_call(cbk):
     ys_bad = (ctypes.c_void_p * 2)(0x8000, 0x9002)
     assert lib.cbk_gemv_group((cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 4, 8, 5, 3)),
                               2, X, ys_bad, None) == 3
+    # grouped GEMM: shared X, per-tensor Y and leading dimension
+    pair = (cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 6, 8, 5, 3))
+    ld = (ctypes.c_uint64 * 2)(4, 6)
+    assert lib.cbk_gemm_group(pair, 0, X, 8, 2, ys, ld, None) == 0                # count 0: no-op
+    assert lib.cbk_gemm_group(None, 2, X, 8, 2, ys, ld, None) == 1
+    assert lib.cbk_gemm_group(pair, 2, X, 8, 2, ys, None, None) == 1              # null ldys
+    assert lib.cbk_gemm_group(pair, 2, X, 8, 0, ys, ld, None) == 1                # batch 0
+    assert lib.cbk_gemm_group(pair, 2, X, 8, 17, ys, ld, None) == 1               # batch 17
+    assert lib.cbk_gemm_group(pair, 2, X, 4, 2, ys, ld, None) == 1                # ldx < cols
+    assert lib.cbk_gemm_group(pair, 2, X, 8, 2, ys, (ctypes.c_uint64 * 2)(4, 5), None) == 1  # ldy < rows
+    assert lib.cbk_gemm_group(arr, 2, X, 16, 2, ys, ld, None) == 1                # differing cols
+    assert lib.cbk_gemm_group(pair, 2, ctypes.c_void_p(0x4001), 8, 2, ys, ld, None) == 3
+    assert lib.cbk_gemm_group(pair, 2, X, 8, 2, ys_bad, ld, None) == 3            # Y not 4-byte aligned
+    assert lib.cbk_gemm_group((cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 4, 8, 5, 2)),
+                              2, X, 8, 2, ys, ld, None) == 1                      # bad b
     # zero-size tensors are accepted without work (no HIP call either)
     assert lib.cbk_gemv(T(rows=0, cols=0, U=0, b=0, cb=0, words=0), None, None, None) == 0
     assert lib.cbk_decode_bf16(T(rows=0, cols=9, U=0, b=0, cb=0, words=0), None, None) == 0

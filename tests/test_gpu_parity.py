@@ -344,3 +344,48 @@ def test_gemv_group_7b_layer_phases(env, oracle_mod):
             ref, absb = oracle_mod.gemv(oracle_mod.encode(w), x, rows=rows)
             got = y.cpu().numpy().astype(np.float64)[rows]
             assert np.all(np.abs(got - ref) <= TOL * absb)
+
+
+@pytest.mark.parametrize("batch", [3, 8, 16])
+def test_gemm_group_matches_oracle_and_single_calls(env, oracle_mod, batch):
+    """Tensors sharing X: different row counts (a partial tile, a 1024-row tensor next to larger
+    ones), padded Y leading dimensions, a width change mid-list (two launches) and more than
+    eight tensors (several launches).  Each Y matches the oracle within tolerance (the tile split,
+    and with it the summation order, depends on the whole group, so no bitwise match with the
+    single call is expected), and the padding columns of Y are left alone."""
+    torch, cbk = env
+    K = 1024
+    rows = [300, 64, 1024, 7, 513]
+    ws = [synth.gaussian_bf16((r, K), 0.02, seed=[66, i]) for i, r in enumerate(rows)]
+    ws.append(synth.with_distinct_count(200 * K, 200, seed=[67], exponents=(120, 130)).reshape(200, K))
+    ws += [synth.gaussian_bf16((96, K), 0.02, seed=[68, i]) for i in range(4)]
+    X = synth.activations_bf16(batch, K, 69)
+    Xd = _up(torch, X, torch.bfloat16)
+    ds = [cbk.encode(w).to("cuda") for w in ws]
+    assert len({d.b for d in ds}) >= 2 and len(ds) > 8
+    bufs = [torch.full((batch, d.rows + 5), -1.0, dtype=torch.float32, device="cuda") for d in ds]
+    Ys = cbk.gemm_group(ds, Xd, Ys=[b[:, :d.rows] for b, d in zip(bufs, ds)])
+    torch.cuda.synchronize()
+    for w, d, Y, buf in zip(ws, ds, Ys, bufs):
+        ref, absb = oracle_mod.gemm(oracle_mod.encode(w), X)
+        got = Y.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - ref) <= TOL * absb)
+        single = cbk.gemm_small(d, Xd).cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(single - ref) <= TOL * absb)
+        assert bool((buf[:, d.rows:] == -1.0).all())  # padding columns untouched
+
+
+def test_gemm_group_70b_qkv_batch16(env, oracle_mod):
+    """The q/k/v phase of a 70B-shaped layer at batch 16 as one grouped launch, sampled rows."""
+    torch, cbk = env
+    group = [t for t in synth.WORKLOADS[5][0] if t.name in ("q", "k", "v")]
+    ws = [synth.workload_tensor(5, 0, t) for t in group]
+    X = synth.workload_x(5, group[0].cols, batch=16)
+    ds = [cbk.encode(w).to("cuda") for w in ws]
+    Ys = cbk.gemm_group(ds, _up(torch, X, torch.bfloat16))
+    torch.cuda.synchronize()
+    for w, t, Y in zip(ws, group, Ys):
+        rows = np.random.default_rng(70).choice(t.rows, 32, replace=False)
+        ref, absb = oracle_mod.gemm(oracle_mod.encode(w), X, rows=rows)
+        got = Y.cpu().numpy().astype(np.float64)[:, rows]
+        assert np.all(np.abs(got - ref) <= TOL * absb)
