@@ -389,3 +389,18 @@ def test_gemm_group_70b_qkv_batch16(env, oracle_mod):
         ref, absb = oracle_mod.gemm(oracle_mod.encode(w), X, rows=rows)
         got = Y.cpu().numpy().astype(np.float64)[:, rows]
         assert np.all(np.abs(got - ref) <= TOL * absb)
+
+
+@pytest.mark.parametrize("b", [14, 15])
+def test_gemm_wide_codebooks_fast_path(env, oracle_mod, b):
+    """b = 14 and 15: the largest widths whose table still fits the fast kernels' LDS budget
+    (a 32 or 64 KB table next to the stages), at batch 5 (VALU) and 16 (MFMA)."""
+    U = 2 ** (b - 1) + 11
+    for batch in (5, 16):
+        for rows, cols in [(40, 1024), (9, 640)]:
+            n = max(rows * cols, U)
+            rows = (n + cols - 1) // cols
+            w = synth.with_distinct_count(rows * cols, U, seed=[71, b, cols],
+                                          exponents=synth.finite_exponents(U)).reshape(rows, cols)
+            X = synth.activations_bf16(batch, cols, 72)
+            _gemm_check(env, oracle_mod, w, X)
