@@ -24,10 +24,10 @@
 //    issued before any weight load (vector-memory data returns in issue order).
 //  * One workgroup of 8 waves per CU shares one codebook table and one copy of x.
 //
-// Skinny GEMM: a wave owns a 16-row tile and walks K in steps of 4 units (128 fields) per row;
-// lane (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded tile to
-// v_mfma_f32_16x16x32_bf16; batches up to 8 use v_dot2c on the vector ALUs.  When K is split
-// across waves the partial sums are added into a zero-filled Y with fp32 atomics.
+// Skinny GEMM: a wave owns a 16-row tile and walks its part of K in steps of 4 units (256 fields)
+// per row; lane (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded
+// tile to v_mfma_f32_16x16x32_bf16; batches up to 8 use v_dot2c on the vector ALUs.  When K is
+// split across the waves of a workgroup, their partial tiles are added in LDS in a fixed order.
 //
 // Generic kernels (any b and shape, runtime field extraction straight from global memory) cover
 // b == 0, rows whose length is not a multiple of 64, misaligned operands and shapes beyond the
@@ -105,11 +105,12 @@ struct Table {
 
 // Codebook staging for the fast kernels: the table of Table<B>::NCH 16-byte chunks (entries >= U
 // read 0x7FC0) is loaded branch-free by NT threads, CPT chunks each: whole 16-byte loads clamped
-// into the codebook's whole chunks (from `dummy`, any readable 16-byte-aligned address, when it has
-// none) plus the eight entries of the chunk that straddles U, one per lane in lanes 0..7 of every
-// wave and broadcast with readlane.  Kernels issue these loads in every wave before a barrier and their first weight loads
-// after it: vector-memory data returns in issue order, so the staging never waits behind the grid's
-// first burst of weight loads.  Needs a 16-byte-aligned codebook.
+// into the codebook's whole chunks (from `dummy`, any readable 16-byte-aligned address, when it
+// has none) plus the eight entries of the chunk that straddles U, one per lane in lanes 0..7 of
+// every wave and broadcast with readlane.  Kernels issue these loads in every wave before a
+// barrier and their first weight loads after it: vector-memory data returns in issue order, so
+// the staging never waits behind the grid's first burst of weight loads.  Needs a 16-byte-aligned
+// codebook.
 template <int B, int NT>
 struct CbStage {
     static constexpr int CPT = (Table<B>::NCH + NT - 1) / NT;
@@ -478,8 +479,9 @@ struct GemmGroup {
     GemmTensor t[kMaxGroup];
 };
 
-// Weight loads of one step: row i of the tile, units [u0, u0 + nu); slot q = i * RCH + c.  Slots past
-// the row's last chunk are clamped to it, rows past M to row M - 1 (their lanes are inactive).
+// Weight loads of one step: row i of the tile, units [u0, u0 + nu) with u0 + nu <= P and nu >= 1;
+// slot q = i * RCH + c.  Slots past the row's last chunk are clamped to it, rows past M to row
+// M - 1 (their lanes are inactive), so every address lies inside the stream.
 template <int B>
 __device__ __forceinline__ void gemm_load_w(u32x4 (&v)[GemmGeo<B>::LPL], const u32x4 *__restrict__ w4,
                                             uint32_t row0, uint32_t u0, uint32_t nu, const GemmShape &s,
@@ -558,7 +560,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
     cs.issue(cb, U, X4, tid);
     issue_barrier();
     u32x4 nw[G::LPL], nx[XG::XL];
-    gemm_load_w<B>(nw, w4, row0, ku0, min(4u, ku1 - ku0), s, lane);
+    // A wave whose part of K is empty (ku0 == P) still issues the first weight loads, branch-free,
+    // but from the last unit of its row so that they stay inside the stream; their data is unused.
+    gemm_load_w<B>(nw, w4, row0, min(ku0, s.P - 1), max(1u, min(4u, ku1 - ku0)), s, lane);
     gemm_load_x<NB>(nx, X4, ku0, min(4u, ku1 - ku0), s, lane);
     cs.store(cbl, U, tid);
     lds_barrier();
