@@ -868,13 +868,21 @@ bool gemm_launch(GemmArgs &a) {
     grp.P = static_cast<uint32_t>(P);
     grp.batch = a.batch;
     grp.ldx = static_cast<uint32_t>(a.ldx);
-    uint64_t tiles = 0;
-    for (uint32_t i = 0; i < a.count; ++i) tiles += (a.ts[i].rows + 15) / 16;
-    // Tiles per workgroup: the most (up to 8) that still leaves a workgroup for every CU; the rest
-    // of the 8 waves split K.
+    // Tiles per workgroup TW (the other 8 / TW waves split K).  The stages and the table take most
+    // of the LDS, so one workgroup runs per CU and the grid drains in ceil(blocks / CUs) rounds of
+    // workgroups that each take TW tiles by the whole of K: pick the TW with the fewest rounds x TW,
+    // and of equal ones the largest (fewer workgroups and partial-sum reductions).
     const uint64_t cus = static_cast<uint64_t>(cu_count());
-    grp.TW = 1;
-    while (grp.TW < kGemmWaves && (tiles + 2 * grp.TW - 1) / (2 * grp.TW) >= cus) grp.TW *= 2;
+    uint64_t best = ~uint64_t(0);
+    for (uint32_t tw = 1; tw <= static_cast<uint32_t>(kGemmWaves); tw *= 2) {
+        uint64_t blocks = 0;
+        for (uint32_t i = 0; i < a.count; ++i) blocks += ((a.ts[i].rows + 15) / 16 + tw - 1) / tw;
+        const uint64_t cost = (blocks + cus - 1) / cus * tw;
+        if (cost <= best) {
+            best = cost;
+            grp.TW = tw;
+        }
+    }
     grp.KW = kGemmWaves / grp.TW;
     grp.part_units = static_cast<uint32_t>(((P + grp.KW - 1) / grp.KW + 3) / 4 * 4);
     const uint32_t lds = kGemmWaves * gemm_stage_bytes<B, NB>() + kGemmWaves * 256 * 4;

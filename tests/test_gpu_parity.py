@@ -295,6 +295,18 @@ def test_gemm_70b_batch16_sampled(env, oracle_mod):
             _gemm_check(env, oracle_mod, w, X, rows=rows)
 
 
+
+@pytest.mark.parametrize("batch", [8, 16])
+def test_gemm_many_tiles_sampled(env, oracle_mod, batch):
+    """16384- and 32768-row tensors (1024 and 2048 row tiles), where a 256-CU device gives each
+    workgroup 4 and 8 tiles; at 4 tiles K = 768 splits into a 512- and a 256-column part.  Sampled
+    rows, the first and the last included, against the oracle."""
+    for rows in (16384, 32768):
+        w = synth.gaussian_bf16((rows, 768), 0.02, seed=[73, rows])
+        X = synth.activations_bf16(batch, 768, 74)
+        sample = np.concatenate([[0, rows - 1], np.random.default_rng(75).choice(rows, 254, replace=False)])
+        _gemm_check(env, oracle_mod, w, X, rows=sample)
+
 def test_repeated_launches_are_identical(env):
     torch, cbk = env
     w = synth.gaussian_bf16((4096, 4096), 0.02, seed=[57])
