@@ -160,15 +160,31 @@ __device__ __forceinline__ void issue_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Step loads: the chunks covering units [us, us + 64) start at chunk (us * UD) / 4; an odd-b
-// step may start half-way into a chunk (the stage read then skips one qword).  Addresses past
-// the stream are clamped to its last chunk: those lanes feed only inactive units.
+// Raw buffer resource over `bytes` bytes from `base`, which must be the same in every lane of the
+// wave.  Loads at offsets at or past `bytes` return zeros without a memory access, so weight loads
+// need neither clamped addresses nor branches, and the base and its arithmetic stay in scalar
+// registers.  Word 3 sets the 32-bit data format, which this chip's untyped buffer loads need.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 rsrc_load(__amdgpu_buffer_rsrc_t rs, uint32_t byte_offset) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(byte_offset), 0, 0);
+}
+
+// Step loads: the chunks covering units [us, us + nl) start at chunk (us * UD) / 4; an odd-b step
+// may start half-way into a chunk (the stage read then skips one qword).  Lane l loads chunks
+// 64 j + l of the step; chunks past the step (or past the stream's nchunks) read as zero, and a
+// wave with no step (valid false) touches no memory.  `us` must be wave-uniform.
 template <int B>
 __device__ __forceinline__ void load_step(u32x4 (&v)[U64<B>::LPL], const u32x4 *__restrict__ w4,
-                                          uint32_t us, uint32_t nchunks, int lane) {
-    const uint32_t c0 = static_cast<uint32_t>((static_cast<uint64_t>(us) * U64<B>::UD) >> 2);
+                                          uint32_t us, uint32_t nl, uint64_t nchunks, bool valid, int lane) {
+    const uint64_t c0 = (static_cast<uint64_t>(us) * U64<B>::UD) >> 2;
+    const uint64_t c1 = min((static_cast<uint64_t>(us + nl) * U64<B>::UD + 3) >> 2, nchunks);
+    const auto rs = wave_rsrc(w4 + c0, valid && c1 > c0 ? static_cast<uint32_t>(c1 - c0) * 16u : 0u);
 #pragma unroll
-    for (int j = 0; j < U64<B>::LPL; ++j) v[j] = w4[min(c0 + j * 64 + lane, nchunks - 1)];
+    for (int j = 0; j < U64<B>::LPL; ++j) v[j] = rsrc_load(rs, static_cast<uint32_t>(j * 64 + lane) * 16u);
 }
 
 // Write a step to the wave's stage and read back this lane's unit (UD dwords).
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
     constexpr int NT = 64 * kDecodeWaves;
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     unsigned char *stb = smem + wave * decode_stage_bytes<B>();
     u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
     const uint32_t NW = gridDim.x * kDecodeWaves, gw = blockIdx.x * kDecodeWaves + wave;
@@ -237,7 +253,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
     cs.issue(cb, U, w4, tid);
     issue_barrier();
     u32x4 nxt[G::LPL];
-    load_step<B>(nxt, w4, min(gw, steps - 1) * 64, nchunks, lane);
+    load_step<B>(nxt, w4, gw * 64, 64, nchunks, gw < steps, lane);
     cs.store(cbl, U, tid);
     lds_barrier();
 
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
         const uint32_t us = st * 64;
         uint32_t d[G::UD];
         transpose_step<B>(d, nxt, stage, us, lane);
-        if (st + NW < steps) load_step<B>(nxt, w4, (st + NW) * 64, nchunks, lane);
+        if (st + NW < steps) load_step<B>(nxt, w4, (st + NW) * 64, 64, nchunks, true, lane);
         // decode this lane's unit into the stage (unit stride kOutUnit bytes)
         uint32_t wv[2][8];
 #pragma unroll
@@ -304,19 +320,6 @@ struct GemvGroup {
     GemvTensor t[kMaxGroup];
 };
 
-// Loads of the wave step (row r, step j): the chunks holding units [rP + 64j, rP + 64j + nl).
-// Loads past the step's last chunk are clamped to it (same cache line, no extra traffic).
-template <int B>
-__device__ __forceinline__ void load_row_step(u32x4 (&v)[U64<B>::LPL], const u32x4 *__restrict__ w4,
-                                              uint32_t us, uint32_t nl, int lane) {
-    const uint64_t c0 = (static_cast<uint64_t>(us) * U64<B>::UD) >> 2;
-    const uint64_t c1 = (static_cast<uint64_t>(us + nl) * U64<B>::UD + 3) >> 2;
-    const uint32_t last = static_cast<uint32_t>(c1 - 1 - c0);
-#pragma unroll
-    for (int j = 0; j < U64<B>::LPL; ++j)
-        v[j] = w4[c0 + min(static_cast<uint32_t>(j * 64 + lane), last)];
-}
-
 template <int B, bool GROUP>
 __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup grp,
                                                                const uint16_t *__restrict__ x) {
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
     const uint32_t P = grp.P, S = grp.S;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
 
     // This workgroup's tensor (uniform).  A single-tensor launch reads only t[0]: one round of
@@ -360,10 +363,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
         if (static_cast<uint32_t>(i * NT + tid) < xch) xv[i] = x4[i * NT + tid];
     issue_barrier();
 
-    // First weight step (clamped to the last row for a wave without rows, so the load is harmless).
+    // First weight step (no memory access for a wave without rows).
     u32x4 nxt[G::LPL];
-    const uint32_t r_first = min(gw, M - 1);
-    load_row_step<B>(nxt, w4, r_first * P, min(64u, P), lane);
+    load_step<B>(nxt, w4, min(gw, M - 1) * P, min(64u, P), ~uint64_t(0), gw < M, lane);
 
     cs.store(cbl, U, tid);
 #pragma unroll
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
         // next step of this wave: the rest of the row, then row r + NW
         const bool row_end = j + 1 == S;
         const uint32_t rn = row_end ? r + NW : r, jn = row_end ? 0 : j + 1;
-        if (rn < M) load_row_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), lane);
+        if (rn < M) load_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), ~uint64_t(0), true, lane);
 
         const uint32_t cu = 64 * j + lane;  // this lane's unit within the row
         if (cu < P) {
@@ -471,6 +473,7 @@ struct GemmTensor {
     const u32x4 *w4;
     const uint16_t *cb;
     float *Y;
+    uint64_t nch;  // 16-byte chunks of the index stream
     uint32_t M, U, ldy, pad;
 };
 struct GemmGroup {
@@ -479,22 +482,27 @@ struct GemmGroup {
     GemmTensor t[kMaxGroup];
 };
 
-// Weight loads of one step: row i of the tile, units [u0, u0 + nu) with u0 + nu <= P and nu >= 1;
-// slot q = i * RCH + c.  Slots past the row's last chunk are clamped to it, rows past M to row
-// M - 1 (their lanes are inactive), so every address lies inside the stream.
+// Weight loads of one step: slot q = i * RCH + c holds chunk c of row i's segment, which starts at
+// the chunk holding unit u0 of row row0 + i.  One buffer resource per tile (base: the chunk of
+// unit u0 of row row0, wave-uniform; extent: to the stream's end), so slots past a segment read the
+// stream's next chunks and rows past M read zeros; the lanes that decode them are inactive.  The
+// host keeps 16 * P * UD dwords below 2^29 so the 32-bit byte offsets cannot wrap.
 template <int B>
 __device__ __forceinline__ void gemm_load_w(u32x4 (&v)[GemmGeo<B>::LPL], const u32x4 *__restrict__ w4,
-                                            uint32_t row0, uint32_t u0, uint32_t nu, const GemmShape &s,
+                                            uint64_t nch, uint32_t row0, uint32_t u0, const GemmShape &s,
                                             int lane) {
     using G = GemmGeo<B>;
+    const uint64_t d0 = (static_cast<uint64_t>(row0) * s.P + u0) * G::UD;  // dwords, wave-uniform
+    const uint64_t b0 = d0 >> 2;
+    const uint32_t ph = static_cast<uint32_t>(d0 & 3u);
+    const uint64_t left = nch > b0 ? (nch - b0) * 16 : 0;
+    const auto rs = wave_rsrc(w4 + b0, static_cast<uint32_t>(min(left, static_cast<uint64_t>(0x7FFFFFF0u))));
+    const uint32_t row_dw = s.P * static_cast<uint32_t>(G::UD);
 #pragma unroll
     for (int j = 0; j < G::LPL; ++j) {
         const uint32_t q = min(static_cast<uint32_t>(j * 64 + lane), static_cast<uint32_t>(G::STEP_CH - 1));
         const uint32_t i = q / G::RCH, c = q - i * G::RCH;
-        const uint64_t r = min(row0 + i, s.M - 1);
-        const uint64_t d0 = (r * s.P + u0) * G::UD, d1 = d0 + static_cast<uint64_t>(nu) * G::UD;
-        const uint64_t c0 = d0 >> 2, c1 = (d1 + 3) >> 2;
-        v[j] = w4[c0 + min(static_cast<uint64_t>(c), c1 - c0 - 1)];
+        v[j] = rsrc_load(rs, (((ph + i * row_dw) >> 2) + c) * 16u);
     }
 }
 
@@ -522,7 +530,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
     constexpr uint32_t SB = gemm_stage_bytes<B, NB>();
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     unsigned char *stb = smem + wave * SB;                    // this wave's stage (weights, then X)
     u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
     float *part = reinterpret_cast<float *>(smem + kGemmWaves * SB);  // [wave][16 rows][16 columns]
@@ -560,9 +568,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
     cs.issue(cb, U, X4, tid);
     issue_barrier();
     u32x4 nw[G::LPL], nx[XG::XL];
-    // A wave whose part of K is empty (ku0 == P) still issues the first weight loads, branch-free,
-    // but from the last unit of its row so that they stay inside the stream; their data is unused.
-    gemm_load_w<B>(nw, w4, row0, min(ku0, s.P - 1), max(1u, min(4u, ku1 - ku0)), s, lane);
+    // A wave whose part of K is empty (ku0 == P) still issues the first weight loads, branch-free;
+    // they read the next row (or zeros past the stream) and their data is unused.
+    gemm_load_w<B>(nw, w4, T.nch, row0, ku0, s, lane);
     gemm_load_x<NB>(nx, X4, ku0, min(4u, ku1 - ku0), s, lane);
     cs.store(cbl, U, tid);
     lds_barrier();
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
         asm volatile("" ::: "memory");
         if (st + 1 < nsteps) {
             const uint32_t nu = min(4u, ku1 - u0 - 4);
-            gemm_load_w<B>(nw, w4, row0, u0 + 4, nu, s, lane);
+            gemm_load_w<B>(nw, w4, T.nch, row0, u0 + 4, s, lane);
             gemm_load_x<NB>(nx, X4, u0 + 4, nu, s, lane);
         }
 
@@ -892,7 +900,8 @@ bool gemm_launch(GemmArgs &a) {
     for (uint32_t i = 0; i < a.count; ++i) {
         const cbk_tensor &t = a.ts[i];
         grp.t[i] = GemmTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.Ys[i],
-                              static_cast<uint32_t>(t.rows), t.U, static_cast<uint32_t>(a.ldys[i]), 0};
+                              cbk_words_for(t.rows * t.cols, B) / 4, static_cast<uint32_t>(t.rows), t.U,
+                              static_cast<uint32_t>(a.ldys[i]), 0};
         grp.first_block[i] = static_cast<uint32_t>(first);
         first += ((t.rows + 15) / 16 + grp.TW - 1) / grp.TW;
     }
@@ -914,6 +923,7 @@ struct GemmRun {
             if (t.b != B || t.cols != K || t.rows == 0) return false;
             if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
             if (t.rows * (K / 64) >= (uint64_t(1) << 32)) return false;
+            if ((K / 64) * GemmGeo<B>::UD * 16 >= (uint64_t(1) << 29)) return false;  // tile offsets fit 31 bits
             if (a.ldys[i] >= (uint64_t(1) << 32)) return false;
         }
         bool ok;
