@@ -84,6 +84,20 @@ __device__ __forceinline__ uint32_t unit_field(const uint32_t *d, int f) {
     return __builtin_amdgcn_alignbit(d[w + 1], d[w], s) & U64<B>::mask;
 }
 
+// Table entry for field f of a unit held in registers: the field is extracted straight into its
+// byte offset 2 * field (shift by one less, mask b bits one place up), two VALU operations whether
+// or not the field crosses a word boundary.
+template <int B>
+__device__ __forceinline__ uint32_t unit_gather(const uint16_t *tbl, const uint32_t *d, int f) {
+    const int bit = f * B, w = bit >> 5, s = bit & 31;
+    constexpr uint32_t m2 = U64<B>::mask << 1;
+    uint32_t off;
+    if (s == 0) off = (d[w] << 1) & m2;
+    else if (s + B <= 32) off = (d[w] >> (s - 1)) & m2;
+    else off = __builtin_amdgcn_alignbit(d[w + 1], d[w], s - 1) & m2;
+    return *reinterpret_cast<const uint16_t *>(reinterpret_cast<const unsigned char *>(tbl) + off);
+}
+
 // Field i of a stream, runtime width (generic kernels).
 __device__ __forceinline__ uint32_t stream_field(const uint32_t *__restrict__ words, uint32_t b,
                                                  uint64_t i) {
@@ -265,30 +279,35 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
         // decode this lane's unit into the stage (unit stride kOutUnit bytes)
         uint32_t wv[2][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+        for (int i = 0; i < 8; ++i) wv[0][i] = unit_gather<B>(cbl, d, i);
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             if (g + 1 < 8) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
+                for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (g + 1) + i);
             }
             const uint32_t *w = wv[g & 1];
             *reinterpret_cast<u32x4 *>(stb + lane * kOutUnit + 16 * g) =
                 (u32x4){w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
         }
         asm volatile("" ::: "memory");
-        // coalesced stores: chunk q = j * 64 + lane of the step (unit q / 8, 8 weights at (q % 8) * 8)
-        const uint64_t base = static_cast<uint64_t>(us) * 64;
+        // Coalesced stores: chunk q = j * 64 + lane of the step (unit q / 8, 8 weights at (q % 8) * 8)
+        // through a resource over the step's whole output chunks, so chunks past the tensor's end
+        // are dropped by the hardware; the one partial chunk a tensor can end with (n % 8 != 0) is
+        // written element by element by the lane that holds it.
+        const uint64_t base = static_cast<uint64_t>(us) * 64;  // first weight of the step
+        const uint64_t left = n - base;                          // > 0 for every step
+        const uint32_t full = static_cast<uint32_t>(min(left / 8, static_cast<uint64_t>(512)));
+        const auto rs = wave_rsrc(out + base, full * 16u);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t q = j * 64 + lane;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(stb + (q >> 3) * kOutUnit + (q & 7) * 16);
-            const uint64_t e0 = base + 8ull * q;
-            if (e0 + 8 <= n) {
-                *reinterpret_cast<u32x4 *>(out + e0) = v;
-            } else if (e0 < n) {
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<int>(q * 16u), 0, 0);
+            if (left < 4096 && (left & 7) != 0 && q == full) {
                 const uint32_t h[4] = {v.x, v.y, v.z, v.w};
-                for (uint32_t k = 0; k < 8 && e0 + k < n; ++k) out[e0 + k] = static_cast<uint16_t>(h[k >> 1] >> (16 * (k & 1)));
+                for (uint32_t k = 0; k < static_cast<uint32_t>(left & 7); ++k)
+                    out[base + 8ull * q + k] = static_cast<uint16_t>(h[k >> 1] >> (16 * (k & 1)));
             }
         }
         asm volatile("" ::: "memory");
@@ -392,12 +411,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
             const unsigned char *xb = xl + cu * XU;
             uint32_t wv[2][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+            for (int i = 0; i < 8; ++i) wv[0][i] = unit_gather<B>(cbl, d, i);
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
                 if (g + 1 < 8) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (g + 1) + i)];
+                    for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (g + 1) + i);
                 }
                 const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + 16 * g);
                 const uint32_t *w = wv[g & 1];
@@ -625,7 +644,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
         uint32_t wv[2][8];
         u32x4 xq[2][XQ];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wv[0][i] = cbl[unit_field<B>(d, i)];
+        for (int i = 0; i < 8; ++i) wv[0][i] = unit_gather<B>(cbl, d, i);
 #pragma unroll
         for (int n = 0; n < XQ; ++n)
             xq[0][n] = *reinterpret_cast<const u32x4 *>(xb + (MFMA ? li : n) * kXRow);
@@ -633,7 +652,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
         for (int f = 0; f < 8; ++f) {
             if (f + 1 < 8) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) wv[(f + 1) & 1][i] = cbl[unit_field<B>(d, 8 * (f + 1) + i)];
+                for (int i = 0; i < 8; ++i) wv[(f + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (f + 1) + i);
 #pragma unroll
                 for (int n = 0; n < XQ; ++n)
                     xq[(f + 1) & 1][n] = *reinterpret_cast<const u32x4 *>(xb + (MFMA ? li : n) * kXRow + 16 * (f + 1));

@@ -108,6 +108,22 @@ def test_decode_tail_and_misaligned_output(env):
     assert int(buf[0].view(torch.int16)) == 0 and not buf[1 + 12345:].view(torch.int16).any()
 
 
+
+def test_decode_fast_path_writes_nothing_past_the_end(env):
+    """16-byte-aligned output (fast kernel) followed by a guard region: lengths ending inside a
+    16-byte chunk, just past a wave step of 4096 weights, and shorter than one chunk."""
+    torch, cbk = env
+    for n in (4096 * 3 + 5, 8 * 700 + 1, 4096 + 8, 7, 3 * 4096):
+        w = synth.with_distinct_count(n, min(n, 3000), seed=[34, n]).reshape(1, n)
+        d = cbk.encode(w).to("cuda")
+        buf = torch.full((n + 64,), -7, dtype=torch.int16, device="cuda")
+        assert buf.data_ptr() % 16 == 0
+        cbk.decode_bf16(d, out=buf[:n].view(torch.bfloat16).view(1, n))
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        assert np.array_equal(got[:n].view(np.uint16), w.reshape(-1)), n
+        assert bool((got[n:] == -7).all()), n
+
 def test_decode_corrupt_index_is_memory_safe(env, oracle_mod):
     torch, cbk = env
     w = synth.with_distinct_count(4096, 5000 // 2, seed=[33]).reshape(32, 128)
