@@ -14,8 +14,11 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are disabled: hipcc would otherwise form v_pk_{add,mul,fma}_f32 from
-# ordinary float code.  (The host pass prints that it ignores the feature; harmless.)
-DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# ordinary float code.  (The host pass prints that it ignores the feature; harmless.)  Kernels
+# have their leading scalar arguments preloaded into SGPRs (up to 16 dwords), so a wave's first
+# address computations do not wait for a kernel-argument load.
+DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
 SOURCES = [("cbk_api.cpp", False), ("cbk_kernels.hip", True)]

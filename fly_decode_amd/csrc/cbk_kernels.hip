@@ -249,10 +249,9 @@ constexpr uint32_t decode_stage_bytes() {
 
 template <int B>
 __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *__restrict__ w4,
-                                                                   uint32_t nchunks,
                                                                    const uint16_t *__restrict__ cb,
-                                                                   uint32_t U, uint16_t *__restrict__ out,
-                                                                   uint64_t n, uint32_t T) {
+                                                                   uint16_t *__restrict__ out, uint64_t n,
+                                                                   uint32_t nchunks, uint32_t U, uint32_t T) {
     using G = U64<B>;
     constexpr int NT = 64 * kDecodeWaves;
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
@@ -339,36 +338,22 @@ struct GemvGroup {
     GemvTensor t[kMaxGroup];
 };
 
-template <int B, bool GROUP>
-__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup grp,
-                                                               const uint16_t *__restrict__ x) {
+// Rows of one tensor for workgroup `blk` of the tensor's `nblk` workgroups.  Every argument is
+// uniform across the workgroup.
+template <int B>
+__device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb,
+                                          float *__restrict__ yt, const uint16_t *__restrict__ x, uint32_t M,
+                                          uint32_t U, uint32_t P, uint32_t S, uint32_t blk, uint32_t nblk) {
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
     constexpr int NT = 64 * kGemvWaves;
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
-    const uint32_t P = grp.P, S = grp.S;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
-
-    // This workgroup's tensor (uniform).  A single-tensor launch reads only t[0]: one round of
-    // kernel-argument loads.  A grouped launch counts the group boundaries at or below blockIdx.x,
-    // then reads that tensor's fields.
-    uint32_t k = 0;
-    if constexpr (GROUP) {
-#pragma unroll
-        for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
-    }
-    const GemvTensor &T = grp.t[k];
-    const u32x4 *w4 = T.w4;
-    const uint16_t *cb = T.cb;
-    float *yt = T.y;
-    const uint32_t M = T.M, U = T.U;
-    const uint32_t b0 = GROUP ? grp.first_block[k] : 0;
-    const uint32_t b1 = GROUP ? grp.first_block[k + 1] : gridDim.x;
-    const uint32_t NW = (b1 - b0) * kGemvWaves;
-    const uint32_t gw = (blockIdx.x - b0) * kGemvWaves + wave;
+    const uint32_t NW = nblk * kGemvWaves;
+    const uint32_t gw = blk * kGemvWaves + wave;
 
     // Staging loads (codebook and this thread's x chunks), issued in every wave before the first
     // weight load.
@@ -437,6 +422,30 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const GemvGroup g
         r = rn;
         j = jn;
     }
+}
+
+// One tensor per launch.  The arguments are plain scalars so that the code object can have them
+// preloaded into scalar registers: the first address computations then wait for no load.
+template <int B>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const u32x4 *__restrict__ w4,
+                                                               const uint16_t *__restrict__ cb,
+                                                               float *__restrict__ y,
+                                                               const uint16_t *__restrict__ x, uint32_t M,
+                                                               uint32_t U, uint32_t P, uint32_t S) {
+    gemv_rows<B>(w4, cb, y, x, M, U, P, S, blockIdx.x, gridDim.x);
+}
+
+// Up to kMaxGroup tensors that share x: this workgroup's tensor is found by counting the group
+// boundaries at or below blockIdx.x (uniform).
+template <int B>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows_group(const GemvGroup grp,
+                                                                     const uint16_t *__restrict__ x) {
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
+    const GemvTensor &T = grp.t[k];
+    const uint32_t b0 = grp.first_block[k], b1 = grp.first_block[k + 1];
+    gemv_rows<B>(T.w4, T.cb, T.y, x, T.M, T.U, grp.P, grp.S, blockIdx.x - b0, b1 - b0);
 }
 
 // ------------------------------------------------------------------------- fast skinny GEMM
@@ -819,8 +828,8 @@ struct DecodeRun {
         const uint64_t steps = (T64 + 63) / 64;
         const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(cu_count(), (steps + kDecodeWaves - 1) / kDecodeWaves)));
         hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(64 * kDecodeWaves), lds, a.s,
-                           reinterpret_cast<const u32x4 *>(t.words), static_cast<uint32_t>(nchunks),
-                           t.codebook, t.U, a.out, n, static_cast<uint32_t>(T64));
+                           reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.out, n,
+                           static_cast<uint32_t>(nchunks), t.U, static_cast<uint32_t>(T64));
         a.st = launched();
         return true;
     }
@@ -849,8 +858,10 @@ struct GemvRun {
         }
         const uint64_t lds = P * (2 * 64 + 16) + uint64_t(kGemvWaves) * G::STAGE_CHUNKS * 16;
         if (lds + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
-        auto kernel = a.count > 1 ? k_gemv_rows<B, true> : k_gemv_rows<B, false>;
-        if (!allow_lds(kernel, static_cast<uint32_t>(lds))) return false;
+        const bool group = a.count > 1;
+        if (!(group ? allow_lds(k_gemv_rows_group<B>, static_cast<uint32_t>(lds))
+                    : allow_lds(k_gemv_rows<B>, static_cast<uint32_t>(lds))))
+            return false;
         // One workgroup per CU (fewer when there are not enough rows for every wave), at least one
         // per tensor.
         const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(
@@ -875,7 +886,14 @@ struct GemvRun {
             first = std::min(end, grid - (a.count - 1 - i));
         }
         grp.first_block[a.count] = grid;
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds), a.s, grp, a.x);
+        if (group) {
+            hipLaunchKernelGGL(k_gemv_rows_group<B>, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds),
+                               a.s, grp, a.x);
+        } else {
+            const GemvTensor &t = grp.t[0];
+            hipLaunchKernelGGL(k_gemv_rows<B>, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds), a.s,
+                               t.w4, t.cb, t.y, a.x, t.M, t.U, grp.P, grp.S);
+        }
         a.st = launched();
         return true;
     }
