@@ -256,7 +256,7 @@ def main():
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors})
     kernel = ("k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
-              else "k_gemm_tile" if batch <= 8 else "k_gemm_tile_mfma")
+              else "k_gemm_valu" if batch <= 8 else "k_gemm_mfma")
     kernel_key = f"{kernel}_b{bits[-1]}"
     traffic = profiling.traffic_for(kernel_key, args.workload)
 

@@ -451,14 +451,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows_group(const GemvG
 // ------------------------------------------------------------------------- fast skinny GEMM
 // Y[n][M] = X[n][K] . W^T for n = batch <= 16.  A wave owns a 16-row tile and a range of K; a wave
 // step covers 256 columns (4 units of 64 fields) of the tile's 16 rows, and lane (i = l % 16,
-// g = l / 16) decodes unit g of row i.  With each step's weight chunks the wave loads the step's
-// columns of X (all batch rows) and passes both through its private LDS stage: the weights are
-// read back per lane, then X is written over them and read per 8-field group, one group ahead of
-// use.  VALU path (batch <= 8): the 16 lanes of a k-group read the same X addresses (broadcast)
-// and v_dot2c accumulates each column.  MFMA path (batch 9..16): the decoded 8-field groups are the
-// A operand of v_mfma_f32_16x16x32_bf16 and X supplies B.  When the tiles alone cannot fill the
-// CUs, the 8 waves of a workgroup take 8/TW parts of K for TW tiles and add their partial sums in
-// LDS, so every Y element is written once (no atomics; results do not depend on timing).
+// g = l / 16) decodes unit g of row i from the wave's private LDS stage.  Batch 9..16
+// (k_gemm_mfma): the step's columns of X (all batch rows) are written over the weights once those
+// have been read back, and the decoded 8-field groups are the A operand of
+// v_mfma_f32_16x16x32_bf16 with X as B.  Batch 1..8 (k_gemm_valu, below) keeps X in registers.
+// When the tiles alone cannot fill the CUs, the 8 waves of a workgroup take 8/TW parts of K for
+// TW tiles and add their partial sums in LDS, so every Y element is written once (no atomics;
+// results do not depend on timing).
 constexpr int kGemmWaves = 8;
 
 template <int B>
@@ -549,9 +548,10 @@ __device__ __forceinline__ void gemm_load_x(u32x4 (&v)[GemmX<NB>::XL], const u32
     }
 }
 
-template <int B, int NB, bool MFMA>
-__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup grp,
+template <int B>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_mfma(const GemmGroup grp,
                                                                const uint16_t *__restrict__ X) {
+    constexpr int NB = 16;
     using G = GemmGeo<B>;
     using XG = GemmX<NB>;
     constexpr int NT = 64 * kGemmWaves;
@@ -606,9 +606,6 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
     const int li = lane & 15, lg = lane >> 4;
     const bool row_ok = row0 + li < s.M;
     f32x4_t cm = {0.f, 0.f, 0.f, 0.f};
-    float acc[NB];
-#pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = 0.f;
 
     for (uint32_t st = 0; st < nsteps; ++st) {
         const uint32_t u0 = ku0 + 4 * st;
@@ -647,67 +644,311 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
             gemm_load_x<NB>(nx, X4, u0 + 4, nu, s, lane);
         }
 
-        const bool valid = row_ok && u0 + lg < ku1;
-        const unsigned char *xb = stb + lg * kXUnit;  // + n * kXRow + 16 * f
-        constexpr int XQ = MFMA ? 1 : NB;
+            const bool valid = row_ok && u0 + lg < ku1;
+        const unsigned char *xb = stb + lg * kXUnit + li * kXRow;  // X row li, unit g: + 16 * f
         uint32_t wv[2][8];
-        u32x4 xq[2][XQ];
+        u32x4 xq[2];
 #pragma unroll
         for (int i = 0; i < 8; ++i) wv[0][i] = unit_gather<B>(cbl, d, i);
-#pragma unroll
-        for (int n = 0; n < XQ; ++n)
-            xq[0][n] = *reinterpret_cast<const u32x4 *>(xb + (MFMA ? li : n) * kXRow);
+        xq[0] = *reinterpret_cast<const u32x4 *>(xb);
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
             if (f + 1 < 8) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) wv[(f + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (f + 1) + i);
-#pragma unroll
-                for (int n = 0; n < XQ; ++n)
-                    xq[(f + 1) & 1][n] = *reinterpret_cast<const u32x4 *>(xb + (MFMA ? li : n) * kXRow + 16 * (f + 1));
+                xq[(f + 1) & 1] = *reinterpret_cast<const u32x4 *>(xb + 16 * (f + 1));
             }
             const uint32_t *w = wv[f & 1];
             u32x4 wp = {w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
             if (!valid) wp = (u32x4){0u, 0u, 0u, 0u};
-            if constexpr (MFMA) {
-                // B operand: lane (n = l % 16, g) holds X[n][unit g, fields 8f .. 8f + 7]
-                cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wp),
-                                                             __builtin_bit_cast(bf16x8_t, xq[f & 1][0]), cm, 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    const u32x4 x = xq[f & 1][n];
-                    acc[n] = dot2(wp.x, x.x, acc[n]);
-                    acc[n] = dot2(wp.y, x.y, acc[n]);
-                    acc[n] = dot2(wp.z, x.z, acc[n]);
-                    acc[n] = dot2(wp.w, x.w, acc[n]);
-                }
-            }
+            // B operand: lane (n = l % 16, g) holds X[n][unit g, fields 8f .. 8f + 7]
+            cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wp),
+                                                         __builtin_bit_cast(bf16x8_t, xq[f & 1]), cm, 0, 0, 0);
         }
     }
 
-    // This wave's partial tile P[row][column]: MFMA lane l holds rows 4 (l / 16) + r of column l % 16;
-    // VALU lanes with g = 0 hold row l % 16 of every column after summing the four k-groups.
-    if constexpr (!MFMA) {
+    // This wave's partial tile: MFMA lane l holds rows 4 (l / 16) + r of column l % 16.
+    if (s.KW == 1) {
+        if (!has_tile) return;
+        if (static_cast<uint32_t>(li) < s.batch) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n) {
-            float v = acc[n];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[n] = v;
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t row = row0 + 4 * lg + r;
+                if (row < s.M) Y[static_cast<uint64_t>(li) * s.ldy + row] = cm[r];
+            }
         }
+        return;
+    }
+    float *mine = part + wave * 256;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mine[(4 * lg + r) * 16 + li] = cm[r];
+    lds_barrier();
+    if (kr != 0 || !has_tile) return;
+    // waves of part 0 sum the KW parts of their tile in a fixed order: lane l takes entries 4l .. 4l + 3
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t e = 4 * lane + k, row = e >> 4, n = e & 15;
+        float v = 0.f;
+        for (uint32_t p = 0; p < s.KW; ++p) v += part[(p * s.TW + tw) * 256 + e];
+        if (n < s.batch && n < static_cast<uint32_t>(NB) && row0 + row < s.M) Y[static_cast<uint64_t>(n) * s.ldy + row0 + row] = v;
+    }
+}
+
+// ---------------------------------------------- skinny GEMM, batch 1..8 (VALU, X in registers)
+// Same tiles, stage and split of K as k_gemm_mfma, but X never goes through LDS.  The 16 lanes of
+// a DPP row (lanes 16g .. 16g + 15) decode unit g of the step for the tile's 16 rows, so they all
+// need the same X values: lane i of the row keeps dwords [2 NB i, 2 NB (i + 1)) of that unit's X
+// block, where dword e = (f NB + n) 4 + c is dword c of batch row n's fields 8f .. 8f + 7, and
+// every v_dot2c reads its X operand from the owning lane with a row_newbcast DPP broadcast.  For
+// group f the owners are lanes 2f and 2f + 1.  The broadcasts are written as inline asm because
+// the compiler does not fold a DPP move into v_dot2c; each block starts with s_nop 1, the wait a
+// DPP read of a VGPR needs after a VALU write to it.
+template <int NB>
+struct DppDot;
+
+template <>
+struct DppDot<1> {
+    template <int F>
+    static __device__ __forceinline__ void group(float (&a)[1], const uint32_t (&xr)[2], const uint32_t (&w)[4]) {
+        asm volatile(
+            "s_nop 1\n"
+            "v_dot2c_f32_bf16_dpp %0, %1, %3 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %2, %4 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %1, %5 row_newbcast:%c8 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %2, %6 row_newbcast:%c8 row_mask:0xf bank_mask:0xf\n"
+            : "+v"(a[0])
+            : "v"(xr[0]), "v"(xr[1]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
+    }
+};
+
+template <>
+struct DppDot<2> {
+    template <int F>
+    static __device__ __forceinline__ void group(float (&a)[2], const uint32_t (&xr)[4], const uint32_t (&w)[4]) {
+        asm volatile(
+            "s_nop 1\n"
+            "v_dot2c_f32_bf16_dpp %0, %2, %6 row_newbcast:%c10 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %3, %7 row_newbcast:%c10 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %4, %8 row_newbcast:%c10 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %5, %9 row_newbcast:%c10 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %2, %6 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %3, %7 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %4, %8 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %5, %9 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
+            : "+v"(a[0]), "+v"(a[1])
+            : "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
+    }
+};
+
+template <>
+struct DppDot<4> {
+    template <int F>
+    static __device__ __forceinline__ void group(float (&a)[4], const uint32_t (&xr)[8], const uint32_t (&w)[4]) {
+        asm volatile(
+            "s_nop 1\n"
+            "v_dot2c_f32_bf16_dpp %0, %4, %12 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %5, %13 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %6, %14 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %7, %15 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %8, %12 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %9, %13 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %10, %14 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %11, %15 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %4, %12 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %5, %13 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %6, %14 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %7, %15 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %8, %12 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %9, %13 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %10, %14 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %11, %15 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+            : "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]), "v"(xr[7]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
+    }
+};
+
+template <>
+struct DppDot<8> {
+    template <int F>
+    static __device__ __forceinline__ void group(float (&a)[8], const uint32_t (&xr)[16], const uint32_t (&w)[4]) {
+        asm volatile(
+            "s_nop 1\n"
+            "v_dot2c_f32_bf16_dpp %0, %8, %24 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %9, %25 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %10, %26 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %0, %11, %27 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %12, %24 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %13, %25 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %14, %26 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %1, %15, %27 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %16, %24 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %17, %25 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %18, %26 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %2, %19, %27 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %20, %24 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %21, %25 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %22, %26 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %3, %23, %27 row_newbcast:%c28 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %4, %8, %24 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %4, %9, %25 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %4, %10, %26 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %4, %11, %27 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %5, %12, %24 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %5, %13, %25 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %5, %14, %26 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %5, %15, %27 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %6, %16, %24 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %6, %17, %25 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %6, %18, %26 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %6, %19, %27 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %7, %20, %24 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %7, %21, %25 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %7, %22, %26 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "v_dot2c_f32_bf16_dpp %7, %23, %27 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+            : "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]), "v"(xr[7]), "v"(xr[8]), "v"(xr[9]), "v"(xr[10]), "v"(xr[11]), "v"(xr[12]), "v"(xr[13]), "v"(xr[14]), "v"(xr[15]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
+    }
+};
+
+// X registers of one step for lane (i, g): chunk q = f NB + n (16 bytes: fields 8f .. 8f + 7 of
+// batch row n, unit u) for q in [i NB / 2, (i + 1) NB / 2); for NB = 1, half of chunk i / 2.  Rows
+// >= batch and units past the wave's range read as zero.
+template <int NB>
+__device__ __forceinline__ void gemm_load_xr(uint32_t (&v)[2 * NB], const uint16_t *__restrict__ X, uint32_t u,
+                                             bool unit_ok, const GemmShape &s, int li) {
+    if constexpr (NB == 1) {
+        const uint32_t f = static_cast<uint32_t>(li) >> 1, c = (static_cast<uint32_t>(li) & 1u) * 2u;
+        u32x2 t = {0u, 0u};
+        if (unit_ok) t = *reinterpret_cast<const u32x2 *>(X + static_cast<uint64_t>(u) * 64 + 8 * f + 2 * c);
+        v[0] = t.x;
+        v[1] = t.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < NB / 2; ++h) {
+            const uint32_t q = static_cast<uint32_t>(li) * (NB / 2) + h;
+            const uint32_t f = q / NB, n = q % NB;
+            u32x4 t = {0u, 0u, 0u, 0u};
+            if (unit_ok && n < s.batch)
+                t = *reinterpret_cast<const u32x4 *>(X + static_cast<uint64_t>(n) * s.ldx + static_cast<uint64_t>(u) * 64 + 8 * f);
+            v[4 * h] = t.x; v[4 * h + 1] = t.y; v[4 * h + 2] = t.z; v[4 * h + 3] = t.w;
+        }
+    }
+}
+
+template <int NB, int... F>
+__device__ __forceinline__ void dpp_groups(float (&acc)[NB], const uint32_t (&xr)[2 * NB], const uint32_t (&wp)[8][4],
+                                           std::integer_sequence<int, F...>) {
+    (DppDot<NB>::template group<F>(acc, xr, wp[F]), ...);
+}
+
+template <int B, int NB>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_valu(const GemmGroup grp,
+                                                               const uint16_t *__restrict__ X) {
+    using G = GemmGeo<B>;
+    constexpr int NT = 64 * kGemmWaves;
+    constexpr uint32_t SB = G::WSTAGE;
+    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    u32x4 *stage = reinterpret_cast<u32x4 *>(smem + wave * SB);  // this wave's weight stage
+    float *part = reinterpret_cast<float *>(smem + kGemmWaves * SB);  // [wave][16 rows][16 columns]
+
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
+    const GemmTensor &T = grp.t[k];
+    const u32x4 *w4 = T.w4;
+    const uint16_t *cb = T.cb;
+    float *Y = T.Y;
+    const uint32_t U = T.U;
+    GemmShape s;
+    s.M = T.M;
+    s.P = grp.P;
+    s.tiles = (T.M + 15) / 16;
+    s.TW = grp.TW;
+    s.KW = grp.KW;
+    s.part_units = grp.part_units;
+    s.batch = grp.batch;
+    s.ldx = grp.ldx;
+    s.ldy = T.ldy;
+
+    const uint32_t tw = wave % s.TW, kr = wave / s.TW;
+    const uint32_t tile = (blockIdx.x - grp.first_block[k]) * s.TW + tw;
+    const bool has_tile = tile < s.tiles;
+    const uint32_t row0 = min(tile, s.tiles - 1) * 16;
+    const uint32_t ku0 = min(kr * s.part_units, s.P), ku1 = min(ku0 + s.part_units, s.P);
+    const uint32_t nsteps = has_tile ? (ku1 - ku0 + 3) / 4 : 0;
+    const int li = lane & 15, lg = lane >> 4;
+
+    CbStage<B, NT> cs;
+    cs.issue(cb, U, reinterpret_cast<const u32x4 *>(X), tid);
+    issue_barrier();
+    u32x4 nw[G::LPL];
+    uint32_t nxr[2 * NB];
+    gemm_load_w<B>(nw, w4, T.nch, row0, ku0, s, lane);
+    gemm_load_xr<NB>(nxr, X, ku0 + lg, ku0 + lg < ku1, s, li);
+    cs.store(cbl, U, tid);
+    lds_barrier();
+
+    const bool row_ok = row0 + li < s.M;
+    float acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = 0.f;
+
+    for (uint32_t st = 0; st < nsteps; ++st) {
+        const uint32_t u0 = ku0 + 4 * st;
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < G::LPL; ++j) {
+            const uint32_t q = j * 64 + lane;
+            if (q < G::STEP_CH) {
+                const uint32_t i = q / G::RCH, c = q - i * G::RCH;
+                stage[i * G::SRC + c] = nw[j];
+            }
+        }
+        asm volatile("" ::: "memory");
+        const uint64_t rr = min(row0 + li, s.M - 1);
+        const uint32_t off = static_cast<uint32_t>(((rr * s.P + u0) * G::UD) & 3u);  // 0 or 2 dwords
+        const u32x2 *st2 = reinterpret_cast<const u32x2 *>(stage + li * G::SRC) + off / 2 + lg * B;
+        uint32_t d[G::UD];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const u32x2 t = st2[j];
+            d[2 * j] = t.x; d[2 * j + 1] = t.y;
+        }
+        asm volatile("" ::: "memory");
+        uint32_t xr[2 * NB];
+#pragma unroll
+        for (int i = 0; i < 2 * NB; ++i) xr[i] = nxr[i];
+        if (st + 1 < nsteps) {
+            gemm_load_w<B>(nw, w4, T.nch, row0, u0 + 4, s, lane);
+            gemm_load_xr<NB>(nxr, X, u0 + 4 + lg, u0 + 4 + lg < ku1, s, li);
+        }
+
+        const bool valid = row_ok && u0 + lg < ku1;
+        uint32_t wp[8][4];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = unit_gather<B>(cbl, d, 8 * f + i);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) wp[f][c] = valid ? (w[2 * c] | (w[2 * c + 1] << 16)) : 0u;
+        }
+        dpp_groups<NB>(acc, xr, wp, std::make_integer_sequence<int, 8>{});
+    }
+
+    // lanes with g = 0 hold row l % 16 of every column after summing the four k-groups
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        float v = acc[n];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[n] = v;
     }
     if (s.KW == 1) {
         if (!has_tile) return;
-        if constexpr (MFMA) {
-            if (static_cast<uint32_t>(li) < s.batch) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t row = row0 + 4 * lg + r;
-                    if (row < s.M) Y[static_cast<uint64_t>(li) * s.ldy + row] = cm[r];
-                }
-            }
-        } else if (lg == 0 && row_ok) {
+        if (lg == 0 && row_ok) {
 #pragma unroll
             for (int n = 0; n < NB; ++n)
                 if (static_cast<uint32_t>(n) < s.batch) Y[static_cast<uint64_t>(n) * s.ldy + row0 + li] = acc[n];
@@ -715,19 +956,15 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_tile(const GemmGroup g
         return;
     }
     float *mine = part + wave * 256;
-    if constexpr (MFMA) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mine[(4 * lg + r) * 16 + li] = cm[r];
-    } else if (lg == 0) {
+    if (lg == 0) {
 #pragma unroll
         for (int n = 0; n < NB; ++n) mine[li * 16 + n] = acc[n];
     }
     lds_barrier();
     if (kr != 0 || !has_tile) return;
-    // waves of part 0 sum the KW parts of their tile in a fixed order: lane l takes entries 4l .. 4l + 3
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t e = 4 * lane + k, row = e >> 4, n = e & 15;
+    for (int k2 = 0; k2 < 4; ++k2) {
+        const uint32_t e = 4 * lane + k2, row = e >> 4, n = e & 15;
         float v = 0.f;
         for (uint32_t p = 0; p < s.KW; ++p) v += part[(p * s.TW + tw) * 256 + e];
         if (n < s.batch && n < static_cast<uint32_t>(NB) && row0 + row < s.M) Y[static_cast<uint64_t>(n) * s.ldy + row0 + row] = v;
@@ -930,9 +1167,16 @@ bool gemm_launch(GemmArgs &a) {
     }
     grp.KW = kGemmWaves / grp.TW;
     grp.part_units = static_cast<uint32_t>(((P + grp.KW - 1) / grp.KW + 3) / 4 * 4);
-    const uint32_t lds = kGemmWaves * gemm_stage_bytes<B, NB>() + kGemmWaves * 256 * 4;
+    // LDS: the waves' stages (weights only for the VALU kernel, whose X stays in registers) and
+    // the partial tiles of the split K.
+    const uint32_t stage = MFMA ? gemm_stage_bytes<B, NB>() : static_cast<uint32_t>(GemmGeo<B>::WSTAGE);
+    const uint32_t lds = kGemmWaves * stage + kGemmWaves * 256 * 4;
     if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
-    if (!allow_lds(k_gemm_tile<B, NB, MFMA>, lds)) return false;
+    if constexpr (MFMA) {
+        if (!allow_lds(k_gemm_mfma<B>, lds)) return false;
+    } else {
+        if (!allow_lds(k_gemm_valu<B, NB>, lds)) return false;
+    }
     uint64_t first = 0;
     for (uint32_t i = 0; i < a.count; ++i) {
         const cbk_tensor &t = a.ts[i];
@@ -944,8 +1188,12 @@ bool gemm_launch(GemmArgs &a) {
     }
     grp.first_block[a.count] = static_cast<uint32_t>(first);
     if (first >= (uint64_t(1) << 31)) return false;
-    hipLaunchKernelGGL((k_gemm_tile<B, NB, MFMA>), dim3(static_cast<uint32_t>(first)), dim3(64 * kGemmWaves), lds,
-                       a.s, grp, a.X);
+    if constexpr (MFMA)
+        hipLaunchKernelGGL((k_gemm_mfma<B>), dim3(static_cast<uint32_t>(first)), dim3(64 * kGemmWaves), lds,
+                           a.s, grp, a.X);
+    else
+        hipLaunchKernelGGL((k_gemm_valu<B, NB>), dim3(static_cast<uint32_t>(first)), dim3(64 * kGemmWaves), lds,
+                           a.s, grp, a.X);
     return true;
 }
 
