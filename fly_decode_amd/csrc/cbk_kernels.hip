@@ -183,8 +183,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *base, ui
                                              static_cast<int>(bytes), 0x00020000);
 }
 
+// Cache policy of the buffer operations on data that is touched exactly once (the packed index
+// stream, the decoded output): the non-temporal bit (NT, bit 1 of the aux operand on this chip), so
+// the stream does not displace the codebook, x and X from the caches.  It took the standalone
+// decode of a 4096^2 tensor from 16.7 to 11.4 us and the GEMV launches 1-3 % faster.
+constexpr int kStreamOnce = 2;
+
 __device__ __forceinline__ u32x4 rsrc_load(__amdgpu_buffer_rsrc_t rs, uint32_t byte_offset) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(byte_offset), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(byte_offset), 0, kStreamOnce);
 }
 
 // Step loads: the chunks covering units [us, us + nl) start at chunk (us * UD) / 4; an odd-b step
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
         for (int j = 0; j < 8; ++j) {
             const uint32_t q = j * 64 + lane;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(stb + (q >> 3) * kOutUnit + (q & 7) * 16);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<int>(q * 16u), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<int>(q * 16u), 0, kStreamOnce);
             if (left < 4096 && (left & 7) != 0 && q == full) {
                 const uint32_t h[4] = {v.x, v.y, v.z, v.w};
                 for (uint32_t k = 0; k < static_cast<uint32_t>(left & 7); ++k)
