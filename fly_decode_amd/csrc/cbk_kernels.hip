@@ -340,20 +340,26 @@ struct GemvTensor {
 };
 struct GemvGroup {
     uint32_t first_block[kMaxGroup + 1];  // first_block[count] = grid size
-    uint32_t count, P, S;
+    uint32_t count, P, S, dyn;
     GemvTensor t[kMaxGroup];
 };
 
 // Rows of one tensor for workgroup `blk` of the tensor's `nblk` workgroups.  Every argument is
-// uniform across the workgroup.
+// uniform across the workgroup.  The workgroup's rows are blk * 8 + j + NW * i (j < 8), taken in
+// the order k = 8 i + j; wave w starts with k = w.  With `dyn` false wave w then takes k + 8, k + 16,
+// ...; with `dyn` true a wave that finishes a row claims the next k from a counter in LDS, so the
+// waves of a workgroup end within about one row of each other (the host sets it when there are
+// enough rows per wave for the tail to matter).
 template <int B>
 __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb,
                                           float *__restrict__ yt, const uint16_t *__restrict__ x, uint32_t M,
-                                          uint32_t U, uint32_t P, uint32_t S, uint32_t blk, uint32_t nblk) {
+                                          uint32_t U, uint32_t P, uint32_t S, uint32_t blk, uint32_t nblk,
+                                          bool dyn) {
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
     constexpr int NT = 64 * kGemvWaves;
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
+    __shared__ uint32_t next_row;  // next k to claim (dyn)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *xl = smem;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -383,6 +389,7 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
         const uint32_t q = i * NT + tid;
         if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[i];
     }
+    if (tid == 0) next_row = kGemvWaves;
     lds_barrier();
     if (gw >= M) return;
 
@@ -392,9 +399,20 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
         const uint32_t us = r * P + 64 * j;
         uint32_t d[G::UD];
         transpose_step<B>(d, nxt, stage, us, lane);
-        // next step of this wave: the rest of the row, then row r + NW
+        // next step of this wave: the rest of the row, then the next row
         const bool row_end = j + 1 == S;
-        const uint32_t rn = row_end ? r + NW : r, jn = row_end ? 0 : j + 1;
+        uint32_t rn = r;
+        if (row_end) {
+            if (dyn) {
+                uint32_t kk = 0;
+                if (lane == 0) kk = atomicAdd(&next_row, 1u);
+                kk = __builtin_amdgcn_readfirstlane(kk);
+                rn = blk * kGemvWaves + (kk & (kGemvWaves - 1)) + NW * (kk / kGemvWaves);
+            } else {
+                rn = r + NW;
+            }
+        }
+        const uint32_t jn = row_end ? 0 : j + 1;
         if (rn < M) load_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), ~uint64_t(0), true, lane);
 
         const uint32_t cu = 64 * j + lane;  // this lane's unit within the row
@@ -437,8 +455,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows(const u32x4 *__re
                                                                const uint16_t *__restrict__ cb,
                                                                float *__restrict__ y,
                                                                const uint16_t *__restrict__ x, uint32_t M,
-                                                               uint32_t U, uint32_t P, uint32_t S) {
-    gemv_rows<B>(w4, cb, y, x, M, U, P, S, blockIdx.x, gridDim.x);
+                                                               uint32_t U, uint32_t P, uint32_t S, uint32_t dyn) {
+    gemv_rows<B>(w4, cb, y, x, M, U, P, S, blockIdx.x, gridDim.x, dyn != 0);
 }
 
 // Up to kMaxGroup tensors that share x: this workgroup's tensor is found by counting the group
@@ -451,7 +469,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows_group(const GemvG
     for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(grp.count) && blockIdx.x >= grp.first_block[j]) ? 1u : 0u;
     const GemvTensor &T = grp.t[k];
     const uint32_t b0 = grp.first_block[k], b1 = grp.first_block[k + 1];
-    gemv_rows<B>(T.w4, T.cb, T.y, x, T.M, T.U, grp.P, grp.S, blockIdx.x - b0, b1 - b0);
+    gemv_rows<B>(T.w4, T.cb, T.y, x, T.M, T.U, grp.P, grp.S, blockIdx.x - b0, b1 - b0, grp.dyn != 0);
 }
 
 // ------------------------------------------------------------------------- fast skinny GEMM
@@ -1114,6 +1132,9 @@ struct GemvRun {
         grp.count = a.count;
         grp.P = static_cast<uint32_t>(P);
         grp.S = static_cast<uint32_t>((P + 63) / 64);
+        // Rows claimed dynamically inside each workgroup from 8 rows per wave on: measured 4-7 %
+        // faster on 28672 x 8192 (14 rows per wave), even at 4 rows per wave and 3 % slower at 2.
+        grp.dyn = rows >= uint64_t(8) * grid * kGemvWaves ? 1u : 0u;
         // Workgroups per tensor in proportion to its rows, at least one each.
         uint32_t first = 0;
         uint64_t rows_before = 0;
@@ -1135,7 +1156,7 @@ struct GemvRun {
         } else {
             const GemvTensor &t = grp.t[0];
             hipLaunchKernelGGL(k_gemv_rows<B>, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds), a.s,
-                               t.w4, t.cb, t.y, a.x, t.M, t.U, grp.P, grp.S);
+                               t.w4, t.cb, t.y, a.x, t.M, t.U, grp.P, grp.S, grp.dyn);
         }
         a.st = launched();
         return true;

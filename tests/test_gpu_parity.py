@@ -230,6 +230,16 @@ def test_gemv_mlp_full_size(env, oracle_mod):
             _gemv_check(env, oracle_mod, w, x, rows=rows)
 
 
+
+@pytest.mark.parametrize("rows,cols", [(16421, 1024), (17000, 640), (20000, 8192 + 64)])
+def test_gemv_dynamic_rows_every_row(env, oracle_mod, rows, cols):
+    """Enough rows per wave (at least 8 on a 256-CU device) for the waves of a workgroup to claim
+    rows dynamically: every row is produced exactly once, checked against the oracle in full."""
+    w = synth.gaussian_bf16((rows, cols), 0.02, seed=[81, rows, cols])
+    x = synth.activation_bf16(cols, seed=[82, cols])
+    _gemv_check(env, oracle_mod, w, x)
+
+
 def test_gemv_70b_shapes_sampled(env, oracle_mod):
     """70B-shaped tensors at full size (one of each shape), 128 sampled rows each."""
     for t in synth.WORKLOADS[5][0]:
