@@ -8,14 +8,16 @@
 //
 // Decode and GEMV (templated on b so every shift and mask is a compile-time constant):
 //  * A lane "unit" is 64 consecutive fields = 2b dwords; a wave step covers 64 units.  The wave
-//    loads the step's bytes with fully coalesced 128-bit loads (lane l takes chunk j*64 + l),
-//    writes them to a wave-private LDS stage and reads back its own unit: 64-bit LDS reads at an
-//    odd qword stride (odd b) or 128-bit reads at an odd chunk stride (even b; b % 4 == 0 pads
-//    one chunk per unit), so the transposition has no bank conflicts.  The next step's loads
-//    are issued before the current step is decoded.
-//  * Fields are unpacked in registers (shift/and, or alignbit + and across a word boundary)
-//    and gathered from the codebook held in static LDS, padded to 2^b entries with 0x7FC0 so a
-//    corrupt index cannot leave the table.  Gathers are issued one 8-field group ahead of use.
+//    loads the step's bytes with coalesced 128-bit non-temporal buffer loads (lane l takes chunk
+//    j*64 + l, through a resource that covers exactly the step), writes them to a wave-private
+//    LDS stage and reads back its own unit: 64-bit LDS reads at an odd qword stride (odd b) or
+//    128-bit reads at an odd chunk stride (even b; b % 4 == 0 pads one chunk per unit), so the
+//    transposition has no bank conflicts.  The next step's loads are issued before the current
+//    step is decoded.
+//  * Fields are unpacked in registers straight into table byte offsets (shift/and, or alignbit +
+//    and across a word boundary) and gathered from the codebook held in static LDS, padded to 2^b
+//    entries with 0x7FC0 so a corrupt index cannot leave the table.  Gathers are issued one
+//    8-field group ahead of use.
 //  * GEMV: rows are dealt round-robin to the waves (the grid sweeps the stream front to back);
 //    a row is ceil(K / 4096) wave steps, lane l of step j taking unit 64j + l of the row.  x sits
 //    in LDS, 16 bytes of padding per unit so the lanes' 128-bit reads are conflict-free; BF16
@@ -26,8 +28,9 @@
 //
 // Skinny GEMM: a wave owns a 16-row tile and walks its part of K in steps of 4 units (256 fields)
 // per row; lane (i = l % 16, g = l / 16) decodes unit g of row i.  Batches 9..16 feed the decoded
-// tile to v_mfma_f32_16x16x32_bf16; batches up to 8 use v_dot2c on the vector ALUs.  When K is
-// split across the waves of a workgroup, their partial tiles are added in LDS in a fixed order.
+// tile to v_mfma_f32_16x16x32_bf16 with X transposed through LDS; batches up to 8 use v_dot2c on
+// the vector ALUs with X held in registers and broadcast across each 16-lane row by DPP.  When K
+// is split across the waves of a workgroup, their partial tiles are added in LDS in a fixed order.
 //
 // Generic kernels (any b and shape, runtime field extraction straight from global memory) cover
 // b == 0, rows whose length is not a multiple of 64, misaligned operands and shapes beyond the
@@ -76,17 +79,10 @@ struct U64 {
     static constexpr uint32_t mask = (1u << B) - 1u;
 };
 
-// Field f of a unit held in registers; f is a constant once the caller's loop is unrolled.
-template <int B>
-__device__ __forceinline__ uint32_t unit_field(const uint32_t *d, int f) {
-    const int bit = f * B, w = bit >> 5, s = bit & 31;
-    if (s + B <= 32) return (d[w] >> s) & U64<B>::mask;
-    return __builtin_amdgcn_alignbit(d[w + 1], d[w], s) & U64<B>::mask;
-}
-
-// Table entry for field f of a unit held in registers: the field is extracted straight into its
-// byte offset 2 * field (shift by one less, mask b bits one place up), two VALU operations whether
-// or not the field crosses a word boundary.
+// Table entry for field f (bits f*B .. f*B + B - 1, LSB first) of a unit held in registers; f is a
+// constant once the caller's loop is unrolled.  The field is extracted straight into its byte
+// offset 2 * field (shift by one less, mask b bits one place up), two VALU operations whether or
+// not the field crosses a word boundary (v_alignbit joins the two words).
 template <int B>
 __device__ __forceinline__ uint32_t unit_gather(const uint16_t *tbl, const uint32_t *d, int f) {
     const int bit = f * B, w = bit >> 5, s = bit & 31;
@@ -243,8 +239,9 @@ __device__ __forceinline__ void transpose_step(uint32_t (&d)[U64<B>::UD], const 
 // ------------------------------------------------------------------------------ fast decode
 // Unit u decodes weights [64u, 64u + 64).  Wave steps (64 units) are dealt round-robin to the
 // waves, so the grid reads the stream front to back.  A step's decoded 8 KB go back through the
-// wave's stage (the weights have been read out of it by then) and leave as fully coalesced 16-byte
-// stores.  Staging as in the GEMV: codebook loads before a barrier, the first weight step after it.
+// wave's stage (the weights have been read out of it by then) and leave as coalesced 16-byte
+// non-temporal buffer stores.  Staging as in the GEMV: codebook loads before a barrier, the first
+// weight step after it.
 constexpr int kDecodeWaves = 8;
 constexpr uint32_t kOutUnit = 2 * 64 + 16;  // LDS bytes per decoded unit (16 bytes of padding)
 
@@ -320,8 +317,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
 }
 
 // -------------------------------------------------------------------------------- fast GEMV
-// Rows are dealt round-robin to the waves of the tensor's workgroups (row gw, gw + NW, ...), so at
-// any moment the grid reads one contiguous window of the stream, front to back.  A row of P units
+// Rows are dealt round-robin to the waves of the tensor's workgroups (row gw, gw + NW, ...; see
+// gemv_rows for the dynamic variant), so at any moment the grid reads one contiguous window of the
+// stream, front to back.  A row of P units
 // is S = ceil(P / 64) wave steps; lane l of step j decodes unit 64j + l of the row (the last step
 // is partial when P % 64 != 0), accumulates in registers across the row's steps, and one wave
 // reduction per row produces y.
