@@ -342,6 +342,28 @@ struct GemvGroup {
     GemvTensor t[kMaxGroup];
 };
 
+// One lane's unit of a GEMV row: gathers one 8-field group ahead of use, BF16 pairs multiplied
+// with x by v_dot2c into four fp32 partial sums.
+template <int B>
+__device__ __forceinline__ void gemv_unit(const uint32_t (&d)[U64<B>::UD], const uint16_t *cbl, const u32x4 (&xq)[8],
+                                          float (&a)[4]) {
+    uint32_t wv[2][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[0][i] = unit_gather<B>(cbl, d, i);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        if (g + 1 < 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (g + 1) + i);
+        }
+        const uint32_t *w = wv[g & 1];
+        a[0] = dot2(w[0] | (w[1] << 16), xq[g].x, a[0]);
+        a[1] = dot2(w[2] | (w[3] << 16), xq[g].y, a[1]);
+        a[2] = dot2(w[4] | (w[5] << 16), xq[g].z, a[2]);
+        a[3] = dot2(w[6] | (w[7] << 16), xq[g].w, a[3]);
+    }
+}
+
 // Rows of one tensor for workgroup `blk` of the tensor's `nblk` workgroups.  Every argument is
 // uniform across the workgroup.  The workgroup's rows are blk * 8 + j + NW * i (j < 8), taken in
 // the order k = 8 i + j; wave w starts with k = w.  With `dyn` false wave w then takes k + 8, k + 16,
@@ -391,7 +413,45 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
     lds_barrier();
     if (gw >= M) return;
 
+    // The row after r: the static order, or the next k claimed from the workgroup's counter.
+    auto next = [&](uint32_t r) -> uint32_t {
+        if (!dyn) return r + NW;
+        uint32_t kk = 0;
+        if (lane == 0) kk = atomicAdd(&next_row, 1u);
+        kk = __builtin_amdgcn_readfirstlane(kk);
+        return blk * kGemvWaves + (kk & (kGemvWaves - 1)) + NW * (kk / kGemvWaves);
+    };
     float a[4] = {0.f, 0.f, 0.f, 0.f};
+    auto reduce_row = [&](uint32_t r) {
+        float acc = (a[0] + a[1]) + (a[2] + a[3]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (lane == 0) yt[r] = acc;
+        a[0] = a[1] = a[2] = a[3] = 0.f;
+    };
+
+    if (S == 1) {
+        // Rows of one step (K <= 4096): lane l multiplies unit l of x in every row, so its 64 x
+        // values are read from LDS into registers once instead of in every step.
+        const bool active = static_cast<uint32_t>(lane) < P;
+        u32x4 xr[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            xr[g] = active ? *reinterpret_cast<const u32x4 *>(xl + lane * XU + 16 * g) : (u32x4){0u, 0u, 0u, 0u};
+        uint32_t r = gw;
+        while (true) {
+            uint32_t d[G::UD];
+            transpose_step<B>(d, nxt, stage, r * P, lane);
+            const uint32_t rn = next(r);
+            if (rn < M) load_step<B>(nxt, w4, rn * P, P, ~uint64_t(0), true, lane);
+            if (active) gemv_unit<B>(d, cbl, xr, a);
+            reduce_row(r);
+            if (rn >= M) break;
+            r = rn;
+        }
+        return;
+    }
+
     uint32_t r = gw, j = 0;
     while (true) {
         const uint32_t us = r * P + 64 * j;
@@ -399,47 +459,19 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
         transpose_step<B>(d, nxt, stage, us, lane);
         // next step of this wave: the rest of the row, then the next row
         const bool row_end = j + 1 == S;
-        uint32_t rn = r;
-        if (row_end) {
-            if (dyn) {
-                uint32_t kk = 0;
-                if (lane == 0) kk = atomicAdd(&next_row, 1u);
-                kk = __builtin_amdgcn_readfirstlane(kk);
-                rn = blk * kGemvWaves + (kk & (kGemvWaves - 1)) + NW * (kk / kGemvWaves);
-            } else {
-                rn = r + NW;
-            }
-        }
+        const uint32_t rn = row_end ? next(r) : r;
         const uint32_t jn = row_end ? 0 : j + 1;
         if (rn < M) load_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), ~uint64_t(0), true, lane);
 
         const uint32_t cu = 64 * j + lane;  // this lane's unit within the row
         if (cu < P) {
-            const unsigned char *xb = xl + cu * XU;
-            uint32_t wv[2][8];
+            const u32x4 *xb = reinterpret_cast<const u32x4 *>(xl + cu * XU);
+            u32x4 xq[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wv[0][i] = unit_gather<B>(cbl, d, i);
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                if (g + 1 < 8) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) wv[(g + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (g + 1) + i);
-                }
-                const u32x4 xq = *reinterpret_cast<const u32x4 *>(xb + 16 * g);
-                const uint32_t *w = wv[g & 1];
-                a[0] = dot2(w[0] | (w[1] << 16), xq.x, a[0]);
-                a[1] = dot2(w[2] | (w[3] << 16), xq.y, a[1]);
-                a[2] = dot2(w[4] | (w[5] << 16), xq.z, a[2]);
-                a[3] = dot2(w[6] | (w[7] << 16), xq.w, a[3]);
-            }
+            for (int g = 0; g < 8; ++g) xq[g] = xb[g];
+            gemv_unit<B>(d, cbl, xq, a);
         }
-        if (row_end) {
-            float acc = (a[0] + a[1]) + (a[2] + a[3]);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-            if (lane == 0) yt[r] = acc;
-            a[0] = a[1] = a[2] = a[3] = 0.f;
-        }
+        if (row_end) reduce_row(r);
         if (rn >= M) break;
         r = rn;
         j = jn;
