@@ -452,6 +452,38 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
         return;
     }
 
+    if (S == 2) {
+        // Rows of two steps (4096 < K <= 8192): lane l multiplies units l and 64 + l of x, both held
+        // in registers; a row's two steps are written out in turn.
+        const bool active1 = static_cast<uint32_t>(64 + lane) < P;
+        u32x4 xr0[8], xr1[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            xr0[g] = *reinterpret_cast<const u32x4 *>(xl + lane * XU + 16 * g);
+            xr1[g] = active1 ? *reinterpret_cast<const u32x4 *>(xl + (64 + lane) * XU + 16 * g) : (u32x4){0u, 0u, 0u, 0u};
+        }
+        uint32_t r = gw;
+        while (true) {
+            {
+                uint32_t d[G::UD];
+                transpose_step<B>(d, nxt, stage, r * P, lane);
+                load_step<B>(nxt, w4, r * P + 64, P - 64, ~uint64_t(0), true, lane);
+                gemv_unit<B>(d, cbl, xr0, a);
+            }
+            const uint32_t rn = next(r);
+            {
+                uint32_t d[G::UD];
+                transpose_step<B>(d, nxt, stage, r * P + 64, lane);
+                if (rn < M) load_step<B>(nxt, w4, rn * P, 64, ~uint64_t(0), true, lane);
+                if (active1) gemv_unit<B>(d, cbl, xr1, a);
+            }
+            reduce_row(r);
+            if (rn >= M) break;
+            r = rn;
+        }
+        return;
+    }
+
     uint32_t r = gw, j = 0;
     while (true) {
         const uint32_t us = r * P + 64 * j;
