@@ -73,6 +73,11 @@ def load_library():
         lib.cbk_gemm_small.restype = ctypes.c_int
         lib.cbk_gemm_small.argtypes = [tp, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        lib.cbk_encode_gpu_workspace_bytes.restype = ctypes.c_size_t
+        lib.cbk_encode_gpu_workspace_bytes.argtypes = []
+        lib.cbk_encode_gpu.restype = ctypes.c_int
+        lib.cbk_encode_gpu.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
         lib.cbk_gemm_group.restype = ctypes.c_int
         lib.cbk_gemm_group.argtypes = [tp, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p),
@@ -156,6 +161,32 @@ def encode(w, rows: int | None = None, cols: int | None = None) -> Compressed:
     if st != CBK_OK:
         raise CbkError(st, "cbk_encode")
     return Compressed(rows, cols, U.value, b.value, cb[:U.value].copy(), words)
+
+
+def encode_gpu(w, rows: int | None = None, cols: int | None = None, stream=None) -> Compressed:
+    """Compress BF16 bit patterns already on the GPU (a contiguous bfloat16/int16/uint16 torch
+    tensor, shape [rows][cols] or 1-D with rows/cols given) with cbk_encode_gpu.  The result is
+    bit-identical to ``encode`` and stays on the device; U and b are read back (one sync)."""
+    import torch
+    if not w.is_contiguous() or w.element_size() != 2:
+        raise ValueError("encode_gpu expects a contiguous tensor of 16-bit patterns")
+    if rows is None:
+        rows, cols = (tuple(w.shape) if w.dim() == 2 else (1, w.numel()))
+    n = w.numel()
+    if n != rows * cols:
+        raise ValueError("rows * cols does not match the tensor size")
+    lib = load_library()
+    dev = w.device
+    ws = torch.empty(int(lib.cbk_encode_gpu_workspace_bytes()), dtype=torch.uint8, device=dev)
+    cb = torch.empty(65536, dtype=torch.int16, device=dev)
+    cap = words_for(n, 16)
+    words = torch.empty(max(cap, 4), dtype=torch.int32, device=dev)
+    meta = torch.zeros(2, dtype=torch.int32, device=dev)
+    _check(lib.cbk_encode_gpu(ctypes.c_void_p(w.data_ptr() if n else None), n, ctypes.c_void_p(ws.data_ptr()),
+                              ctypes.c_void_p(cb.data_ptr()), ctypes.c_void_p(words.data_ptr()), cap,
+                              ctypes.c_void_p(meta.data_ptr()), _stream(stream)), "cbk_encode_gpu")
+    U, b = (int(v) for v in meta.cpu().tolist())
+    return Compressed(rows, cols, U, b, cb[:U], words[:words_for(n, b)])
 
 
 def _stream(stream):

@@ -21,7 +21,7 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang
                 "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
-SOURCES = [("cbk_api.cpp", False), ("cbk_kernels.hip", True)]
+SOURCES = [("cbk_api.cpp", False), ("cbk_kernels.hip", True), ("cbk_encode.hip", True)]
 
 
 def _run(cmd):

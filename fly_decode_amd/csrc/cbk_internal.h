@@ -1,4 +1,5 @@
-// Internal interface between the host API (cbk_api.cpp) and the HIP launchers (cbk_kernels.hip).
+// Internal interface between the host API (cbk_api.cpp) and the HIP launchers (cbk_kernels.hip,
+// cbk_encode.hip).
 // Arguments reaching these launchers are already validated.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -16,5 +17,10 @@ cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uin
                        float *Y, uint64_t ldy, hipStream_t s);
 cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_t *X, uint64_t ldx,
                              uint32_t batch, float *const *Ys, const uint64_t *ldys, hipStream_t s);
+
+// GPU encoder (cbk_encode.hip).
+size_t encode_gpu_workspace_bytes();
+cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
+                             uint32_t *words, uint32_t *meta, hipStream_t s);
 
 }  // namespace cbk

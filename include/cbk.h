@@ -94,6 +94,27 @@ cbk_status cbk_encode(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_
  */
 
 /*
+ * cbk_encode_gpu -- the same encoding as cbk_encode, computed on the GPU for the load-time path
+ * (the codebook overview's "Pitfalls": loading a compressed model is slower; this moves the
+ * compression step onto the device).  Enqueued on `stream`; nothing is copied to the host.
+ *   w          in, device, n 16-bit patterns, 16-byte aligned (when n > 0).
+ *   workspace  device scratch of cbk_encode_gpu_workspace_bytes() bytes, 16-byte aligned, owned by
+ *              the caller; its contents on entry do not matter and are left undefined.
+ *   codebook   out, device, capacity 65536 entries; receives the U sorted distinct patterns.
+ *   words      out, device, 16-byte aligned, capacity words_cap >= cbk_words_for(n, 16) words (b is
+ *              known only on the device); receives cbk_words_for(n, b) words, the last ones
+ *              zero-padded exactly as cbk_encode writes them.  Words past that are not written.
+ *   meta       out, device, two uint32: meta[0] = U, meta[1] = b.
+ * The result is bit-identical to cbk_encode on the same input.  Several calls may run at once
+ * only with separate workspaces.
+ * Errors: CBK_E_INVALID (null pointer), CBK_E_ALIGN, CBK_E_CAPACITY (words_cap too small),
+ * CBK_E_UNSUPPORTED (n >= 2^40), CBK_E_HIP (launch failure).
+ */
+size_t cbk_encode_gpu_workspace_bytes(void);
+cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook, uint32_t *words,
+                          uint64_t words_cap, uint32_t *meta, void *stream);
+
+/*
  * cbk_decode_bf16 -- GPU.  Standalone decode: out[i] = codebook[index i] for i < rows*cols,
  * the exact original bit patterns (no float conversion anywhere).
  *   out   device, rows*cols uint16, 2-byte aligned.

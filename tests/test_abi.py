@@ -32,7 +32,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemv_group", "cbk_gemm_small", "cbk_gemm_group", "cbk_bits_for",
-              "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str"]:
+              "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str", "cbk_encode_gpu",
+              "cbk_encode_gpu_workspace_bytes"]:
         assert n in names
 
 
@@ -167,3 +168,21 @@ def test_gpu_calls_validate_before_any_hip_call(cbk):
     # zero-size tensors are accepted without work (no HIP call either)
     assert lib.cbk_gemv(T(rows=0, cols=0, U=0, b=0, cb=0, words=0), None, None, None) == 0
     assert lib.cbk_decode_bf16(T(rows=0, cols=9, U=0, b=0, cb=0, words=0), None, None) == 0
+
+
+def test_gpu_encoder_validates_before_any_hip_call(cbk):
+    """cbk_encode_gpu rejects bad arguments on the host (no device is present here)."""
+    lib = cbk.load_library()
+    assert lib.cbk_encode_gpu_workspace_bytes() == 2048 * 4 + 65536 * 2
+    W, WS, CB, WD, M = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
+    cap = cbk.words_for(1000, 16)
+    assert lib.cbk_encode_gpu(None, 1000, WS, CB, WD, cap, M, None) == 1          # null w
+    assert lib.cbk_encode_gpu(W, 1000, None, CB, WD, cap, M, None) == 1           # null workspace
+    assert lib.cbk_encode_gpu(W, 1000, WS, None, WD, cap, M, None) == 1           # null codebook
+    assert lib.cbk_encode_gpu(W, 1000, WS, CB, None, cap, M, None) == 1           # null words
+    assert lib.cbk_encode_gpu(W, 1000, WS, CB, WD, cap, None, None) == 1          # null meta
+    assert lib.cbk_encode_gpu(ctypes.c_void_p(0x10008), 1000, WS, CB, WD, cap, M, None) == 3  # w not 16 B
+    assert lib.cbk_encode_gpu(W, 1000, ctypes.c_void_p(0x20004), CB, WD, cap, M, None) == 3
+    assert lib.cbk_encode_gpu(W, 1000, WS, CB, ctypes.c_void_p(0x40004), cap, M, None) == 3
+    assert lib.cbk_encode_gpu(W, 1000, WS, CB, WD, cap - 1, M, None) == 2         # words_cap too small
+    assert lib.cbk_encode_gpu(W, 1 << 40, WS, CB, WD, 1 << 62, M, None) == 4      # n beyond the limit

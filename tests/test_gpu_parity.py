@@ -442,3 +442,48 @@ def test_gemm_wide_codebooks_fast_path(env, oracle_mod, b):
                                           exponents=synth.finite_exponents(U)).reshape(rows, cols)
             X = synth.activations_bf16(batch, cols, 72)
             _gemm_check(env, oracle_mod, w, X)
+
+
+
+# ------------------------------------------------------------------------------- GPU encoder
+def _encode_gpu_check(env, w):
+    torch, cbk = env
+    host = cbk.encode(w.reshape(1, -1))
+    dev = torch.from_numpy(np.ascontiguousarray(w.reshape(-1)).view(np.int16)).to("cuda")
+    got = cbk.encode_gpu(dev, rows=1, cols=w.size)
+    torch.cuda.synchronize()
+    assert (got.U, got.b) == (host.U, host.b), (w.size, got.U, host.U)
+    assert np.array_equal(got.codebook.cpu().numpy().view(np.uint16), host.codebook)
+    assert np.array_equal(got.words.cpu().numpy().view(np.uint32), host.words), (w.size, host.U)
+    return got
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 31, 32, 33, 2047, 2048, 2049, 2048 * 64 + 5, 100003])
+def test_encode_gpu_matches_host_ragged_lengths(env, n):
+    """Empty input and ragged lengths around the 8-pattern load chunk and the 32-field and 2048-field pack blocks."""
+    w = synth.gaussian_bf16((n,), 0.02, seed=[91, n])
+    _encode_gpu_check(env, w)
+
+
+@pytest.mark.parametrize("U", [1, 2, 3, 255, 256, 257, 4097, 32768, 32769, 65536])
+def test_encode_gpu_matches_host_every_width(env, U):
+    """Distinct counts at both ends of the widths, up to every 16-bit pattern (+0/-0, NaNs)."""
+    n = max(U, 50000)
+    w = synth.with_distinct_count(n, U, seed=[92, U])
+    got = _encode_gpu_check(env, w)
+    assert got.U == U
+
+
+def test_encode_gpu_workload_tensor_and_oracle(env, oracle_mod):
+    """A 4096^2 tensor of the attention workload: equal to the host encoder and to the oracle, and
+    the device result decodes back to the input."""
+    torch, cbk = env
+    w = synth.workload_tensor(1, 0, synth.WORKLOADS[1][0][0])
+    got = _encode_gpu_check(env, w)
+    e = oracle_mod.encode(w)
+    assert got.U == e.U and got.b == e.b
+    n = w.size
+    assert np.array_equal(got.words.cpu().numpy().view(np.uint32)[:oracle_mod.stream_words(n, e.b)], e.words)
+    out = cbk.decode_bf16(got)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape), w)
