@@ -21,6 +21,9 @@ each tensor with its own codebook):
   l70b_b1    the same tensors at batch 1, phases grouped as in llama7b.
   decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors, one launch
              per tensor; bytes = compressed reads + 2 bytes written per weight.
+  encode4096 the load-time path: cbk_encode_gpu of the attn4096 tensors from raw BF16 already in
+             HBM (three launches per tensor); bytes = 2 bytes read per weight + the compressed
+             form written; the result of the last step is checked against the host encoder.
 
 The step is captured once in a HIP graph and replayed; the timed region is bracketed by
 torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
@@ -57,10 +60,10 @@ def workload_tensors(name: str, count: int, layers: int):
     """(specs, phases, batch, layer_count): specs are (cfg, layer, tensor) triples; phases are lists
     of spec indices launched together (one launch per phase, phases run in order)."""
     import synth
-    if name in ("attn4096", "decode4096"):
+    if name in ("attn4096", "decode4096", "encode4096"):
         t = synth.WORKLOADS[2][0][0]
         specs = [(2, layer, t) for layer in range(count)]
-        return specs, [[i] for i in range(len(specs))], (0 if name == "decode4096" else 1), len(specs)
+        return specs, [[i] for i in range(len(specs))], (1 if name == "attn4096" else 0), len(specs)
     if name in ("llama7b", "l70b_b1", "l70b_b16"):
         cfg = 4 if name == "llama7b" else 5
         tensors, n_layers = synth.WORKLOADS[cfg]
@@ -81,23 +84,30 @@ def workload_tensors(name: str, count: int, layers: int):
     raise SystemExit(f"unknown workload {name}")
 
 
-def prepare(specs, threads):
-    """Generate and encode every tensor on the host (threads), upload to the GPU."""
+def prepare(specs, threads, raw=False):
+    """Generate and encode every tensor on the host (threads), upload to the GPU.  With raw=True
+    the uploaded form is the BF16 patterns themselves (int16, flat) and the host encodings stay on
+    the host, as (raw tensors, host encodings)."""
+    import torch
     import synth
     import fly_decode_amd as cbk
 
     def make(spec):
         cfg, layer, t = spec
         w = synth.workload_tensor(cfg, layer, t)
-        return cbk.encode(w)
+        return w, cbk.encode(w)
 
-    out = []
+    out, hosts = [], []
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        for i, c in enumerate(ex.map(make, specs)):
-            out.append(c.to("cuda"))
+        for i, (w, c) in enumerate(ex.map(make, specs)):
+            if raw:
+                out.append(torch.from_numpy(w.reshape(-1).view(np.int16)).to("cuda"))
+                hosts.append(c)
+            else:
+                out.append(c.to("cuda"))
             if (i + 1) % 16 == 0 or i + 1 == len(specs):
                 log(f"encoded + uploaded {i + 1}/{len(specs)} tensors")
-    return out
+    return (out, hosts) if raw else out
 
 
 def cpu_baseline(specs, seconds: float, threads: int):
@@ -133,12 +143,52 @@ def cpu_baseline(specs, seconds: float, threads: int):
     }
 
 
+def cpu_baseline_encode(specs, seconds: float):
+    """The oracle's encoder (plain C, one host thread) on whole tensors of the workload, until about
+    `seconds` of wall time have been spent."""
+    import oracle
+    import synth
+
+    oracle.build(force=False)
+    cfg, layer, t = specs[0]
+    w = synth.workload_tensor(cfg, layer, t)
+    t_total, used = 0.0, 0
+    while t_total < seconds and used < 4096:
+        t0 = time.perf_counter()
+        oracle.encode(w)
+        t_total += time.perf_counter() - t0
+        used += 1
+    return {
+        "value": round(2.0 * used * w.size / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{used} full encodes of one {t.rows}x{t.cols} tensor of the workload with the "
+                  f"oracle's encoder (one host thread), {t_total:.1f} s",
+    }
+
+
+def check_encoded(raws, hosts, codebooks, words, metas, which):
+    """The device encodings of tensors `which` against the host encoder (exact)."""
+    import fly_decode_amd as cbk
+    for i in which:
+        h = hosts[i]
+        U, b = (int(v) for v in metas[i].cpu().tolist())
+        nw = cbk.words_for(raws[i].numel(), b)
+        ok = (U, b) == (h.U, h.b) and \
+            np.array_equal(codebooks[i][:U].cpu().numpy().view(np.uint16), h.codebook) and \
+            np.array_equal(words[i][:nw].cpu().numpy().view(np.uint32), h.words)
+        if not ok:
+            raise SystemExit(f"GPU encoding of tensor {i} differs from the host encoder")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096"])
+    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096",
+                                                           "encode4096"])
     ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers for mlp_b8 (8) and l70b_* (2)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -175,8 +225,17 @@ def main():
     if args.no_group:
         phases = [[i] for ph in phases for i in ph]
     log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
+    encode = args.workload == "encode4096"
     t0 = time.perf_counter()
-    tensors = prepare(specs, threads)
+    if encode:
+        raws, hosts = prepare(specs, threads, raw=True)
+        tensors = hosts
+        ws = torch.empty(cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
+        enc_cb = [torch.empty(65536, dtype=torch.int16, device="cuda") for _ in raws]
+        enc_words = [torch.empty(cbk.words_for(r.numel(), 16), dtype=torch.int32, device="cuda") for r in raws]
+        enc_meta = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in raws]
+    else:
+        tensors = prepare(specs, threads)
     log(f"setup {time.perf_counter() - t0:.1f} s")
 
     import synth
@@ -185,7 +244,9 @@ def main():
         if d.cols not in xs and batch > 0:
             x = synth.workload_x(specs[0][0], d.cols, batch)
             xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
-    if batch == 0:
+    if encode:
+        ys = []
+    elif batch == 0:
         ys = [torch.empty((d.rows, d.cols), dtype=torch.bfloat16, device="cuda") for d in tensors]
     elif batch == 1:
         xs = {k: v[0] for k, v in xs.items()}
@@ -195,7 +256,10 @@ def main():
 
     def step():
         for ph in phases:
-            if batch == 0:
+            if encode:
+                i = ph[0]
+                cbk.encode_gpu_launch(raws[i], ws, enc_cb[i], enc_words[i], enc_meta[i])
+            elif batch == 0:
                 cbk.decode_bf16(tensors[ph[0]], out=ys[ph[0]])
             elif batch > 1 and len(ph) == 1:
                 cbk.gemm_small(tensors[ph[0]], xs[tensors[ph[0]].cols], Y=ys[ph[0]])
@@ -236,10 +300,15 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (event), wall {wall:.3f} s")
+    if encode:
+        check_encoded(raws, hosts, enc_cb, enc_words, enc_meta, sorted({0, len(raws) - 1}))
+        log("device encodings of the first and last tensor equal the host encoder's")
 
     # The step is one graph of back-to-back GEMV launches on `stream`, so the event-timed step
     # divided by its launch count is the kernels' average launch duration (inter-kernel gaps
     # included, which makes it a slight overestimate; rocprofv3 kernel traces agree to ~2 %).
+    # The encoder is three launches per tensor (clear, presence, pack); its figure below is
+    # for the whole encode of one tensor, with the per-kernel split in the rocprofv3 summary.
     launches = len(phases)
     avg_launch_s = ms_step * 1e-3 / launches
 
@@ -247,7 +316,7 @@ def main():
     # algorithmic bytes: packed indices + codebook + Y for every tensor, X once per launch
     comp_total = sum(d.compressed_bytes + 4 * batch * d.rows for d in tensors) + \
         sum(2 * batch * tensors[ph[0]].cols for ph in phases)
-    if batch == 0:  # decode: compressed reads + the BF16 written
+    if batch == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
         comp_total = sum(d.compressed_bytes + 2 * d.n for d in tensors)
     step_s = ms_step * 1e-3
     value = 2.0 * n_total / step_s / 1e9
@@ -255,13 +324,15 @@ def main():
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors})
-    kernel = ("k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
+    kernel = ("k_enc" if encode else "k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
               else "k_gemm_valu" if batch <= 8 else "k_gemm_mfma")
     kernel_key = f"{kernel}_b{bits[-1]}"
     traffic = profiling.traffic_for(kernel_key, args.workload)
 
     result = {
-        "metric": ("fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
+        "metric": ("GPU codebook encode of BF16 weights resident in HBM, raw-weight GB/s; % of HBM peak"
+                   if encode else
+                   "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
                    else "standalone codebook decode to BF16 in HBM, decompressed-weight GB/s; % of HBM peak"
                    if batch == 0 else
                    f"fused codebook skinny-GEMM decompressed-weight GB/s at batch {batch}; % of HBM peak"),
@@ -286,15 +357,15 @@ def main():
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
-            "launches_per_step": launches,
+            "launches_per_step": 3 * launches if encode else launches,
         },
         "compressed_GBps": round(comp_gbps, 2),
         "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),
         "layer_time_us": round(ms_step * 1e3 / n_layers, 3),
-        "tokens_per_s_equiv": round(1.0 / step_s, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{kernel}<{bits[-1]}>",
+            "kernel": ("cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
+                       if encode else f"{kernel}<{bits[-1]}>"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -302,15 +373,21 @@ def main():
             "traffic": round(traffic["traffic_bytes_per_launch"]) if traffic else None,
             "bytes_per_launch": int(algo_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "launches_per_unit": 3 if encode else 1,
             "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, args.workload), ROOT) if traffic else None,
         },
     }
+    if not encode:
+        result["tokens_per_s_equiv"] = round(1.0 / step_s, 2)
     if batch > 1:
         flops = 2.0 * batch * n_total / step_s
         result["effective_TFLOPs"] = round(flops / 1e12, 3)
     if not args.no_cpu_baseline and batch == 1:
         log("CPU baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
+    elif not args.no_cpu_baseline and encode:
+        log("CPU baseline (oracle encoder) ...")
+        result["cpu_baseline"] = cpu_baseline_encode(specs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

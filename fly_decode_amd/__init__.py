@@ -163,6 +163,22 @@ def encode(w, rows: int | None = None, cols: int | None = None) -> Compressed:
     return Compressed(rows, cols, U.value, b.value, cb[:U.value].copy(), words)
 
 
+def encode_gpu_workspace_bytes() -> int:
+    return int(load_library().cbk_encode_gpu_workspace_bytes())
+
+
+def encode_gpu_launch(w, workspace, codebook, words, meta, stream=None) -> None:
+    """Enqueue cbk_encode_gpu on the stream without waiting: w holds n 16-bit patterns; workspace,
+    codebook (65536 entries), words (at least words_for(n, 16) words) and meta (two uint32: U, b)
+    are device tensors the caller owns."""
+    n = w.numel()
+    _check(load_library().cbk_encode_gpu(
+        ctypes.c_void_p(w.data_ptr() if n else None), n, ctypes.c_void_p(workspace.data_ptr()),
+        ctypes.c_void_p(codebook.data_ptr()), ctypes.c_void_p(words.data_ptr()),
+        words.numel() * words.element_size() // 4, ctypes.c_void_p(meta.data_ptr()), _stream(stream)),
+        "cbk_encode_gpu")
+
+
 def encode_gpu(w, rows: int | None = None, cols: int | None = None, stream=None) -> Compressed:
     """Compress BF16 bit patterns already on the GPU (a contiguous bfloat16/int16/uint16 torch
     tensor, shape [rows][cols] or 1-D with rows/cols given) with cbk_encode_gpu.  The result is
@@ -175,16 +191,12 @@ def encode_gpu(w, rows: int | None = None, cols: int | None = None, stream=None)
     n = w.numel()
     if n != rows * cols:
         raise ValueError("rows * cols does not match the tensor size")
-    lib = load_library()
     dev = w.device
-    ws = torch.empty(int(lib.cbk_encode_gpu_workspace_bytes()), dtype=torch.uint8, device=dev)
+    ws = torch.empty(encode_gpu_workspace_bytes(), dtype=torch.uint8, device=dev)
     cb = torch.empty(65536, dtype=torch.int16, device=dev)
-    cap = words_for(n, 16)
-    words = torch.empty(max(cap, 4), dtype=torch.int32, device=dev)
+    words = torch.empty(max(words_for(n, 16), 4), dtype=torch.int32, device=dev)
     meta = torch.zeros(2, dtype=torch.int32, device=dev)
-    _check(lib.cbk_encode_gpu(ctypes.c_void_p(w.data_ptr() if n else None), n, ctypes.c_void_p(ws.data_ptr()),
-                              ctypes.c_void_p(cb.data_ptr()), ctypes.c_void_p(words.data_ptr()), cap,
-                              ctypes.c_void_p(meta.data_ptr()), _stream(stream)), "cbk_encode_gpu")
+    encode_gpu_launch(w, ws, cb, words, meta, stream)
     U, b = (int(v) for v in meta.cpu().tolist())
     return Compressed(rows, cols, U, b, cb[:U], words[:words_for(n, b)])
 

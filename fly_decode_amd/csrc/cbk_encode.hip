@@ -2,16 +2,18 @@
 // of the distinct 16-bit patterns, b = ceil(log2 U), indices packed LSB first into little-endian
 // uint32 words) on the device, for the load-time path.  The codebook method itself (codebook
 // lossless compression overview, "How it works"; Codebook-Quantization digest, "Key points")
-// fixes the result; the three passes below are this library's way of computing it:
+// fixes the result; the passes below are this library's way of computing it:
 //
-//  1. presence: each workgroup marks the patterns it sees in a 65,536-bit LDS bitmap (testing
-//     before setting, so repeated values cost a read), then ORs its nonzero words into the
-//     global bitmap;
-//  2. rank: one workgroup turns the bitmap into the ascending codebook, the pattern -> index
-//     table, U and b (prefix sums of the words' popcounts);
-//  3. pack: a lane packs 32 consecutive fields into exactly b words in registers; a wave's 64 x b
-//     words go through LDS and leave as coalesced stores.  b is read from device memory, so the
-//     three launches need no host round trip.
+//  1. clear: zero the global presence bitmaps;
+//  2. presence: each workgroup marks the patterns it sees in a 65,536-bit LDS bitmap (testing
+//     before setting, so repeated values cost a read) and ORs its nonzero words into one of eight
+//     global copies of the bitmap;
+//  3. pack: every workgroup ORs the copies and ranks the bitmap into an LDS table (prefix sums of the words'
+//     popcounts), which gives U, b, the ascending codebook and each pattern's index; a wave takes
+//     2,048 consecutive fields with coalesced loads, looks their indices up and writes them to LDS
+//     in field order; each lane then packs 32 consecutive indices into exactly b words (b fixed at
+//     compile time per instantiation) and the wave's 64 b words leave through LDS as coalesced
+//     16-byte stores.  U and b never leave the device, so the launches need no host round trip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,16 +28,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kPatterns = 65536;
 constexpr uint32_t kMapWords = kPatterns / 32;  // 2048
-constexpr int kEncThreads = 512;
-constexpr int kPackWaves = 8;
+constexpr int kPresThreads = 1024;
+constexpr int kPresUnroll = 4;                  // 16-byte loads per thread per pass
+// Copies of the global bitmap: workgroup g ORs into copy g % kCopies, which spreads the atomics on
+// each hot word over kCopies addresses (and keeps them on one XCD when workgroups are dealt to the
+// eight XCDs round-robin); the pack kernel ORs the copies back together.
+constexpr int kCopies = 8;
+constexpr int kPackWaves = 16;                  // two bitmap words per thread in the ranking
 constexpr uint32_t kPackFields = 64 * 32;       // fields per wave block
 
-// Workspace layout: the global bitmap, then the pattern -> index table.
-constexpr size_t kWsMapBytes = kMapWords * 4;
-constexpr size_t kWsIndexBytes = kPatterns * 2;
+// Non-temporal cache policy for loads of data read once.
+constexpr int kStreamOnce = 2;
+
+// Workspace: kCopies global presence bitmaps.
+constexpr size_t kWsMapBytes = kCopies * kMapWords * 4;
 
 __global__ __launch_bounds__(256) void k_enc_clear(uint32_t *__restrict__ map) {
-    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < kMapWords; i += gridDim.x * 256) map[i] = 0;
+    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < kCopies * kMapWords; i += gridDim.x * 256) map[i] = 0;
 }
 
 __device__ __forceinline__ void mark(uint32_t *bm, uint32_t v) {
@@ -43,126 +52,256 @@ __device__ __forceinline__ void mark(uint32_t *bm, uint32_t v) {
     if (!(bm[v >> 5] & bit)) atomicOr(&bm[v >> 5], bit);
 }
 
-// Grid-stride over 16-byte chunks of w (16-byte aligned), then the n % 8 tail.
-__global__ __launch_bounds__(kEncThreads) void k_enc_presence(const uint16_t *__restrict__ w, uint64_t n,
-                                                              uint32_t *__restrict__ map) {
+__device__ __forceinline__ void mark8(uint32_t *bm, u32x4 v) {
+    mark(bm, v.x & 0xFFFFu); mark(bm, v.x >> 16);
+    mark(bm, v.y & 0xFFFFu); mark(bm, v.y >> 16);
+    mark(bm, v.z & 0xFFFFu); mark(bm, v.z >> 16);
+    mark(bm, v.w & 0xFFFFu); mark(bm, v.w >> 16);
+}
+
+// Passes of gridDim.x * kPresThreads * kPresUnroll 16-byte chunks (w is 16-byte aligned), two
+// passes in flight: the next pass's loads are issued before this pass is marked.  The loads go
+// through a wave-uniform buffer resource per pass, clipped to the tensor, so they are unconditional
+// (bytes past the end read as zero with no memory access and are not marked) and the waits on them
+// can count.  Then the n % 8 tail.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pass_rsrc(const u32x4 *w4, uint64_t chunks, uint64_t pass,
+                                                            uint64_t span) {
+    const uint64_t start = std::min<uint64_t>(pass * span, chunks);
+    const uint64_t bytes = std::min<uint64_t>((chunks - start) * 16, span * 16);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(w4 + start), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+__global__ __launch_bounds__(kPresThreads) void k_enc_presence(const uint16_t *__restrict__ w, uint64_t n,
+                                                               uint32_t *__restrict__ map) {
     __shared__ uint32_t bm[kMapWords];
-    for (uint32_t i = threadIdx.x; i < kMapWords; i += kEncThreads) bm[i] = 0;
+    const uint32_t t = threadIdx.x;
+    for (uint32_t i = t; i < kMapWords; i += kPresThreads) bm[i] = 0;
     __syncthreads();
     const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w);
     const uint64_t chunks = n / 8;
-    for (uint64_t c = static_cast<uint64_t>(blockIdx.x) * kEncThreads + threadIdx.x; c < chunks;
-         c += static_cast<uint64_t>(gridDim.x) * kEncThreads) {
-        const u32x4 v = __builtin_nontemporal_load(w4 + c);
-        mark(bm, v.x & 0xFFFFu); mark(bm, v.x >> 16);
-        mark(bm, v.y & 0xFFFFu); mark(bm, v.y >> 16);
-        mark(bm, v.z & 0xFFFFu); mark(bm, v.z >> 16);
-        mark(bm, v.w & 0xFFFFu); mark(bm, v.w >> 16);
+    const uint32_t stride = gridDim.x * kPresThreads;      // chunks between a thread's loads
+    const uint64_t span = static_cast<uint64_t>(stride) * kPresUnroll;  // chunks per pass
+    const uint64_t passes = (chunks + span - 1) / span;
+    const uint32_t mine = blockIdx.x * kPresThreads + t;   // chunk of this thread's first load
+    u32x4 a[kPresUnroll], b[kPresUnroll];
+    auto load = [&](u32x4 (&v)[kPresUnroll], uint64_t pass) {
+        const __amdgpu_buffer_rsrc_t rs = pass_rsrc(w4, chunks, pass, span);
+#pragma unroll
+        for (int j = 0; j < kPresUnroll; ++j)
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>((mine + j * stride) * 16u), 0,
+                                                         kStreamOnce);
+    };
+    auto mark_pass = [&](const u32x4 (&v)[kPresUnroll], uint64_t pass) {
+#pragma unroll
+        for (int j = 0; j < kPresUnroll; ++j)
+            if (pass * span + mine + static_cast<uint64_t>(j) * stride < chunks) mark8(bm, v[j]);
+    };
+    load(a, 0);
+    for (uint64_t p = 0; p < passes; p += 2) {
+        load(b, p + 1);
+        mark_pass(a, p);
+        load(a, p + 2);
+        mark_pass(b, p + 1);
     }
-    if (blockIdx.x == 0 && threadIdx.x < n % 8) mark(bm, w[chunks * 8 + threadIdx.x]);
+    if (blockIdx.x == 0 && t < n % 8) mark(bm, w[chunks * 8 + t]);
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < kMapWords; i += kEncThreads)
-        if (bm[i]) atomicOr(&map[i], bm[i]);
+    uint32_t *copy = map + (blockIdx.x % kCopies) * kMapWords;
+    for (uint32_t i = t; i < kMapWords; i += kPresThreads)
+        if (bm[i]) atomicOr(&copy[i], bm[i]);
 }
 
-// One workgroup of 1024 threads, two bitmap words each.
-__global__ __launch_bounds__(1024) void k_enc_rank(const uint32_t *__restrict__ map, uint16_t *__restrict__ codebook,
-                                                   uint16_t *__restrict__ index_of, uint32_t *__restrict__ meta) {
-    __shared__ uint32_t part[1024];
-    const uint32_t t = threadIdx.x;
-    const uint32_t m0 = map[2 * t], m1 = map[2 * t + 1];
-    const uint32_t c = __popc(m0) + __popc(m1);
-    part[t] = c;
-    __syncthreads();
-    // inclusive scan (Hillis-Steele) of the per-thread counts
-    for (uint32_t off = 1; off < 1024; off <<= 1) {
-        const uint32_t v = t >= off ? part[t - off] : 0u;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
-    }
-    uint32_t rank = part[t] - c;  // entries before this thread's 64 patterns
+// Lane packs its 32 indices (two per word of p, low half first) into B words at out[0..B).
+template <int B>
+__device__ __forceinline__ void pack32(const uint32_t (&p)[16], uint32_t *out) {
+    uint32_t o[B];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t m = h ? m1 : m0;
-        while (m) {
-            const uint32_t bit = __ffs(m) - 1;
-            const uint32_t v = (2 * t + h) * 32 + bit;
-            codebook[rank] = static_cast<uint16_t>(v);
-            index_of[v] = static_cast<uint16_t>(rank);
-            ++rank;
-            m &= m - 1;
-        }
+    for (int k = 0; k < B; ++k) o[k] = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t idx = (i & 1) ? (p[i >> 1] >> 16) : (p[i >> 1] & 0xFFFFu);
+        const int bit = i * B, word = bit >> 5, off = bit & 31;
+        o[word] |= idx << off;
+        if (off + B > 32) o[word + 1] |= idx >> (32 - off);
     }
-    if (t == 1023) {
-        const uint32_t U = part[1023];
-        uint32_t b = 0;
-        while ((1u << b) < U) ++b;
+#pragma unroll
+    for (int k = 0; k < B; ++k) out[k] = o[k];
+}
+
+// The index of a present pattern v is its rank among the present patterns: the number of set
+// bits before it in the bitmap, i.e. the exclusive prefix of its bitmap word plus the set bits
+// below it within that word.  rt[i] = {bitmap word i, present patterns in words < i}.
+__device__ __forceinline__ uint32_t index_of(const uint2 *rt, uint32_t v) {
+    const uint2 e = rt[v >> 5];
+    return e.y + __popc(e.x & ((1u << (v & 31)) - 1u));
+}
+
+template <int B>
+__device__ void pack_blocks(const uint16_t *__restrict__ w, uint64_t n, const uint2 *rt,
+                            uint32_t *__restrict__ words, uint16_t *sidx, uint32_t *sout,
+                            const u32x4 (&pre)[4]) {
+    const uint64_t words_total = ((n * B + 31) / 32 + 3) / 4 * 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t blocks = (n + kPackFields - 1) / kPackFields;
+    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kPackWaves + wave;
+    u32x4 *words4 = reinterpret_cast<u32x4 *>(words);
+    for (uint64_t blk = first; blk < blocks; blk += static_cast<uint64_t>(gridDim.x) * kPackWaves) {
+        const uint64_t f0 = blk * kPackFields;
+        // coalesced: load q covers fields [q*512 + lane*8, +8) of the block
+        if (f0 + kPackFields <= n) {
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(w + f0);
+            u32x4 v[4];
+            if (blk == first) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = pre[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = __builtin_nontemporal_load(p + q * 64 + lane);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t h[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+                uint32_t r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = index_of(rt, h[e] & 0xFFFFu) | (index_of(rt, h[e] >> 16) << 16);
+                u32x4 o;
+                o.x = r[0]; o.y = r[1]; o.z = r[2]; o.w = r[3];
+                *reinterpret_cast<u32x4 *>(sidx + q * 512 + lane * 8) = o;
+            }
+        } else {
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q)
+#pragma unroll 1
+                for (int e = 0; e < 8; ++e) {
+                    const uint64_t f = f0 + q * 512 + lane * 8 + e;
+                    sidx[q * 512 + lane * 8 + e] = f < n ? static_cast<uint16_t>(index_of(rt, w[f])) : uint16_t(0);
+                }
+        }
+        // sidx and sout are the same wave-private stage.  LDS runs one wave's accesses in issue
+        // order, so each phase reads what the previous one wrote and the next one overwrites it
+        // only afterwards; the compiler barriers keep each phase's accesses on its side.
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        uint32_t pr[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(sidx + lane * 32 + j * 8);
+            pr[4 * j] = v.x; pr[4 * j + 1] = v.y; pr[4 * j + 2] = v.z; pr[4 * j + 3] = v.w;
+        }
+        pack32<B>(pr, sout + lane * B);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        // the block's 64 B words (16 B quads) are contiguous in the stream; clip at the end
+        const uint64_t q0 = blk * 16 * B;
+        for (uint32_t j = static_cast<uint32_t>(lane); j < 16u * B; j += 64)
+            if ((q0 + j) * 4 < words_total)
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(sout + 4 * j), words4 + q0 + j);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+}
+
+// Every workgroup ranks the bitmap itself (prefix sums of its 2,048 words' popcounts into an LDS
+// table), so no separate rank launch is needed; workgroups share out the codebook writes and
+// workgroup 0 writes U and b.  Each wave's first block is loaded before the ranking so that the
+// stream is already in flight while the table is built.
+__global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__restrict__ w, uint64_t n,
+                                                              const uint32_t *__restrict__ map,
+                                                              uint16_t *__restrict__ codebook,
+                                                              uint32_t *__restrict__ meta,
+                                                              uint32_t *__restrict__ words) {
+    // one 4 KB stage per wave: first the block's 2,048 indices, then (after every lane has read its
+    // 32) the block's 64 b packed words
+    __shared__ u32x4 stage[kPackWaves][256];
+    __shared__ uint2 rt[kMapWords];
+    __shared__ uint32_t wave_sum[kPackWaves];
+    const uint32_t t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(t >> 6);
+
+    // rank table: thread t owns bitmap words 2t and 2t+1, the OR of their copies (loaded first:
+    // the wait for them then leaves the four block loads below in flight)
+    static_assert(kPackWaves * 64 * 2 == kMapWords, "two bitmap words per thread");
+    uint2 m = make_uint2(0, 0);
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+        const uint2 e = reinterpret_cast<const uint2 *>(map + c * kMapWords)[t];
+        m.x |= e.x;
+        m.y |= e.y;
+    }
+    // unconditional buffer loads through a wave-uniform resource clipped to the tensor: bytes past
+    // its end read as zero without a memory access (a partial block's values go unused)
+    u32x4 pre[4];
+    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kPackWaves + wave_u;
+    const uint64_t f_first = std::min<uint64_t>(first * kPackFields, n);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(w + f_first), static_cast<short>(0),
+        static_cast<int>(std::min<uint64_t>((n - f_first) * 2, kPackFields * 2)), 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        pre[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, q * 1024 + lane * 16, 0, kStreamOnce);
+    const uint32_t c0 = __popc(m.x), cnt = c0 + __popc(m.y);
+    uint32_t incl = cnt;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0, U = 0;
+#pragma unroll
+    for (int i = 0; i < kPackWaves; ++i) {
+        base += i < wave ? wave_sum[i] : 0u;
+        U += wave_sum[i];
+    }
+    const uint32_t excl = base + incl - cnt;
+    rt[2 * t] = make_uint2(m.x, excl);
+    rt[2 * t + 1] = make_uint2(m.y, excl + c0);
+    uint32_t b = 0;
+    while ((1u << b) < U) ++b;
+    b = __builtin_amdgcn_readfirstlane(b);
+    if (blockIdx.x == 0 && t == 0) {
         meta[0] = U;
         meta[1] = b;
     }
-}
+    __syncthreads();
+    // the codebook: word i (handled by workgroup i % grid) holds entries [its prefix, ...) in order
+    for (uint32_t i = blockIdx.x + t * gridDim.x; i < kMapWords; i += gridDim.x * (64 * kPackWaves)) {
+        const uint2 e = rt[i];
+        uint32_t bits = e.x, r = e.y;
+        while (bits) {
+            codebook[r++] = static_cast<uint16_t>(i * 32 + __ffs(bits) - 1);
+            bits &= bits - 1;
+        }
+    }
 
-// Each lane packs fields [32 q, 32 q + 32) of its wave block into b words; fields >= n pack as 0.
-__global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__restrict__ w, uint64_t n,
-                                                              const uint16_t *__restrict__ index_of,
-                                                              const uint32_t *__restrict__ meta,
-                                                              uint32_t *__restrict__ words) {
-    __shared__ uint32_t stage[kPackWaves][64 * 16];
-    const uint32_t b = meta[1];
-    if (b == 0) return;
-    const uint64_t words_total = ((n * b + 31) / 32 + 3) / 4 * 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t *st = stage[wave];
-    const uint64_t blocks = (n + kPackFields - 1) / kPackFields;
-    for (uint64_t blk = static_cast<uint64_t>(blockIdx.x) * kPackWaves + wave; blk < blocks;
-         blk += static_cast<uint64_t>(gridDim.x) * kPackWaves) {
-        const uint64_t f0 = blk * kPackFields + static_cast<uint64_t>(lane) * 32;
-        uint32_t idx[32];
-        if (f0 + 32 <= n) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(w + f0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 v = __builtin_nontemporal_load(p + q);
-                const uint32_t h[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    idx[8 * q + 2 * e] = index_of[h[e] & 0xFFFFu];
-                    idx[8 * q + 2 * e + 1] = index_of[h[e] >> 16];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) idx[i] = f0 + i < n ? index_of[w[f0 + i]] : 0u;
-        }
-        // 32 fields of b bits = exactly b words
-        uint64_t acc = 0;
-        uint32_t nb = 0, k = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            acc |= static_cast<uint64_t>(idx[i]) << nb;
-            nb += b;
-            if (nb >= 32) {
-                st[lane * b + k] = static_cast<uint32_t>(acc);
-                ++k;
-                acc >>= 32;
-                nb -= 32;
-            }
-        }
-        // LDS executes one wave's accesses in order; the compiler barriers keep the reads below the
-        // writes and the next block's writes below these reads.
-        asm volatile("" ::: "memory");
-        // the wave's 64 b words are contiguous in the stream: coalesced stores, clipped at the end
-        const uint64_t w0 = blk * 64 * b;
-        for (uint32_t j = static_cast<uint32_t>(lane); j < 64 * b; j += 64)
-            if (w0 + j < words_total) words[w0 + j] = st[j];
-        asm volatile("" ::: "memory");
+    uint16_t *si = reinterpret_cast<uint16_t *>(stage[wave]);
+    uint32_t *so = reinterpret_cast<uint32_t *>(stage[wave]);
+    switch (b) {
+    case 1: pack_blocks<1>(w, n, rt, words, si, so, pre); break;
+    case 2: pack_blocks<2>(w, n, rt, words, si, so, pre); break;
+    case 3: pack_blocks<3>(w, n, rt, words, si, so, pre); break;
+    case 4: pack_blocks<4>(w, n, rt, words, si, so, pre); break;
+    case 5: pack_blocks<5>(w, n, rt, words, si, so, pre); break;
+    case 6: pack_blocks<6>(w, n, rt, words, si, so, pre); break;
+    case 7: pack_blocks<7>(w, n, rt, words, si, so, pre); break;
+    case 8: pack_blocks<8>(w, n, rt, words, si, so, pre); break;
+    case 9: pack_blocks<9>(w, n, rt, words, si, so, pre); break;
+    case 10: pack_blocks<10>(w, n, rt, words, si, so, pre); break;
+    case 11: pack_blocks<11>(w, n, rt, words, si, so, pre); break;
+    case 12: pack_blocks<12>(w, n, rt, words, si, so, pre); break;
+    case 13: pack_blocks<13>(w, n, rt, words, si, so, pre); break;
+    case 14: pack_blocks<14>(w, n, rt, words, si, so, pre); break;
+    case 15: pack_blocks<15>(w, n, rt, words, si, so, pre); break;
+    case 16: pack_blocks<16>(w, n, rt, words, si, so, pre); break;
+    default: break;  // b == 0: no words
     }
 }
 
 }  // namespace
 
-size_t encode_gpu_workspace_bytes() { return kWsMapBytes + kWsIndexBytes; }
+size_t encode_gpu_workspace_bytes() { return kWsMapBytes; }
 
 cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
                              uint32_t *words, uint32_t *meta, hipStream_t s) {
@@ -171,15 +310,18 @@ cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uin
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return CBK_E_HIP;
     uint32_t *map = static_cast<uint32_t *>(workspace);
-    uint16_t *index_of = reinterpret_cast<uint16_t *>(static_cast<unsigned char *>(workspace) + kWsMapBytes);
-    hipLaunchKernelGGL(k_enc_clear, dim3(kMapWords / 256), dim3(256), 0, s, map);
-    const uint64_t chunk_blocks = (n / 8 + kEncThreads - 1) / kEncThreads;
-    const uint32_t pgrid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(static_cast<uint64_t>(cus) * 2, chunk_blocks)));
-    hipLaunchKernelGGL(k_enc_presence, dim3(pgrid), dim3(kEncThreads), 0, s, w, n, map);
-    hipLaunchKernelGGL(k_enc_rank, dim3(1), dim3(1024), 0, s, map, codebook, index_of, meta);
+    hipLaunchKernelGGL(k_enc_clear, dim3(kCopies * kMapWords / 256), dim3(256), 0, s, map);
+    const uint64_t per_block = static_cast<uint64_t>(kPresThreads) * kPresUnroll;
+    const uint64_t chunk_blocks = (n / 8 + per_block - 1) / per_block;
+    const uint32_t pgrid = static_cast<uint32_t>(
+        std::max<uint64_t>(1, std::min<uint64_t>(static_cast<uint64_t>(cus), chunk_blocks)));
+    hipLaunchKernelGGL(k_enc_presence, dim3(pgrid), dim3(kPresThreads), 0, s, w, n, map);
+    // one workgroup per CU (the LDS stage and rank table take half a CU's LDS); at least one, so
+    // that U, b and the codebook are written even for n == 0
     const uint64_t blocks = (n + kPackFields - 1) / kPackFields;
-    const uint32_t kgrid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(static_cast<uint64_t>(cus) * 4, (blocks + kPackWaves - 1) / kPackWaves)));
-    hipLaunchKernelGGL(k_enc_pack, dim3(kgrid), dim3(64 * kPackWaves), 0, s, w, n, index_of, meta, words);
+    const uint32_t kgrid = static_cast<uint32_t>(std::max<uint64_t>(
+        1, std::min<uint64_t>(static_cast<uint64_t>(cus), (blocks + kPackWaves - 1) / kPackWaves)));
+    hipLaunchKernelGGL(k_enc_pack, dim3(kgrid), dim3(64 * kPackWaves), 0, s, w, n, map, codebook, meta, words);
     return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
 }
 

@@ -19,12 +19,19 @@ import os
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCE = os.path.join(ROOT, "fly_decode_amd", "csrc", "cbk_kernels.hip")
+CSRC = os.path.join(ROOT, "fly_decode_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "cbk_kernels.hip")
+ENCODER_SOURCE = os.path.join(CSRC, "cbk_encode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def source_for(kernel: str) -> str:
+    """The source file that defines a kernel (the encoder's kernels are named k_enc_*)."""
+    return ENCODER_SOURCE if kernel.startswith("k_enc") else KERNEL_SOURCE
+
+
+def kernel_source_sha256(kernel: str = "") -> str:
+    with open(source_for(kernel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -60,17 +67,21 @@ def counter_per_dispatch(run_dir: str, counter: str, kernel_prefix: str):
 
 def summarize_traffic(out_json: str, kernel_prefix: str, fetch_dir: str, write_dir: str,
                       copy_fetch_dir: str, copy_write_dir: str, copy_bytes: int,
-                      algorithmic_bytes: float, command: str, copy_kernel_prefix: str = "__amd_rocclr_copyBuffer"):
+                      algorithmic_bytes: float, command: str, copy_kernel_prefix: str = "__amd_rocclr_copyBuffer",
+                      dispatches_per_unit: int = 1):
+    """Traffic per unit of work: the mean counter value over the matching dispatches times
+    `dispatches_per_unit` (a unit that is several different kernels, one dispatch each, sums them)."""
     f_k, n_f = counter_per_dispatch(fetch_dir, "FETCH_SIZE", kernel_prefix)
     w_k, n_w = counter_per_dispatch(write_dir, "WRITE_SIZE", kernel_prefix)
     f_c, _ = counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", copy_kernel_prefix)
     w_c, _ = counter_per_dispatch(copy_write_dir, "WRITE_SIZE", copy_kernel_prefix)
     # scale: bytes per counter unit, from the copy of known size (reads copy_bytes, writes copy_bytes)
     fetch_scale, write_scale = copy_bytes / f_c, copy_bytes / w_c
-    read_b, write_b = f_k * fetch_scale, w_k * write_scale
+    read_b, write_b = f_k * fetch_scale * dispatches_per_unit, w_k * write_scale * dispatches_per_unit
     rec = {
         "kernel": kernel_prefix,
-        "source_sha256": kernel_source_sha256(),
+        "dispatches_per_unit": dispatches_per_unit,
+        "source_sha256": kernel_source_sha256(kernel_prefix),
         "fetch_size_per_dispatch": f_k, "fetch_dispatches": n_f,
         "write_size_per_dispatch": w_k, "write_dispatches": n_w,
         "copy_bytes": copy_bytes, "copy_fetch_size": f_c, "copy_write_size": w_c,
@@ -100,7 +111,7 @@ def traffic_for(kernel_key: str, workload: str):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_sha256():
+    if rec.get("source_sha256") != kernel_source_sha256(kernel_key):
         return None
     return rec
 

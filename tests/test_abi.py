@@ -173,7 +173,8 @@ def test_gpu_calls_validate_before_any_hip_call(cbk):
 def test_gpu_encoder_validates_before_any_hip_call(cbk):
     """cbk_encode_gpu rejects bad arguments on the host (no device is present here)."""
     lib = cbk.load_library()
-    assert lib.cbk_encode_gpu_workspace_bytes() == 2048 * 4 + 65536 * 2
+    # eight copies of the 65,536-bit presence bitmap
+    assert lib.cbk_encode_gpu_workspace_bytes() == 8 * 2048 * 4
     W, WS, CB, WD, M = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
     cap = cbk.words_for(1000, 16)
     assert lib.cbk_encode_gpu(None, 1000, WS, CB, WD, cap, M, None) == 1          # null w
