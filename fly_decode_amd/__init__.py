@@ -1,6 +1,7 @@
 """fly_decode_amd -- lossless codebook-compressed BF16 weights decoded on MI355X (gfx950).
 
-A thin ctypes binding over ``libcbk.so`` (C ABI declared in ``include/cbk.h``).  Every step of the
+A thin ctypes binding over ``libcbk.so`` (C ABI declared in ``include/cbk.h`` and, for the
+exponent entropy-coded format, ``include/cbk_ec.h``).  Every step of the
 hot path runs in the library's HIP kernels; this module only marshals arguments.  PyTorch is used
 for device memory and streams: inputs and outputs are torch tensors whose ``data_ptr()`` is handed
 to the library, and GPU calls are enqueued on ``torch.cuda.current_stream()``.
@@ -17,7 +18,7 @@ import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
            "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
-           "load_library"]
+           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcbk.so")
@@ -37,6 +38,16 @@ class CbkError(RuntimeError):
 class _Tensor(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64), ("U", ctypes.c_uint32),
                 ("b", ctypes.c_uint32), ("codebook", ctypes.c_void_p), ("words", ctypes.c_void_p)]
+
+
+class _ECHeader(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64), ("lengths", ctypes.c_uint8 * 256)]
+
+
+class _ECTensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64), ("sm", ctypes.c_void_p),
+                ("stream", ctypes.c_void_p), ("gaps", ctypes.c_void_p), ("bases", ctypes.c_void_p),
+                ("lut", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -82,6 +93,17 @@ def load_library():
         lib.cbk_gemm_group.argtypes = [tp, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p),
                                        ctypes.POINTER(ctypes.c_uint64), ctypes.c_void_p]
+        hp = ctypes.POINTER(_ECHeader)
+        for name in ("cbk_ec_spans", "cbk_ec_stream_words", "cbk_ec_gap_words", "cbk_ec_blocks",
+                     "cbk_ec_stored_bytes"):
+            getattr(lib, name).restype = ctypes.c_uint64
+            getattr(lib, name).argtypes = [hp]
+        lib.cbk_ec_plan.restype = ctypes.c_int
+        lib.cbk_ec_plan.argtypes = [ctypes.c_void_p, ctypes.c_uint64, hp]
+        lib.cbk_ec_encode.restype = ctypes.c_int
+        lib.cbk_ec_encode.argtypes = [ctypes.c_void_p, hp] + [ctypes.c_void_p] * 5
+        lib.cbk_ec_decode_bf16.restype = ctypes.c_int
+        lib.cbk_ec_decode_bf16.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -290,3 +312,89 @@ def gemm_group(ts, X, Ys=None, stream=None):
     _check(load_library().cbk_gemm_group(arr, len(ts), ctypes.c_void_p(X.data_ptr() or None), X.stride(0),
                                          batch, yp, ld, _stream(stream)), "cbk_gemm_group")
     return Ys
+
+
+# ---- exponent entropy-coded format (include/cbk_ec.h)
+
+class ECTensor:
+    """A tensor in the exponent entropy-coded format: code lengths, stream length and the arrays
+    sm (uint8[n]), stream (uint32), gaps (uint32), bases (uint32) and lut (uint16[4096]).  Host
+    numpy arrays after ``ec_encode``; ``to(device)`` gives torch tensors on the device."""
+
+    def __init__(self, rows, cols, total_bits, lengths, sm, stream, gaps, bases, lut):
+        self.rows, self.cols, self.total_bits = int(rows), int(cols), int(total_bits)
+        self.lengths = list(lengths)
+        self.sm, self.stream, self.gaps, self.bases, self.lut = sm, stream, gaps, bases, lut
+
+    @property
+    def n(self) -> int:
+        return self.rows * self.cols
+
+    def _header(self) -> _ECHeader:
+        h = _ECHeader()
+        h.n, h.total_bits = self.n, self.total_bits
+        for s, l in enumerate(self.lengths):
+            h.lengths[s] = l
+        return h
+
+    @property
+    def stored_bytes(self) -> int:
+        return int(load_library().cbk_ec_stored_bytes(ctypes.byref(self._header())))
+
+    def to(self, device) -> "ECTensor":
+        import torch
+
+        def put(a, view, pad16=False):
+            a = np.ascontiguousarray(a)
+            if pad16:  # the decoder may read the sm bytes up to a 16-byte boundary
+                a = np.concatenate([a, np.zeros((-a.size) % 16, dtype=a.dtype)])
+            return torch.from_numpy(a.view(view)).to(device)
+        return ECTensor(self.rows, self.cols, self.total_bits, self.lengths, put(self.sm, np.uint8, True),
+                        put(self.stream, np.int32), put(self.gaps, np.int32), put(self.bases, np.int32),
+                        put(self.lut, np.int16))
+
+    def _struct(self) -> _ECTensor:
+        def ptr(a):
+            return a.data_ptr() if a.numel() else None
+        return _ECTensor(self.n, self.total_bits, ptr(self.sm), ptr(self.stream), ptr(self.gaps),
+                         ptr(self.bases), ptr(self.lut))
+
+
+def ec_encode(w, rows: int | None = None, cols: int | None = None) -> ECTensor:
+    """Host encode (cbk_ec_plan, then cbk_ec_encode) of 16-bit patterns [rows][cols]."""
+    if hasattr(w, "detach"):
+        w = w.detach().contiguous().cpu().view(__import__("torch").int16).numpy()
+    w = np.ascontiguousarray(w)
+    if w.dtype not in (np.uint16, np.int16):
+        raise TypeError("ec_encode expects 16-bit patterns")
+    if rows is None:
+        rows, cols = (w.shape if w.ndim == 2 else (1, w.size))
+    flat = w.reshape(-1).view(np.uint16)
+    if flat.size != rows * cols:
+        raise ValueError("rows * cols does not match the array size")
+    lib = load_library()
+    h = _ECHeader()
+    src = flat.ctypes.data if flat.size else None
+    _check(lib.cbk_ec_plan(src, flat.size, ctypes.byref(h)), "cbk_ec_plan")
+    hp = ctypes.byref(h)
+    sm = np.zeros(flat.size, dtype=np.uint8)
+    stream = np.zeros(int(lib.cbk_ec_stream_words(hp)), dtype=np.uint32)
+    gaps = np.zeros(int(lib.cbk_ec_gap_words(hp)), dtype=np.uint32)
+    bases = np.zeros(int(lib.cbk_ec_blocks(hp)), dtype=np.uint32)
+    lut = np.zeros(4096, dtype=np.uint16)
+
+    def p(a):
+        return a.ctypes.data if a.size else None
+    _check(lib.cbk_ec_encode(src, hp, p(sm), p(stream), p(gaps), p(bases), p(lut)), "cbk_ec_encode")
+    return ECTensor(rows, cols, h.total_bits, list(h.lengths), sm, stream, gaps, bases, lut)
+
+
+def ec_decode_bf16(t: ECTensor, out=None, stream=None):
+    """GPU decode of an ECTensor on the device into a [rows][cols] torch.bfloat16 tensor."""
+    import torch
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device=t.sm.device)
+    st = t._struct()
+    _check(load_library().cbk_ec_decode_bf16(ctypes.byref(st), ctypes.c_void_p(out.data_ptr() if out.numel() else None),
+                                             _stream(stream)), "cbk_ec_decode_bf16")
+    return out

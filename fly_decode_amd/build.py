@@ -21,7 +21,8 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang
                 "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
-SOURCES = [("cbk_api.cpp", False), ("cbk_kernels.hip", True), ("cbk_encode.hip", True)]
+SOURCES = [("cbk_api.cpp", False), ("cbk_kernels.hip", True), ("cbk_encode.hip", True),
+           ("cbk_ec_host.cpp", False), ("cbk_ec.hip", True)]
 
 
 def _run(cmd):

@@ -1,11 +1,12 @@
-// Internal interface between the host API (cbk_api.cpp) and the HIP launchers (cbk_kernels.hip,
-// cbk_encode.hip).
+// Internal interface between the host API (cbk_api.cpp, cbk_ec_host.cpp) and the HIP launchers
+// (cbk_kernels.hip, cbk_encode.hip, cbk_ec.hip).
 // Arguments reaching these launchers are already validated.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/cbk.h"
+#include "../../include/cbk_ec.h"
 
 namespace cbk {
 
@@ -22,5 +23,8 @@ cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_
 size_t encode_gpu_workspace_bytes();
 cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
                              uint32_t *words, uint32_t *meta, hipStream_t s);
+
+// Exponent entropy-coded format (cbk_ec.hip).
+cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s);
 
 }  // namespace cbk

@@ -1,0 +1,109 @@
+/*
+ * cbk_ec.h -- C ABI of libcbk's exponent entropy-coded BF16 format: the sign and the 7 mantissa
+ * bits of every weight stay as they are (one byte), and only the 8 exponent bits are replaced by
+ * a prefix (Huffman) code, decoded on an MI355X (gfx950) GPU back to the exact BF16 patterns.
+ *
+ * The method (DFloat11 article on gadzety360.pl, sections "Przełom: DFloat11" and "Jak to działa
+ * w praktyce?"): of the 16 bits of a BF16 weight, the sign and mantissa carry nearly their full
+ * information but the exponent only about 2.6 bits, so an entropy code on the exponent alone
+ * gives a lossless format of about 11 bits per weight; the GPU decoder keeps small lookup tables
+ * in on-chip memory, and its threads first find how many values they will decode, synchronise,
+ * then write the values to their places.  The format fixed here:
+ *
+ *   sm        n bytes, sm[i] = sign << 7 | mantissa of weight i;
+ *   code      for every exponent value present, a length in 1..12: an optimal prefix code
+ *             among those with lengths <= 12 (a tensor with one exponent value gets length 1);
+ *             codes are canonical: ordered by (length, exponent value), each the previous plus
+ *             one, shifted left where the length grows;
+ *   stream    the exponents' codes in weight order, first code bit first, packed into a
+ *             little-endian uint32 stream read least significant bit first; total_bits long,
+ *             padded with zero bits to whole 64-bit spans (2 words per span);
+ *   gaps      per span j, 4 bits (eight per uint32, span j at bits 4*(j%8) of word j/8): the
+ *             offset within the span of the first code that starts in it (the stream end if none
+ *             does), so every span decodes on its own;
+ *   bases     per block of 256 spans, the index of the first weight whose code starts in it;
+ *   lut       4096 uint16: entry v = exponent | length << 8 of the code that the 12 stream bits
+ *             v (first bit = bit 0) begin with; entries no code reaches hold 12 << 8.
+ *
+ * Conventions as in cbk.h: status codes, host-side validation before any HIP call, device
+ * pointers in a host struct, caller-owned buffers, no allocation, asynchronous on `stream`.
+ */
+#ifndef CBK_EC_H
+#define CBK_EC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "cbk.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CBK_EC_MAX_LEN 12
+#define CBK_EC_SPAN_BITS 64
+#define CBK_EC_BLOCK_SPANS 256
+#define CBK_EC_LUT_ENTRIES 4096
+
+/* What the host encoder's first pass decides; fixes every array size. */
+typedef struct {
+    uint64_t n;            /* weights, < 2^32                                          */
+    uint64_t total_bits;   /* length of the exponent code stream in bits              */
+    uint8_t lengths[256];  /* code length of each exponent value; 0 = value absent    */
+} cbk_ec_header;
+
+/* Sizes that follow from a header: spans = ceil(total_bits / 64); stream words = 2 * spans;
+ * gap words = ceil(spans / 8); blocks = ceil(spans / 256).  Stored bytes (the accounting size):
+ * n + 4 * (stream words + gap words + blocks) + 2 * 4096 + 256. */
+uint64_t cbk_ec_spans(const cbk_ec_header *h);
+uint64_t cbk_ec_stream_words(const cbk_ec_header *h);
+uint64_t cbk_ec_gap_words(const cbk_ec_header *h);
+uint64_t cbk_ec_blocks(const cbk_ec_header *h);
+uint64_t cbk_ec_stored_bytes(const cbk_ec_header *h);
+
+/*
+ * cbk_ec_plan -- host, synchronous.  First pass over n patterns w: exponent counts, the capped
+ * optimal code lengths and the stream length, into *h.
+ * Errors: CBK_E_INVALID (NULL h, or NULL w with n > 0), CBK_E_UNSUPPORTED (n >= 2^32).
+ */
+cbk_status cbk_ec_plan(const uint16_t *w, uint64_t n, cbk_ec_header *h);
+
+/*
+ * cbk_ec_encode -- host, synchronous.  Second pass: writes the arrays for the header that
+ * cbk_ec_plan produced on the same w (sizes as above; lut has 4096 entries).  Arrays of size 0
+ * may be NULL.  Errors: CBK_E_INVALID (NULL pointer where a size is nonzero, or a header that
+ * does not describe w: an exponent without a code, a length above 12 or a wrong total_bits).
+ */
+cbk_status cbk_ec_encode(const uint16_t *w, const cbk_ec_header *h, uint8_t *sm, uint32_t *stream,
+                         uint32_t *gaps, uint32_t *bases, uint16_t *lut);
+
+/* An encoded tensor as the GPU sees it.  Host struct, device pointers, each 16-byte aligned. */
+typedef struct {
+    uint64_t n;
+    uint64_t total_bits;
+    const uint8_t *sm;       /* n bytes, in an allocation readable up to n rounded up
+                                to a multiple of 16 bytes     */
+    const uint32_t *stream;  /* cbk_ec_stream_words words     */
+    const uint32_t *gaps;    /* cbk_ec_gap_words words        */
+    const uint32_t *bases;   /* cbk_ec_blocks words           */
+    const uint16_t *lut;     /* 4096 entries                  */
+} cbk_ec_tensor;
+
+/*
+ * cbk_ec_decode_bf16 -- GPU.  out[i] = the original pattern of weight i, for i < n.  One
+ * workgroup per block of 256 spans: each thread decodes its span from its gap with the table
+ * (held in LDS) into LDS, a prefix sum of the per-thread counts places the values, and the
+ * block's outputs are joined with their sign-mantissa bytes and written with coalesced stores.
+ *   out   device, n uint16, 16-byte aligned.
+ * A corrupt stream cannot make the kernel read or write outside the arrays given (a span emits
+ * at most 64 values and the block writes at most its own range); the values are then undefined.
+ * Errors: CBK_E_INVALID (NULL pointer with n > 0, total_bits > 12 n or < n), CBK_E_ALIGN,
+ * CBK_E_UNSUPPORTED (n >= 2^32), CBK_E_HIP.
+ */
+cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBK_EC_H */

@@ -24,16 +24,22 @@ def cbk():
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "cbk.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(cbk_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(cbk_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["cbk_encode", "cbk_decode_bf16", "cbk_gemv", "cbk_gemv_group", "cbk_gemm_small", "cbk_gemm_group", "cbk_bits_for",
               "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str", "cbk_encode_gpu",
-              "cbk_encode_gpu_workspace_bytes"]:
+              "cbk_encode_gpu_workspace_bytes", "cbk_ec_plan", "cbk_ec_encode", "cbk_ec_decode_bf16",
+              "cbk_ec_spans", "cbk_ec_stream_words", "cbk_ec_gap_words", "cbk_ec_blocks",
+              "cbk_ec_stored_bytes"]:
         assert n in names
 
 

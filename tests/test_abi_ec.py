@@ -1,0 +1,116 @@
+"""CPU tests of the exponent entropy-coded format's C ABI (include/cbk_ec.h): the library's host
+encoder writes exactly the oracle's bytes, its code lengths are optimal under the 12-bit cap, and
+the GPU decode rejects bad arguments before any HIP call (no GPU is needed here)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import entropy as ec
+
+
+@pytest.fixture(scope="module")
+def cbk():
+    import os
+    import fly_decode_amd
+    if not os.path.exists(fly_decode_amd.library_path()):
+        from fly_decode_amd import build
+        build.build()
+    fly_decode_amd.load_library()
+    return fly_decode_amd
+
+
+def _inputs():
+    rng = np.random.default_rng(3)
+    return {
+        "gaussian_300x777": synth.gaussian_bf16((300, 777), 0.02, seed=[11]),
+        "t2_heavy_tail": synth.student_t_bf16((200, 1000), 2.0, 0.02, seed=[12]),
+        "t4_workload_like": synth.student_t_bf16((64, 4096), 4.0, 0.02, seed=[13]),
+        "constant": np.full((10, 100), 0x3F80, dtype=np.uint16),
+        "two_exponents": rng.choice(np.array([0x3F80, 0x4012], dtype=np.uint16), (7, 13)),
+        "every_pattern": rng.permutation(np.arange(65536, dtype=np.uint32)).astype(np.uint16).reshape(256, 256),
+        "specials": rng.choice(np.array([0x7F80, 0xFF80, 0x7FC1, 0x0000, 0x8000, 0x0001, 0x807F], dtype=np.uint16), (9, 111)),
+        "one": np.array([[0xC2F7]], dtype=np.uint16),
+    }
+
+
+@pytest.mark.parametrize("name", list(_inputs()))
+def test_host_encoder_matches_oracle(cbk, name):
+    w = _inputs()[name]
+    t = cbk.ec_encode(w)
+    # optimal under the cap: the same stream length as the oracle's own package-merge lengths
+    ref = ec.encode(w)
+    assert t.total_bits == ref.total_bits
+    assert max(t.lengths) <= ec.L_MAX
+    # given the library's lengths, every array equals the oracle's encoding byte for byte
+    o = ec.encode_with_lengths(w, t.lengths)
+    for a in ("sm", "stream", "gaps", "bases", "lut"):
+        assert np.array_equal(getattr(t, a), getattr(o, a)), a
+    assert t.stored_bytes == o.stored_bytes
+    assert np.array_equal(ec.decode(o), w.reshape(-1)) if w.size <= 70000 else True
+
+
+def test_empty_tensor(cbk):
+    t = cbk.ec_encode(np.zeros((0, 5), dtype=np.uint16))
+    assert t.total_bits == 0 and t.stream.size == 0 and t.gaps.size == 0 and t.bases.size == 0
+    assert t.lut.size == 4096
+
+
+def _hdr(cbk, n, total_bits, lengths):
+    h = cbk._ECHeader()
+    h.n, h.total_bits = n, total_bits
+    for s, l in lengths.items():
+        h.lengths[s] = l
+    return h
+
+
+def test_encode_rejects_a_header_that_does_not_describe_w(cbk):
+    lib = cbk.load_library()
+    w = np.array([0x3F80, 0x4000, 0x3F80], dtype=np.uint16)   # exponents 127, 128, 127
+    buf = [np.zeros(64, dtype=np.uint8), np.zeros(16, dtype=np.uint32), np.zeros(16, dtype=np.uint32),
+           np.zeros(16, dtype=np.uint32), np.zeros(4096, dtype=np.uint16)]
+    ptrs = [b.ctypes.data for b in buf]
+    ok = _hdr(cbk, 3, 3, {127: 1, 128: 1})
+    assert lib.cbk_ec_encode(w.ctypes.data, ctypes.byref(ok), *ptrs) == 0
+    assert lib.cbk_ec_encode(w.ctypes.data, ctypes.byref(_hdr(cbk, 3, 4, {127: 1, 128: 1})), *ptrs) == 1  # wrong length sum
+    assert lib.cbk_ec_encode(w.ctypes.data, ctypes.byref(_hdr(cbk, 3, 2, {127: 1})), *ptrs) == 1          # 128 has no code
+    assert lib.cbk_ec_encode(w.ctypes.data, ctypes.byref(_hdr(cbk, 3, 39, {127: 13, 128: 13})), *ptrs) == 1  # above 12
+    assert lib.cbk_ec_encode(w.ctypes.data, ctypes.byref(_hdr(cbk, 3, 3, {127: 1, 128: 1, 5: 1})), *ptrs) == 1  # Kraft > 1
+    assert lib.cbk_ec_encode(None, ctypes.byref(ok), *ptrs) == 1
+    assert lib.cbk_ec_plan(None, 5, ctypes.byref(ok)) == 1
+    assert lib.cbk_ec_plan(w.ctypes.data, 1 << 32, ctypes.byref(ok)) == 4
+
+
+def test_decode_validates_before_any_hip_call(cbk):
+    lib = cbk.load_library()
+    T = cbk._ECTensor
+    A = 0x10000   # 16-byte aligned stand-ins; nothing is dereferenced on these paths
+    good = dict(n=1000, total_bits=3000, sm=A, stream=A, gaps=A, bases=A, lut=A)
+
+    def call(out=A, **kw):
+        d = dict(good)
+        d.update(kw)
+        return lib.cbk_ec_decode_bf16(ctypes.byref(T(**d)), ctypes.c_void_p(out), None)
+    assert lib.cbk_ec_decode_bf16(None, ctypes.c_void_p(A), None) == 1
+    assert call(n=0, sm=None, stream=None, gaps=None, bases=None, lut=None, out=0) == 0   # empty: no-op
+    assert call(n=1 << 32, total_bits=1 << 33) == 4
+    for k in ("sm", "stream", "gaps", "bases", "lut"):
+        assert call(**{k: None}) == 1, k
+    assert call(out=0) == 1
+    assert call(total_bits=999) == 1            # fewer bits than weights
+    assert call(total_bits=12001) == 1          # more than 12 bits per weight
+    for k in ("sm", "stream", "gaps", "bases", "lut"):
+        assert call(**{k: A + 8}) == 3, k
+    assert call(out=A + 2) == 3
+
+
+def test_size_helpers(cbk):
+    lib = cbk.load_library()
+    for bits in [0, 1, 63, 64, 65, 64 * 256, 64 * 256 + 1, 10 ** 7]:
+        h = _hdr(cbk, max(1, bits // 3), bits, {})
+        spans = (bits + 63) // 64
+        assert lib.cbk_ec_spans(ctypes.byref(h)) == spans
+        assert lib.cbk_ec_stream_words(ctypes.byref(h)) == 2 * spans
+        assert lib.cbk_ec_gap_words(ctypes.byref(h)) == (spans + 7) // 8
+        assert lib.cbk_ec_blocks(ctypes.byref(h)) == (spans + 255) // 256

@@ -1,0 +1,119 @@
+"""GPU parity for the exponent entropy-coded format: cbk_ec_decode_bf16 (through the C ABI) must
+give back the exact input patterns, which the oracle's decoder also reproduces (the oracle's own
+pins are in test_oracle_entropy.py; the host encoder's bytes equal the oracle's in
+test_abi_ec.py)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import entropy as ec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import fly_decode_amd as cbk
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cbk.load_library()
+    return torch, cbk
+
+
+def _check(env, w, oracle_too=False):
+    torch, cbk = env
+    print(f"ec decode shape={w.shape}", flush=True)
+    t = cbk.ec_encode(w)
+    d = t.to("cuda")
+    out = cbk.ec_decode_bf16(d)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape)
+    assert np.array_equal(got, w), f"mismatch at {np.flatnonzero(got.reshape(-1) != w.reshape(-1))[:10]}"
+    if oracle_too:
+        o = ec.encode_with_lengths(w, t.lengths)
+        assert np.array_equal(ec.decode(o), got.reshape(-1))
+    return t
+
+
+def _cases():
+    rng = np.random.default_rng(21)
+    return {
+        "gaussian_300x777": synth.gaussian_bf16((300, 777), 0.02, seed=[41]),
+        "t2_heavy_tail": synth.student_t_bf16((200, 1000), 2.0, 0.02, seed=[42]),
+        "t4_64x4096": synth.student_t_bf16((64, 4096), 4.0, 0.02, seed=[43]),
+        "constant": np.full((10, 1000), 0x3F80, dtype=np.uint16),
+        "two_exponents": rng.choice(np.array([0x3F80, 0x4012], dtype=np.uint16), (70, 130)),
+        "every_pattern": rng.permutation(np.arange(65536, dtype=np.uint32)).astype(np.uint16).reshape(256, 256),
+        "specials": rng.choice(np.array([0x7F80, 0xFF80, 0x7FC1, 0x0000, 0x8000, 0x0001, 0x807F], dtype=np.uint16), (9, 111)),
+        "one": np.array([[0xC2F7]], dtype=np.uint16),
+    }
+
+
+@pytest.mark.parametrize("name", list(_cases()))
+def test_ec_decode_bit_exact(env, name):
+    w = _cases()[name]
+    t = _check(env, w, oracle_too=w.size <= 70000)
+    if name == "constant":
+        assert t.total_bits == w.size   # 64 one-bit codes in every span
+    if name == "t2_heavy_tail":
+        assert max(t.lengths) >= 10     # long codes, spans that start inside a code
+
+
+@pytest.mark.parametrize("n", [7, 8, 9, 63, 64, 65, 1000, 16383, 16384, 16385, 64 * 256 * 3 + 11])
+def test_ec_decode_ragged_lengths(env, n):
+    """Lengths around the 8-weight output segment, the 64-bit span and the 256-span block."""
+    w = synth.gaussian_bf16((1, n), 0.02, seed=[44, n])
+    _check(env, w)
+
+
+def test_ec_decode_workload_tensor(env):
+    """A 4096^2 tensor of the attention workload: every weight exact; the format stores about
+    10.6 bits per weight."""
+    w = synth.workload_tensor(2, 0, synth.WORKLOADS[2][0][0])
+    t = _check(env, w)
+    bits = 8.0 * t.stored_bytes / w.size
+    assert 10.0 < bits < 11.5, bits
+
+
+def test_ec_decode_writes_nothing_past_the_end(env):
+    torch, cbk = env
+    for n in (64 * 256 * 2 + 5, 8 * 700 + 1, 4096 + 8, 7, 3 * 4096):
+        print(f"ec guard n={n}", flush=True)
+        w = synth.gaussian_bf16((1, n), 0.02, seed=[45, n])
+        d = cbk.ec_encode(w).to("cuda")
+        buf = torch.full((n + 64,), -7, dtype=torch.int16, device="cuda")
+        assert buf.data_ptr() % 16 == 0
+        cbk.ec_decode_bf16(d, out=buf[:n].view(torch.bfloat16).view(1, n))
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        assert np.array_equal(got[:n].view(np.uint16), w.reshape(-1)), n
+        assert bool((got[n:] == -7).all()), n
+
+
+def test_ec_decode_repeated_launches_identical(env):
+    torch, cbk = env
+    w = synth.gaussian_bf16((512, 1024), 0.02, seed=[46])
+    d = cbk.ec_encode(w).to("cuda")
+    a = cbk.ec_decode_bf16(d).clone()
+    for _ in range(3):
+        b = cbk.ec_decode_bf16(d)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_ec_decode_corrupt_stream_stays_in_bounds(env):
+    """Random stream words and gaps (the table, bases and sizes valid): the values are undefined,
+    but nothing is written outside the output."""
+    torch, cbk = env
+    n = 64 * 256 * 2 + 100
+    w = synth.gaussian_bf16((1, n), 0.02, seed=[47])
+    t = cbk.ec_encode(w)
+    rng = np.random.default_rng(48)
+    bad = cbk.ECTensor(t.rows, t.cols, t.total_bits, t.lengths, t.sm,
+                       rng.integers(0, 2 ** 32, t.stream.size, dtype=np.uint64).astype(np.uint32),
+                       rng.integers(0, 2 ** 32, t.gaps.size, dtype=np.uint64).astype(np.uint32),
+                       t.bases, t.lut).to("cuda")
+    buf = torch.full((n + 64,), -7, dtype=torch.int16, device="cuda")
+    cbk.ec_decode_bf16(bad, out=buf[:n].view(torch.bfloat16).view(1, n))
+    torch.cuda.synchronize()
+    assert bool((buf[n:].cpu() == -7).all())
