@@ -21,6 +21,9 @@ each tensor with its own codebook):
   l70b_b1    the same tensors at batch 1, phases grouped as in llama7b.
   decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors, one launch
              per tensor; bytes = compressed reads + 2 bytes written per weight.
+  ecdecode4096 the attn4096 tensors in the exponent entropy-coded format (sign-mantissa bytes
+             raw, exponent Huffman-coded), decoded to BF16 in HBM by cbk_ec_decode_bf16, one launch
+             per tensor; bytes = the stored format read + 2 bytes written per weight.
   encode4096 the load-time path: cbk_encode_gpu of the attn4096 tensors from raw BF16 already in
              HBM (three launches per tensor); bytes = 2 bytes read per weight + the compressed
              form written; the result of the last step is checked against the host encoder.
@@ -60,7 +63,7 @@ def workload_tensors(name: str, count: int, layers: int):
     """(specs, phases, batch, layer_count): specs are (cfg, layer, tensor) triples; phases are lists
     of spec indices launched together (one launch per phase, phases run in order)."""
     import synth
-    if name in ("attn4096", "decode4096", "encode4096"):
+    if name in ("attn4096", "decode4096", "encode4096", "ecdecode4096"):
         t = synth.WORKLOADS[2][0][0]
         specs = [(2, layer, t) for layer in range(count)]
         return specs, [[i] for i in range(len(specs))], (1 if name == "attn4096" else 0), len(specs)
@@ -168,6 +171,32 @@ def cpu_baseline_encode(specs, seconds: float):
     }
 
 
+def cpu_baseline_ec(specs, seconds: float):
+    """The oracle's bit-by-bit decoder of the entropy-coded format (pure Python, one thread) on
+    leading rows of one tensor of the workload, growing the sample until about `seconds` pass."""
+    from oracle import entropy as ec
+    import synth
+
+    cfg, layer, t = specs[0]
+    w = synth.workload_tensor(cfg, layer, t)
+    rows, spent, done = 4, 0.0, 0
+    while spent < seconds and rows <= t.rows:
+        enc = ec.encode(w[:rows])
+        t0 = time.perf_counter()
+        ec.decode(enc)
+        spent += time.perf_counter() - t0
+        done += rows * t.cols
+        rows *= 2
+    return {
+        "value": round(2.0 * done / spent / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the oracle's bit-by-bit decoder (pure Python, one thread) on the leading 4, 8, ... "
+                  f"rows of one {t.rows}x{t.cols} tensor of the workload, {done} weights, {spent:.1f} s",
+    }
+
+
 def check_encoded(raws, hosts, codebooks, words, metas, which):
     """The device encodings of tensors `which` against the host encoder (exact)."""
     import fly_decode_amd as cbk
@@ -188,7 +217,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096",
-                                                           "encode4096"])
+                                                           "encode4096", "ecdecode4096"])
     ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers for mlp_b8 (8) and l70b_* (2)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -226,8 +255,17 @@ def main():
         phases = [[i] for ph in phases for i in ph]
     log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
     encode = args.workload == "encode4096"
+    ecfmt = args.workload == "ecdecode4096"
     t0 = time.perf_counter()
-    if encode:
+    if ecfmt:
+        def make_ec(spec):
+            cfg, layer, t = spec
+            return cbk.ec_encode(synth.workload_tensor(cfg, layer, t))
+        import synth
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            tensors = [e.to("cuda") for e in ex.map(make_ec, specs)]
+        log(f"entropy-coded {len(tensors)} tensors")
+    elif encode:
         raws, hosts = prepare(specs, threads, raw=True)
         tensors = hosts
         ws = torch.empty(cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
@@ -246,7 +284,7 @@ def main():
             xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
     if encode:
         ys = []
-    elif batch == 0:
+    elif batch == 0:  # decode outputs (both formats)
         ys = [torch.empty((d.rows, d.cols), dtype=torch.bfloat16, device="cuda") for d in tensors]
     elif batch == 1:
         xs = {k: v[0] for k, v in xs.items()}
@@ -259,6 +297,8 @@ def main():
             if encode:
                 i = ph[0]
                 cbk.encode_gpu_launch(raws[i], ws, enc_cb[i], enc_words[i], enc_meta[i])
+            elif ecfmt:
+                cbk.ec_decode_bf16(tensors[ph[0]], out=ys[ph[0]])
             elif batch == 0:
                 cbk.decode_bf16(tensors[ph[0]], out=ys[ph[0]])
             elif batch > 1 and len(ph) == 1:
@@ -313,25 +353,29 @@ def main():
     avg_launch_s = ms_step * 1e-3 / launches
 
     n_total = sum(d.n for d in tensors)
-    # algorithmic bytes: packed indices + codebook + Y for every tensor, X once per launch
-    comp_total = sum(d.compressed_bytes + 4 * batch * d.rows for d in tensors) + \
-        sum(2 * batch * tensors[ph[0]].cols for ph in phases)
-    if batch == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
+    if ecfmt:  # the stored entropy-coded form read + the BF16 written
+        comp_total = sum(d.stored_bytes + 2 * d.n for d in tensors)
+    elif batch == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
         comp_total = sum(d.compressed_bytes + 2 * d.n for d in tensors)
+    else:  # packed indices + codebook + Y for every tensor, X once per launch
+        comp_total = sum(d.compressed_bytes + 4 * batch * d.rows for d in tensors) + \
+            sum(2 * batch * tensors[ph[0]].cols for ph in phases)
     step_s = ms_step * 1e-3
     value = 2.0 * n_total / step_s / 1e9
     comp_gbps = comp_total / step_s / 1e9
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
-    bits = sorted({d.b for d in tensors})
-    kernel = ("k_enc" if encode else "k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
+    bits = sorted({d.b for d in tensors}) if not ecfmt else [max(max(d.lengths) for d in tensors)]
+    kernel = ("k_enc" if encode else "k_ec_decode" if ecfmt else "k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
               else "k_gemm_valu" if batch <= 8 else "k_gemm_mfma")
-    kernel_key = f"{kernel}_b{bits[-1]}"
+    kernel_key = kernel if ecfmt else f"{kernel}_b{bits[-1]}"
     traffic = profiling.traffic_for(kernel_key, args.workload)
 
     result = {
         "metric": ("GPU codebook encode of BF16 weights resident in HBM, raw-weight GB/s; % of HBM peak"
                    if encode else
+                   "exponent entropy-coded BF16 decode to HBM, decompressed-weight GB/s; % of HBM peak"
+                   if ecfmt else
                    "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
                    else "standalone codebook decode to BF16 in HBM, decompressed-weight GB/s; % of HBM peak"
                    if batch == 0 else
@@ -353,7 +397,7 @@ def main():
             "shapes": sorted({f"{d.rows}x{d.cols}" for d in tensors}),
             "batch": batch,
             "layers": n_layers,
-            "index_bits": bits,
+            ("max_code_bits" if ecfmt else "index_bits"): bits,
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
@@ -365,7 +409,7 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": ("cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
-                       if encode else f"{kernel}<{bits[-1]}>"),
+                       if encode else kernel if ecfmt else f"{kernel}<{bits[-1]}>"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -385,6 +429,9 @@ def main():
     if not args.no_cpu_baseline and batch == 1:
         log("CPU baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
+    elif not args.no_cpu_baseline and ecfmt:
+        log("CPU baseline (oracle entropy decoder) ...")
+        result["cpu_baseline"] = cpu_baseline_ec(specs, args.cpu_seconds)
     elif not args.no_cpu_baseline and encode:
         log("CPU baseline (oracle encoder) ...")
         result["cpu_baseline"] = cpu_baseline_encode(specs, args.cpu_seconds)

@@ -4,17 +4,19 @@
 // lookup table held in on-chip memory, and a two-phase pass in which each thread first finds how
 // many values it will decode and, after a synchronisation, decodes them into their places.  Here
 // one workgroup of 256 threads takes one block of 256 spans (64 stream bits each):
-//   1. the 4,096-entry table (exponent | length << 8 for every 12-bit window) is staged in LDS
-//      once per workgroup;
+//   1. the format's 4,096-entry table (exponent | length << 8 for every 12-bit window) is turned,
+//      once per workgroup, into an LDS table that also gives the second code of the window when
+//      both fit in its 12 bits, which halves the lookups of the serial walk below;
 //   2. each thread loads its span's three stream words (the span and the 32 bits after it, which
-//      cover the longest code that starts in it) and its 4-bit gap, and walks the codes that start
-//      in the span, counting them;
+//      cover the longest code that starts in it) and its 4-bit gap (the next block's are loaded
+//      while the current one is written out), and walks the codes that start in the span,
+//      counting them;
 //   3. a workgroup prefix sum of the counts gives every thread the offset of its first value
 //      within the block; the thread walks its span again and writes the exponents to an LDS
 //      array at those offsets;
 //   4. the block's values, bases[k] .. bases[k] + total, are joined with their sign-mantissa bytes
-//      (coalesced 8-byte loads) and written as 16-byte non-temporal stores (element stores at the
-//      two ragged ends of the block's range).
+//      (coalesced 8-byte loads, issued with the block's stream loads) and written as 16-byte
+//      non-temporal stores (element stores at the two ragged ends of the block's range).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,6 +34,7 @@ constexpr int kSpansPerBlock = CBK_EC_BLOCK_SPANS;  // = threads per workgroup
 constexpr int kMaxPerSpan = CBK_EC_SPAN_BITS;       // codes are at least one bit long
 constexpr int kLutEntries = CBK_EC_LUT_ENTRIES;
 constexpr int kStreamOnce = 2;                      // non-temporal: data touched once
+constexpr int kJoinAhead = 4;                       // join segments per thread loaded in advance
 
 static_assert(kSpansPerBlock == 256, "one thread per span, 256 spans per block");
 
@@ -53,48 +56,92 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
                                                               const uint16_t *__restrict__ lut,
                                                               uint16_t *__restrict__ out, uint64_t n,
                                                               uint64_t total_bits, uint32_t spans, uint32_t blocks) {
-    __shared__ u32x4 table4[kLutEntries / 8];
+    // two codes per lookup: entry = first exponent | second exponent << 8 | first length << 16 |
+    // both lengths << 20 | count << 24, count 2 when the second code also lies in the 12 bits
+    __shared__ uint32_t multi[kLutEntries];
     // exponents of one block, placed so that index i holds the value of weight (base & ~7) + i;
     // 16 spare bytes cover the 8-byte reads at the end of the range
     __shared__ uint64_t exps8[(kSpansPerBlock * kMaxPerSpan + 16) / 8];
     __shared__ uint32_t wave_sum[kSpansPerBlock / 64];
-    const uint16_t *table = reinterpret_cast<const uint16_t *>(table4);
     uint8_t *exps = reinterpret_cast<uint8_t *>(exps8);
     const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
+    // the format's one-code table goes through the (still unused) exponent array
+    static_assert(sizeof(exps8) >= kLutEntries * 2, "table staging fits the exponent array");
+    const uint16_t *single = reinterpret_cast<const uint16_t *>(exps8);
     for (uint32_t i = t; i < kLutEntries / 8; i += kSpansPerBlock)
-        table4[i] = reinterpret_cast<const u32x4 *>(lut)[i];
+        reinterpret_cast<u32x4 *>(exps8)[i] = reinterpret_cast<const u32x4 *>(lut)[i];
+    __syncthreads();
+    for (uint32_t v = t; v < kLutEntries; v += kSpansPerBlock) {
+        const uint32_t e1 = single[v], l1 = e1 >> 8;
+        const uint32_t e2 = single[v >> l1], l2 = e2 >> 8;
+        const bool two = l1 + l2 <= CBK_EC_MAX_LEN;
+        multi[v] = (e1 & 0xFFu) | (two ? (e2 & 0xFFu) << 8 : 0u) | (l1 << 16) | ((two ? l1 + l2 : l1) << 20) |
+                   ((two ? 2u : 1u) << 24);
+    }
     __syncthreads();
 
     const uint64_t stream_bytes = 8 * static_cast<uint64_t>(spans);
     const uint64_t gap_bytes = 4 * ((static_cast<uint64_t>(spans) + 7) / 8);
+    // one block's inputs: its stream words and gaps go through resources clipped to the arrays
+    // (reads past their ends give zero without touching memory; a block past the last reads
+    // nothing)
+    // the sm allocation is readable up to n rounded up to 16 bytes, so whole dwords are in range
+    const uint64_t sm_bytes = (n + 15) & ~uint64_t(15);
+    struct BlockIn {
+        u32x2 ab;
+        uint32_t c, gword;
+        uint64_t base;
+        u32x2 smp[kJoinAhead];  // sm bytes of the block's first kJoinAhead segments per thread
+    };
+    // base: bases[k], read one block earlier so that the sm loads need not wait for it
+    auto fetch = [&](uint32_t k, uint64_t base) {
+        BlockIn in;
+        const bool live = k < blocks;
+        const uint64_t sw0 = static_cast<uint64_t>(k) * kSpansPerBlock * 8;  // byte offset
+        const __amdgpu_buffer_rsrc_t rs = rsrc(reinterpret_cast<const uint8_t *>(stream) + (live ? sw0 : 0),
+                                               live ? std::min<uint64_t>(stream_bytes - sw0, kSpansPerBlock * 8 + 4) : 0);
+        in.ab = __builtin_amdgcn_raw_buffer_load_b64(rs, static_cast<int>(t * 8), 0, kStreamOnce);
+        in.c = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(t * 8 + 8), 0, kStreamOnce);
+        const uint64_t gw0 = static_cast<uint64_t>(k) * (kSpansPerBlock / 8) * 4;
+        const __amdgpu_buffer_rsrc_t rg = rsrc(reinterpret_cast<const uint8_t *>(gaps) + (live ? gw0 : 0),
+                                               live ? std::min<uint64_t>(gap_bytes - gw0, kSpansPerBlock / 2) : 0);
+        in.gword = __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>((t / 8) * 4), 0, 0);
+        in.base = base;
+        const uint64_t m0 = (base / 8) * 8;
+        const bool sm_live = live && m0 < sm_bytes;
+        const __amdgpu_buffer_rsrc_t rm = rsrc(sm + (sm_live ? m0 : 0),
+                                               sm_live ? std::min<uint64_t>(sm_bytes - m0, kJoinAhead * kSpansPerBlock * 8) : 0);
+#pragma unroll
+        for (int i = 0; i < kJoinAhead; ++i)
+            in.smp[i] = __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((t + i * kSpansPerBlock) * 8), 0, kStreamOnce);
+        return in;
+    };
+
+    BlockIn cur = fetch(blockIdx.x, blockIdx.x < blocks ? bases[blockIdx.x] : 0);
     for (uint32_t k = blockIdx.x; k < blocks; k += gridDim.x) {
         const uint64_t j = static_cast<uint64_t>(k) * kSpansPerBlock + t;
-        // this block's stream words and gaps through resources clipped to the arrays: reads past
-        // their ends give zero without touching memory
-        const uint64_t sw0 = static_cast<uint64_t>(k) * kSpansPerBlock * 8;  // byte offset
-        const __amdgpu_buffer_rsrc_t rs = rsrc(reinterpret_cast<const uint8_t *>(stream) + sw0,
-                                               std::min<uint64_t>(stream_bytes - sw0, kSpansPerBlock * 8 + 4));
-        const u32x2 ab = __builtin_amdgcn_raw_buffer_load_b64(rs, static_cast<int>(t * 8), 0, kStreamOnce);
-        const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(t * 8 + 8), 0, kStreamOnce);
-        const uint64_t gw0 = static_cast<uint64_t>(k) * (kSpansPerBlock / 8) * 4;
-        const __amdgpu_buffer_rsrc_t rg = rsrc(reinterpret_cast<const uint8_t *>(gaps) + gw0,
-                                               std::min<uint64_t>(gap_bytes - gw0, kSpansPerBlock / 2));
-        const uint32_t gword = __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>((t / 8) * 4), 0, 0);
-        const uint64_t base = bases[k];  // first weight of the block (wave-uniform)
-        const uint32_t gap = (gword >> (4 * (t % 8))) & 15u;
+        const uint64_t base = cur.base;
+        const uint64_t base_after = k + gridDim.x < blocks ? bases[k + gridDim.x] : 0;
+        const uint32_t gap = (cur.gword >> (4 * (t % 8))) & 15u;
         uint32_t end = 0;
         if (j < spans) {
             const uint64_t rem = total_bits - j * CBK_EC_SPAN_BITS;
             end = rem < CBK_EC_SPAN_BITS ? static_cast<uint32_t>(rem) : CBK_EC_SPAN_BITS;
         }
-        const uint64_t lo = static_cast<uint64_t>(ab.y) << 32 | ab.x;
-        const uint64_t hi = static_cast<uint64_t>(c) << 32 | ab.y;
+        const uint64_t lo = static_cast<uint64_t>(cur.ab.y) << 32 | cur.ab.x;
+        const uint64_t hi = static_cast<uint64_t>(cur.c) << 32 | cur.ab.y;
 
-        // phase 1: how many codes start in this span
+        // phase 1: how many codes start in this span (a lookup's second code counts only when it
+        // starts inside the span)
         uint32_t cnt = 0;
-        for (uint32_t pos = gap; pos < end && cnt < kMaxPerSpan; ++cnt)
-            pos += table[window12(lo, hi, pos)] >> 8;
+        for (uint32_t pos = gap; pos < end && cnt < kMaxPerSpan;) {
+            const uint32_t m = multi[window12(lo, hi, pos)];
+            const uint32_t l1 = (m >> 16) & 15u;
+            const bool both = (m >> 24) == 2u && pos + l1 < end && cnt + 1 < kMaxPerSpan;
+            cnt += both ? 2u : 1u;
+            pos += both ? ((m >> 20) & 15u) : l1;
+        }
 
         // prefix sum of the counts over the workgroup
         uint32_t incl = cnt;
@@ -111,29 +158,30 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
             before += static_cast<uint32_t>(i) < wave ? wave_sum[i] : 0u;
             total += wave_sum[i];
         }
-        const uint32_t shift = static_cast<uint32_t>(base & 7);
-        uint32_t at = shift + before + incl - cnt;
+        uint32_t at = static_cast<uint32_t>(base & 7) + before + incl - cnt;
 
-        // phase 2: decode again, exponents to their places
-        uint32_t pos = gap;
-        for (uint32_t q = 0; q < cnt; ++q) {
-            const uint32_t e = table[window12(lo, hi, pos)];
-            exps[at++] = static_cast<uint8_t>(e);
-            pos += e >> 8;
+        // phase 2: the same walk again, exponents to their places
+        for (uint32_t pos = gap, q = 0; q < cnt;) {
+            const uint32_t m = multi[window12(lo, hi, pos)];
+            const uint32_t l1 = (m >> 16) & 15u;
+            const bool both = (m >> 24) == 2u && pos + l1 < end && q + 1 < kMaxPerSpan;
+            exps[at] = static_cast<uint8_t>(m);
+            if (both) exps[at + 1] = static_cast<uint8_t>(m >> 8);
+            at += both ? 2u : 1u;
+            q += both ? 2u : 1u;
+            pos += both ? ((m >> 20) & 15u) : l1;
         }
         __syncthreads();
+        const BlockIn nxt = fetch(k + gridDim.x, base_after);  // in flight during the join below
 
-        // join with the sign-mantissa bytes: weights [base, base + total), clipped to n
+        // join with the sign-mantissa bytes: weights [base, base + total), clipped to n, in
+        // 8-weight segments s0 .. s1 (segment s0 + t + i * 256 for the thread's i-th)
         const uint64_t stop = std::min<uint64_t>(base + total, n);
         if (base < stop) {
-            const uint64_t s0 = base / 8, s1 = (stop + 7) / 8;  // 8-weight segments
-            // the sm allocation is readable up to n rounded up to 16 bytes, so whole dwords are in range
-            const uint64_t sm_bytes = (n + 15) & ~uint64_t(15);
-            const __amdgpu_buffer_rsrc_t rm = rsrc(sm + s0 * 8, std::min<uint64_t>(sm_bytes - s0 * 8, (s1 - s0) * 8));
-            for (uint64_t s = s0 + t; s < s1; s += kSpansPerBlock) {
-                const uint64_t g0 = s * 8;
-                const u32x2 smv = __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((s - s0) * 8), 0, kStreamOnce);
-                const uint64_t ev = exps8[s - s0];
+            const uint64_t s0 = base / 8, s1 = (stop + 7) / 8;
+            auto join = [&](uint64_t sg, u32x2 smv) {
+                const uint64_t g0 = sg * 8;
+                const uint64_t ev = exps8[sg - s0];
                 uint32_t v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -153,9 +201,21 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
                     for (int e = 0; e < 8; ++e)
                         if (g0 + e >= base && g0 + e < stop) out[g0 + e] = static_cast<uint16_t>(v[e]);
                 }
+            };
+#pragma unroll
+            for (int i = 0; i < kJoinAhead; ++i) {
+                const uint64_t sg = s0 + t + i * kSpansPerBlock;
+                if (sg < s1) join(sg, cur.smp[i]);
+            }
+            // blocks with more than kJoinAhead * 2048 values (codes under 2 bits on average)
+            if (s0 + kJoinAhead * kSpansPerBlock < s1) {
+                const __amdgpu_buffer_rsrc_t rm = rsrc(sm + s0 * 8, std::min<uint64_t>(sm_bytes - s0 * 8, (s1 - s0) * 8));
+                for (uint64_t sg = s0 + t + kJoinAhead * kSpansPerBlock; sg < s1; sg += kSpansPerBlock)
+                    join(sg, __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((sg - s0) * 8), 0, kStreamOnce));
             }
         }
         __syncthreads();  // the next block reuses wave_sum and exps
+        cur = nxt;
     }
 }
 
@@ -168,8 +228,9 @@ cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return CBK_E_HIP;
-    // blocks loop inside each workgroup so the table is staged once per workgroup
-    const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(blocks, 8ull * cus)));
+    // four workgroups fit a CU's LDS; they loop over the blocks, so the tables are built once per
+    // workgroup and the next block's loads overlap the current block's output
+    const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(blocks, 4ull * cus)));
     hipLaunchKernelGGL(k_ec_decode, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream, t->gaps, t->bases,
                        t->lut, out, t->n, t->total_bits, static_cast<uint32_t>(spans),
                        static_cast<uint32_t>(blocks));

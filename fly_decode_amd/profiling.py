@@ -22,12 +22,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fly_decode_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "cbk_kernels.hip")
 ENCODER_SOURCE = os.path.join(CSRC, "cbk_encode.hip")
+EC_SOURCE = os.path.join(CSRC, "cbk_ec.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def source_for(kernel: str) -> str:
-    """The source file that defines a kernel (the encoder's kernels are named k_enc_*)."""
-    return ENCODER_SOURCE if kernel.startswith("k_enc") else KERNEL_SOURCE
+    """The source file that defines a kernel: the GPU encoder's are named k_enc_*, the entropy-coded
+    format's k_ec_*, the rest live in cbk_kernels.hip."""
+    if kernel.startswith("k_enc"):
+        return ENCODER_SOURCE
+    if kernel.startswith("k_ec"):
+        return EC_SOURCE
+    return KERNEL_SOURCE
 
 
 def kernel_source_sha256(kernel: str = "") -> str:
