@@ -87,7 +87,7 @@ def workload_tensors(name: str, count: int, layers: int):
     raise SystemExit(f"unknown workload {name}")
 
 
-def prepare(specs, threads, raw=False):
+def prepare(specs, threads, raw=False, cap=None):
     """Generate and encode every tensor on the host (threads), upload to the GPU.  With raw=True
     the uploaded form is the BF16 patterns themselves (int16, flat) and the host encodings stay on
     the host, as (raw tensors, host encodings)."""
@@ -98,7 +98,7 @@ def prepare(specs, threads, raw=False):
     def make(spec):
         cfg, layer, t = spec
         w = synth.workload_tensor(cfg, layer, t)
-        return w, cbk.encode(w)
+        return w, cbk.encode(w, cap=cap)
 
     out, hosts = [], []
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
@@ -223,6 +223,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--cap", type=int, default=0, metavar="K",
+                    help="lossy: cap every codebook at K entries (cbk_cap_patterns) before encoding")
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (counter calibration for the "
@@ -273,7 +275,7 @@ def main():
         enc_words = [torch.empty(cbk.words_for(r.numel(), 16), dtype=torch.int32, device="cuda") for r in raws]
         enc_meta = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in raws]
     else:
-        tensors = prepare(specs, threads)
+        tensors = prepare(specs, threads, cap=args.cap or None)
     log(f"setup {time.perf_counter() - t0:.1f} s")
 
     import synth
@@ -402,6 +404,7 @@ def main():
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
             "launches_per_step": 3 * launches if encode else launches,
+            "codebook_cap": args.cap or None,
         },
         "compressed_GBps": round(comp_gbps, 2),
         "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),

@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
            "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
-           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16"]
+           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "cap_patterns"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcbk.so")
@@ -84,6 +84,9 @@ def load_library():
         lib.cbk_gemm_small.restype = ctypes.c_int
         lib.cbk_gemm_small.argtypes = [tp, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        lib.cbk_cap_patterns.restype = ctypes.c_int
+        lib.cbk_cap_patterns.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                         _u32p]
         lib.cbk_encode_gpu_workspace_bytes.restype = ctypes.c_size_t
         lib.cbk_encode_gpu_workspace_bytes.argtypes = []
         lib.cbk_encode_gpu.restype = ctypes.c_int
@@ -154,15 +157,30 @@ class Compressed:
         return _Tensor(self.rows, self.cols, self.U, self.b, cb, wd)
 
 
-def encode(w, rows: int | None = None, cols: int | None = None) -> Compressed:
+def cap_patterns(w, K: int):
+    """cbk_cap_patterns: the lossy capped-codebook step.  Returns (patterns with at most K
+    distinct values, same shape as w, uint16; their distinct count)."""
+    w = np.ascontiguousarray(w).view(np.uint16)
+    out = np.empty_like(w)
+    U = ctypes.c_uint32()
+    _check(load_library().cbk_cap_patterns(w.ctypes.data if w.size else None, w.size, K,
+                                           out.ctypes.data if w.size else None, ctypes.byref(U)),
+           "cbk_cap_patterns")
+    return out, int(U.value)
+
+
+def encode(w, rows: int | None = None, cols: int | None = None, cap: int | None = None) -> Compressed:
     """Compress a host array of BF16 bit patterns (numpy uint16/int16, or a CPU torch tensor of
-    bfloat16/int16/uint16), shape [rows][cols] (or 1-D with rows/cols given)."""
+    bfloat16/int16/uint16), shape [rows][cols] (or 1-D with rows/cols given).  With ``cap`` the
+    tensor first goes through cbk_cap_patterns (lossy when it has more than cap distinct values)."""
     if hasattr(w, "detach"):
         w = w.detach().contiguous().cpu()
         w = w.view(__import__("torch").int16).numpy()
     w = np.ascontiguousarray(w)
     if w.dtype not in (np.uint16, np.int16):
         raise TypeError("encode expects 16-bit patterns")
+    if cap is not None:
+        w, _ = cap_patterns(w, cap)
     if rows is None:
         rows, cols = (w.shape if w.ndim == 2 else (1, w.size))
     flat = w.reshape(-1).view(np.uint16)

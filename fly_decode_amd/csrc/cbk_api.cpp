@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <thread>
 #include <vector>
 
@@ -140,6 +141,80 @@ cbk_status cbk_encode(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_
         }
         for (auto &th : pool) th.join();
     }
+    return CBK_OK;
+}
+
+cbk_status cbk_cap_patterns(const uint16_t *w, uint64_t n, uint32_t K, uint16_t *w_out, uint32_t *U_out) {
+    if ((n > 0 && (!w || !w_out)) || !U_out || K == 0) return CBK_E_INVALID;
+    if (n > (uint64_t(1) << 40)) return CBK_E_UNSUPPORTED;
+    std::vector<uint64_t> count(65536, 0);
+    for (uint64_t i = 0; i < n; ++i) ++count[w[i]];
+    uint32_t U = 0, specials = 0;
+    for (uint32_t v = 0; v < 65536; ++v) {
+        if (!count[v]) continue;
+        ++U;
+        if (((v >> 7) & 0xFF) == 0xFF) ++specials;
+    }
+    if (U <= K) {
+        if (w_out != w && n > 0) memcpy(w_out, w, n * sizeof(uint16_t));
+        *U_out = U;
+        return CBK_OK;
+    }
+    if (specials > K || (specials == K && U > specials)) return CBK_E_UNSUPPORTED;
+    // keep every Inf/NaN pattern, then the most frequent finite ones (ties: smaller pattern)
+    std::vector<uint8_t> kept(65536, 0);
+    std::vector<uint32_t> finite;
+    for (uint32_t v = 0; v < 65536; ++v) {
+        if (!count[v]) continue;
+        if (((v >> 7) & 0xFF) == 0xFF)
+            kept[v] = 1;
+        else
+            finite.push_back(v);
+    }
+    const size_t room = K - specials;
+    std::partial_sort(finite.begin(), finite.begin() + room, finite.end(), [&](uint32_t a, uint32_t b) {
+        return count[a] != count[b] ? count[a] > count[b] : a < b;
+    });
+    auto value = [](uint32_t p) {
+        uint32_t bits = p << 16;
+        float f;
+        memcpy(&f, &bits, 4);
+        return static_cast<double>(f);
+    };
+    std::vector<uint32_t> near(finite.begin(), finite.begin() + room);
+    for (uint32_t v : near) kept[v] = 1;
+    std::sort(near.begin(), near.end(), [&](uint32_t a, uint32_t b) {
+        return value(a) != value(b) ? value(a) < value(b) : a < b;
+    });
+    // every other pattern goes to the nearest kept finite value (ties: closer to zero, then the
+    // smaller pattern); the candidates are the neighbours of its place in value order
+    std::vector<uint16_t> map(65536, 0);
+    for (uint32_t v = 0; v < 65536; ++v) {
+        if (!count[v]) continue;
+        if (kept[v]) {
+            map[v] = static_cast<uint16_t>(v);
+            continue;
+        }
+        const double f = value(v);
+        const size_t i = std::lower_bound(near.begin(), near.end(), f,
+                                          [&](uint32_t r, double x) { return value(r) < x; }) - near.begin();
+        uint32_t best = 0;
+        bool have = false;
+        for (size_t j = (i >= 2 ? i - 2 : 0); j < std::min(near.size(), i + 2); ++j) {
+            const uint32_t r = near[j];
+            if (!have) {
+                best = r;
+                have = true;
+                continue;
+            }
+            const double dr = std::fabs(f - value(r)), db = std::fabs(f - value(best));
+            const double ar = std::fabs(value(r)), ab = std::fabs(value(best));
+            if (dr < db || (dr == db && (ar < ab || (ar == ab && r < best)))) best = r;
+        }
+        map[v] = static_cast<uint16_t>(best);
+    }
+    for (uint64_t i = 0; i < n; ++i) w_out[i] = map[w[i]];
+    *U_out = K;
     return CBK_OK;
 }
 

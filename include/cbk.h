@@ -87,6 +87,22 @@ cbk_status cbk_encode(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_
                       uint32_t *words, uint64_t words_cap, uint64_t *words_needed);
 
 /*
+ * cbk_cap_patterns -- host, synchronous.  The lossy "capped codebook" step that comes before
+ * cbk_encode when the stored codebook may hold at most K entries (the codebook overview's how-to
+ * section sets codebook_size=8192; the Codebook-Quantization digest mentions lossy, balanced
+ * variants).  w_out[i] receives w[i] mapped as follows:
+ *   - a tensor with at most K distinct patterns is copied unchanged (the lossless case);
+ *   - otherwise exactly K patterns are kept: every Inf/NaN pattern present (exponent field 255),
+ *     then the most frequent finite ones, ties to the smaller pattern;
+ *   - every other pattern becomes the kept finite value nearest to it as a real number, ties
+ *     going to the value closer to zero, then to the smaller pattern.
+ *   U_out  out: distinct patterns in w_out (min(U, K)).
+ * w_out may equal w.  Errors: CBK_E_INVALID (NULL pointer, K == 0), CBK_E_UNSUPPORTED (the
+ * Inf/NaN patterns alone leave no room for a finite value, or n > 2^40).
+ */
+cbk_status cbk_cap_patterns(const uint16_t *w, uint64_t n, uint32_t K, uint16_t *w_out, uint32_t *U_out);
+
+/*
  * Kernel choice (all calls): a width b >= 1 whose rows hold a whole number of lane units
  * (cols % (128 >> ctz(b)) == 0) takes the fast kernels, which stage the codebook (and x) in LDS;
  * b == 0, ragged rows, misaligned operands and shapes beyond the LDS budget take generic kernels
