@@ -94,8 +94,9 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
         uint64_t base;
         u32x2 smp[kJoinAhead];  // sm bytes of the block's first kJoinAhead segments per thread
     };
-    // base: bases[k], read one block earlier so that the sm loads need not wait for it
-    auto fetch = [&](uint32_t k, uint64_t base) {
+    // base, limit: bases[k] and bases[k + 1] (n for the last block), read one block earlier so that
+    // the sm loads need not wait for them; the loads stay within the block's own bytes
+    auto fetch = [&](uint32_t k, uint64_t base, uint64_t limit) {
         BlockIn in;
         const bool live = k < blocks;
         const uint64_t sw0 = static_cast<uint64_t>(k) * kSpansPerBlock * 8;  // byte offset
@@ -109,20 +110,22 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
         in.gword = __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>((t / 8) * 4), 0, 0);
         in.base = base;
         const uint64_t m0 = (base / 8) * 8;
-        const bool sm_live = live && m0 < sm_bytes;
+        const uint64_t m1 = std::min<uint64_t>((std::min(limit, n) + 7) / 8 * 8, sm_bytes);
+        const bool sm_live = live && m0 < m1;
         const __amdgpu_buffer_rsrc_t rm = rsrc(sm + (sm_live ? m0 : 0),
-                                               sm_live ? std::min<uint64_t>(sm_bytes - m0, kJoinAhead * kSpansPerBlock * 8) : 0);
+                                               sm_live ? std::min<uint64_t>(m1 - m0, kJoinAhead * kSpansPerBlock * 8) : 0);
 #pragma unroll
         for (int i = 0; i < kJoinAhead; ++i)
             in.smp[i] = __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((t + i * kSpansPerBlock) * 8), 0, kStreamOnce);
         return in;
     };
 
-    BlockIn cur = fetch(blockIdx.x, blockIdx.x < blocks ? bases[blockIdx.x] : 0);
+    auto base_of = [&](uint32_t k) { return k < blocks ? static_cast<uint64_t>(bases[k]) : n; };
+    BlockIn cur = fetch(blockIdx.x, base_of(blockIdx.x), base_of(blockIdx.x + 1));
     for (uint32_t k = blockIdx.x; k < blocks; k += gridDim.x) {
         const uint64_t j = static_cast<uint64_t>(k) * kSpansPerBlock + t;
         const uint64_t base = cur.base;
-        const uint64_t base_after = k + gridDim.x < blocks ? bases[k + gridDim.x] : 0;
+        const uint64_t base_after = base_of(k + gridDim.x), limit_after = base_of(k + gridDim.x + 1);
         const uint32_t gap = (cur.gword >> (4 * (t % 8))) & 15u;
         uint32_t end = 0;
         if (j < spans) {
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
             pos += both ? ((m >> 20) & 15u) : l1;
         }
         __syncthreads();
-        const BlockIn nxt = fetch(k + gridDim.x, base_after);  // in flight during the join below
+        const BlockIn nxt = fetch(k + gridDim.x, base_after, limit_after);  // in flight during the join
 
         // join with the sign-mantissa bytes: weights [base, base + total), clipped to n, in
         // 8-weight segments s0 .. s1 (segment s0 + t + i * 256 for the thread's i-th)
