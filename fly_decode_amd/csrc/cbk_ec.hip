@@ -6,7 +6,7 @@
 // one workgroup of 256 threads takes one block of 256 spans (64 stream bits each):
 //   1. the format's 4,096-entry table (exponent | length << 8 for every 12-bit window) is turned,
 //      once per workgroup, into an LDS table that also gives the second code of the window when
-//      both fit in its 12 bits, which halves the lookups of the serial walk below;
+//      both fit in its 12 bits, which halves the lookups of the serial walks below;
 //   2. each thread loads its span's three stream words (the span and the 32 bits after it, which
 //      cover the longest code that starts in it) and its 4-bit gap (the next block's are loaded
 //      while the current one is written out), and walks the codes that start in the span,
@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "cbk_internal.h"
 
@@ -43,10 +44,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint64_
                                              static_cast<int>(static_cast<uint32_t>(bytes)), 0x00020000);
 }
 
-// The 12 stream bits starting at bit pos (< 64) of the 96-bit window w0 | w1 << 32 | w2 << 64.
-__device__ __forceinline__ uint32_t window12(uint64_t lo, uint64_t hi, uint32_t pos) {
-    const uint64_t v = pos < 32 ? (lo >> pos) : (hi >> (pos - 32));
-    return static_cast<uint32_t>(v) & (kLutEntries - 1);
+// The 12 stream bits starting at bit pos (< 64) of the 96-bit window w0 | w1 << 32 | w2 << 64:
+// one funnel shift of the two words that hold them.
+__device__ __forceinline__ uint32_t window12(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t pos) {
+    const bool low = pos < 32;
+    return __builtin_amdgcn_alignbit(low ? w1 : w2, low ? w0 : w1, pos & 31u) & (kLutEntries - 1);
 }
 
 __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__restrict__ sm,
@@ -72,9 +74,10 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
     for (uint32_t i = t; i < kLutEntries / 8; i += kSpansPerBlock)
         reinterpret_cast<u32x4 *>(exps8)[i] = reinterpret_cast<const u32x4 *>(lut)[i];
     __syncthreads();
+    // lengths are clamped to 1..12, so every walk below advances (a corrupt table cannot stall it)
     for (uint32_t v = t; v < kLutEntries; v += kSpansPerBlock) {
-        const uint32_t e1 = single[v], l1 = e1 >> 8;
-        const uint32_t e2 = single[v >> l1], l2 = e2 >> 8;
+        const uint32_t e1 = single[v], l1 = std::min(std::max(e1 >> 8, 1u), 12u);
+        const uint32_t e2 = single[v >> l1], l2 = std::min(std::max(e2 >> 8, 1u), 12u);
         const bool two = l1 + l2 <= CBK_EC_MAX_LEN;
         multi[v] = (e1 & 0xFFu) | (two ? (e2 & 0xFFu) << 8 : 0u) | (l1 << 16) | ((two ? l1 + l2 : l1) << 20) |
                    ((two ? 2u : 1u) << 24);
@@ -132,19 +135,22 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
             const uint64_t rem = total_bits - j * CBK_EC_SPAN_BITS;
             end = rem < CBK_EC_SPAN_BITS ? static_cast<uint32_t>(rem) : CBK_EC_SPAN_BITS;
         }
-        const uint64_t lo = static_cast<uint64_t>(cur.ab.y) << 32 | cur.ab.x;
-        const uint64_t hi = static_cast<uint64_t>(cur.c) << 32 | cur.ab.y;
+        const uint32_t w0 = cur.ab.x, w1 = cur.ab.y, w2 = cur.c;
+        // While the whole 12-bit window lies before the span's end, both codes of a lookup start
+        // inside the span; the last few bits go one code at a time.  Every step advances by at
+        // least one bit per code, so no span yields more than 64 codes.
 
-        // phase 1: how many codes start in this span (a lookup's second code counts only when it
-        // starts inside the span)
-        uint32_t cnt = 0;
-        for (uint32_t pos = gap; pos < end && cnt < kMaxPerSpan;) {
-            const uint32_t m = multi[window12(lo, hi, pos)];
-            const uint32_t l1 = (m >> 16) & 15u;
-            const bool both = (m >> 24) == 2u && pos + l1 < end && cnt + 1 < kMaxPerSpan;
-            cnt += both ? 2u : 1u;
-            pos += both ? ((m >> 20) & 15u) : l1;
+        // phase 1: how many codes start in this span.  While the whole 12-bit window lies before
+        // the span's end, both codes of a lookup start inside the span; the last few bits go one
+        // code at a time.  Every step advances at least one bit per code, so no span yields more
+        // than 64 codes.
+        uint32_t cnt = 0, pos = gap;
+        for (; pos + CBK_EC_MAX_LEN <= end;) {
+            const uint32_t m = multi[window12(w0, w1, w2, pos)];
+            cnt += m >> 24;
+            pos += (m >> 20) & 15u;
         }
+        for (; pos < end; ++cnt) pos += (multi[window12(w0, w1, w2, pos)] >> 16) & 15u;
 
         // prefix sum of the counts over the workgroup
         uint32_t incl = cnt;
@@ -164,15 +170,18 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
         uint32_t at = static_cast<uint32_t>(base & 7) + before + incl - cnt;
 
         // phase 2: the same walk again, exponents to their places
-        for (uint32_t pos = gap, q = 0; q < cnt;) {
-            const uint32_t m = multi[window12(lo, hi, pos)];
-            const uint32_t l1 = (m >> 16) & 15u;
-            const bool both = (m >> 24) == 2u && pos + l1 < end && q + 1 < kMaxPerSpan;
+        pos = gap;
+        for (; pos + CBK_EC_MAX_LEN <= end;) {
+            const uint32_t m = multi[window12(w0, w1, w2, pos)];
             exps[at] = static_cast<uint8_t>(m);
-            if (both) exps[at + 1] = static_cast<uint8_t>(m >> 8);
-            at += both ? 2u : 1u;
-            q += both ? 2u : 1u;
-            pos += both ? ((m >> 20) & 15u) : l1;
+            if ((m >> 24) == 2u) exps[at + 1] = static_cast<uint8_t>(m >> 8);
+            at += m >> 24;
+            pos += (m >> 20) & 15u;
+        }
+        for (; pos < end; ++at) {
+            const uint32_t m = multi[window12(w0, w1, w2, pos)];
+            exps[at] = static_cast<uint8_t>(m);
+            pos += (m >> 16) & 15u;
         }
         __syncthreads();
         const BlockIn nxt = fetch(k + gridDim.x, base_after, limit_after);  // in flight during the join
@@ -185,24 +194,26 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
             auto join = [&](uint64_t sg, u32x2 smv) {
                 const uint64_t g0 = sg * 8;
                 const uint64_t ev = exps8[sg - s0];
-                uint32_t v[8];
+                // four weights per word: high byte = sign | exponent >> 1, low byte = exponent
+                // bit 0 << 7 | mantissa; v_perm interleaves the low and high bytes
+                u32x4 o;
+                uint32_t *op = reinterpret_cast<uint32_t *>(&o);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t b = ((e < 4 ? smv.x : smv.y) >> (8 * (e & 3))) & 0xFFu;
-                    const uint32_t x = static_cast<uint32_t>(ev >> (8 * e)) & 0xFFu;
-                    v[e] = ((b & 0x80u) << 8) | (x << 7) | (b & 0x7Fu);
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t b4 = h ? smv.y : smv.x;
+                    const uint32_t e4 = static_cast<uint32_t>(ev >> (32 * h));
+                    const uint32_t hi4 = (b4 & 0x80808080u) | ((e4 >> 1) & 0x7F7F7F7Fu);
+                    const uint32_t lo4 = ((e4 & 0x01010101u) << 7) | (b4 & 0x7F7F7F7Fu);
+                    op[2 * h] = __builtin_amdgcn_perm(hi4, lo4, 0x05010400u);
+                    op[2 * h + 1] = __builtin_amdgcn_perm(hi4, lo4, 0x07030602u);
                 }
                 if (g0 >= base && g0 + 8 <= stop) {
-                    u32x4 o;
-                    o.x = v[0] | (v[1] << 16);
-                    o.y = v[2] | (v[3] << 16);
-                    o.z = v[4] | (v[5] << 16);
-                    o.w = v[6] | (v[7] << 16);
                     __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + g0));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (g0 + e >= base && g0 + e < stop) out[g0 + e] = static_cast<uint16_t>(v[e]);
+                        if (g0 + e >= base && g0 + e < stop)
+                            out[g0 + e] = static_cast<uint16_t>(op[e >> 1] >> (16 * (e & 1)));
                 }
             };
 #pragma unroll
@@ -231,9 +242,20 @@ cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return CBK_E_HIP;
-    // four workgroups fit a CU's LDS; they loop over the blocks, so the tables are built once per
-    // workgroup and the next block's loads overlap the current block's output
-    const uint32_t grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(blocks, 4ull * cus)));
+    // as many workgroups as fit the CUs at once (LDS bound); they loop over the blocks, so the
+    // tables are built once per workgroup and the next block's loads overlap the current block's
+    // output
+    // (the per-device count is queried once; concurrent first calls store the same value)
+    static std::atomic<int> per_cu[64];
+    if (dev < 0 || dev >= 64) return CBK_E_HIP;
+    int occ = per_cu[dev].load(std::memory_order_relaxed);
+    if (occ <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_ec_decode, kSpansPerBlock, 0) != hipSuccess || occ <= 0)
+            return CBK_E_HIP;
+        per_cu[dev].store(occ, std::memory_order_relaxed);
+    }
+    const uint32_t grid = static_cast<uint32_t>(
+        std::max<uint64_t>(1, std::min<uint64_t>(blocks, static_cast<uint64_t>(occ) * cus)));
     hipLaunchKernelGGL(k_ec_decode, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream, t->gaps, t->bases,
                        t->lut, out, t->n, t->total_bits, static_cast<uint32_t>(spans),
                        static_cast<uint32_t>(blocks));
