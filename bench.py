@@ -29,7 +29,8 @@ each tensor with its own codebook):
              form written; the result of the last step is checked against the host encoder.
 
 The step is captured once in a HIP graph and replayed; the timed region is bracketed by
-torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
+torch.cuda.synchronize().  Untimed warm-up runs for --warmup steps and at least --warmup-seconds
+(0.3 s) of wall time, so that the timed steps see the GPU at its sustained clocks.  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
 feeds the multiply) / step time.  The dominant kernel's roofline uses its algorithmic bytes per
 launch (packed indices ceil(n*b/8) + codebook 2U + X 2*batch*K + Y 4*batch*M) over its average launch
 duration, measured with HIP events on the launch stream.  The CPU baseline times the oracle (decode
@@ -216,6 +217,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="after the warm-up steps, keep replaying untimed steps until this much wall "
+                         "time has passed (the GPU's clocks rise over the first tens of ms of load)")
     ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096",
                                                            "encode4096", "ecdecode4096"])
     ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
@@ -312,6 +316,7 @@ def main():
             else:
                 cbk.gemv_group([tensors[i] for i in ph], xs[tensors[ph[0]].cols], ys=[ys[i] for i in ph])
 
+    warm0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -326,6 +331,20 @@ def main():
         for _ in range(2):
             graph.replay()
         torch.cuda.synchronize()
+    # Sustained rate: the GPU raises its clocks over the first tens of milliseconds of load (the
+    # 70B-shaped layer runs at about 60 % of peak after 5 steps, 67 % after 50, 73 % after 200), so
+    # untimed steps continue until --warmup-seconds of wall time have passed since the first one.
+    extra = 0
+    while time.perf_counter() - warm0 < args.warmup_seconds:
+        for _ in range(4):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+            extra += 1
+        torch.cuda.synchronize()
+    if extra:
+        log(f"warm-up: {args.warmup} steps + {extra} more to reach {args.warmup_seconds:.2f} s")
 
     # ---- timed region: K steps
     torch.cuda.synchronize()
