@@ -424,6 +424,8 @@ def main():
             "graph_replay": graph is not None,
             "launches_per_step": 3 * launches if encode else launches,
             "codebook_cap": args.cap or None,
+            "warmup_seconds_min": args.warmup_seconds,
+            "warmup_extra_steps": extra,
         },
         "compressed_GBps": round(comp_gbps, 2),
         "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),
