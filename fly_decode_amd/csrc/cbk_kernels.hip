@@ -545,7 +545,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows_group(const GemvG
 // When the tiles alone cannot fill the CUs, the 8 waves of a workgroup take 8/TW parts of K for
 // TW tiles and add their partial sums in LDS, so every Y element is written once (no atomics;
 // results do not depend on timing).
-constexpr int kGemmWaves = 8;
+constexpr int kGemmWaves = 4;  // two or more workgroups per CU (see the planner in gemm_launch)
 
 template <int B>
 struct GemmGeo {
@@ -1241,11 +1241,19 @@ bool gemm_launch(GemmArgs &a) {
     grp.P = static_cast<uint32_t>(P);
     grp.batch = a.batch;
     grp.ldx = static_cast<uint32_t>(a.ldx);
-    // Tiles per workgroup TW (the other 8 / TW waves split K).  The stages and the table take most
-    // of the LDS, so one workgroup runs per CU and the grid drains in ceil(blocks / CUs) rounds of
-    // workgroups that each take TW tiles by the whole of K: pick the TW with the fewest rounds x TW,
-    // and of equal ones the largest (fewer workgroups and partial-sum reductions).
-    const uint64_t cus = static_cast<uint64_t>(cu_count());
+    // LDS: the waves' stages (weights only for the VALU kernel, whose X stays in registers) and
+    // the partial tiles of the split K, plus the codebook table.
+    const uint32_t stage = MFMA ? gemm_stage_bytes<B, NB>() : static_cast<uint32_t>(GemmGeo<B>::WSTAGE);
+    const uint32_t lds = kGemmWaves * stage + kGemmWaves * 256 * 4;
+    if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
+    // Tiles per workgroup TW (the other kGemmWaves / TW waves split K).  The LDS decides how many
+    // workgroups run on a CU at once (two at b = 13), and the grid drains in ceil(blocks / slots)
+    // rounds of workgroups that each take TW tiles by the whole of K: pick the TW with the fewest
+    // rounds x TW, and of equal ones the largest (fewer workgroups and partial-sum reductions).
+    // Four-wave workgroups, two per CU, measured 5.6 % (batch 8) and 3.6 % (batch 16) faster than
+    // one eight-wave workgroup per CU.
+    const uint64_t per_cu = std::max<uint64_t>(1, kLdsLimit / (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2));
+    const uint64_t cus = static_cast<uint64_t>(cu_count()) * per_cu;
     uint64_t best = ~uint64_t(0);
     for (uint32_t tw = 1; tw <= static_cast<uint32_t>(kGemmWaves); tw *= 2) {
         uint64_t blocks = 0;
@@ -1258,11 +1266,6 @@ bool gemm_launch(GemmArgs &a) {
     }
     grp.KW = kGemmWaves / grp.TW;
     grp.part_units = static_cast<uint32_t>(((P + grp.KW - 1) / grp.KW + 3) / 4 * 4);
-    // LDS: the waves' stages (weights only for the VALU kernel, whose X stays in registers) and
-    // the partial tiles of the split K.
-    const uint32_t stage = MFMA ? gemm_stage_bytes<B, NB>() : static_cast<uint32_t>(GemmGeo<B>::WSTAGE);
-    const uint32_t lds = kGemmWaves * stage + kGemmWaves * 256 * 4;
-    if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
     if constexpr (MFMA) {
         if (!allow_lds(k_gemm_mfma<B>, lds)) return false;
     } else {
