@@ -24,6 +24,8 @@ each tensor with its own codebook):
   ecdecode4096 the attn4096 tensors in the exponent entropy-coded format (sign-mantissa bytes
              raw, exponent Huffman-coded), decoded to BF16 in HBM by cbk_ec_decode_bf16, one launch
              per tensor; bytes = the stored format read + 2 bytes written per weight.
+  ecgemv4096 the same entropy-coded tensors, decode fused into the batch-1 GEMV (cbk_ec_gemv: a
+             y zero-fill and the fused kernel per tensor); bytes = the stored format + x + y.
   encode4096 the load-time path: cbk_encode_gpu of the attn4096 tensors from raw BF16 already in
              HBM (three launches per tensor); bytes = 2 bytes read per weight + the compressed
              form written; the result of the last step is checked against the host encoder.
@@ -64,10 +66,10 @@ def workload_tensors(name: str, count: int, layers: int):
     """(specs, phases, batch, layer_count): specs are (cfg, layer, tensor) triples; phases are lists
     of spec indices launched together (one launch per phase, phases run in order)."""
     import synth
-    if name in ("attn4096", "decode4096", "encode4096", "ecdecode4096"):
+    if name in ("attn4096", "decode4096", "encode4096", "ecdecode4096", "ecgemv4096"):
         t = synth.WORKLOADS[2][0][0]
         specs = [(2, layer, t) for layer in range(count)]
-        return specs, [[i] for i in range(len(specs))], (1 if name == "attn4096" else 0), len(specs)
+        return specs, [[i] for i in range(len(specs))], (1 if name in ("attn4096", "ecgemv4096") else 0), len(specs)
     if name in ("llama7b", "l70b_b1", "l70b_b16"):
         cfg = 4 if name == "llama7b" else 5
         tensors, n_layers = synth.WORKLOADS[cfg]
@@ -221,7 +223,7 @@ def main():
                     help="after the warm-up steps, keep replaying untimed steps until this much wall "
                          "time has passed (the GPU's clocks rise over the first tens of ms of load)")
     ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096",
-                                                           "encode4096", "ecdecode4096"])
+                                                           "encode4096", "ecdecode4096", "ecgemv4096"])
     ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers for mlp_b8 (8) and l70b_* (2)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -261,7 +263,8 @@ def main():
         phases = [[i] for ph in phases for i in ph]
     log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
     encode = args.workload == "encode4096"
-    ecfmt = args.workload == "ecdecode4096"
+    ecfmt = args.workload in ("ecdecode4096", "ecgemv4096")
+    ecgemv = args.workload == "ecgemv4096"
     t0 = time.perf_counter()
     if ecfmt:
         def make_ec(spec):
@@ -303,6 +306,8 @@ def main():
             if encode:
                 i = ph[0]
                 cbk.encode_gpu_launch(raws[i], ws, enc_cb[i], enc_words[i], enc_meta[i])
+            elif ecgemv:
+                cbk.ec_gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
             elif ecfmt:
                 cbk.ec_decode_bf16(tensors[ph[0]], out=ys[ph[0]])
             elif batch == 0:
@@ -374,7 +379,9 @@ def main():
     avg_launch_s = ms_step * 1e-3 / launches
 
     n_total = sum(d.n for d in tensors)
-    if ecfmt:  # the stored entropy-coded form read + the BF16 written
+    if ecgemv:  # the stored entropy-coded form + x read, y written
+        comp_total = sum(d.stored_bytes + 2 * d.cols + 4 * d.rows for d in tensors)
+    elif ecfmt:  # the stored entropy-coded form read + the BF16 written
         comp_total = sum(d.stored_bytes + 2 * d.n for d in tensors)
     elif batch == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
         comp_total = sum(d.compressed_bytes + 2 * d.n for d in tensors)
@@ -387,7 +394,7 @@ def main():
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
     bits = sorted({d.b for d in tensors}) if not ecfmt else [max(max(d.lengths) for d in tensors)]
-    kernel = ("k_enc" if encode else "k_ec_decode" if ecfmt else "k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
+    kernel = ("k_enc" if encode else "k_ec_gemv" if ecgemv else "k_ec_decode" if ecfmt else "k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
               else "k_gemm_valu" if batch <= 8 else "k_gemm_mfma")
     kernel_key = kernel if ecfmt else f"{kernel}_b{bits[-1]}"
     traffic = profiling.traffic_for(kernel_key, args.workload)
@@ -395,6 +402,8 @@ def main():
     result = {
         "metric": ("GPU codebook encode of BF16 weights resident in HBM, raw-weight GB/s; % of HBM peak"
                    if encode else
+                   "exponent entropy-coded fused GEMV decompressed-weight GB/s at batch 1; % of HBM peak"
+                   if ecgemv else
                    "exponent entropy-coded BF16 decode to HBM, decompressed-weight GB/s; % of HBM peak"
                    if ecfmt else
                    "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
@@ -422,7 +431,7 @@ def main():
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
-            "launches_per_step": 3 * launches if encode else launches,
+            "launches_per_step": 3 * launches if encode else 2 * launches if ecgemv else launches,
             "codebook_cap": args.cap or None,
             "warmup_seconds_min": args.warmup_seconds,
             "warmup_extra_steps": extra,
@@ -441,7 +450,7 @@ def main():
             "traffic": round(traffic["traffic_bytes_per_launch"]) if traffic else None,
             "bytes_per_launch": int(algo_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
-            "launches_per_unit": 3 if encode else 1,
+            "launches_per_unit": 3 if encode else 2 if ecgemv else 1,
             "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, args.workload), ROOT) if traffic else None,
         },
     }
@@ -450,10 +459,10 @@ def main():
     if batch > 1:
         flops = 2.0 * batch * n_total / step_s
         result["effective_TFLOPs"] = round(flops / 1e12, 3)
-    if not args.no_cpu_baseline and batch == 1:
+    if not args.no_cpu_baseline and batch == 1 and not ecgemv:
         log("CPU baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
-    elif not args.no_cpu_baseline and ecfmt:
+    elif not args.no_cpu_baseline and ecfmt and not ecgemv:
         log("CPU baseline (oracle entropy decoder) ...")
         result["cpu_baseline"] = cpu_baseline_ec(specs, args.cpu_seconds)
     elif not args.no_cpu_baseline and encode:

@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
            "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
-           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "cap_patterns"]
+           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "cap_patterns"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcbk.so")
@@ -107,6 +107,9 @@ def load_library():
         lib.cbk_ec_encode.argtypes = [ctypes.c_void_p, hp] + [ctypes.c_void_p] * 5
         lib.cbk_ec_decode_bf16.restype = ctypes.c_int
         lib.cbk_ec_decode_bf16.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_ec_gemv.restype = ctypes.c_int
+        lib.cbk_ec_gemv.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -416,3 +419,16 @@ def ec_decode_bf16(t: ECTensor, out=None, stream=None):
     _check(load_library().cbk_ec_decode_bf16(ctypes.byref(st), ctypes.c_void_p(out.data_ptr() if out.numel() else None),
                                              _stream(stream)), "cbk_ec_decode_bf16")
     return out
+
+
+def ec_gemv(t: ECTensor, x, y=None, stream=None):
+    """Fused decode + GEMV for an ECTensor on the device: x bfloat16[cols] -> float32[rows]."""
+    import torch
+    if y is None:
+        y = torch.empty(t.rows, dtype=torch.float32, device=t.sm.device)
+    st = t._struct()
+    _check(load_library().cbk_ec_gemv(ctypes.byref(st), t.rows, t.cols,
+                                      ctypes.c_void_p(x.data_ptr() if x.numel() else None),
+                                      ctypes.c_void_p(y.data_ptr() if y.numel() else None), _stream(stream)),
+           "cbk_ec_gemv")
+    return y

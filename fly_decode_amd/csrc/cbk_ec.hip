@@ -51,13 +51,26 @@ __device__ __forceinline__ uint32_t window12(uint32_t w0, uint32_t w1, uint32_t 
     return __builtin_amdgcn_alignbit(low ? w1 : w2, low ? w0 : w1, pos & 31u) & (kLutEntries - 1);
 }
 
-__global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__restrict__ sm,
-                                                              const uint32_t *__restrict__ stream,
-                                                              const uint32_t *__restrict__ gaps,
-                                                              const uint32_t *__restrict__ bases,
-                                                              const uint16_t *__restrict__ lut,
-                                                              uint16_t *__restrict__ out, uint64_t n,
-                                                              uint64_t total_bits, uint32_t spans, uint32_t blocks) {
+// Rows a block can touch in the fused GEMV: its at most 16,384 weights over rows of at least
+// kGemvMinCols columns, plus the two partial rows at its ends.
+constexpr uint32_t kGemvMinCols = 64;
+constexpr uint32_t kGemvBlockRows = kSpansPerBlock * kMaxPerSpan / kGemvMinCols + 2;
+
+// Fused GEMV output: y (zero-filled beforehand) and x, for rows of `cols` weights.
+struct EcGemvOut {
+    const uint16_t *x;
+    float *y;
+    uint32_t cols;
+};
+
+// GEMV == false: decode to BF16 in out.  GEMV == true: y[r] += sum of W[r][k] x[k] over the
+// block's weights, per row in LDS first, then one global atomic add per row the block touches.
+template <bool GEMV>
+__device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const uint32_t *__restrict__ stream,
+                                          const uint32_t *__restrict__ gaps, const uint32_t *__restrict__ bases,
+                                          const uint16_t *__restrict__ lut, uint16_t *__restrict__ out,
+                                          EcGemvOut gv, uint64_t n, uint64_t total_bits, uint32_t spans,
+                                          uint32_t blocks) {
     // two codes per lookup: entry = first exponent | second exponent << 8 | first length << 16 |
     // both lengths << 20 | count << 24, count 2 when the second code also lies in the 12 bits
     __shared__ uint32_t multi[kLutEntries];
@@ -65,6 +78,7 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
     // 16 spare bytes cover the 8-byte reads at the end of the range
     __shared__ uint64_t exps8[(kSpansPerBlock * kMaxPerSpan + 16) / 8];
     __shared__ uint32_t wave_sum[kSpansPerBlock / 64];
+    __shared__ float row_sum[GEMV ? kGemvBlockRows : 1];
     uint8_t *exps = reinterpret_cast<uint8_t *>(exps8);
     const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
@@ -73,6 +87,8 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
     const uint16_t *single = reinterpret_cast<const uint16_t *>(exps8);
     for (uint32_t i = t; i < kLutEntries / 8; i += kSpansPerBlock)
         reinterpret_cast<u32x4 *>(exps8)[i] = reinterpret_cast<const u32x4 *>(lut)[i];
+    if constexpr (GEMV)
+        for (uint32_t i = t; i < kGemvBlockRows; i += kSpansPerBlock) row_sum[i] = 0.f;
     __syncthreads();
     // lengths are clamped to 1..12, so every walk below advances (a corrupt table cannot stall it)
     for (uint32_t v = t; v < kLutEntries; v += kSpansPerBlock) {
@@ -191,9 +207,12 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
         const uint64_t stop = std::min<uint64_t>(base + total, n);
         if (base < stop) {
             const uint64_t s0 = base / 8, s1 = (stop + 7) / 8;
-            auto join = [&](uint64_t sg, u32x2 smv) {
+            // GEMV: one wave-wide call (every lane, `valid` false past s1) can reduce the wave's
+            // partial sums in registers when they all belong to one row, the common case
+            const uint32_t r0 = GEMV ? static_cast<uint32_t>(base / gv.cols) : 0u;
+            auto join = [&](uint64_t sg, u32x2 smv, bool valid, bool whole_wave) {
                 const uint64_t g0 = sg * 8;
-                const uint64_t ev = exps8[sg - s0];
+                const uint64_t ev = valid ? exps8[sg - s0] : 0;
                 // four weights per word: high byte = sign | exponent >> 1, low byte = exponent
                 // bit 0 << 7 | mantissa; v_perm interleaves the low and high bytes
                 u32x4 o;
@@ -207,7 +226,38 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
                     op[2 * h] = __builtin_amdgcn_perm(hi4, lo4, 0x05010400u);
                     op[2 * h + 1] = __builtin_amdgcn_perm(hi4, lo4, 0x07030602u);
                 }
-                if (g0 >= base && g0 + 8 <= stop) {
+                if constexpr (GEMV) {
+                    // 8 weights of one row (cols % 8 == 0): products in fp32 (exact for BF16 x
+                    // BF16), summed, added to the row's LDS partial
+                    uint32_t rl = ~0u;
+                    float acc = 0.f;
+                    if (valid) {
+                        const uint32_t g32 = static_cast<uint32_t>(g0);
+                        const uint32_t r = g32 / gv.cols, k0 = g32 - r * gv.cols;
+                        const u32x4 xq = *reinterpret_cast<const u32x4 *>(gv.x + k0);
+                        const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xq);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t wb = (op[e >> 1] >> (16 * (e & 1))) << 16;
+                            const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) << 16;
+                            const bool in = g0 + e >= base && g0 + e < stop;
+                            acc += in ? __uint_as_float(wb) * __uint_as_float(xb) : 0.f;
+                        }
+                        rl = r - r0;
+                    }
+                    if (whole_wave) {
+                        const uint32_t first = __builtin_amdgcn_readfirstlane(rl);
+                        if (__all(!valid || rl == first)) {
+#pragma unroll
+                            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+                            if (lane == 0 && first != ~0u) atomicAdd(&row_sum[first], acc);
+                            return;
+                        }
+                    }
+                    if (valid) atomicAdd(&row_sum[rl], acc);
+                } else if (!valid) {
+                    return;
+                } else if (g0 >= base && g0 + 8 <= stop) {
                     __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + g0));
                 } else {
 #pragma unroll
@@ -219,13 +269,30 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
 #pragma unroll
             for (int i = 0; i < kJoinAhead; ++i) {
                 const uint64_t sg = s0 + t + i * kSpansPerBlock;
-                if (sg < s1) join(sg, cur.smp[i]);
+                if (GEMV)
+                    join(sg, cur.smp[i], sg < s1, true);
+                else if (sg < s1)
+                    join(sg, cur.smp[i], true, false);
             }
             // blocks with more than kJoinAhead * 2048 values (codes under 2 bits on average)
             if (s0 + kJoinAhead * kSpansPerBlock < s1) {
                 const __amdgpu_buffer_rsrc_t rm = rsrc(sm + s0 * 8, std::min<uint64_t>(sm_bytes - s0 * 8, (s1 - s0) * 8));
                 for (uint64_t sg = s0 + t + kJoinAhead * kSpansPerBlock; sg < s1; sg += kSpansPerBlock)
-                    join(sg, __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((sg - s0) * 8), 0, kStreamOnce));
+                    join(sg, __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((sg - s0) * 8), 0, kStreamOnce),
+                         true, false);
+            }
+        }
+        if constexpr (GEMV) {
+            // the block's rows: one global add each (rows at the block's ends are shared with the
+            // neighbouring blocks), then the partials are cleared for the next block
+            __syncthreads();
+            if (base < stop) {
+                const uint32_t r0 = static_cast<uint32_t>(base / gv.cols);
+                const uint32_t nr = static_cast<uint32_t>((stop - 1) / gv.cols) - r0 + 1;
+                for (uint32_t i = t; i < nr; i += kSpansPerBlock) {
+                    atomicAdd(&gv.y[r0 + i], row_sum[i]);
+                    row_sum[i] = 0.f;
+                }
             }
         }
         __syncthreads();  // the next block reuses wave_sum and exps
@@ -233,9 +300,34 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__r
     }
 }
 
-}  // namespace
+__global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__restrict__ sm,
+                                                              const uint32_t *__restrict__ stream,
+                                                              const uint32_t *__restrict__ gaps,
+                                                              const uint32_t *__restrict__ bases,
+                                                              const uint16_t *__restrict__ lut,
+                                                              uint16_t *__restrict__ out, EcGemvOut gv, uint64_t n,
+                                                              uint64_t total_bits, uint32_t spans, uint32_t blocks) {
+    ec_blocks<false>(sm, stream, gaps, bases, lut, out, gv, n, total_bits, spans, blocks);
+}
 
-cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s) {
+__global__ __launch_bounds__(kSpansPerBlock) void k_ec_gemv(const uint8_t *__restrict__ sm,
+                                                            const uint32_t *__restrict__ stream,
+                                                            const uint32_t *__restrict__ gaps,
+                                                            const uint32_t *__restrict__ bases,
+                                                            const uint16_t *__restrict__ lut,
+                                                            uint16_t *__restrict__ out, EcGemvOut gv, uint64_t n,
+                                                            uint64_t total_bits, uint32_t spans, uint32_t blocks) {
+    ec_blocks<true>(sm, stream, gaps, bases, lut, out, gv, n, total_bits, spans, blocks);
+}
+
+__global__ __launch_bounds__(256) void k_ec_zero(float *__restrict__ y, uint64_t rows) {
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < rows;
+         i += static_cast<uint64_t>(gridDim.x) * 256)
+        y[i] = 0.f;
+}
+
+template <bool GEMV>
+cbk_status launch_ec(const cbk_ec_tensor *t, uint16_t *out, EcGemvOut gv, hipStream_t s) {
     const uint64_t spans = (t->total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
     const uint64_t blocks = (spans + kSpansPerBlock - 1) / kSpansPerBlock;
     int dev = 0, cus = 0;
@@ -250,16 +342,36 @@ cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s
     if (dev < 0 || dev >= 64) return CBK_E_HIP;
     int occ = per_cu[dev].load(std::memory_order_relaxed);
     if (occ <= 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_ec_decode, kSpansPerBlock, 0) != hipSuccess || occ <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, GEMV ? k_ec_gemv : k_ec_decode, kSpansPerBlock, 0) !=
+                hipSuccess ||
+            occ <= 0)
             return CBK_E_HIP;
         per_cu[dev].store(occ, std::memory_order_relaxed);
     }
     const uint32_t grid = static_cast<uint32_t>(
         std::max<uint64_t>(1, std::min<uint64_t>(blocks, static_cast<uint64_t>(occ) * cus)));
-    hipLaunchKernelGGL(k_ec_decode, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream, t->gaps, t->bases,
-                       t->lut, out, t->n, t->total_bits, static_cast<uint32_t>(spans),
+    hipLaunchKernelGGL(GEMV ? k_ec_gemv : k_ec_decode, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream,
+                       t->gaps, t->bases,
+                       t->lut, out, gv, t->n, t->total_bits, static_cast<uint32_t>(spans),
                        static_cast<uint32_t>(blocks));
     return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
+}
+
+}  // namespace
+
+cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s) {
+    return launch_ec<false>(t, out, EcGemvOut{nullptr, nullptr, 1}, s);
+}
+
+cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
+                          hipStream_t s) {
+    // y is accumulated with atomics, so it starts from zeros (a fill kernel, which graph capture
+    // records as an ordinary node)
+    const uint32_t zgrid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>((rows + 255) / 256, 1024)));
+    hipLaunchKernelGGL(k_ec_zero, dim3(zgrid), dim3(256), 0, s, y, rows);
+    if (hipGetLastError() != hipSuccess) return CBK_E_HIP;
+    if (t->n == 0) return CBK_OK;
+    return launch_ec<true>(t, nullptr, EcGemvOut{x, y, static_cast<uint32_t>(cols)}, s);
 }
 
 }  // namespace cbk

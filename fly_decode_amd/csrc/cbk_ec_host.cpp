@@ -201,4 +201,25 @@ cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *strea
     return cbk::launch_ec_decode(t, out, static_cast<hipStream_t>(stream));
 }
 
+cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
+                       void *stream) {
+    if (!t) return CBK_E_INVALID;
+    const uint64_t n = t->n;
+    if (n >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
+    if (cols != 0 && rows > (uint64_t(1) << 32) / cols) return CBK_E_INVALID;
+    if (rows * cols != n) return CBK_E_INVALID;
+    if (rows == 0) return CBK_OK;
+    if (!x || !y) return CBK_E_INVALID;
+    if ((reinterpret_cast<uintptr_t>(y) & 3u) != 0) return CBK_E_ALIGN;
+    if (n > 0) {
+        if (cols % 8 != 0 || cols < 64) return CBK_E_UNSUPPORTED;
+        if (!t->sm || !t->stream || !t->gaps || !t->bases || !t->lut) return CBK_E_INVALID;
+        if (t->total_bits < n || t->total_bits > uint64_t(CBK_EC_MAX_LEN) * n) return CBK_E_INVALID;
+        if (!aligned16(x) || !aligned16(t->sm) || !aligned16(t->stream) || !aligned16(t->gaps) ||
+            !aligned16(t->bases) || !aligned16(t->lut))
+            return CBK_E_ALIGN;
+    }
+    return cbk::launch_ec_gemv(t, rows, cols, x, y, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

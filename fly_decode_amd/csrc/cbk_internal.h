@@ -26,5 +26,7 @@ cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uin
 
 // Exponent entropy-coded format (cbk_ec.hip).
 cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s);
+cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
+                          hipStream_t s);
 
 }  // namespace cbk

@@ -102,6 +102,21 @@ typedef struct {
  */
 cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *stream);
 
+/*
+ * cbk_ec_gemv -- GPU.  Decode fused into the batch-1 GEMV for a tensor of rows x cols weights
+ * (row-major, rows * cols == t->n): y[r] = sum_k W[r][k] * x[k], fp32 products and sums.  The same
+ * two-phase block decode as cbk_ec_decode_bf16, with each block's weights multiplied by x as they
+ * are joined, summed per row in LDS and added to y with one atomic per row the block touches (a
+ * row can span blocks), so the summation order varies between calls; y is zero-filled first by a
+ * kernel on the same stream.  The BF16 weights never reach HBM.
+ *   x     device, cols BF16 patterns, 16-byte aligned.
+ *   y     device, rows fp32, 4-byte aligned; fully overwritten.
+ * Errors: as cbk_ec_decode_bf16; CBK_E_INVALID for rows * cols != n or a NULL x or y with rows > 0;
+ * CBK_E_UNSUPPORTED for cols % 8 != 0 or cols < 64 (when n > 0); CBK_E_ALIGN for x or y.
+ */
+cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

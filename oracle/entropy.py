@@ -239,6 +239,15 @@ def decode(enc: EncodedEC):
     return join(e, enc.sm)
 
 
+def gemv(enc: EncodedEC, rows: int, cols: int, x):
+    """(y, absb) in float64: the weights decoded bit by bit, y = W . x and absb = |W| . |x| (the
+    scale of the fused GEMV's tolerance)."""
+    w = decode(enc).reshape(rows, cols)
+    wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xf = (np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return wf @ xf, np.abs(wf) @ np.abs(xf)
+
+
 def gap_of(enc: EncodedEC, j: int) -> int:
     return (int(enc.gaps[j // 8]) >> (4 * (j % 8))) & 0xF
 

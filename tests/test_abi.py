@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
               "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str", "cbk_encode_gpu",
               "cbk_encode_gpu_workspace_bytes", "cbk_ec_plan", "cbk_ec_encode", "cbk_ec_decode_bf16",
               "cbk_ec_spans", "cbk_ec_stream_words", "cbk_ec_gap_words", "cbk_ec_blocks",
-              "cbk_ec_stored_bytes", "cbk_cap_patterns"]:
+              "cbk_ec_stored_bytes", "cbk_cap_patterns", "cbk_ec_gemv"]:
         assert n in names
 
 

@@ -114,3 +114,22 @@ def test_size_helpers(cbk):
         assert lib.cbk_ec_stream_words(ctypes.byref(h)) == 2 * spans
         assert lib.cbk_ec_gap_words(ctypes.byref(h)) == (spans + 7) // 8
         assert lib.cbk_ec_blocks(ctypes.byref(h)) == (spans + 255) // 256
+
+
+def test_gemv_validates_before_any_hip_call(cbk):
+    """cbk_ec_gemv rejects bad arguments on the host (no device is present here)."""
+    lib = cbk.load_library()
+    T = cbk._ECTensor
+    A = 0x10000   # 16-byte aligned stand-ins; nothing is dereferenced on these paths
+
+    def call(n=6400, rows=100, cols=64, x=A, y=A, none=False):
+        t = T(n=n, total_bits=3 * n, sm=A, stream=A, gaps=A, bases=A, lut=A)
+        return lib.cbk_ec_gemv(None if none else ctypes.byref(t), rows, cols, ctypes.c_void_p(x),
+                               ctypes.c_void_p(y), None)
+    assert call(none=True) == 1
+    assert call(rows=99) == 1                        # rows * cols != n
+    assert call(x=0) == 1 and call(y=0) == 1
+    assert call(n=6400, rows=200, cols=32) == 4      # fewer than 64 columns
+    assert call(n=6000, rows=100, cols=60) == 4      # columns not a multiple of 8
+    assert call(x=A + 2) == 3 and call(y=A + 2) == 3
+    assert call(n=0, rows=0, cols=64, x=0, y=0) == 0  # nothing to do

@@ -117,3 +117,74 @@ def test_ec_decode_corrupt_stream_stays_in_bounds(env):
     cbk.ec_decode_bf16(bad, out=buf[:n].view(torch.bfloat16).view(1, n))
     torch.cuda.synchronize()
     assert bool((buf[n:].cpu() == -7).all())
+
+
+# ---------------------------------------------------------------- fused GEMV on the same format
+TOL = 1e-3
+
+
+def _gemv_check(env, w, x, rows=None):
+    """cbk_ec_gemv against the oracle: the oracle decodes (bit by bit) the rows it checks, from its
+    own encoding of them, and forms y = W x in float64."""
+    torch, cbk = env
+    R, C = w.shape
+    print(f"ec gemv shape={w.shape}", flush=True)
+    d = cbk.ec_encode(w).to("cuda")
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+    y = cbk.ec_gemv(d, xd)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    sub = w if rows is None else np.ascontiguousarray(w[np.asarray(rows)])
+    ref, absb = ec.gemv(ec.encode(sub), sub.shape[0], C, x)
+    if rows is not None:
+        got = got[np.asarray(rows)]
+    err = np.abs(got - ref)
+    assert np.all(err <= TOL * absb), f"max err/bound {np.max(err / np.maximum(absb, 1e-300))}"
+    return y
+
+
+def _gemv_cases():
+    rng = np.random.default_rng(31)
+    return {
+        "gaussian_300x776": synth.gaussian_bf16((300, 776), 0.02, seed=[51]),
+        "t2_200x1000": synth.student_t_bf16((200, 1000), 2.0, 0.02, seed=[52]),
+        "t4_64x4096": synth.student_t_bf16((64, 4096), 4.0, 0.02, seed=[53]),
+        "one_bit_codes_10x1000": np.full((10, 1000), 0x3F80, dtype=np.uint16),
+        "narrow_rows_300x64": synth.gaussian_bf16((300, 64), 0.02, seed=[54]),
+        "specials_free_mix_37x128": rng.choice(np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4000, 0x3C00],
+                                                        dtype=np.uint16), (37, 128)),
+    }
+
+
+@pytest.mark.parametrize("name", list(_gemv_cases()))
+def test_ec_gemv_matches_oracle(env, name):
+    w = _gemv_cases()[name]
+    x = synth.activation_bf16(w.shape[1], seed=[55, w.shape[1]])
+    _gemv_check(env, w, x)
+
+
+def test_ec_gemv_workload_tensor_sampled_rows(env):
+    """A 4096^2 attention-workload tensor; 64 sampled rows, the first and last included."""
+    w = synth.workload_tensor(2, 0, synth.WORKLOADS[2][0][0])
+    x = synth.workload_x(2, 4096)[0]
+    rows = np.concatenate([[0, 4095], np.random.default_rng(56).choice(np.arange(1, 4095), 62, replace=False)])
+    _gemv_check(env, w, x, rows=rows)
+
+
+def test_ec_gemv_overwrites_y_and_repeats_within_tolerance(env):
+    """y is overwritten (not accumulated into) and repeated calls agree to the tolerance (the
+    atomic adds may sum a row's block partials in any order)."""
+    torch, cbk = env
+    w = synth.gaussian_bf16((512, 1024), 0.02, seed=[57])
+    x = synth.activation_bf16(1024, seed=[58])
+    d = cbk.ec_encode(w).to("cuda")
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    y = torch.full((512,), 1e30, dtype=torch.float32, device="cuda")
+    cbk.ec_gemv(d, xd, y=y)
+    y0 = y.clone()
+    for _ in range(3):
+        cbk.ec_gemv(d, xd, y=y)
+    torch.cuda.synchronize()
+    ref, absb = ec.gemv(ec.encode(w), 512, 1024, x)
+    for v in (y0, y):
+        assert np.all(np.abs(v.cpu().numpy().astype(np.float64) - ref) <= TOL * absb)
