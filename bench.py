@@ -174,28 +174,34 @@ def cpu_baseline_encode(specs, seconds: float):
     }
 
 
-def cpu_baseline_ec(specs, seconds: float):
+def cpu_baseline_ec(specs, seconds: float, gemv: bool = False):
     """The oracle's bit-by-bit decoder of the entropy-coded format (pure Python, one thread) on
-    leading rows of one tensor of the workload, growing the sample until about `seconds` pass."""
+    leading rows of one tensor of the workload, growing the sample until about `seconds` pass.
+    With `gemv`, the oracle's GEMV of those rows (decode, then float64 products) is timed."""
     from oracle import entropy as ec
     import synth
 
     cfg, layer, t = specs[0]
     w = synth.workload_tensor(cfg, layer, t)
+    x = synth.workload_x(cfg, t.cols)[0]
     rows, spent, done = 4, 0.0, 0
     while spent < seconds and rows <= t.rows:
         enc = ec.encode(w[:rows])
         t0 = time.perf_counter()
-        ec.decode(enc)
+        if gemv:
+            ec.gemv(enc, rows, t.cols, x)
+        else:
+            ec.decode(enc)
         spent += time.perf_counter() - t0
         done += rows * t.cols
         rows *= 2
+    what = "decoder and float64 GEMV" if gemv else "decoder"
     return {
         "value": round(2.0 * done / spent / 1e9, 6),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"the oracle's bit-by-bit decoder (pure Python, one thread) on the leading 4, 8, ... "
+        "sample": f"the oracle's bit-by-bit {what} (pure Python, one thread) on the leading 4, 8, ... "
                   f"rows of one {t.rows}x{t.cols} tensor of the workload, {done} weights, {spent:.1f} s",
     }
 
@@ -462,9 +468,9 @@ def main():
     if not args.no_cpu_baseline and batch == 1 and not ecgemv:
         log("CPU baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
-    elif not args.no_cpu_baseline and ecfmt and not ecgemv:
+    elif not args.no_cpu_baseline and ecfmt:
         log("CPU baseline (oracle entropy decoder) ...")
-        result["cpu_baseline"] = cpu_baseline_ec(specs, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_ec(specs, args.cpu_seconds, gemv=ecgemv)
     elif not args.no_cpu_baseline and encode:
         log("CPU baseline (oracle encoder) ...")
         result["cpu_baseline"] = cpu_baseline_encode(specs, args.cpu_seconds)
