@@ -30,6 +30,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kSpansPerBlock = CBK_EC_BLOCK_SPANS;  // = threads per workgroup
 constexpr int kMaxPerSpan = CBK_EC_SPAN_BITS;       // codes are at least one bit long
@@ -56,12 +57,46 @@ __device__ __forceinline__ uint32_t window12(uint32_t w0, uint32_t w1, uint32_t 
 constexpr uint32_t kGemvMinCols = 64;
 constexpr uint32_t kGemvBlockRows = kSpansPerBlock * kMaxPerSpan / kGemvMinCols + 2;
 
-// Fused GEMV output: y (zero-filled beforehand) and x, for rows of `cols` weights.
+// Fused GEMV output: y (zero-filled beforehand) and x, for rows of `cols` weights.  Row indices
+// come from v / cols computed by a multiply and shifts (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, section 4): with l = ceil(log2 cols),
+// magic = floor(2^32 (2^l - cols) / cols) + 1, sh1 = min(l, 1), sh2 = max(l - 1, 0), exact for every
+// 32-bit v.
 struct EcGemvOut {
     const uint16_t *x;
     float *y;
-    uint32_t cols;
+    uint32_t cols, magic, sh1, sh2;
 };
+
+__device__ __forceinline__ uint32_t row_of(uint32_t v, const EcGemvOut &gv) {
+    const uint32_t hi = __umulhi(v, gv.magic);
+    return (hi + ((v - hi) >> gv.sh1)) >> gv.sh2;
+}
+
+// One step of a wave sum: v plus v moved by the DPP control CTRL within the rows in ROWS (lanes
+// whose source is out of range add zero).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// The sum of v over the 64 lanes, in lane 63: prefix sums within each 16-lane row (row_shr 1, 2,
+// 4, 8), then lane 15 of rows 0 and 2 carried into rows 1 and 3 (row_bcast:15) and lane 31 into
+// rows 2 and 3 (row_bcast:31).  All VALU; no LDS round trips.
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v = dpp_add<0x111, 0xF>(v);
+    v = dpp_add<0x112, 0xF>(v);
+    v = dpp_add<0x114, 0xF>(v);
+    v = dpp_add<0x118, 0xF>(v);
+    v = dpp_add<0x142, 0xA>(v);
+    return dpp_add<0x143, 0xC>(v);
+}
+
+// a.lo * b.lo + a.hi * b.hi + acc for two BF16 pairs, products and sum in fp32
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                           false);
+}
 
 // GEMV == false: decode to BF16 in out.  GEMV == true: y[r] += sum of W[r][k] x[k] over the
 // block's weights, per row in LDS first, then one global atomic add per row the block touches.
@@ -112,6 +147,9 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
         uint32_t c, gword;
         uint64_t base;
         u32x2 smp[kJoinAhead];  // sm bytes of the block's first kJoinAhead segments per thread
+        // GEMV: x under those segments and their rows
+        u32x4 xq[GEMV ? kJoinAhead : 1];
+        uint32_t row[GEMV ? kJoinAhead : 1];
     };
     // base, limit: bases[k] and bases[k + 1] (n for the last block), read one block earlier so that
     // the sm loads need not wait for them; the loads stay within the block's own bytes
@@ -136,6 +174,19 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
 #pragma unroll
         for (int i = 0; i < kJoinAhead; ++i)
             in.smp[i] = __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((t + i * kSpansPerBlock) * 8), 0, kStreamOnce);
+        if constexpr (GEMV) {
+            // Loaded here, one block ahead, with the block's other inputs: the memory counter is
+            // in order, so an x load issued in the join would also wait for the next block's
+            // prefetch.  Weight index g (wrapped to 32 bits past the end) lies in row g / cols
+            // at column g - row * cols < cols, so every load is inside x.
+#pragma unroll
+            for (int i = 0; i < kJoinAhead; ++i) {
+                const uint32_t g32 = static_cast<uint32_t>((base / 8 + t + i * kSpansPerBlock) * 8);
+                const uint32_t r = row_of(g32, gv);
+                in.row[i] = r;
+                in.xq[i] = *reinterpret_cast<const u32x4 *>(gv.x + (g32 - r * gv.cols));
+            }
+        }
         return in;
     };
 
@@ -152,9 +203,6 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
             end = rem < CBK_EC_SPAN_BITS ? static_cast<uint32_t>(rem) : CBK_EC_SPAN_BITS;
         }
         const uint32_t w0 = cur.ab.x, w1 = cur.ab.y, w2 = cur.c;
-        // While the whole 12-bit window lies before the span's end, both codes of a lookup start
-        // inside the span; the last few bits go one code at a time.  Every step advances by at
-        // least one bit per code, so no span yields more than 64 codes.
 
         // phase 1: how many codes start in this span.  While the whole 12-bit window lies before
         // the span's end, both codes of a lookup start inside the span; the last few bits go one
@@ -209,8 +257,9 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
             const uint64_t s0 = base / 8, s1 = (stop + 7) / 8;
             // GEMV: one wave-wide call (every lane, `valid` false past s1) can reduce the wave's
             // partial sums in registers when they all belong to one row, the common case
-            const uint32_t r0 = GEMV ? static_cast<uint32_t>(base / gv.cols) : 0u;
-            auto join = [&](uint64_t sg, u32x2 smv, bool valid, bool whole_wave) {
+            const uint32_t r0 = GEMV ? row_of(static_cast<uint32_t>(base), gv) : 0u;
+            // (xq, r: x under segment sg and its row, GEMV only)
+            auto join = [&](uint64_t sg, u32x2 smv, u32x4 xq, uint32_t r, bool valid, bool whole_wave) {
                 const uint64_t g0 = sg * 8;
                 const uint64_t ev = valid ? exps8[sg - s0] : 0;
                 // four weights per word: high byte = sign | exponent >> 1, low byte = exponent
@@ -227,30 +276,33 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
                     op[2 * h + 1] = __builtin_amdgcn_perm(hi4, lo4, 0x07030602u);
                 }
                 if constexpr (GEMV) {
-                    // 8 weights of one row (cols % 8 == 0): products in fp32 (exact for BF16 x
-                    // BF16), summed, added to the row's LDS partial
+                    // 8 weights of one row (cols % 8 == 0): BF16 pair products summed in fp32,
+                    // added to the row's LDS partial
                     uint32_t rl = ~0u;
                     float acc = 0.f;
                     if (valid) {
-                        const uint32_t g32 = static_cast<uint32_t>(g0);
-                        const uint32_t r = g32 / gv.cols, k0 = g32 - r * gv.cols;
-                        const u32x4 xq = *reinterpret_cast<const u32x4 *>(gv.x + k0);
-                        const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xq);
+                        uint32_t *xw = reinterpret_cast<uint32_t *>(&xq);
+                        if (g0 < base || g0 + 8 > stop) {
+                            // a segment at an end of the block: the weights outside [base, stop)
+                            // belong to the neighbouring block, so both operands of theirs are
+                            // zeroed (0 x 0, whatever x holds)
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const uint32_t wb = (op[e >> 1] >> (16 * (e & 1))) << 16;
-                            const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) << 16;
-                            const bool in = g0 + e >= base && g0 + e < stop;
-                            acc += in ? __uint_as_float(wb) * __uint_as_float(xb) : 0.f;
+                            for (int h = 0; h < 4; ++h) {
+                                const uint64_t e = g0 + 2 * h;
+                                const uint32_t keep = (e >= base && e < stop ? 0x0000FFFFu : 0u) |
+                                                      (e + 1 >= base && e + 1 < stop ? 0xFFFF0000u : 0u);
+                                op[h] &= keep;
+                                xw[h] &= keep;
+                            }
                         }
+                        acc = dot2(op[3], xw[3], dot2(op[2], xw[2], dot2(op[1], xw[1], dot2(op[0], xw[0], 0.f))));
                         rl = r - r0;
                     }
                     if (whole_wave) {
                         const uint32_t first = __builtin_amdgcn_readfirstlane(rl);
                         if (__all(!valid || rl == first)) {
-#pragma unroll
-                            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-                            if (lane == 0 && first != ~0u) atomicAdd(&row_sum[first], acc);
+                            acc = wave_sum_last(acc);
+                            if (lane == 63 && first != ~0u) atomicAdd(&row_sum[first], acc);
                             return;
                         }
                     }
@@ -270,16 +322,22 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
             for (int i = 0; i < kJoinAhead; ++i) {
                 const uint64_t sg = s0 + t + i * kSpansPerBlock;
                 if (GEMV)
-                    join(sg, cur.smp[i], sg < s1, true);
+                    join(sg, cur.smp[i], cur.xq[i], cur.row[i], sg < s1, true);
                 else if (sg < s1)
-                    join(sg, cur.smp[i], true, false);
+                    join(sg, cur.smp[i], u32x4{}, 0, true, false);
             }
             // blocks with more than kJoinAhead * 2048 values (codes under 2 bits on average)
             if (s0 + kJoinAhead * kSpansPerBlock < s1) {
                 const __amdgpu_buffer_rsrc_t rm = rsrc(sm + s0 * 8, std::min<uint64_t>(sm_bytes - s0 * 8, (s1 - s0) * 8));
-                for (uint64_t sg = s0 + t + kJoinAhead * kSpansPerBlock; sg < s1; sg += kSpansPerBlock)
-                    join(sg, __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((sg - s0) * 8), 0, kStreamOnce),
-                         true, false);
+                for (uint64_t sg = s0 + t + kJoinAhead * kSpansPerBlock; sg < s1; sg += kSpansPerBlock) {
+                    const u32x2 smv = __builtin_amdgcn_raw_buffer_load_b64(rm, static_cast<int>((sg - s0) * 8), 0, kStreamOnce);
+                    if constexpr (GEMV) {
+                        const uint32_t g32 = static_cast<uint32_t>(sg * 8), r = row_of(g32, gv);
+                        join(sg, smv, *reinterpret_cast<const u32x4 *>(gv.x + (g32 - r * gv.cols)), r, true, false);
+                    } else {
+                        join(sg, smv, u32x4{}, 0, true, false);
+                    }
+                }
             }
         }
         if constexpr (GEMV) {
@@ -287,8 +345,8 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
             // neighbouring blocks), then the partials are cleared for the next block
             __syncthreads();
             if (base < stop) {
-                const uint32_t r0 = static_cast<uint32_t>(base / gv.cols);
-                const uint32_t nr = static_cast<uint32_t>((stop - 1) / gv.cols) - r0 + 1;
+                const uint32_t r0 = row_of(static_cast<uint32_t>(base), gv);
+                const uint32_t nr = row_of(static_cast<uint32_t>(stop - 1), gv) - r0 + 1;
                 for (uint32_t i = t; i < nr; i += kSpansPerBlock) {
                     atomicAdd(&gv.y[r0 + i], row_sum[i]);
                     row_sum[i] = 0.f;
@@ -360,7 +418,7 @@ cbk_status launch_ec(const cbk_ec_tensor *t, uint16_t *out, EcGemvOut gv, hipStr
 }  // namespace
 
 cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s) {
-    return launch_ec<false>(t, out, EcGemvOut{nullptr, nullptr, 1}, s);
+    return launch_ec<false>(t, out, EcGemvOut{nullptr, nullptr, 1, 1, 0, 0}, s);
 }
 
 cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
@@ -371,7 +429,14 @@ cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, 
     hipLaunchKernelGGL(k_ec_zero, dim3(zgrid), dim3(256), 0, s, y, rows);
     if (hipGetLastError() != hipSuccess) return CBK_E_HIP;
     if (t->n == 0) return CBK_OK;
-    return launch_ec<true>(t, nullptr, EcGemvOut{x, y, static_cast<uint32_t>(cols)}, s);
+    // the divisor constants of row_of (cols < 2^32 here, so the product fits 64 bits)
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < cols) ++l;
+    const uint32_t magic = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << l) - cols)) / cols + 1);
+    return launch_ec<true>(t, nullptr,
+                           EcGemvOut{x, y, static_cast<uint32_t>(cols), magic, std::min<uint32_t>(l, 1),
+                                     l > 0 ? l - 1 : 0},
+                           s);
 }
 
 }  // namespace cbk

@@ -151,6 +151,11 @@ def _gemv_cases():
         "t4_64x4096": synth.student_t_bf16((64, 4096), 4.0, 0.02, seed=[53]),
         "one_bit_codes_10x1000": np.full((10, 1000), 0x3F80, dtype=np.uint16),
         "narrow_rows_300x64": synth.gaussian_bf16((300, 64), 0.02, seed=[54]),
+        # row lengths whose segment count (cols / 8) is odd or prime: the row index of a segment
+        # comes from a multiply-and-shift division by cols
+        "cols_8x1049_40x8392": synth.gaussian_bf16((40, 8392), 0.02, seed=[59]),
+        "cols_11008_24x11008": synth.gaussian_bf16((24, 11008), 0.02, seed=[60]),
+        "cols_72_500x72": synth.gaussian_bf16((500, 72), 0.02, seed=[61]),
         "specials_free_mix_37x128": rng.choice(np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4000, 0x3C00],
                                                         dtype=np.uint16), (37, 128)),
     }
