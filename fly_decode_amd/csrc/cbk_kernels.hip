@@ -61,6 +61,26 @@ __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
                                            __builtin_bit_cast(bf16x2_t, x), acc, false);
 }
 
+// One step of a wave sum: v plus v moved by the DPP control CTRL within the rows in ROWS (lanes
+// whose source is out of range add zero).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// The sum of v over the 64 lanes (all active), in lane 63: prefix sums within each 16-lane row
+// (row_shr 1, 2, 4, 8), then lane 15 of rows 0 and 2 carried into rows 1 and 3 (row_bcast:15) and
+// lane 31 into rows 2 and 3 (row_bcast:31).  VALU only, where lane shuffles would be six LDS round
+// trips.
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v = dpp_add<0x111, 0xF>(v);
+    v = dpp_add<0x112, 0xF>(v);
+    v = dpp_add<0x114, 0xF>(v);
+    v = dpp_add<0x118, 0xF>(v);
+    v = dpp_add<0x142, 0xA>(v);
+    return dpp_add<0x143, 0xC>(v);
+}
+
 __device__ __forceinline__ float bf16_value(uint16_t h) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
 }
@@ -424,10 +444,8 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
     };
     float a[4] = {0.f, 0.f, 0.f, 0.f};
     auto reduce_row = [&](uint32_t r) {
-        float acc = (a[0] + a[1]) + (a[2] + a[3]);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (lane == 0) yt[r] = acc;
+        const float acc = wave_sum_last((a[0] + a[1]) + (a[2] + a[3]));
+        if (lane == 63) yt[r] = acc;
         a[0] = a[1] = a[2] = a[3] = 0.f;
     };
 
