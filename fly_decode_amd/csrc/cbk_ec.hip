@@ -92,6 +92,22 @@ __device__ __forceinline__ float wave_sum_last(float v) {
     return dpp_add<0x143, 0xC>(v);
 }
 
+// Inclusive prefix sum of v over the wave's 64 lanes (all active), on the VALU: the same row
+// shifts and row broadcasts as wave_sum_last leave every lane with the sum up to itself.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_addu(uint32_t v) {
+    return v + static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+    v = dpp_addu<0x111, 0xF>(v);
+    v = dpp_addu<0x112, 0xF>(v);
+    v = dpp_addu<0x114, 0xF>(v);
+    v = dpp_addu<0x118, 0xF>(v);
+    v = dpp_addu<0x142, 0xA>(v);
+    return dpp_addu<0x143, 0xC>(v);
+}
+
 // a.lo * b.lo + a.hi * b.hi + acc for two BF16 pairs, products and sum in fp32
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
@@ -217,12 +233,7 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
         for (; pos < end; ++cnt) pos += (multi[window12(w0, w1, w2, pos)] >> 16) & 15u;
 
         // prefix sum of the counts over the workgroup
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o);
-            if (lane >= static_cast<uint32_t>(o)) incl += y;
-        }
+        const uint32_t incl = wave_scan(cnt);
         if (lane == 63) wave_sum[wave] = incl;
         __syncthreads();
         uint32_t before = 0, total = 0;
