@@ -457,16 +457,19 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
 #pragma unroll
         for (int g = 0; g < 8; ++g)
             xr[g] = active ? *reinterpret_cast<const u32x4 *>(xl + lane * XU + 16 * g) : (u32x4){0u, 0u, 0u, 0u};
-        uint32_t r = gw;
+        // rn, the row after r, is claimed one row ahead, so the claim's LDS round trip is not
+        // between a row's read-back and the next row's loads
+        uint32_t r = gw, rn = next(gw);
         while (true) {
             uint32_t d[G::UD];
             transpose_step<B>(d, nxt, stage, r * P, lane);
-            const uint32_t rn = next(r);
             if (rn < M) load_step<B>(nxt, w4, rn * P, P, ~uint64_t(0), true, lane);
+            const uint32_t rnn = rn < M ? next(rn) : M;
             if (active) gemv_unit<B>(d, cbl, xr, a);
             reduce_row(r);
             if (rn >= M) break;
             r = rn;
+            rn = rnn;
         }
         return;
     }
