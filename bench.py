@@ -244,8 +244,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the GEMV shards by output rows; see the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (the GEMV would "
+              "shard by output rows, each GPU holding a contiguous row slice of every tensor's "
+              "stream).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -167,7 +167,8 @@ def test_padding_bits_are_zero(oracle_mod):
 
 
 def test_corrupt_index_reading(oracle_mod):
-    """An index >= U (never written by the encoder) decodes to 0x7FC0 under this build's reading."""
+    """An index >= U (never written by the encoder) decodes to 0x7FC0, the reading taken where the
+    pages say nothing about corrupt indices."""
     e = oracle_mod.encode(np.array([0x1111, 0x2222, 0x3333, 0x1111], dtype=np.uint16))
     assert e.b == 2 and e.U == 3
     words = e.words.copy()
