@@ -209,7 +209,7 @@ cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, con
     if (cols != 0 && rows > (uint64_t(1) << 32) / cols) return CBK_E_INVALID;
     if (rows * cols != n) return CBK_E_INVALID;
     if (rows == 0) return CBK_OK;
-    if (!x || !y) return CBK_E_INVALID;
+    if (!y || (cols > 0 && !x)) return CBK_E_INVALID;  // cols == 0: y is zero-filled, x unread
     if ((reinterpret_cast<uintptr_t>(y) & 3u) != 0) return CBK_E_ALIGN;
     if (n > 0) {
         if (cols % 8 != 0 || cols < 64) return CBK_E_UNSUPPORTED;

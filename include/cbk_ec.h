@@ -111,7 +111,8 @@ cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *strea
  * kernel on the same stream.  The BF16 weights never reach HBM.
  *   x     device, cols BF16 patterns, 16-byte aligned.
  *   y     device, rows fp32, 4-byte aligned; fully overwritten.
- * Errors: as cbk_ec_decode_bf16; CBK_E_INVALID for rows * cols != n or a NULL x or y with rows > 0;
+ * Errors: as cbk_ec_decode_bf16; CBK_E_INVALID for rows * cols != n, a NULL y with rows > 0 or a
+ * NULL x with cols > 0 (with cols == 0 and rows > 0, y is set to zeros and x is not read);
  * CBK_E_UNSUPPORTED for cols % 8 != 0 or cols < 64 (when n > 0); CBK_E_ALIGN for x or y.
  */
 cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,

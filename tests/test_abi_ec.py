@@ -133,3 +133,4 @@ def test_gemv_validates_before_any_hip_call(cbk):
     assert call(n=6000, rows=100, cols=60) == 4      # columns not a multiple of 8
     assert call(x=A + 2) == 3 and call(y=A + 2) == 3
     assert call(n=0, rows=0, cols=64, x=0, y=0) == 0  # nothing to do
+    assert call(n=0, rows=8, cols=0, x=0, y=0) == 1   # rows to write need y, even with no columns

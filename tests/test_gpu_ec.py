@@ -193,3 +193,22 @@ def test_ec_gemv_overwrites_y_and_repeats_within_tolerance(env):
     ref, absb = ec.gemv(ec.encode(w), 512, 1024, x)
     for v in (y0, y):
         assert np.all(np.abs(v.cpu().numpy().astype(np.float64) - ref) <= TOL * absb)
+
+
+def test_ec_gemv_zero_cols_gives_zeros(env):
+    """rows x 0 weights: y = W x is all zeros, x (empty) is not read and may be NULL."""
+    torch, cbk = env
+    d = cbk.ec_encode(np.zeros((8, 0), dtype=np.uint16)).to("cuda")
+    y = torch.full((8,), 5.0, dtype=torch.float32, device="cuda")
+    x = torch.zeros(8, dtype=torch.bfloat16, device="cuda")[:0]
+    cbk.ec_gemv(d, x, y=y)
+    torch.cuda.synchronize()
+    assert not y.any()
+
+
+def test_ec_decode_empty_tensor(env):
+    torch, cbk = env
+    d = cbk.ec_encode(np.zeros((0, 64), dtype=np.uint16)).to("cuda")
+    out = cbk.ec_decode_bf16(d)
+    torch.cuda.synchronize()
+    assert out.numel() == 0
