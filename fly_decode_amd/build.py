@@ -1,6 +1,7 @@
 """Build libcbk.so in-tree for gfx950 with hipcc (explicit flags, no JIT cache)."""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -36,15 +37,17 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    objs, cmds = [], []
     for src, is_hip in SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         lang = [] if is_hip else ["-x", "hip"]
-        cmd = [HIPCC] + DEVICE_FLAGS + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
-        out = _run(cmd)
-        if verbose and out:
-            print(out)
+        cmds.append([HIPCC] + DEVICE_FLAGS + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the translation units are independent: compile them side by side
+    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), max(1, (os.cpu_count() or 1)))) as ex:
+        for out in ex.map(_run, cmds):
+            if verbose and out:
+                print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC] + DEVICE_FLAGS + ["-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)
