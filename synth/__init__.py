@@ -12,16 +12,22 @@ Gaussian weights are N(0, sigma) drawn in float32 and rounded to BF16 by round-t
 heavy-tailed weights are Student-t with nu = 4, scaled by 0.02.  Activations are N(0, 1) BF16.
 
 Seeds: ``numpy.random.default_rng([cfg_id, layer, tensor_id])`` for weights and
-``default_rng([cfg_id, 1000 + length, column])`` for activation vectors.
+``default_rng([cfg_id, 1000 + length, column])`` for activation vectors.  The two decode-step
+workloads (the 7B- and 70B-shaped steps, 6.5 and 68 billion weights) are too large to draw on the
+host in a benchmark run: their N(0, sigma) weights come from the counter-based generator in
+``synth.counter`` with state ``counter.key_of([cfg_id, layer, tensor_id])``, which gives the same
+bits from numpy on the host (any single row on its own) and from torch on a GPU.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import counter
+
 __all__ = [
     "f32_to_bf16", "bf16_to_f32", "gaussian_bf16", "student_t_bf16", "activation_bf16",
     "activations_bf16", "from_alphabet", "with_distinct_count", "finite_exponents", "WORKLOADS", "Workload",
-    "workload_tensor", "workload_x",
+    "workload_tensor", "workload_x", "workload_rows", "workload_tensor_device", "counter",
 ]
 
 
@@ -109,7 +115,9 @@ def finite_exponents(distinct: int):
 
 
 class Workload:
-    """One weight tensor shape of a workload: name, rows (out features), cols (in features)."""
+    """One weight tensor shape of a workload: name, rows (out features), cols (in features);
+    dist is "normal" (PCG64 draws), "t4" (PCG64 Student-t) or "normal_ctr" (the counter-based
+    generator)."""
 
     def __init__(self, name: str, rows: int, cols: int, dist: str, scale: float, tensor_id: int):
         self.name, self.rows, self.cols = name, rows, cols
@@ -129,9 +137,9 @@ WORKLOADS = {
     2: (_layer([("attn", 4096, 4096)], "normal", 0.02), 1),
     3: (_layer([("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)], "t4", 0.02), 1),
     4: (_layer([("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
-                ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)], "normal", 0.02), 32),
+                ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)], "normal_ctr", 0.02), 32),
     5: (_layer([("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192, 8192),
-                ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)], "normal", 0.015), 80),
+                ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)], "normal_ctr", 0.015), 80),
 }
 
 
@@ -143,7 +151,38 @@ def workload_tensor(cfg_id: int, layer: int, tensor: Workload) -> np.ndarray:
         return gaussian_bf16(shape, tensor.scale, seed)
     if tensor.dist == "t4":
         return student_t_bf16(shape, 4.0, tensor.scale, seed)
+    if tensor.dist == "normal_ctr":
+        return counter.gaussian_bf16_host(counter.key_of(seed), 0, tensor.rows * tensor.cols,
+                                          tensor.scale).reshape(shape)
     raise ValueError(tensor.dist)
+
+
+def workload_rows(cfg_id: int, layer: int, tensor: Workload, rows) -> np.ndarray:
+    """The listed rows of a workload tensor, [len(rows)][cols] BF16, generated on their own when
+    the tensor comes from the counter-based generator (else sliced from the whole tensor)."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    if tensor.dist != "normal_ctr":
+        return np.ascontiguousarray(workload_tensor(cfg_id, layer, tensor)[rows])
+    key = counter.key_of([cfg_id, layer, tensor.tensor_id])
+    out = np.empty((rows.size, tensor.cols), dtype=np.uint16)
+    for i, r in enumerate(rows):
+        out[i] = counter.gaussian_bf16_np(key, int(r) * tensor.cols, tensor.cols, tensor.scale)
+    return out
+
+
+def workload_tensor_device(cfg_id: int, layer: int, tensor: Workload, device, out=None):
+    """A workload tensor as a flat int16 torch tensor of BF16 patterns on `device`: computed there
+    by the counter-based generator, or drawn on the host and copied for the PCG64 workloads."""
+    import torch
+    n = tensor.rows * tensor.cols
+    if tensor.dist == "normal_ctr":
+        return counter.gaussian_bf16_torch(counter.key_of([cfg_id, layer, tensor.tensor_id]), 0, n,
+                                           tensor.scale, device, out=out)
+    w = torch.from_numpy(workload_tensor(cfg_id, layer, tensor).reshape(-1).view(np.int16))
+    if out is None:
+        return w.to(device)
+    out.copy_(w)
+    return out
 
 
 def workload_x(cfg_id: int, length: int, batch: int = 1) -> np.ndarray:
