@@ -8,6 +8,9 @@ Sources of truth used here (none is the oracle's own code path being pinned):
     textbook example (frequencies 45, 13, 12, 16, 9, 5: cost 224);
   * Kraft equality and prefix-freeness of the canonical codes;
   * round trips through the bit-by-bit decoder, and span-by-span table decoding against it;
+  * for the GEMV: exact integer results computed with Python integers from the known weights,
+    one-hot x returning a column exactly, and the codebook oracle's float64 GEMV of the same
+    weights (a different format, decoder and summation);
   * the DFloat11 article's observation (section "Przełom: DFloat11") that the BF16 exponent of
     LLM weights carries about 2.6 bits: the coded exponent of Gaussian weights costs between its
     Shannon entropy and one bit more.
@@ -200,3 +203,62 @@ def test_exponent_cost_between_entropy_and_one_more_bit():
     assert h <= avg < h + 1
     # the DFloat11 article's ~2.6 bits for LLM exponents; Gaussian synthetic weights land nearby
     assert 2.0 < avg < 3.2
+
+
+def _int_patterns(values):
+    """BF16 bit patterns of small integers (exact in BF16)."""
+    return synth.f32_to_bf16(np.asarray(values, dtype=np.float32))
+
+
+@pytest.mark.parametrize("rows,cols", [(7, 40), (33, 9), (1, 128)])
+def test_gemv_integer_data_exact(rows, cols):
+    """Integer weights in [-8, 7] and x in [-4, 4]: every product and partial sum is an integer far
+    below 2^53, so the float64 result equals the Python-integer dot product exactly."""
+    rng = np.random.default_rng(rows * 1000 + cols)
+    wi = rng.integers(-8, 8, size=(rows, cols))
+    xi = rng.integers(-4, 5, size=cols)
+    y, absb = ec.gemv(ec.encode(_int_patterns(wi)), rows, cols, _int_patterns(xi))
+    for r in range(rows):
+        assert y[r] == sum(int(a) * int(b) for a, b in zip(wi[r], xi))
+        assert absb[r] == sum(abs(int(a)) * abs(int(b)) for a, b in zip(wi[r], xi))
+
+
+def test_gemv_one_hot_returns_a_column():
+    rows, cols = 12, 50
+    w = synth.gaussian_bf16((rows, cols), 0.02, seed=[91])
+    for k in (0, 17, cols - 1):
+        x = np.zeros(cols, dtype=np.uint16)
+        x[k] = 0x3F80  # 1.0
+        y, _ = ec.gemv(ec.encode(w), rows, cols, x)
+        assert np.array_equal(y, synth.bf16_to_f32(w[:, k]).astype(np.float64))
+
+
+def test_gemv_agrees_with_the_codebook_oracle(oracle_mod):
+    """The same Gaussian weights through the codebook format's C oracle: both are float64 sums of
+    exact products, so they agree to rounding (1e-12 of sum|W x|)."""
+    rows, cols = 64, 300
+    w = synth.gaussian_bf16((rows, cols), 0.02, seed=[92])
+    x = synth.activation_bf16(cols, seed=[93])
+    y, absb = ec.gemv(ec.encode(w), rows, cols, x)
+    ref, ref_abs = oracle_mod.gemv(oracle_mod.encode(w), x)
+    assert np.all(np.abs(y - ref) <= 1e-12 * ref_abs)
+    assert np.allclose(absb, ref_abs, rtol=1e-12, atol=0)
+
+
+def test_gemv_pin_catches_a_transposed_reshape():
+    """A planted mistake (the decoded weights read as [cols][rows] and transposed) fails the
+    integer pin."""
+    rows, cols = 5, 8
+    rng = np.random.default_rng(94)
+    wi = rng.integers(-8, 8, size=(rows, cols))
+    xi = rng.integers(-4, 5, size=cols)
+    enc = ec.encode(_int_patterns(wi))
+
+    def wrong(enc, rows, cols, x):
+        w = ec.decode(enc).reshape(cols, rows).T
+        wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        xf = (np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return wf @ xf
+    y = wrong(enc, rows, cols, _int_patterns(xi))
+    exact = np.array([sum(int(a) * int(b) for a, b in zip(wi[r], xi)) for r in range(rows)])
+    assert not np.array_equal(y, exact)
