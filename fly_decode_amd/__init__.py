@@ -92,6 +92,9 @@ def load_library():
         lib.cbk_encode_gpu.restype = ctypes.c_int
         lib.cbk_encode_gpu.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_encode_gpu_noalloc.restype = ctypes.c_int
+        lib.cbk_encode_gpu_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
         lib.cbk_gemm_group.restype = ctypes.c_int
         lib.cbk_gemm_group.argtypes = [tp, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p),
@@ -220,6 +223,16 @@ def encode_gpu_launch(w, workspace, codebook, words, meta, stream=None) -> None:
         ctypes.c_void_p(codebook.data_ptr()), ctypes.c_void_p(words.data_ptr()),
         words.numel() * words.element_size() // 4, ctypes.c_void_p(meta.data_ptr()), _stream(stream)),
         "cbk_encode_gpu")
+
+
+def encode_gpu_noalloc_launch(w, codebook, words, meta, stream=None) -> None:
+    """Enqueue cbk_encode_gpu_noalloc: as ``encode_gpu_launch`` with the library's static scratch
+    in place of a workspace (nothing is allocated; calls that overlap on one GPU race)."""
+    n = w.numel()
+    _check(load_library().cbk_encode_gpu_noalloc(
+        ctypes.c_void_p(w.data_ptr() if n else None), n, ctypes.c_void_p(codebook.data_ptr()),
+        ctypes.c_void_p(words.data_ptr()), words.numel() * words.element_size() // 4,
+        ctypes.c_void_p(meta.data_ptr()), _stream(stream)), "cbk_encode_gpu_noalloc")
 
 
 def encode_gpu(w, rows: int | None = None, cols: int | None = None, stream=None) -> Compressed:

@@ -231,6 +231,19 @@ cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16
     return cbk::launch_encode_gpu(w, n, workspace, codebook, words, meta, static_cast<hipStream_t>(stream));
 }
 
+cbk_status cbk_encode_gpu_noalloc(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_t *words,
+                                  uint64_t words_cap, uint32_t *meta, void *stream) {
+    if (!codebook || !meta || (n > 0 && (!w || !words))) return CBK_E_INVALID;
+    if (n >= (uint64_t(1) << 40)) return CBK_E_UNSUPPORTED;
+    if (!aligned(codebook, 2) || !aligned(meta, 4) || (n > 0 && (!aligned(w, 16) || !aligned(words, 16))))
+        return CBK_E_ALIGN;
+    if (words_cap < cbk_words_for(n, 16)) return CBK_E_CAPACITY;
+    void *ws = nullptr;
+    const cbk_status st = cbk::encode_gpu_scratch(&ws);
+    if (st != CBK_OK) return st;
+    return cbk::launch_encode_gpu(w, n, ws, codebook, words, meta, static_cast<hipStream_t>(stream));
+}
+
 cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream) {
     cbk_status st = check_tensor(t);
     if (st != CBK_OK) return st;

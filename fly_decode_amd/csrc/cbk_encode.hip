@@ -18,8 +18,16 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "cbk_internal.h"
+
+// The presence bitmaps of cbk_encode_gpu_noalloc: eight copies of a 65,536-bit map, 64 KB, the
+// same layout as the caller-owned workspace of cbk_encode_gpu.  Each GPU the library runs on holds
+// one copy of this array until the process ends; every no-allocation call on that GPU uses it.
+// Host code never passes the array's name to a kernel (on the host it only stands in for the
+// symbol): it uses the device address looked up once per device below.
+static __device__ __align__(256) uint32_t scratch[8 * 2048];
 
 namespace cbk {
 namespace {
@@ -307,9 +315,31 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__
     }
 }
 
+static_assert(sizeof(scratch) == kWsMapBytes, "the static scratch holds exactly one workspace");
+
+// Device address of `scratch` on each device, looked up with the device current on that device's
+// first no-allocation call.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint32_t *scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
 
 size_t encode_gpu_workspace_bytes() { return kWsMapBytes; }
+
+cbk_status encode_gpu_scratch(void **ws) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return CBK_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return CBK_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CBK_E_HIP;
+        scratch_ptr[dev] = static_cast<uint32_t *>(p);
+    }
+    *ws = scratch_ptr[dev];
+    return CBK_OK;
+}
 
 cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
                              uint32_t *words, uint32_t *meta, hipStream_t s) {

@@ -23,6 +23,9 @@ cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_
 size_t encode_gpu_workspace_bytes();
 cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
                              uint32_t *words, uint32_t *meta, hipStream_t s);
+// Device address of the library's static encoder scratch on the current device (a workspace of
+// encode_gpu_workspace_bytes() bytes); looked up on the device's first call.
+cbk_status encode_gpu_scratch(void **ws);
 
 // Exponent entropy-coded format (cbk_ec.hip).
 cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s);

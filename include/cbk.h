@@ -25,7 +25,8 @@
  *    in host memory), enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  *    return without waiting.  Buffers must stay alive until that work completes.
  *  - The caller owns every buffer.  The library allocates no memory and keeps no per-call state,
- *    so calls are safe from several host threads and streams at once.
+ *    so calls are safe from several host threads and streams at once.  The one exception is
+ *    cbk_encode_gpu_noalloc, which uses a static device array of the library (see there).
  *  - Outputs must not alias inputs.
  *  - An index >= U in a (corrupt) stream never causes an out-of-bounds access; the weight it
  *    names reads as 0x7FC0 (a quiet NaN).
@@ -129,6 +130,23 @@ cbk_status cbk_cap_patterns(const uint16_t *w, uint64_t n, uint32_t K, uint16_t 
 size_t cbk_encode_gpu_workspace_bytes(void);
 cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook, uint32_t *words,
                           uint64_t words_cap, uint32_t *meta, void *stream);
+
+/*
+ * cbk_encode_gpu_noalloc -- GPU.  For callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same encoding as
+ * cbk_encode_gpu (arguments, result, alignment and errors as there), without the workspace
+ * argument: the 65,536 bytes of presence bitmaps live in a static device array of the library,
+ * one per GPU, held until the process ends.  Nothing is allocated by this call.
+ *   Scratch limit: the array is a fixed 65,536 bytes, enough for every n the encoder accepts
+ *   (n < 2^40; larger n gives CBK_E_UNSUPPORTED before any HIP call).
+ *   Sharing: every call on one GPU uses that GPU's array, and each call clears it (with a kernel,
+ *   no memset) before use.  Calls that overlap on one GPU (from several streams or threads
+ *   without ordering between them) race on it and give undefined results; order them.
+ *   The first call on a device looks up the array's device address (hipGetSymbolAddress, not a
+ *   stream operation) with that device current; CBK_E_HIP if the lookup fails.
+ */
+cbk_status cbk_encode_gpu_noalloc(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_t *words,
+                                  uint64_t words_cap, uint32_t *meta, void *stream);
 
 /*
  * cbk_decode_bf16 -- GPU.  Standalone decode: out[i] = codebook[index i] for i < rows*cols,

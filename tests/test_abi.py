@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
               "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str", "cbk_encode_gpu",
               "cbk_encode_gpu_workspace_bytes", "cbk_ec_plan", "cbk_ec_encode", "cbk_ec_decode_bf16",
               "cbk_ec_spans", "cbk_ec_stream_words", "cbk_ec_gap_words", "cbk_ec_blocks",
-              "cbk_ec_stored_bytes", "cbk_cap_patterns", "cbk_ec_gemv"]:
+              "cbk_ec_stored_bytes", "cbk_cap_patterns", "cbk_ec_gemv", "cbk_encode_gpu_noalloc"]:
         assert n in names
 
 
@@ -193,3 +193,21 @@ def test_gpu_encoder_validates_before_any_hip_call(cbk):
     assert lib.cbk_encode_gpu(W, 1000, WS, CB, ctypes.c_void_p(0x40004), cap, M, None) == 3
     assert lib.cbk_encode_gpu(W, 1000, WS, CB, WD, cap - 1, M, None) == 2         # words_cap too small
     assert lib.cbk_encode_gpu(W, 1 << 40, WS, CB, WD, 1 << 62, M, None) == 4      # n beyond the limit
+
+
+def test_gpu_encoder_noalloc_validates_before_any_hip_call(cbk):
+    """cbk_encode_gpu_noalloc rejects bad arguments on the host, before it looks up its static
+    scratch or launches anything (no device is present here)."""
+    lib = cbk.load_library()
+    W, CB, WD, M = (ctypes.c_void_p(a) for a in (0x10000, 0x30000, 0x40000, 0x50000))
+    cap = cbk.words_for(1000, 16)
+    f = lib.cbk_encode_gpu_noalloc
+    assert f(None, 1000, CB, WD, cap, M, None) == 1                     # null w
+    assert f(W, 1000, None, WD, cap, M, None) == 1                      # null codebook
+    assert f(W, 1000, CB, None, cap, M, None) == 1                      # null words
+    assert f(W, 1000, CB, WD, cap, None, None) == 1                     # null meta
+    assert f(ctypes.c_void_p(0x10008), 1000, CB, WD, cap, M, None) == 3  # w not 16 B aligned
+    assert f(W, 1000, CB, ctypes.c_void_p(0x40004), cap, M, None) == 3   # words not 16 B aligned
+    assert f(W, 1000, ctypes.c_void_p(0x30001), WD, cap, M, None) == 3   # codebook not 2 B aligned
+    assert f(W, 1000, CB, WD, cap - 1, M, None) == 2                    # words_cap too small
+    assert f(W, 1 << 40, CB, WD, 1 << 62, M, None) == 4                 # n beyond the limit
