@@ -151,6 +151,11 @@ cbk_status cbk_encode_gpu_noalloc(const uint16_t *w, uint64_t n, uint16_t *codeb
 /*
  * cbk_decode_bf16 -- GPU.  Standalone decode: out[i] = codebook[index i] for i < rows*cols,
  * the exact original bit patterns (no float conversion anywhere).
+ * Passage: the codebook overview ("Codebook Lossless Compression", ai-manual.ru), section
+ * "Как работает эта магия?" (how it works): at inference every dictionary index is replaced by the
+ * original value it stands for, with nothing approximated; and the Codebook-Quantization digest
+ * (setupai.cc), section "關鍵要點" (key points): the indices of the unique weights are bit-packed.
+ * This call performs that substitution for a whole tensor and writes the BF16 weights to HBM.
  *   out   device, rows*cols uint16, 2-byte aligned.
  */
 cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream);
@@ -158,6 +163,10 @@ cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream);
 /*
  * cbk_gemv -- GPU.  Fused decode + GEMV at batch 1: y[r] = sum_k W[r][k] * x[k], products and
  * sums in fp32 (the summation order is unspecified; each BF16 x BF16 product is exact in fp32).
+ * Passage: the same two sections as cbk_decode_bf16 (the overview's "Как работает эта магия?":
+ * original values substituted back at inference; the digest's "關鍵要點": bit-packed indices of
+ * the unique weights).  Here the substituted weights feed the decode step's matrix-vector product
+ * directly, in registers, without being written to memory.
  *   x   device, cols BF16 patterns, 2-byte aligned (16-byte aligned for the fast kernels).
  *   y   device, rows fp32, 4-byte aligned.  Fully overwritten (zeros when cols == 0).
  */
@@ -182,6 +191,9 @@ cbk_status cbk_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *
 /*
  * cbk_gemm_small -- GPU.  Fused decode + skinny GEMM: Y[j][r] = sum_k W[r][k] * X[j][k] for
  * j < batch, fp32 products and sums.
+ * Passage: as cbk_gemv (the overview's "Как работает эта магия?" and the digest's "關鍵要點"),
+ * for a decode step that serves up to 16 sequences at once: each substituted weight meets every
+ * row of X.
  *   X     device, [batch][ldx] BF16, 2-byte aligned, ldx >= cols.  The fast kernels need X
  *         16-byte aligned and ldx % 8 == 0; other layouts take the generic kernel.
  *   batch 1..16.  Batches up to 8 run on the vector ALUs; 9..16 run on the matrix cores.
