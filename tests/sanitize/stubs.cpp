@@ -1,0 +1,36 @@
+// The GPU launchers, replaced for the host-only sanitizer build.  Argument validation must return
+// before any of them is reached in the cases the harness runs, so each one aborts if called.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "cbk_internal.h"
+
+namespace cbk {
+namespace {
+[[noreturn]] void reached(const char *what) {
+    fprintf(stderr, "launcher %s reached in the host-only build\n", what);
+    abort();
+}
+}  // namespace
+cbk_status launch_decode(const cbk_tensor &, uint16_t *, hipStream_t) { reached("decode"); }
+cbk_status launch_gemv(const cbk_tensor &, const uint16_t *, float *, hipStream_t) { reached("gemv"); }
+cbk_status launch_gemv_group(const cbk_tensor *, uint32_t, const uint16_t *, float *const *, hipStream_t) {
+    reached("gemv_group");
+}
+cbk_status launch_gemm(const cbk_tensor &, const uint16_t *, uint64_t, uint32_t, float *, uint64_t, hipStream_t) {
+    reached("gemm");
+}
+cbk_status launch_gemm_group(const cbk_tensor *, uint32_t, const uint16_t *, uint64_t, uint32_t, float *const *,
+                             const uint64_t *, hipStream_t) {
+    reached("gemm_group");
+}
+size_t encode_gpu_workspace_bytes() { return 65536; }
+cbk_status launch_encode_gpu(const uint16_t *, uint64_t, void *, uint16_t *, uint32_t *, uint32_t *, hipStream_t) {
+    reached("encode_gpu");
+}
+cbk_status encode_gpu_scratch(void **) { reached("encode_gpu_scratch"); }
+cbk_status launch_ec_decode(const cbk_ec_tensor *, uint16_t *, hipStream_t) { reached("ec_decode"); }
+cbk_status launch_ec_gemv(const cbk_ec_tensor *, uint64_t, uint64_t, const uint16_t *, float *, hipStream_t) {
+    reached("ec_gemv");
+}
+}  // namespace cbk
