@@ -5,38 +5,43 @@ One step = one pass of the fused decode + GEMV (or skinny GEMM) over every tenso
 with the compressed tensors already resident in HBM.  Workloads (seeded synthetic BF16 weights,
 each tensor with its own codebook):
 
-  attn4096   (default) Llama-7B-shaped 4096x4096 attention projections, N(0, 0.02); 24 distinct
-             tensors (654 MB compressed, well above the 256 MB Infinity Cache) so every step reads
-             HBM; one cbk_gemv launch per tensor.
-  llama7b    full 7B-shaped decode step: 32 layers x {q,k,v,o 4096x4096, gate/up 11008x4096,
-             down 4096x11008}, N(0, 0.02) (224 tensors, 10.5 GB).  Per layer four dependent phases:
-             [q,k,v] and [gate,up] each one cbk_gemv_group launch (they share their input), o and
-             down one cbk_gemv launch each.
-  mlp_b8     Llama-7B MLP at batch 8: gate/up 11008x4096 and down 4096x11008, 0.02 * Student-t(4);
-             --layers distinct copies (default 8, 1.76 GB); per layer [gate, up] one cbk_gemm_group
-             launch (they share X), down one cbk_gemm_small launch.
-  l70b_b16   70B-shaped layer at batch 16: q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192,
-             down 8192x28672, N(0, 0.015); --layers distinct layers (default 2, 2.8 GB); phases
-             grouped as in llama7b (cbk_gemm_group for [q, k, v] and [gate, up]).
-  l70b_b1    the same tensors at batch 1, phases grouped as in llama7b.
-  decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors, one launch
-             per tensor; bytes = compressed reads + 2 bytes written per weight.
-  ecdecode4096 the attn4096 tensors in the exponent entropy-coded format (sign-mantissa bytes
-             raw, exponent Huffman-coded), decoded to BF16 in HBM by cbk_ec_decode_bf16, one launch
-             per tensor; bytes = the stored format read + 2 bytes written per weight.
-  ecgemv4096 the same entropy-coded tensors, decode fused into the batch-1 GEMV (cbk_ec_gemv: a
-             y zero-fill and the fused kernel per tensor); bytes = the stored format + x + y.
-  encode4096 the load-time path: cbk_encode_gpu of the attn4096 tensors from raw BF16 already in
-             HBM (three launches per tensor); bytes = 2 bytes read per weight + the compressed
-             form written; the result of the last step is checked against the host encoder.
+  l70b_b1    (default) the 70B-shaped decode step at batch 1: 80 distinct layers of q/o 8192x8192,
+             k/v 1024x8192, gate/up 28672x8192 and down 8192x28672, N(0, 0.015) (560 tensors,
+             about 111 GB compressed, resident together).  Per layer four dependent phases:
+             [q, k, v] and [gate, up] each one cbk_gemv_group launch (they share their input),
+             o and down one cbk_gemv launch each.  --layers L times the first L layers instead.
+  l70b_b16   the same step at batch 16 (cbk_gemm_group / cbk_gemm_small on the matrix cores).
+  llama7b    the 7B-shaped decode step: 32 layers of q/k/v/o 4096x4096, gate/up 11008x4096 and
+             down 4096x11008, N(0, 0.02) (224 tensors, 10.5 GB), phases as in l70b_b1.
+  mlp_b1     the Llama-7B MLP at batch 1: gate/up 11008x4096 and down 4096x11008, 0.02 * t(4),
+             --layers distinct copies (default 8, 1.76 GB, well past the 256 MB Infinity Cache);
+             per layer [gate, up] one grouped launch, then down.
+  mlp_b8     the same tensors at batch 8 (VALU skinny GEMM).
+  attn4096   24 distinct 4096x4096 attention projections, N(0, 0.02), one cbk_gemv launch each.
+  decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors.
+  ecdecode4096 / ecgemv4096  the attn4096 tensors in the exponent entropy-coded format, decoded to
+             HBM (cbk_ec_decode_bf16) or decoded inside the batch-1 GEMV (cbk_ec_gemv).
+  encode4096 cbk_encode_gpu of the attn4096 tensors from raw BF16 in HBM (three launches each).
 
-The step is captured once in a HIP graph and replayed; the timed region is bracketed by
-torch.cuda.synchronize().  Untimed warm-up runs for --warmup steps and at least --warmup-seconds
-(0.3 s) of wall time, so that the timed steps see the GPU at its sustained clocks.  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
-feeds the multiply) / step time.  The dominant kernel's roofline uses its algorithmic bytes per
-launch (packed indices ceil(n*b/8) + codebook 2U + X 2*batch*K + Y 4*batch*M) over its average launch
-duration, measured with HIP events on the launch stream.  The CPU baseline times the oracle (decode
-+ GEMV in float64) on a bounded sample with host threads.
+The step workloads (l70b_*, llama7b) draw their weights on the GPU with the counter-based
+generator of ``synth.counter`` and compress them there with cbk_encode_gpu, one tensor at a time,
+so that 68 billion weights are ready in seconds; the other workloads draw on the host and upload.
+
+Timing: untimed warm-up for --warmup steps and at least --warmup-seconds of wall time (the GPU
+raises its clocks over the first tens of milliseconds of load), then --steps timed steps, each
+bracketed by its own pair of HIP events on the launch stream (one HIP graph replay per step);
+`ms_per_step` is their mean, `step_ms` their median, p10 and p90.  The timed region is bracketed by
+torch.cuda.synchronize().  `value` = sum over the step of 2*rows*cols (the BF16 bytes the decode
+feeds the multiply) / step time.  The roofline block uses the algorithmic bytes of the step's
+launches (packed indices ceil(n*b/8) + codebook 2U + X 2*batch*K per launch + Y 4*batch*M) over
+their time.  A device-to-device copy measured in the same run gives the copy bandwidth.
+
+The CPU baseline (the oracle, decode + GEMV in float64) runs on sampled rows of every tensor of
+the step, on the host threads the run may use and on one thread; its results for those rows are
+compared with the GPU's output of the last timed step (the run fails on a mismatch).
+
+Other modes: --summarize-trace and --summarize-traffic turn rocprofv3 output into the summaries
+kept under profiles/; --copy-calibration runs the copy the traffic figures are scaled by.
 
 Prints one JSON line.
 """
@@ -46,6 +51,7 @@ import argparse
 import concurrent.futures as cf
 import json
 import os
+import platform
 import sys
 import time
 
@@ -56,13 +62,40 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+TOL = 1e-3  # |y - y_ref| <= TOL * sum_k |W x| per element
+STEP_WORKLOADS = ("l70b_b1", "l70b_b16", "llama7b")
+ALL_WORKLOADS = ["l70b_b1", "l70b_b16", "llama7b", "mlp_b1", "mlp_b8", "attn4096", "decode4096",
+                 "encode4096", "ecdecode4096", "ecgemv4096"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def workload_tensors(name: str, count: int, layers: int):
+def host_threads() -> int:
+    """Host threads this run may use: the CPUs it is allowed to run on, at most 16 (one GPU's
+    share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ------------------------------------------------------------------------------------ workloads
+
+def workload_specs(name: str, count: int, layers: int):
     """(specs, phases, batch, layer_count): specs are (cfg, layer, tensor) triples; phases are lists
     of spec indices launched together (one launch per phase, phases run in order)."""
     import synth
@@ -70,93 +103,350 @@ def workload_tensors(name: str, count: int, layers: int):
         t = synth.WORKLOADS[2][0][0]
         specs = [(2, layer, t) for layer in range(count)]
         return specs, [[i] for i in range(len(specs))], (1 if name in ("attn4096", "ecgemv4096") else 0), len(specs)
-    if name in ("llama7b", "l70b_b1", "l70b_b16"):
+    if name in STEP_WORKLOADS:
         cfg = 4 if name == "llama7b" else 5
         tensors, n_layers = synth.WORKLOADS[cfg]
-        n_layers = n_layers if name == "llama7b" else layers
+        n_layers = min(n_layers, layers) if layers else n_layers
         specs, phases = [], []
+        names = [t.name for t in tensors]
         for layer in range(n_layers):
             base = len(specs)
             specs += [(cfg, layer, t) for t in tensors]
-            names = [t.name for t in tensors]
             for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
                 phases.append([base + names.index(g) for g in group])
         return specs, phases, (16 if name == "l70b_b16" else 1), n_layers
-    if name == "mlp_b8":
+    if name in ("mlp_b1", "mlp_b8"):
         tensors, _ = synth.WORKLOADS[3]
+        layers = layers or 8
         specs = [(3, layer, t) for layer in range(layers) for t in tensors]
-        # per layer: [gate, up] share X (one grouped launch), then down
-        return specs, [p for l in range(layers) for p in ([3 * l, 3 * l + 1], [3 * l + 2])], 8, layers
+        # per layer: [gate, up] share their input (one grouped launch), then down
+        phases = [p for l in range(layers) for p in ([3 * l, 3 * l + 1], [3 * l + 2])]
+        return specs, phases, (8 if name == "mlp_b8" else 1), layers
     raise SystemExit(f"unknown workload {name}")
 
 
-def prepare(specs, threads, raw=False, cap=None):
-    """Generate and encode every tensor on the host (threads), upload to the GPU.  With raw=True
-    the uploaded form is the BF16 patterns themselves (int16, flat) and the host encodings stay on
-    the host, as (raw tensors, host encodings)."""
+def prepare(specs, threads, cap=None, on_device=None):
+    """Generate and compress every tensor, leaving the compressed forms on the GPU.  Tensors of
+    the counter-based generator are drawn on the GPU and compressed by cbk_encode_gpu (no host
+    copy); the others are drawn and compressed on the host (threads) and uploaded."""
     import torch
     import synth
     import fly_decode_amd as cbk
 
+    if on_device is None:
+        on_device = cap is None and all(t.dist == "normal_ctr" for _, _, t in specs)
+    out = []
+    if on_device:
+        nmax = max(t.rows * t.cols for _, _, t in specs)
+        raw = torch.empty(nmax, dtype=torch.int16, device="cuda")
+        ws = torch.empty(cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
+        cb = torch.empty(65536, dtype=torch.int16, device="cuda")
+        words = torch.empty(cbk.words_for(nmax, 16), dtype=torch.int32, device="cuda")
+        meta = torch.zeros(2, dtype=torch.int32, device="cuda")
+        for i, (cfg, layer, t) in enumerate(specs):
+            n = t.rows * t.cols
+            w = synth.workload_tensor_device(cfg, layer, t, "cuda", out=raw[:n])
+            cbk.encode_gpu_launch(w, ws, cb, words, meta)
+            U, b = (int(v) for v in meta.cpu().tolist())
+            out.append(cbk.Compressed(t.rows, t.cols, U, b, cb[:U].clone(),
+                                      words[:cbk.words_for(n, b)].clone()))
+            if (i + 1) % 56 == 0 or i + 1 == len(specs):
+                log(f"generated + encoded on the GPU {i + 1}/{len(specs)} tensors")
+        del raw, ws, cb, words, meta
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return out
+
     def make(spec):
         cfg, layer, t = spec
-        w = synth.workload_tensor(cfg, layer, t)
-        return w, cbk.encode(w, cap=cap)
+        return cbk.encode(synth.workload_tensor(cfg, layer, t), cap=cap)
 
-    out, hosts = [], []
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        for i, (w, c) in enumerate(ex.map(make, specs)):
-            if raw:
-                out.append(torch.from_numpy(w.reshape(-1).view(np.int16)).to("cuda"))
-                hosts.append(c)
-            else:
-                out.append(c.to("cuda"))
+        for i, c in enumerate(ex.map(make, specs)):
+            out.append(c.to("cuda"))
             if (i + 1) % 16 == 0 or i + 1 == len(specs):
-                log(f"encoded + uploaded {i + 1}/{len(specs)} tensors")
-    return (out, hosts) if raw else out
+                log(f"encoded on the host + uploaded {i + 1}/{len(specs)} tensors")
+    return out
 
 
-def cpu_baseline(specs, seconds: float, threads: int):
-    """The oracle (decode + GEMV, float64) on whole tensors of the workload, rows split over host
-    threads, until about `seconds` of wall time have been spent."""
+class Workload:
+    """A workload's tensors, inputs and outputs on the GPU, and its step (one pass of every phase's
+    launch, in order), built exactly as the benchmark times it."""
+
+    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None):
+        import torch
+        import synth
+        import fly_decode_amd as cbk
+
+        self.name = name
+        self.specs, self.phases, self.batch, self.n_layers = workload_specs(name, count, layers)
+        self.encode = name == "encode4096"
+        self.ecfmt = name in ("ecdecode4096", "ecgemv4096")
+        self.ecgemv = name == "ecgemv4096"
+        threads = threads or host_threads()
+        t0 = time.perf_counter()
+        if tensors is not None:
+            self.tensors = tensors
+        elif self.ecfmt:
+            def make_ec(spec):
+                cfg, layer, t = spec
+                return cbk.ec_encode(synth.workload_tensor(cfg, layer, t))
+            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+                self.tensors = [e.to("cuda") for e in ex.map(make_ec, self.specs)]
+        elif self.encode:
+            def make_raw(spec):
+                cfg, layer, t = spec
+                w = synth.workload_tensor(cfg, layer, t)
+                return w, cbk.encode(w)
+            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+                pairs = list(ex.map(make_raw, self.specs))
+            self.raws = [torch.from_numpy(w.reshape(-1).view(np.int16)).to("cuda") for w, _ in pairs]
+            # the host encodings: sizes for the byte count, and the check after timing
+            self.tensors = [c for _, c in pairs]
+            self.ws = torch.empty(cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
+            self.enc_cb = [torch.empty(65536, dtype=torch.int16, device="cuda") for _ in self.raws]
+            self.enc_words = [torch.empty(cbk.words_for(r.numel(), 16), dtype=torch.int32, device="cuda")
+                              for r in self.raws]
+            self.enc_meta = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in self.raws]
+        else:
+            self.tensors = prepare(self.specs, threads, cap=cap)
+        self.setup_s = time.perf_counter() - t0
+
+        self.xs = {}
+        if self.batch > 0:
+            for d in self.tensors:
+                if d.cols not in self.xs:
+                    x = synth.workload_x(self.specs[0][0], d.cols, self.batch)
+                    self.xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+        if self.encode:
+            self.ys = []
+        elif self.batch == 0:
+            self.ys = [torch.empty((d.rows, d.cols), dtype=torch.bfloat16, device="cuda") for d in self.tensors]
+        elif self.batch == 1:
+            self.xs = {k: v[0] for k, v in self.xs.items()}
+            self.ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in self.tensors]
+        else:
+            self.ys = [torch.empty((self.batch, d.rows), dtype=torch.float32, device="cuda") for d in self.tensors]
+
+    def step(self):
+        import fly_decode_amd as cbk
+        T, xs, ys = self.tensors, self.xs, self.ys
+        for ph in self.phases:
+            if self.encode:
+                i = ph[0]
+                cbk.encode_gpu_launch(self.raws[i], self.ws, self.enc_cb[i], self.enc_words[i], self.enc_meta[i])
+            elif self.ecgemv:
+                cbk.ec_gemv(T[ph[0]], xs[T[ph[0]].cols], y=ys[ph[0]])
+            elif self.ecfmt:
+                cbk.ec_decode_bf16(T[ph[0]], out=ys[ph[0]])
+            elif self.batch == 0:
+                cbk.decode_bf16(T[ph[0]], out=ys[ph[0]])
+            elif self.batch > 1 and len(ph) == 1:
+                cbk.gemm_small(T[ph[0]], xs[T[ph[0]].cols], Y=ys[ph[0]])
+            elif self.batch > 1:
+                cbk.gemm_group([T[i] for i in ph], xs[T[ph[0]].cols], Ys=[ys[i] for i in ph])
+            elif len(ph) == 1:
+                cbk.gemv(T[ph[0]], xs[T[ph[0]].cols], y=ys[ph[0]])
+            else:
+                cbk.gemv_group([T[i] for i in ph], xs[T[ph[0]].cols], ys=[ys[i] for i in ph])
+
+    def phase_pattern(self):
+        """The launches of one layer (the step repeats them), with their algorithmic bytes: a list
+        of [tensor names, bytes] (None for workloads of independent single-tensor launches)."""
+        if self.name not in STEP_WORKLOADS and not self.name.startswith("mlp_"):
+            return None
+        per = 4 if self.name in STEP_WORKLOADS else 2
+        b, T = max(1, self.batch), self.tensors
+        out = []
+        for ph in self.phases[:per]:
+            nbytes = sum(T[i].compressed_bytes + 4 * b * T[i].rows for i in ph) + 2 * b * T[ph[0]].cols
+            out.append(["+".join(self.specs[i][2].name for i in ph), int(nbytes)])
+        return out
+
+    def capture(self):
+        """The step captured once in a HIP graph (after one eager step)."""
+        import torch
+        self.step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        torch.cuda.synchronize()
+        return graph
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the method must move per step (the roofline's numerator)."""
+        T, b = self.tensors, self.batch
+        if self.ecgemv:  # the stored entropy-coded form + x read, y written
+            return sum(d.stored_bytes + 2 * d.cols + 4 * d.rows for d in T)
+        if self.ecfmt:  # the stored entropy-coded form read + the BF16 written
+            return sum(d.stored_bytes + 2 * d.n for d in T)
+        if b == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
+            return sum(d.compressed_bytes + 2 * d.n for d in T)
+        # packed indices + codebook + Y for every tensor, X once per launch
+        return sum(d.compressed_bytes + 4 * b * d.rows for d in T) + \
+            sum(2 * b * T[ph[0]].cols for ph in self.phases)
+
+    def kernel_name(self):
+        bits = sorted({d.b for d in self.tensors}) if not self.ecfmt else None
+        if self.encode:
+            return "k_enc", "cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
+        if self.ecfmt:
+            k = "k_ec_gemv" if self.ecgemv else "k_ec_decode"
+            return k, k
+        if self.batch == 0:
+            k = "k_decode_fast"
+        elif self.batch == 1:
+            k = "k_gemv_rows"
+        else:
+            k = "k_gemm_valu" if self.batch <= 8 else "k_gemm_mfma"
+        grouped = any(len(ph) > 1 for ph in self.phases)
+        desc = f"{k}<{bits[-1]}>" + (f" and {k}_group<{bits[-1]}>, every launch of the step" if grouped else "")
+        return f"{k}_b{bits[-1]}", desc
+
+
+# ------------------------------------------------------------------------------------- timing
+
+def time_steps(run_step, steps, stream):
+    """Per-step times (ms) from one pair of HIP events per step on the launch stream, plus the
+    whole timed region's event time and wall time."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        run_step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return per, evs[0].elapsed_time(evs[-1]), wall
+
+
+def copy_bandwidth(nbytes: int, reps: int = 10):
+    """Device-to-device copy of nbytes (read + write counted), median over reps, in GB/s."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / float(np.median(times)) / 1e9
+
+
+def pct(vals, q):
+    return float(np.percentile(np.asarray(vals, dtype=np.float64), q))
+
+
+# ------------------------------------------------------------------------------- CPU baseline
+
+def sample_rows(rows: int, per: int, seed) -> np.ndarray:
+    """The first and last row and per - 2 seeded others."""
+    rng = np.random.default_rng(seed)
+    k = max(0, min(rows, per) - 2)
+    mid = rng.choice(np.arange(1, rows - 1), size=k, replace=False) if rows > 2 and k else np.array([], np.int64)
+    return np.unique(np.concatenate([[0, rows - 1], mid]).astype(np.int64))
+
+
+def cpu_baseline(work: Workload, rows_per_tensor: int, seconds: float, threads: int):
+    """The oracle (decode + GEMV/GEMM in float64) on sampled rows of every tensor of the workload:
+    timed on `threads` host threads and on one, then its results compared with the GPU's output
+    of the last timed step.  Returns (cpu_baseline record, check record)."""
     import oracle
     import synth
 
     oracle.build(force=False)
-    done_w, t_total, used = 0, 0.0, 0
-    cfg, layer, t = specs[0]
-    w = synth.workload_tensor(cfg, layer, t)
-    e = oracle.encode(w)
-    x = synth.workload_x(cfg, t.cols)[0]
-    y = np.zeros(t.rows, dtype=np.float64)
-    ab = np.zeros(t.rows, dtype=np.float64)
-    chunk = max(1, t.rows // (threads * 4))
-    spans = [(r, min(t.rows, r + chunk)) for r in range(0, t.rows, chunk)]
-    while t_total < seconds and used < 4096:
-        t0 = time.perf_counter()
-        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-            list(ex.map(lambda s: oracle.gemv_rows_into(e, x, s[0], s[1], y, ab), spans))
-        t_total += time.perf_counter() - t0
-        done_w += t.rows * t.cols
-        used += 1
-    return {
-        "value": round(2.0 * done_w / t_total / 1e9, 4),
+    X = {}
+    for d in work.tensors:
+        if d.cols not in X:
+            X[d.cols] = synth.workload_x(work.specs[0][0], d.cols, max(1, work.batch))
+    # inputs: the sampled rows of every tensor, drawn on the host and encoded by the oracle (not timed)
+    t_prep = time.perf_counter()
+    jobs = []
+
+    def prep(i):
+        cfg, layer, t = work.specs[i]
+        rows = sample_rows(t.rows, rows_per_tensor, [cfg, layer, t.tensor_id, 77])
+        return i, rows, oracle.encode(synth.workload_rows(cfg, layer, t, rows))
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        jobs = list(ex.map(prep, range(len(work.specs))))
+    prep_s = time.perf_counter() - t_prep
+
+    def run(job):
+        i, rows, e = job
+        Xi = X[work.tensors[i].cols]
+        return oracle.gemm(e, Xi) if work.batch > 1 else oracle.gemv(e, Xi[0])
+
+    def timed(nthreads, budget):
+        weights, spent, passes, results = 0, 0.0, 0, None
+        while spent < budget and passes < 1000:
+            t0 = time.perf_counter()
+            if nthreads == 1:
+                res = [run(j) for j in jobs]
+            else:
+                with cf.ThreadPoolExecutor(max_workers=nthreads) as ex:
+                    res = list(ex.map(run, jobs))
+            spent += time.perf_counter() - t0
+            results = results or res
+            weights += sum(len(rows) * work.tensors[i].cols for i, rows, _ in jobs)
+            passes += 1
+        return 2.0 * weights / spent / 1e9, passes, spent, results
+
+    v_all, p_all, s_all, results = timed(threads, seconds)
+    v_one, p_one, s_one, _ = timed(1, seconds / 2)
+
+    # the check: the GPU's last timed step against the oracle on the sampled rows
+    worst, checked = 0.0, 0
+    for (i, rows, _), (ref, absb) in zip(jobs, results):
+        y = work.ys[i].float().cpu().numpy().astype(np.float64)
+        got = y[rows] if work.batch == 1 else y[:, rows]
+        err = np.abs(got - ref)
+        ratio = float(np.max(err / np.maximum(TOL * absb, 1e-300))) if err.size else 0.0
+        worst = max(worst, ratio)
+        checked += got.size
+        if not np.all(err <= TOL * absb):
+            raise SystemExit(f"output of tensor {i} ({work.specs[i][2].name}, layer {work.specs[i][1]}) "
+                             f"differs from the oracle beyond 1e-3 * sum|W x| (worst ratio {ratio:.3g})")
+    n_rows = sum(len(rows) for _, rows, _ in jobs)
+    record = {
+        "value": round(v_all, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{used} full passes of decode+GEMV (float64) over one {t.rows}x{t.cols} tensor "
-                  f"of the workload, rows split over {threads} host threads, {t_total:.1f} s",
+        "one_thread_value": round(v_one, 4),
+        "host_cpus": os.cpu_count(),
+        "host_cpus_allowed": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+        "cpu_model": cpu_model(),
+        "sample": (f"decode + {'GEMM' if work.batch > 1 else 'GEMV'} (float64) of {n_rows} sampled rows "
+                   f"({rows_per_tensor} per tensor, first and last included) of all {len(jobs)} tensors "
+                   f"of the step; {p_all} passes in {s_all:.1f} s on {threads} threads, {p_one} passes "
+                   f"in {s_one:.1f} s on one thread; drawing and encoding the rows ({prep_s:.1f} s) not "
+                   f"timed"),
     }
+    check = {"rows": n_rows, "outputs": checked, "tensors": len(jobs),
+             "worst_err_over_bound": round(worst, 6), "tolerance": "1e-3 * sum_k |W x|"}
+    return record, check
 
 
-def cpu_baseline_encode(specs, seconds: float):
-    """The oracle's encoder (plain C, one host thread) on whole tensors of the workload, until about
-    `seconds` of wall time have been spent."""
+def cpu_baseline_encode(work: Workload, seconds: float):
+    """The oracle's encoder (plain C, one host thread) on whole tensors of the workload."""
     import oracle
     import synth
 
     oracle.build(force=False)
-    cfg, layer, t = specs[0]
+    cfg, layer, t = work.specs[0]
     w = synth.workload_tensor(cfg, layer, t)
     t_total, used = 0.0, 0
     while t_total < seconds and used < 4096:
@@ -169,56 +459,82 @@ def cpu_baseline_encode(specs, seconds: float):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{used} full encodes of one {t.rows}x{t.cols} tensor of the workload with the "
                   f"oracle's encoder (one host thread), {t_total:.1f} s",
     }
 
 
-def cpu_baseline_ec(specs, seconds: float, gemv: bool = False):
+def cpu_baseline_ec(work: Workload, seconds: float):
     """The oracle's bit-by-bit decoder of the entropy-coded format (pure Python, one thread) on
     leading rows of one tensor of the workload, growing the sample until about `seconds` pass.
-    With `gemv`, the oracle's GEMV of those rows (decode, then float64 products) is timed."""
+    With the fused GEMV, the oracle's GEMV of those rows (decode, then float64 products)."""
     from oracle import entropy as ec
     import synth
 
-    cfg, layer, t = specs[0]
+    cfg, layer, t = work.specs[0]
     w = synth.workload_tensor(cfg, layer, t)
     x = synth.workload_x(cfg, t.cols)[0]
     rows, spent, done = 4, 0.0, 0
     while spent < seconds and rows <= t.rows:
         enc = ec.encode(w[:rows])
         t0 = time.perf_counter()
-        if gemv:
+        if work.ecgemv:
             ec.gemv(enc, rows, t.cols, x)
         else:
             ec.decode(enc)
         spent += time.perf_counter() - t0
         done += rows * t.cols
         rows *= 2
-    what = "decoder and float64 GEMV" if gemv else "decoder"
+    what = "decoder and float64 GEMV" if work.ecgemv else "decoder"
     return {
         "value": round(2.0 * done / spent / 1e9, 6),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"the oracle's bit-by-bit {what} (pure Python, one thread) on the leading 4, 8, ... "
                   f"rows of one {t.rows}x{t.cols} tensor of the workload, {done} weights, {spent:.1f} s",
     }
 
 
-def check_encoded(raws, hosts, codebooks, words, metas, which):
+def check_encoded(work: Workload, which):
     """The device encodings of tensors `which` against the host encoder (exact)."""
     import fly_decode_amd as cbk
     for i in which:
-        h = hosts[i]
-        U, b = (int(v) for v in metas[i].cpu().tolist())
-        nw = cbk.words_for(raws[i].numel(), b)
+        h = work.tensors[i]
+        U, b = (int(v) for v in work.enc_meta[i].cpu().tolist())
+        nw = cbk.words_for(work.raws[i].numel(), b)
         ok = (U, b) == (h.U, h.b) and \
-            np.array_equal(codebooks[i][:U].cpu().numpy().view(np.uint16), h.codebook) and \
-            np.array_equal(words[i][:nw].cpu().numpy().view(np.uint32), h.words)
+            np.array_equal(work.enc_cb[i][:U].cpu().numpy().view(np.uint16), h.codebook) and \
+            np.array_equal(work.enc_words[i][:nw].cpu().numpy().view(np.uint32), h.words)
         if not ok:
             raise SystemExit(f"GPU encoding of tensor {i} differs from the host encoder")
 
+
+# ------------------------------------------------------------------------- profile summaries
+
+def summarize_trace_main(args):
+    """--summarize-trace DIR: the kernel-trace CSV of a rocprofv3 run of this benchmark, reduced to
+    the dispatches of its timed steps (the last steps x launches_per_step dispatches of the
+    library's kernels), against the JSON line the same run printed."""
+    from fly_decode_amd import profiling
+    line = json.loads(open(args.line).read().strip().splitlines()[-1])
+    profiling.summarize_timed_trace(args.summarize_trace, line, args.out, args.title or line["config"]["workload"],
+                                    args.command)
+    print(open(args.out).read())
+
+
+def summarize_traffic_main(args):
+    from fly_decode_amd import profiling
+    fetch, write, cfetch, cwrite = args.summarize_traffic
+    rec = profiling.summarize_traffic(args.out, args.kernel, fetch, write, cfetch, cwrite, args.copy_bytes,
+                                      args.algorithmic_bytes, args.command,
+                                      dispatches_per_unit=args.dispatches_per_unit)
+    print(json.dumps(rec, indent=1))
+
+
+# ------------------------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -228,20 +544,39 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="after the warm-up steps, keep replaying untimed steps until this much wall "
                          "time has passed (the GPU's clocks rise over the first tens of ms of load)")
-    ap.add_argument("--workload", default="attn4096", choices=["attn4096", "llama7b", "mlp_b8", "l70b_b16", "l70b_b1", "decode4096",
-                                                           "encode4096", "ecdecode4096", "ecgemv4096"])
-    ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for attn4096")
-    ap.add_argument("--layers", type=int, default=0, help="distinct layers for mlp_b8 (8) and l70b_* (2)")
+    ap.add_argument("--workload", default="l70b_b1", choices=ALL_WORKLOADS)
+    ap.add_argument("--tensors", type=int, default=24, help="distinct tensors for the 4096x4096 workloads")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers: the first L of the step workloads (default all), distinct copies for mlp_* (8)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8, help="sampled rows per tensor for the CPU baseline and check")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU baseline (and with it the check)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--cap", type=int, default=0, metavar="K",
                     help="lossy: cap every codebook at K entries (cbk_cap_patterns) before encoding")
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30, help="size of the in-run copy-bandwidth measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (counter calibration for the "
                          "traffic figure) and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="write a timed-steps kernel summary and exit")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write a traffic record from four --pmc runs and exit")
+    ap.add_argument("--line", help="the JSON line the profiled run printed (for --summarize-trace)")
+    ap.add_argument("--out", help="output file of a summary")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="", help="the command the summarized run executed")
+    ap.add_argument("--kernel", default="", help="kernel name prefix (for --summarize-traffic)")
+    ap.add_argument("--copy-bytes-calibrated", dest="copy_bytes_cal", type=int, default=0)
+    ap.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    ap.add_argument("--dispatches-per-unit", type=int, default=1)
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        return summarize_trace_main(args)
+    if args.summarize_traffic:
+        args.copy_bytes = args.copy_bytes_cal
+        return summarize_traffic_main(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (the GEMV would "
@@ -263,160 +598,74 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 3}), flush=True)
         return
     cbk.load_library()
-    threads = min(16, os.cpu_count() or 1)
-    layers_arg = args.layers or (8 if args.workload == "mlp_b8" else 2)
-    specs, phases, batch, n_layers = workload_tensors(args.workload, args.tensors, layers_arg)
+    threads = host_threads()
+    log(f"workload {args.workload}; host threads {threads} of {os.cpu_count()} CPUs")
+    work = Workload(args.workload, count=args.tensors, layers=args.layers, threads=threads, cap=args.cap or None)
     if args.no_group:
-        phases = [[i] for ph in phases for i in ph]
-    log(f"workload {args.workload}: {len(specs)} tensors, host threads {threads}")
-    encode = args.workload == "encode4096"
-    ecfmt = args.workload in ("ecdecode4096", "ecgemv4096")
-    ecgemv = args.workload == "ecgemv4096"
-    t0 = time.perf_counter()
-    if ecfmt:
-        def make_ec(spec):
-            cfg, layer, t = spec
-            return cbk.ec_encode(synth.workload_tensor(cfg, layer, t))
-        import synth
-        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-            tensors = [e.to("cuda") for e in ex.map(make_ec, specs)]
-        log(f"entropy-coded {len(tensors)} tensors")
-    elif encode:
-        raws, hosts = prepare(specs, threads, raw=True)
-        tensors = hosts
-        ws = torch.empty(cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
-        enc_cb = [torch.empty(65536, dtype=torch.int16, device="cuda") for _ in raws]
-        enc_words = [torch.empty(cbk.words_for(r.numel(), 16), dtype=torch.int32, device="cuda") for r in raws]
-        enc_meta = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in raws]
-    else:
-        tensors = prepare(specs, threads, cap=args.cap or None)
-    log(f"setup {time.perf_counter() - t0:.1f} s")
-
-    import synth
-    xs = {}
-    for d in tensors:
-        if d.cols not in xs and batch > 0:
-            x = synth.workload_x(specs[0][0], d.cols, batch)
-            xs[d.cols] = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
-    if encode:
-        ys = []
-    elif batch == 0:  # decode outputs (both formats)
-        ys = [torch.empty((d.rows, d.cols), dtype=torch.bfloat16, device="cuda") for d in tensors]
-    elif batch == 1:
-        xs = {k: v[0] for k, v in xs.items()}
-        ys = [torch.empty(d.rows, dtype=torch.float32, device="cuda") for d in tensors]
-    else:
-        ys = [torch.empty((batch, d.rows), dtype=torch.float32, device="cuda") for d in tensors]
-
-    def step():
-        for ph in phases:
-            if encode:
-                i = ph[0]
-                cbk.encode_gpu_launch(raws[i], ws, enc_cb[i], enc_words[i], enc_meta[i])
-            elif ecgemv:
-                cbk.ec_gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
-            elif ecfmt:
-                cbk.ec_decode_bf16(tensors[ph[0]], out=ys[ph[0]])
-            elif batch == 0:
-                cbk.decode_bf16(tensors[ph[0]], out=ys[ph[0]])
-            elif batch > 1 and len(ph) == 1:
-                cbk.gemm_small(tensors[ph[0]], xs[tensors[ph[0]].cols], Y=ys[ph[0]])
-            elif batch > 1:
-                cbk.gemm_group([tensors[i] for i in ph], xs[tensors[ph[0]].cols], Ys=[ys[i] for i in ph])
-            elif len(ph) == 1:
-                cbk.gemv(tensors[ph[0]], xs[tensors[ph[0]].cols], y=ys[ph[0]])
-            else:
-                cbk.gemv_group([tensors[i] for i in ph], xs[tensors[ph[0]].cols], ys=[ys[i] for i in ph])
+        work.phases = [[i] for ph in work.phases for i in ph]
+    log(f"setup {work.setup_s:.1f} s: {len(work.tensors)} tensors, {len(work.phases)} launches per step, "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated on the GPU")
 
     warm0 = time.perf_counter()
     for _ in range(args.warmup):
-        step()
+        work.step()
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
+    graph = None if args.no_graph else work.capture()
+    run_step = graph.replay if graph is not None else work.step
+    if graph is not None:
         for _ in range(2):
             graph.replay()
         torch.cuda.synchronize()
-    # Sustained rate: the GPU raises its clocks over the first tens of milliseconds of load (the
-    # 70B-shaped layer runs at about 60 % of peak after 5 steps, 67 % after 50, 73 % after 200), so
-    # untimed steps continue until --warmup-seconds of wall time have passed since the first one.
     extra = 0
     while time.perf_counter() - warm0 < args.warmup_seconds:
         for _ in range(4):
-            if graph is not None:
-                graph.replay()
-            else:
-                step()
+            run_step()
             extra += 1
         torch.cuda.synchronize()
     if extra:
         log(f"warm-up: {args.warmup} steps + {extra} more to reach {args.warmup_seconds:.2f} s")
 
-    # ---- timed region: K steps
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (event), wall {wall:.3f} s")
-    if encode:
-        check_encoded(raws, hosts, enc_cb, enc_words, enc_meta, sorted({0, len(raws) - 1}))
+    # ---- timed region: K steps, one event pair each
+    per_step, region_ms, wall = time_steps(run_step, args.steps, stream)
+    ms_step = region_ms / args.steps
+    log(f"timed {args.steps} steps: mean {ms_step:.4f} ms/step, median {pct(per_step, 50):.4f} "
+        f"(p10 {pct(per_step, 10):.4f}, p90 {pct(per_step, 90):.4f}), wall {wall:.3f} s")
+    if work.encode:
+        check_encoded(work, sorted({0, len(work.raws) - 1}))
         log("device encodings of the first and last tensor equal the host encoder's")
 
-    # The step is one graph of back-to-back GEMV launches on `stream`, so the event-timed step
-    # divided by its launch count is the kernels' average launch duration (inter-kernel gaps
-    # included, which makes it a slight overestimate; rocprofv3 kernel traces agree to ~2 %).
-    # The encoder is three launches per tensor (clear, presence, pack); its figure below is
-    # for the whole encode of one tensor, with the per-kernel split in the rocprofv3 summary.
-    launches = len(phases)
-    avg_launch_s = ms_step * 1e-3 / launches
+    copy_gbps = copy_bandwidth(args.copy_bytes)
+    log(f"device-to-device copy of {args.copy_bytes} B: {copy_gbps:.1f} GB/s (read + write)")
 
-    n_total = sum(d.n for d in tensors)
-    if ecgemv:  # the stored entropy-coded form + x read, y written
-        comp_total = sum(d.stored_bytes + 2 * d.cols + 4 * d.rows for d in tensors)
-    elif ecfmt:  # the stored entropy-coded form read + the BF16 written
-        comp_total = sum(d.stored_bytes + 2 * d.n for d in tensors)
-    elif batch == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
-        comp_total = sum(d.compressed_bytes + 2 * d.n for d in tensors)
-    else:  # packed indices + codebook + Y for every tensor, X once per launch
-        comp_total = sum(d.compressed_bytes + 4 * batch * d.rows for d in tensors) + \
-            sum(2 * batch * tensors[ph[0]].cols for ph in phases)
+    launches = len(work.phases)
     step_s = ms_step * 1e-3
+    n_total = sum(d.n for d in work.tensors)
+    comp_total = work.algorithmic_bytes()
     value = 2.0 * n_total / step_s / 1e9
     comp_gbps = comp_total / step_s / 1e9
+    # The step is one graph of back-to-back launches on `stream`, so the step time divided by the
+    # launch count is the launches' average duration (inter-launch gaps included, which makes it a
+    # slight overestimate; the rocprofv3 summary of the timed steps gives the kernels' own time).
+    avg_launch_s = step_s / launches
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
-    bits = sorted({d.b for d in tensors}) if not ecfmt else [max(max(d.lengths) for d in tensors)]
-    kernel = ("k_enc" if encode else "k_ec_gemv" if ecgemv else "k_ec_decode" if ecfmt else "k_decode_fast" if batch == 0 else "k_gemv_rows" if batch == 1
-              else "k_gemm_valu" if batch <= 8 else "k_gemm_mfma")
-    kernel_key = kernel if ecfmt else f"{kernel}_b{bits[-1]}"
+    kernel_key, kernel_desc = work.kernel_name()
     traffic = profiling.traffic_for(kernel_key, args.workload)
+    bits = sorted({d.b for d in work.tensors}) if not work.ecfmt else [max(max(d.lengths) for d in work.tensors)]
 
+    metric = ("GPU codebook encode of BF16 weights resident in HBM, raw-weight GB/s; % of HBM peak"
+              if work.encode else
+              "exponent entropy-coded fused GEMV decompressed-weight GB/s at batch 1; % of HBM peak"
+              if work.ecgemv else
+              "exponent entropy-coded BF16 decode to HBM, decompressed-weight GB/s; % of HBM peak"
+              if work.ecfmt else
+              "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if work.batch == 1
+              else "standalone codebook decode to BF16 in HBM, decompressed-weight GB/s; % of HBM peak"
+              if work.batch == 0 else
+              f"fused codebook skinny-GEMM decompressed-weight GB/s at batch {work.batch}; % of HBM peak")
     result = {
-        "metric": ("GPU codebook encode of BF16 weights resident in HBM, raw-weight GB/s; % of HBM peak"
-                   if encode else
-                   "exponent entropy-coded fused GEMV decompressed-weight GB/s at batch 1; % of HBM peak"
-                   if ecgemv else
-                   "exponent entropy-coded BF16 decode to HBM, decompressed-weight GB/s; % of HBM peak"
-                   if ecfmt else
-                   "fused codebook-GEMV decompressed-weight GB/s at batch 1; % of HBM peak" if batch == 1
-                   else "standalone codebook decode to BF16 in HBM, decompressed-weight GB/s; % of HBM peak"
-                   if batch == 0 else
-                   f"fused codebook skinny-GEMM decompressed-weight GB/s at batch {batch}; % of HBM peak"),
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -430,26 +679,33 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "tensors": len(tensors),
-            "shapes": sorted({f"{d.rows}x{d.cols}" for d in tensors}),
-            "batch": batch,
-            "layers": n_layers,
-            ("max_code_bits" if ecfmt else "index_bits"): bits,
+            "tensors": len(work.tensors),
+            "shapes": sorted({f"{d.rows}x{d.cols}" for d in work.tensors}),
+            "batch": work.batch,
+            "layers": work.n_layers,
+            ("max_code_bits" if work.ecfmt else "index_bits"): bits,
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
-            "launches_per_step": 3 * launches if encode else 2 * launches if ecgemv else launches,
+            "launches_per_step": 3 * launches if work.encode else 2 * launches if work.ecgemv else launches,
             "codebook_cap": args.cap or None,
             "warmup_seconds_min": args.warmup_seconds,
             "warmup_extra_steps": extra,
+            "setup_s": round(work.setup_s, 1),
+            "phase_pattern": work.phase_pattern(),
+            "weights_generated_on": "gpu" if args.workload in STEP_WORKLOADS and not args.cap else "host",
         },
+        "step_ms": {"mean": round(ms_step, 5), "median": round(pct(per_step, 50), 5),
+                    "p10": round(pct(per_step, 10), 5), "p90": round(pct(per_step, 90), 5),
+                    "min": round(min(per_step), 5), "max": round(max(per_step), 5), "n": len(per_step)},
         "compressed_GBps": round(comp_gbps, 2),
         "pct_hbm_peak": round(100.0 * comp_gbps / HBM_PEAK_GBPS, 2),
-        "layer_time_us": round(ms_step * 1e3 / n_layers, 3),
+        "copy_bw": {"GBps": round(copy_gbps, 1), "bytes": args.copy_bytes,
+                    "pct_of_copy_bw": round(100.0 * comp_gbps / copy_gbps, 2),
+                    "what": "device-to-device copy in the same run, read + write bytes over its time"},
         "roofline": {
             "bound": "hbm",
-            "kernel": ("cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
-                       if encode else kernel if ecfmt else f"{kernel}<{bits[-1]}>"),
+            "kernel": kernel_desc,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -457,24 +713,28 @@ def main():
             "traffic": round(traffic["traffic_bytes_per_launch"]) if traffic else None,
             "bytes_per_launch": int(algo_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
-            "launches_per_unit": 3 if encode else 2 if ecgemv else 1,
+            "launches_per_unit": 3 if work.encode else 2 if work.ecgemv else 1,
             "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, args.workload), ROOT) if traffic else None,
         },
     }
-    if not encode:
+    if args.workload in STEP_WORKLOADS:
+        result["layer_time_us"] = round(ms_step * 1e3 / work.n_layers, 3)
         result["tokens_per_s_equiv"] = round(1.0 / step_s, 2)
-    if batch > 1:
-        flops = 2.0 * batch * n_total / step_s
-        result["effective_TFLOPs"] = round(flops / 1e12, 3)
-    if not args.no_cpu_baseline and batch == 1 and not ecgemv:
-        log("CPU baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds, threads)
-    elif not args.no_cpu_baseline and ecfmt:
+    elif not work.encode:
+        result["launch_time_us"] = round(avg_launch_s * 1e6, 3)
+    if work.batch > 1:
+        result["effective_TFLOPs"] = round(2.0 * work.batch * n_total / step_s / 1e12, 3)
+
+    if not args.no_cpu_baseline and work.batch >= 1 and not work.ecgemv:
+        log("CPU baseline (oracle on sampled rows of every tensor) and output check ...")
+        result["cpu_baseline"], result["check"] = cpu_baseline(work, args.cpu_rows, args.cpu_seconds, threads)
+        log(f"check: {result['check']}")
+    elif not args.no_cpu_baseline and work.ecfmt:
         log("CPU baseline (oracle entropy decoder) ...")
-        result["cpu_baseline"] = cpu_baseline_ec(specs, args.cpu_seconds, gemv=ecgemv)
-    elif not args.no_cpu_baseline and encode:
+        result["cpu_baseline"] = cpu_baseline_ec(work, args.cpu_seconds)
+    elif not args.no_cpu_baseline and work.encode:
         log("CPU baseline (oracle encoder) ...")
-        result["cpu_baseline"] = cpu_baseline_encode(specs, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_encode(work, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -142,3 +142,70 @@ def summarize_trace(stats_csv: str, out_md: str, title: str, command: str, notes
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return rows
+
+
+def _trace_rows(trace_dir: str):
+    rows = []
+    for p in _csvs(trace_dir, "kernel_trace.csv"):
+        with open(p, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_name(r["Kernel_Name"])))
+    if not rows:
+        raise ValueError(f"no kernel_trace.csv under {trace_dir}")
+    rows.sort()
+    return rows
+
+
+def summarize_timed_trace(trace_dir: str, line: dict, out_md: str, title: str, command: str,
+                          peak_gbps: float = 8000.0):
+    """Per-kernel and per-step figures of the benchmark's timed steps only.
+
+    The library's dispatches (kernel names starting with ``k_``) are taken in start order; the last
+    steps x launches_per_step of them are the timed steps (after the timed region the benchmark
+    launches only copies).  Reports each kernel's mean duration over those dispatches, each step's
+    summed kernel time and span (first start to last end), and the fraction of the HBM peak that the
+    step's algorithmic bytes give over each, next to the fraction the JSON line reports."""
+    cfg = line["config"]
+    steps, per_step = int(line["steps"]), int(cfg["launches_per_step"])
+    lib = [r for r in _trace_rows(trace_dir) if r[2].startswith("k_")]
+    if len(lib) < steps * per_step:
+        raise ValueError(f"{len(lib)} library dispatches, fewer than {steps} x {per_step}")
+    timed = lib[-steps * per_step:]
+    by_name = {}
+    for s0, s1, name in timed:
+        by_name.setdefault(name, []).append(s1 - s0)
+    sums, spans = [], []
+    for k in range(steps):
+        chunk = timed[k * per_step:(k + 1) * per_step]
+        sums.append(sum(s1 - s0 for s0, s1, _ in chunk))
+        spans.append(chunk[-1][1] - chunk[0][0])
+    step_bytes = float(cfg["compressed_bytes_per_step"])
+    sum_ns, span_ns = statistics.fmean(sums), statistics.fmean(spans)
+    lines = [f"# {title}", "",
+             "Command (run from /tmp with TMPDIR=/tmp on one MI355X; committed files only):", "",
+             "```", command, "```", "",
+             f"Timed steps only: the last {steps} steps x {per_step} launches of the library's kernels "
+             f"({len(lib)} library dispatches in the trace, warm-up included).", "",
+             "| kernel | dispatches | mean ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for name, d in sorted(by_name.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {len(d)} | {statistics.fmean(d):.0f} | {min(d)} | {max(d)} |")
+    lines += ["", "| per step | mean | fraction of HBM peak from the step's algorithmic bytes |",
+              "|---|---|---|",
+              f"| summed kernel time | {sum_ns / 1e3:.2f} us | {step_bytes / sum_ns / peak_gbps:.4f} |",
+              f"| span, first start to last end | {span_ns / 1e3:.2f} us | {step_bytes / span_ns / peak_gbps:.4f} |",
+              f"| HIP events in the same run (the JSON line) | {float(line['ms_per_step']) * 1e3:.2f} us | "
+              f"{line['roofline']['frac']:.4f} |", "",
+              f"Algorithmic bytes per step: {int(step_bytes)} ({cfg['workload']}, {cfg['tensors']} tensors)."]
+    pattern = cfg.get("phase_pattern")
+    if pattern:
+        per = len(pattern)
+        lines += ["", "Per launch of a layer (position in the repeating pattern):", "",
+                  "| launch | tensors | algorithmic bytes | mean ns | fraction of HBM peak |", "|---|---|---|---|---|"]
+        for j, (names, nbytes) in enumerate(pattern):
+            d = [s1 - s0 for i, (s0, s1, _) in enumerate(timed) if (i % per_step) % per == j]
+            m = statistics.fmean(d)
+            lines.append(f"| {j} | {names} | {nbytes} | {m:.0f} | {nbytes / m / peak_gbps:.4f} |")
+    os.makedirs(os.path.dirname(out_md), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return {"sum_ns": sum_ns, "span_ns": span_ns}
