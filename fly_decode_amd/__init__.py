@@ -21,7 +21,8 @@ __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "e
            "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "cap_patterns"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libcbk.so")
+# CBK_LIBRARY names another build of the same library (for side-by-side comparisons)
+_LIB_PATH = os.environ.get("CBK_LIBRARY") or os.path.join(_HERE, "libcbk.so")
 _lib = None
 
 CBK_OK = 0

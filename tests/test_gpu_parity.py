@@ -494,3 +494,26 @@ def test_encode_gpu_workload_tensor_and_oracle(env, oracle_mod):
     out = cbk.decode_bf16(got)
     torch.cuda.synchronize()
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape), w)
+
+
+@pytest.mark.parametrize("rows,K,U", [([1, 4097, 33], 1024, 600), ([8193, 1, 2, 1023], 640, 600),
+                                      ([300, 7], 4160, 4500), ([2049, 1025, 513, 3], 8192, 4500),
+                                      ([100, 31, 7, 1], 12288, 4500)])
+def test_gemv_group_ragged_rows_every_row(env, oracle_mod, rows, K, U):
+    """Groups of 2-4 tensors of one width: row counts that do not divide over the waves or the
+    workgroups, tensors of one row, rows of one, two and three wave steps.  Every row of every
+    tensor against the oracle, and bit for bit against the single-tensor call."""
+    torch, cbk = env
+    ws = [synth.with_distinct_count(r * K, U, seed=[95, i, r], exponents=synth.finite_exponents(U)).reshape(r, K)
+          for i, r in enumerate(rows)]
+    x = synth.activation_bf16(K, seed=[96, K])
+    xd = _up(torch, x, torch.bfloat16)
+    ds = [cbk.encode(w).to("cuda") for w in ws]
+    assert len({d.b for d in ds}) == 1
+    ys = cbk.gemv_group(ds, xd)
+    torch.cuda.synchronize()
+    for w, d, y in zip(ws, ds, ys):
+        ref, absb = oracle_mod.gemv(oracle_mod.encode(w), x)
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - ref) <= TOL * absb)
+        assert torch.equal(cbk.gemv(d, xd), y)
