@@ -1,9 +1,11 @@
 """Summaries of rocprofv3 output for the benchmark's roofline block.
 
-Two kinds of summary are written under ``profiles/`` (short text, nothing executable):
+Two kinds of summary are written under ``profiles/`` (short text, nothing executable); the
+benchmark calls them (``bench.py --summarize-trace`` and ``--summarize-traffic``):
 
-* ``summarize_trace``: the per-kernel table of a ``rocprofv3 --kernel-trace --stats`` run
-  (``*_kernel_stats.csv``), as markdown, with the command that produced it.
+* ``summarize_timed_trace``: the per-kernel and per-step figures of a ``rocprofv3 --kernel-trace``
+  run of the benchmark, restricted to its timed steps, as markdown, with the command that produced
+  it.
 * ``summarize_traffic``: HBM bytes per dispatch of one kernel from two ``--pmc`` runs (``FETCH_SIZE``,
   then ``WRITE_SIZE``), each scaled by what the same counter reads for a plain device-to-device copy
   of known size (``bench.py --copy-calibration``).  The JSON records the SHA-256 of the kernel
@@ -120,28 +122,6 @@ def traffic_for(kernel_key: str, workload: str):
     if rec.get("source_sha256") != kernel_source_sha256(kernel_key):
         return None
     return rec
-
-
-def summarize_trace(stats_csv: str, out_md: str, title: str, command: str, notes: str = ""):
-    rows = []
-    for p in _csvs(stats_csv, "kernel_stats.csv"):
-        with open(p, newline="") as f:
-            for r in csv.DictReader(f):
-                rows.append(r)
-    if not rows:
-        raise ValueError(f"no kernel_stats.csv under {stats_csv}")
-    lines = [f"# {title}", "", "Command (run from /tmp with TMPDIR=/tmp on one MI355X; committed files only):", "",
-             "```", command, "```", "", "Kernel statistics (`kernel_stats.csv`):", "",
-             "| kernel | calls | average ns | min ns | max ns | share |", "|---|---|---|---|---|---|"]
-    for r in sorted(rows, key=lambda r: -float(r.get("Percentage", 0) or 0)):
-        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | {float(r['Percentage']):.2f} % |")
-    if notes:
-        lines += ["", notes]
-    os.makedirs(os.path.dirname(out_md), exist_ok=True)
-    with open(out_md, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    return rows
 
 
 def _trace_rows(trace_dir: str):
