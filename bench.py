@@ -525,6 +525,12 @@ def summarize_trace_main(args):
     print(open(args.out).read())
 
 
+def summarize_counters_main(args):
+    from fly_decode_amd import profiling
+    profiling.summarize_counters(args.summarize_counters, args.kernel, args.out, args.title, args.command)
+    print(open(args.out).read())
+
+
 def summarize_traffic_main(args):
     from fly_decode_amd import profiling
     fetch, write, cfetch, cwrite = args.summarize_traffic
@@ -562,6 +568,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR", help="write a timed-steps kernel summary and exit")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write a traffic record from four --pmc runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="write the mean per dispatch of the --pmc runs under DIR... for --kernel and exit")
     ap.add_argument("--line", help="the JSON line the profiled run printed (for --summarize-trace)")
     ap.add_argument("--out", help="output file of a summary")
     ap.add_argument("--title", default="")
@@ -574,6 +582,8 @@ def main():
 
     if args.summarize_trace:
         return summarize_trace_main(args)
+    if args.summarize_counters:
+        return summarize_counters_main(args)
     if args.summarize_traffic:
         args.copy_bytes = args.copy_bytes_cal
         return summarize_traffic_main(args)

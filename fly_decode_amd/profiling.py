@@ -189,3 +189,56 @@ def summarize_timed_trace(trace_dir: str, line: dict, out_md: str, title: str, c
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return {"sum_ns": sum_ns, "span_ns": span_ns}
+
+
+def summarize_counters(run_dirs, kernel_prefix: str, out_md: str, title: str, command: str,
+                       clock_ghz: float = 2.4, cus: int = 256):
+    """Mean per dispatch of every counter in the ``--pmc`` runs under run_dirs, for the kernels whose
+    short name starts with kernel_prefix, plus the ratios used to read them: the fraction of the
+    dispatch's CU-cycles the LDS was busy (SQ_LDS_IDX_ACTIVE) and, of those, lost to bank conflicts
+    (SQ_LDS_BANK_CONFLICT); the fraction of wave time spent waiting to issue (SQ_WAIT_INST_ANY, of
+    which on the LDS queue: SQ_WAIT_INST_LDS) and waiting on dependencies (SQ_WAIT_ANY), both over
+    SQ_WAVE_CYCLES; and instructions per wave."""
+    vals, durs = {}, []
+    for d in run_dirs:
+        for p in _csvs(d, "counter_collection.csv"):
+            with open(p, newline="") as f:
+                for r in csv.DictReader(f):
+                    if not _short_name(r["Kernel_Name"]).startswith(kernel_prefix):
+                        continue
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    if r["Counter_Name"] == "SQ_WAVES":
+                        durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not vals:
+        raise ValueError(f"no counter samples for {kernel_prefix!r}")
+    m = {k: statistics.fmean(v) for k, v in vals.items()}
+    lines = [f"# {title}", "", "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; committed files only):", "",
+             "```", command, "```", "",
+             f"Mean per dispatch over the dispatches of kernels named `{kernel_prefix}*` "
+             f"({len(vals.get('SQ_WAVES', []))} in the SQ pass).", "",
+             "| counter | mean per dispatch |", "|---|---|"]
+    for k in sorted(m):
+        lines.append(f"| `{k}` | {m[k]:.1f} |")
+    derived = []
+    if durs:
+        cyc = statistics.fmean(durs) * clock_ghz  # ns * GHz = cycles
+        derived.append(("mean dispatch duration", f"{statistics.fmean(durs) / 1e3:.2f} us"))
+        if "SQ_LDS_IDX_ACTIVE" in m:
+            derived.append(("LDS busy, fraction of the dispatch's CU-cycles", f"{m['SQ_LDS_IDX_ACTIVE'] / cus / cyc:.3f}"))
+    if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m:
+        derived.append(("bank-conflict cycles over LDS busy cycles", f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.3f}"))
+    if "SQ_WAVE_CYCLES" in m:
+        for c, what in (("SQ_WAIT_INST_ANY", "waiting to issue"), ("SQ_WAIT_INST_LDS", "waiting to issue to the LDS"),
+                        ("SQ_WAIT_ANY", "waiting on dependencies")):
+            if c in m:
+                derived.append((f"wave time {what}", f"{m[c] / m['SQ_WAVE_CYCLES']:.3f}"))
+    if "SQ_WAVES" in m:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"):
+            if c in m:
+                derived.append((f"{c} per wave", f"{m[c] / m['SQ_WAVES']:.0f}"))
+    if derived:
+        lines += ["", "| derived | value |", "|---|---|"] + [f"| {a} | {b} |" for a, b in derived]
+    os.makedirs(os.path.dirname(out_md), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return m
