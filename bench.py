@@ -250,6 +250,17 @@ class Workload:
             else:
                 cbk.gemv_group([T[i] for i in ph], xs[T[ph[0]].cols], ys=[ys[i] for i in ph])
 
+    def make_chain(self):
+        """The step's phases as one GEMV chain (cbk_gemv_chain_*): one persistent launch per step."""
+        import fly_decode_amd as cbk
+        T, xs, ys = self.tensors, self.xs, self.ys
+        self.chain = cbk.GemvChain([([T[i] for i in ph], xs[T[ph[0]].cols], [ys[i] for i in ph])
+                                    for ph in self.phases])
+        return self.chain
+
+    def run_chain(self):
+        self.chain.run()
+
     def phase_pattern(self):
         """The launches of one layer (the step repeats them), with their algorithmic bytes: a list
         of [tensor names, bytes] (None for workloads of independent single-tensor launches)."""
@@ -289,6 +300,8 @@ class Workload:
 
     def kernel_name(self):
         bits = sorted({d.b for d in self.tensors}) if not self.ecfmt else None
+        if getattr(self, "chain", None) is not None:
+            return f"k_gemv_chain_b{bits[-1]}", f"k_gemv_chain<{bits[-1]}>, one cooperative launch per step"
         if self.encode:
             return "k_enc", "cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
         if self.ecfmt:
@@ -561,6 +574,9 @@ def main():
     ap.add_argument("--cap", type=int, default=0, metavar="K",
                     help="lossy: cap every codebook at K entries (cbk_cap_patterns) before encoding")
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
+    ap.add_argument("--launch", choices=("phases", "chain"), default="phases",
+                    help="batch 1: one launch per phase (graph-replayed), or the whole step as one GEMV "
+                         "chain (a persistent cooperative launch)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30, help="size of the in-run copy-bandwidth measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (counter calibration for the "
@@ -616,13 +632,20 @@ def main():
     log(f"setup {work.setup_s:.1f} s: {len(work.tensors)} tensors, {len(work.phases)} launches per step, "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated on the GPU")
 
+    chain = args.launch == "chain"
+    if chain and (work.batch != 1 or work.ecfmt):
+        print("--launch chain applies to the batch-1 GEMV workloads", file=sys.stderr)
+        sys.exit(2)
+    if chain:
+        work.make_chain()
+        log(f"GEMV chain: {len(work.phases)} phases over {work.chain.grid} workgroups, one launch per step")
     warm0 = time.perf_counter()
     for _ in range(args.warmup):
-        work.step()
+        work.run_chain() if chain else work.step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    graph = None if args.no_graph else work.capture()
-    run_step = graph.replay if graph is not None else work.step
+    graph = None if (args.no_graph or chain) else work.capture()
+    run_step = work.run_chain if chain else graph.replay if graph is not None else work.step
     if graph is not None:
         for _ in range(2):
             graph.replay()
@@ -641,6 +664,11 @@ def main():
     ms_step = region_ms / args.steps
     log(f"timed {args.steps} steps: mean {ms_step:.4f} ms/step, median {pct(per_step, 50):.4f} "
         f"(p10 {pct(per_step, 10):.4f}, p90 {pct(per_step, 90):.4f}), wall {wall:.3f} s")
+    if chain:
+        st = work.chain.check()
+        if st != 0:
+            print(f"the GEMV chain gave up waiting (status {st})", file=sys.stderr)
+            sys.exit(1)
     if work.encode:
         check_encoded(work, sorted({0, len(work.raws) - 1}))
         log("device encodings of the first and last tensor equal the host encoder's")
@@ -648,7 +676,7 @@ def main():
     copy_gbps = copy_bandwidth(args.copy_bytes)
     log(f"device-to-device copy of {args.copy_bytes} B: {copy_gbps:.1f} GB/s (read + write)")
 
-    launches = len(work.phases)
+    launches = 1 if chain else len(work.phases)
     step_s = ms_step * 1e-3
     n_total = sum(d.n for d in work.tensors)
     comp_total = work.algorithmic_bytes()
@@ -697,7 +725,8 @@ def main():
             "compressed_bytes_per_step": comp_total,
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
-            "launches_per_step": 3 * launches if work.encode else 2 * launches if work.ecgemv else launches,
+            "launch": args.launch if work.batch == 1 and not work.ecfmt else "phases",
+            "launches_per_step": 2 if chain else 3 * launches if work.encode else 2 * launches if work.ecgemv else launches,
             "codebook_cap": args.cap or None,
             "warmup_seconds_min": args.warmup_seconds,
             "warmup_extra_steps": extra,

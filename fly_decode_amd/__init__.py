@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
            "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
-           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "cap_patterns"]
+           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "cap_patterns", "GemvChain"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # CBK_LIBRARY names another build of the same library (for side-by-side comparisons)
@@ -39,6 +39,17 @@ class CbkError(RuntimeError):
 class _Tensor(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64), ("U", ctypes.c_uint32),
                 ("b", ctypes.c_uint32), ("codebook", ctypes.c_void_p), ("words", ctypes.c_void_p)]
+
+
+class _GemvPhase(ctypes.Structure):
+    _fields_ = [("ts", ctypes.POINTER(_Tensor)), ("count", ctypes.c_uint32), ("x", ctypes.c_void_p),
+                ("ys", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class _GemvChain(ctypes.Structure):
+    _fields_ = [("buffer", ctypes.c_void_p), ("phases", ctypes.c_uint32), ("b", ctypes.c_uint32),
+                ("grid", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32), ("x_bytes", ctypes.c_uint32),
+                ("device", ctypes.c_uint32)]
 
 
 class _ECHeader(ctypes.Structure):
@@ -100,6 +111,15 @@ def load_library():
         lib.cbk_gemm_group.argtypes = [tp, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p),
                                        ctypes.POINTER(ctypes.c_uint64), ctypes.c_void_p]
+        lib.cbk_gemv_chain_bytes.restype = ctypes.c_size_t
+        lib.cbk_gemv_chain_bytes.argtypes = [ctypes.c_uint32]
+        lib.cbk_gemv_chain_init.restype = ctypes.c_int
+        lib.cbk_gemv_chain_init.argtypes = [ctypes.POINTER(_GemvPhase), ctypes.c_uint32, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.POINTER(_GemvChain)]
+        lib.cbk_gemv_chain_run.restype = ctypes.c_int
+        lib.cbk_gemv_chain_run.argtypes = [ctypes.POINTER(_GemvChain), ctypes.c_uint32, ctypes.c_void_p]
+        lib.cbk_gemv_chain_check.restype = ctypes.c_int
+        lib.cbk_gemv_chain_check.argtypes = [ctypes.POINTER(_GemvChain)]
         hp = ctypes.POINTER(_ECHeader)
         for name in ("cbk_ec_spans", "cbk_ec_stream_words", "cbk_ec_gap_words", "cbk_ec_blocks",
                      "cbk_ec_stored_bytes"):
@@ -347,6 +367,49 @@ def gemm_group(ts, X, Ys=None, stream=None):
     _check(load_library().cbk_gemm_group(arr, len(ts), ctypes.c_void_p(X.data_ptr() or None), X.stride(0),
                                          batch, yp, ld, _stream(stream)), "cbk_gemm_group")
     return Ys
+
+
+class GemvChain:
+    """cbk_gemv_chain_*: dependent GEMV phases run by one persistent launch.
+
+    ``phases`` is a list of (tensors, x, ys): device ``Compressed`` tensors that share the
+    bfloat16 vector x (same cols and, across the whole chain, the same b), and their float32
+    outputs ys (rows_i each).  The library records the device pointers, so every tensor, x and y
+    must stay alive (this object keeps references).  ``run()`` enqueues one pass over every phase
+    on the current stream; ``check()`` (after synchronizing) returns 0, or CBK_E_TIMEOUT (6) when a
+    barrier wait of the last run gave up."""
+
+    def __init__(self, phases, device=None):
+        import torch
+        phases = [(list(ts), x, list(ys)) for ts, x, ys in phases]
+        if not phases:
+            raise ValueError("a chain needs at least one phase")
+        lib = load_library()
+        arr = (_GemvPhase * len(phases))()
+        keep = []
+        for i, (ts, x, ys) in enumerate(phases):
+            if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.numel() != ts[0].cols:
+                raise ValueError("x must be a contiguous bfloat16 vector of length cols")
+            tarr = (_Tensor * len(ts))(*[t._struct() for t in ts])
+            yarr = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+            keep += [tarr, yarr]
+            arr[i] = _GemvPhase(tarr, len(ts), x.data_ptr(), yarr)
+        nbytes = int(lib.cbk_gemv_chain_bytes(len(phases)))
+        dev = device if device is not None else phases[0][1].device
+        self.buffer = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        off = (-self.buffer.data_ptr()) % 256
+        self._chain = _GemvChain()
+        _check(lib.cbk_gemv_chain_init(arr, len(phases), ctypes.c_void_p(self.buffer.data_ptr() + off), nbytes,
+                                       ctypes.byref(self._chain)), "cbk_gemv_chain_init")
+        self.phases = phases
+        self.grid = int(self._chain.grid)
+
+    def run(self, timeout_us: int = 1_000_000, stream=None) -> None:
+        _check(load_library().cbk_gemv_chain_run(ctypes.byref(self._chain), timeout_us, _stream(stream)),
+               "cbk_gemv_chain_run")
+
+    def check(self) -> int:
+        return int(load_library().cbk_gemv_chain_check(ctypes.byref(self._chain)))
 
 
 # ---- exponent entropy-coded format (include/cbk_ec.h)

@@ -87,6 +87,7 @@ const char *cbk_status_str(int status) {
         case CBK_E_ALIGN: return "misaligned pointer or leading dimension";
         case CBK_E_UNSUPPORTED: return "unsupported shape";
         case CBK_E_HIP: return "HIP runtime error";
+        case CBK_E_TIMEOUT: return "a chained launch gave up waiting";
         default: return "unknown status";
     }
 }
@@ -278,6 +279,46 @@ cbk_status cbk_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *
     if (K > 0 && !x) return CBK_E_INVALID;
     if (x && !aligned(x, 2)) return CBK_E_ALIGN;
     return cbk::launch_gemv_group(ts, count, x, ys, static_cast<hipStream_t>(stream));
+}
+
+size_t cbk_gemv_chain_bytes(uint32_t phases) { return cbk::gemv_chain_bytes(phases); }
+
+cbk_status cbk_gemv_chain_init(const cbk_gemv_phase *phases, uint32_t count, void *buffer, size_t bytes,
+                               cbk_gemv_chain *chain) {
+    if (!phases || !buffer || !chain || count == 0 || count > 65536) return CBK_E_INVALID;
+    uint32_t b = 0;
+    for (uint32_t p = 0; p < count; ++p) {
+        const cbk_gemv_phase &ph = phases[p];
+        if (!ph.ts || !ph.ys || !ph.x || ph.count == 0 || ph.count > 8) return CBK_E_INVALID;
+        const uint64_t K = ph.ts[0].cols;
+        for (uint32_t i = 0; i < ph.count; ++i) {
+            const cbk_status st = check_tensor(&ph.ts[i]);
+            if (st != CBK_OK) return st;
+            if (ph.ts[i].cols != K || ph.ts[i].rows == 0 || !ph.ys[i]) return CBK_E_INVALID;
+            if (!aligned(ph.ys[i], 4)) return CBK_E_ALIGN;
+        }
+        if (p == 0) b = ph.ts[0].b;
+        for (uint32_t i = 0; i < ph.count; ++i) {
+            if (ph.ts[i].b != b || b < 1 || b > 15) return CBK_E_UNSUPPORTED;
+            if (!aligned(ph.ts[i].codebook, 16)) return CBK_E_ALIGN;
+            if (ph.ts[i].rows * (K / 64) >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
+        }
+        if (K == 0 || K % 64 != 0 || K > 32768) return CBK_E_UNSUPPORTED;
+        if (!aligned(ph.x, 16)) return CBK_E_ALIGN;
+    }
+    if (!aligned(buffer, 256)) return CBK_E_ALIGN;
+    if (bytes < cbk::gemv_chain_bytes(count)) return CBK_E_CAPACITY;
+    return cbk::build_gemv_chain(phases, count, buffer, chain);
+}
+
+cbk_status cbk_gemv_chain_run(const cbk_gemv_chain *chain, uint32_t timeout_us, void *stream) {
+    if (!chain || !chain->buffer || chain->phases == 0) return CBK_E_INVALID;
+    return cbk::launch_gemv_chain(*chain, timeout_us, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_gemv_chain_check(const cbk_gemv_chain *chain) {
+    if (!chain || !chain->buffer) return CBK_E_INVALID;
+    return cbk::gemv_chain_check(*chain);
 }
 
 cbk_status cbk_gemm_small(const cbk_tensor *t, const uint16_t *X, uint64_t ldx, uint32_t batch,

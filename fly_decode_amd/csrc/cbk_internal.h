@@ -14,6 +14,11 @@ cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s);
 cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s);
 cbk_status launch_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x,
                              float *const *ys, hipStream_t s);
+// Chained GEMV phases (validated by cbk_gemv_chain_init).
+size_t gemv_chain_bytes(uint32_t phases);
+cbk_status build_gemv_chain(const cbk_gemv_phase *phases, uint32_t count, void *buffer, cbk_gemv_chain *chain);
+cbk_status launch_gemv_chain(const cbk_gemv_chain &chain, uint32_t timeout_us, hipStream_t s);
+cbk_status gemv_chain_check(const cbk_gemv_chain &chain);
 cbk_status launch_gemm(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,
                        float *Y, uint64_t ldy, hipStream_t s);
 cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_t *X, uint64_t ldx,

@@ -39,6 +39,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstddef>
+#include <cstring>
+#include <vector>
 #include <atomic>
 #include <utility>
 
@@ -385,67 +388,43 @@ __device__ __forceinline__ void gemv_unit(const uint32_t (&d)[U64<B>::UD], const
     }
 }
 
-// Rows of one tensor for workgroup `blk` of the tensor's `nblk` workgroups.  Every argument is
-// uniform across the workgroup.  The workgroup's rows are blk * 8 + j + NW * i (j < 8), taken in
-// the order k = 8 i + j; wave w starts with k = w.  With `dyn` false wave w then takes k + 8, k + 16,
-// ...; with `dyn` true a wave that finishes a row claims the next k from a counter in LDS, so the
-// waves of a workgroup end within about one row of each other (the host sets it when there are
-// enough rows per wave for the tail to matter).
-template <int B>
-__device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb,
-                                          float *__restrict__ yt, const uint16_t *__restrict__ x, uint32_t M,
-                                          uint32_t U, uint32_t P, uint32_t S, uint32_t blk, uint32_t nblk,
-                                          bool dyn) {
+// The row loops of one wave: rows of one tensor for workgroup `blk` of the tensor's `nblk`
+// workgroups, from the wave's first row gw (< M), whose first step's loads are in `nxt` on entry;
+// the codebook table and x are staged in LDS.  Every argument is uniform across the workgroup.
+// The workgroup's rows are blk * 8 + j + NW * i (j < 8), taken in the order k = 8 i + j; wave w
+// starts with k = w.  With `dyn` false wave w then takes k + 8, k + 16, ...; with `dyn` true a wave
+// that finishes a row claims the next k from the counter at next_row (LDS), so the waves of a
+// workgroup end within about one row of each other (the host sets it when there are enough rows
+// per wave for the tail to matter).  tail() is called exactly once, where the wave would issue
+// its next weight loads but has no row left: the chained launch issues the next phase's first
+// step there.  WT: y is stored at device scope (written through to memory, visible to every
+// XCD once the store has completed), as the chained launch's barrier needs.
+template <int B, bool WT, class Tail>
+__device__ __forceinline__ void gemv_rows_loop(u32x4 (&nxt)[U64<B>::LPL], u32x4 *stage, const unsigned char *xl,
+                                               const uint16_t *cbl, uint32_t *next_row,
+                                               const u32x4 *__restrict__ w4, float *__restrict__ yt, uint32_t M,
+                                               uint32_t P, uint32_t S, uint32_t blk, uint32_t nblk, bool dyn,
+                                               uint32_t gw, int lane, Tail &&tail) {
     using G = U64<B>;
     constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
-    constexpr int NT = 64 * kGemvWaves;
-    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
-    __shared__ uint32_t next_row;  // next k to claim (dyn)
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned char *xl = smem;
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
     const uint32_t NW = nblk * kGemvWaves;
-    const uint32_t gw = blk * kGemvWaves + wave;
-
-    // Staging loads (codebook and this thread's x chunks), issued in every wave before the first
-    // weight load.
-    const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
-    const uint32_t xch = P * 8;
-    CbStage<B, NT> cs;
-    cs.issue(cb, U, x4, tid);
-    u32x4 xv[kXPerThread];
-#pragma unroll
-    for (int i = 0; i < kXPerThread; ++i)
-        if (static_cast<uint32_t>(i * NT + tid) < xch) xv[i] = x4[i * NT + tid];
-    issue_barrier();
-
-    // First weight step (no memory access for a wave without rows).
-    u32x4 nxt[G::LPL];
-    load_step<B>(nxt, w4, min(gw, M - 1) * P, min(64u, P), ~uint64_t(0), gw < M, lane);
-
-    cs.store(cbl, U, tid);
-#pragma unroll
-    for (int i = 0; i < kXPerThread; ++i) {
-        const uint32_t q = i * NT + tid;
-        if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[i];
-    }
-    if (tid == 0) next_row = kGemvWaves;
-    lds_barrier();
-    if (gw >= M) return;
-
     // The row after r: the static order, or the next k claimed from the workgroup's counter.
     auto next = [&](uint32_t r) -> uint32_t {
         if (!dyn) return r + NW;
         uint32_t kk = 0;
-        if (lane == 0) kk = atomicAdd(&next_row, 1u);
+        if (lane == 0) kk = atomicAdd(next_row, 1u);
         kk = __builtin_amdgcn_readfirstlane(kk);
         return blk * kGemvWaves + (kk & (kGemvWaves - 1)) + NW * (kk / kGemvWaves);
     };
     float a[4] = {0.f, 0.f, 0.f, 0.f};
     auto reduce_row = [&](uint32_t r) {
         const float acc = wave_sum_last((a[0] + a[1]) + (a[2] + a[3]));
-        if (lane == 63) yt[r] = acc;
+        if (lane == 63) {
+            if constexpr (WT)
+                __hip_atomic_store(yt + r, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                yt[r] = acc;
+        }
         a[0] = a[1] = a[2] = a[3] = 0.f;
     };
 
@@ -464,6 +443,7 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
             uint32_t d[G::UD];
             transpose_step<B>(d, nxt, stage, r * P, lane);
             if (rn < M) load_step<B>(nxt, w4, rn * P, P, ~uint64_t(0), true, lane);
+            else tail();
             const uint32_t rnn = rn < M ? next(rn) : M;
             if (active) gemv_unit<B>(d, cbl, xr, a);
             reduce_row(r);
@@ -497,6 +477,7 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
                 uint32_t d[G::UD];
                 transpose_step<B>(d, nxt, stage, r * P + 64, lane);
                 if (rn < M) load_step<B>(nxt, w4, rn * P, 64, ~uint64_t(0), true, lane);
+                else tail();
                 if (active1) gemv_unit<B>(d, cbl, xr1, a);
             }
             reduce_row(r);
@@ -516,6 +497,7 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
         const uint32_t rn = row_end ? next(r) : r;
         const uint32_t jn = row_end ? 0 : j + 1;
         if (rn < M) load_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), ~uint64_t(0), true, lane);
+        else tail();
 
         const uint32_t cu = 64 * j + lane;  // this lane's unit within the row
         if (cu < P) {
@@ -530,6 +512,52 @@ __device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const ui
         r = rn;
         j = jn;
     }
+}
+
+// Rows of one tensor for workgroup `blk` of the tensor's `nblk` workgroups (one launch): stages the
+// codebook and x, loads the wave's first step and runs the row loops.
+template <int B>
+__device__ __forceinline__ void gemv_rows(const u32x4 *__restrict__ w4, const uint16_t *__restrict__ cb,
+                                          float *__restrict__ yt, const uint16_t *__restrict__ x, uint32_t M,
+                                          uint32_t U, uint32_t P, uint32_t S, uint32_t blk, uint32_t nblk,
+                                          bool dyn) {
+    using G = U64<B>;
+    constexpr uint32_t XU = 2 * 64 + 16;  // LDS bytes per unit of x (16 bytes of padding)
+    constexpr int NT = 64 * kGemvWaves;
+    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
+    __shared__ uint32_t next_row;  // next k to claim (dyn)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *xl = smem;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    u32x4 *stage = reinterpret_cast<u32x4 *>(xl + P * XU) + wave * G::STAGE_CHUNKS;
+    const uint32_t gw = blk * kGemvWaves + wave;
+
+    // Staging loads (codebook and this thread's x chunks), issued in every wave before the first
+    // weight load.
+    const u32x4 *x4 = reinterpret_cast<const u32x4 *>(x);
+    const uint32_t xch = P * 8;
+    CbStage<B, NT> cs;
+    cs.issue(cb, U, x4, tid);
+    u32x4 xv[kXPerThread];
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i)
+        if (static_cast<uint32_t>(i * NT + tid) < xch) xv[i] = x4[i * NT + tid];
+    issue_barrier();
+
+    // First weight step (no memory access for a wave without rows).
+    u32x4 nxt[G::LPL];
+    load_step<B>(nxt, w4, min(gw, M - 1) * P, min(64u, P), ~uint64_t(0), gw < M, lane);
+
+    cs.store(cbl, U, tid);
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i) {
+        const uint32_t q = i * NT + tid;
+        if (q < xch) *reinterpret_cast<u32x4 *>(xl + (q >> 3) * XU + (q & 7) * 16) = xv[i];
+    }
+    if (tid == 0) next_row = kGemvWaves;
+    lds_barrier();
+    if (gw >= M) return;
+    gemv_rows_loop<B, false>(nxt, stage, xl, cbl, &next_row, w4, yt, M, P, S, blk, nblk, dyn, gw, lane, [] {});
 }
 
 // One tensor per launch.  The arguments are plain scalars so that the code object can have them
@@ -554,6 +582,191 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_rows_group(const GemvG
     const GemvTensor &T = grp.t[k];
     const uint32_t b0 = grp.first_block[k], b1 = grp.first_block[k + 1];
     gemv_rows<B>(T.w4, T.cb, T.y, x, T.M, T.U, grp.P, grp.S, blockIdx.x - b0, b1 - b0, grp.dyn != 0);
+}
+
+// ------------------------------------------------------------ chained GEMV phases, one launch
+// A chain of dependent GEMV phases, such as a decode step's [q, k, v] -> [o] -> [gate, up] ->
+// [down] over its layers: phase p + 1 reads its x only after every workgroup has finished phase p,
+// as if x were computed from phase p's outputs.  One persistent workgroup per CU runs all phases,
+// and the grid meets at a barrier between two of them.  A launch per phase pays at every boundary
+// for the dispatch, the codebook and x staging, the first loads' latency on an idle machine and
+// the tail in which the last waves run alone.  Here a wave that has issued its last weight load of
+// phase p issues its first step of phase p + 1 (the weights do not depend on x), and the
+// workgroup's next codebook loads go out before the barrier, so the memory system keeps working
+// while the grid drains and meets.  This carries the DFloat11 page's block-level decompression
+// ("How it works in practice": a transformer block's matrices decompressed together to hide
+// latency) across the dependent phases of a block.
+//
+// The barrier is an arrival counter in device memory, used by one thread per workgroup.  The
+// launch is cooperative, so the runtime guarantees that the whole grid is resident before any
+// workgroup waits; every wait is also bounded by a wall-clock limit, and a workgroup that reaches
+// it (or sees that another one has) records the failure and leaves, so the kernel always ends.  Rows are computed exactly as by k_gemv_rows (same loops), so every y equals the
+// single-launch result bit for bit.
+struct ChainPhase {
+    GemvGroup g;  // tensors, workgroup split over the chain's grid, P, S, dyn
+    const uint16_t *x;
+};
+struct ChainSync {
+    uint32_t arrived;  // arrivals so far in this run: barrier i is passed at (i + 1) * grid
+    uint32_t failed;   // nonzero: a wait gave up, the outputs are incomplete
+    uint32_t pad[62];  // the block fills 256 bytes
+};
+static_assert(sizeof(ChainSync) == 256, "sync block size");
+
+// Member of a group that workgroup blockIdx.x works on (uniform).
+__device__ __forceinline__ uint32_t group_member(const GemvGroup &g) {
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGroup; ++j) k += (j < static_cast<int>(g.count) && blockIdx.x >= g.first_block[j]) ? 1u : 0u;
+    return k;
+}
+
+// Grid barrier number i of a run, called by one thread per workgroup after the workgroup's
+// outputs of the phase have completed: true once all workgroups have arrived, false if the wait
+// gave up (after `limit` wall-clock ticks, or because another workgroup did).  The counter only
+// grows during a run (cleared before each run), so no reset races the next barrier's arrivals.
+// Every access is a relaxed device-scope atomic, which this chip performs coherently for all its
+// XCDs without touching the caches' other lines.  (An acquire load would invalidate the whole L2
+// of the poller's XCD; polled in a loop by every workgroup, that made each barrier cost about
+// 30 us.)  The ordering the phases need comes from the data accesses themselves: outputs are
+// written through at device scope and waited for before arriving, and the next phase's x is read
+// with device-coherent loads after the wait.
+__device__ bool chain_barrier(ChainSync *s, uint32_t i, uint32_t nblocks, uint64_t limit) {
+    const uint32_t target = (i + 1) * nblocks;
+    if (__hip_atomic_fetch_add(&s->arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == target) return true;
+    // a poll (a round trip past the L2) takes well over 8 ticks of the 100 MHz wall clock, so the
+    // poll count bounds the wait too, should the clock not advance
+    const uint64_t t0 = wall_clock64(), max_polls = (limit >> 3) + 1024;
+    uint64_t polls = 0;
+    while (__hip_atomic_load(&s->arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__hip_atomic_load(&s->failed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+        if (wall_clock64() - t0 > limit || ++polls > max_polls) {
+            __hip_atomic_store(&s->failed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+// Cache policy of x loads after a barrier: device-coherent (SC0 | SC1), so they read what another
+// XCD wrote before the barrier rather than a line left in this XCD's caches.
+constexpr int kCoherent = 1 | 16;
+
+template <int NT, int AUX>
+__device__ __forceinline__ void x_stage_load(u32x4 (&xv)[kXPerThread], const uint16_t *x, uint32_t P, int tid) {
+    const auto rs = wave_rsrc(x, P * 128u);  // chunks past the P units read as zero
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i)
+        if (static_cast<uint32_t>(i * NT + tid) < P * 8)
+            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>((i * NT + tid) * 16u), 0, AUX);
+}
+template <int NT>
+__device__ __forceinline__ void x_stage_store(unsigned char *xl, const u32x4 (&xv)[kXPerThread], uint32_t P, int tid) {
+#pragma unroll
+    for (int i = 0; i < kXPerThread; ++i) {
+        const uint32_t c = i * NT + tid;
+        if (c < P * 8) *reinterpret_cast<u32x4 *>(xl + (c >> 3) * (2 * 64 + 16) + (c & 7) * 16) = xv[i];
+    }
+}
+
+template <int B>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_chain(const ChainPhase *__restrict__ ph, uint32_t nph,
+                                                                uint32_t xbytes, ChainSync *sync, uint64_t limit) {
+    using G = U64<B>;
+    constexpr int NT = 64 * kGemvWaves;
+    __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
+    __shared__ uint32_t next_row;  // next k to claim (dyn)
+    __shared__ uint32_t go_on;     // the grid barrier's outcome
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *xl = smem;      // x of the current phase (xbytes: the largest phase's)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    u32x4 *stage = reinterpret_cast<u32x4 *>(smem + xbytes) + wave * G::STAGE_CHUNKS;
+
+    // This workgroup's part of a phase (uniform): its tensor, its block among the tensor's, and
+    // this wave's first row.
+    struct Part {
+        const u32x4 *w4;
+        const uint16_t *cb, *x;
+        float *y;
+        uint32_t M, U, P, S, blk, nblk, gw;
+        bool dyn;
+    };
+    auto part = [&](uint32_t p) {
+        const ChainPhase &c = ph[p];
+        const uint32_t k = group_member(c.g);
+        const GemvTensor &T = c.g.t[k];
+        Part q;
+        q.w4 = T.w4;
+        q.cb = T.cb;
+        q.x = c.x;
+        q.y = T.y;
+        q.M = T.M;
+        q.U = T.U;
+        q.P = c.g.P;
+        q.S = c.g.S;
+        q.blk = blockIdx.x - c.g.first_block[k];
+        q.nblk = c.g.first_block[k + 1] - c.g.first_block[k];
+        q.gw = q.blk * kGemvWaves + wave;
+        q.dyn = c.g.dyn != 0;
+        return q;
+    };
+    // the wave's first step of a phase (no memory access for a wave without rows)
+    auto first_step = [&](u32x4 (&v)[G::LPL], const Part &q) {
+        load_step<B>(v, q.w4, min(q.gw, q.M - 1) * q.P, min(64u, q.P), ~uint64_t(0), q.gw < q.M, lane);
+    };
+    // Phase 0 is staged as in a single launch: codebook and x loads first, then the first step.
+    Part cur = part(0);
+    u32x4 nxt[G::LPL];
+    {
+        CbStage<B, NT> cs;
+        cs.issue(cur.cb, cur.U, reinterpret_cast<const u32x4 *>(cur.x), tid);
+        u32x4 xv[kXPerThread];
+        x_stage_load<NT, 0>(xv, cur.x, cur.P, tid);
+        issue_barrier();
+        first_step(nxt, cur);
+        cs.store(cbl, cur.U, tid);
+        x_stage_store<NT>(xl, xv, cur.P, tid);
+        if (tid == 0) next_row = kGemvWaves;
+        lds_barrier();
+    }
+    for (uint32_t p = 0;; ++p) {
+        const bool more = p + 1 < nph;
+        Part nx{};
+        if (more) nx = part(p + 1);
+        auto tail = [&] {
+            if (more) first_step(nxt, nx);
+        };
+        if (cur.gw < cur.M)
+            gemv_rows_loop<B, true>(nxt, stage, xl, cbl, &next_row, cur.w4, cur.y, cur.M, cur.P, cur.S, cur.blk,
+                                    cur.nblk, cur.dyn, cur.gw, lane, tail);
+        else
+            tail();
+        if (!more) return;
+        // End of phase p: each wave's y stores have completed (waitcnt), and after the workgroup
+        // barrier no wave uses the table, x or the row counter any more.  The next codebook's
+        // loads go out before the grid barrier (they do not depend on x), x's after it.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        CbStage<B, NT> cs;
+        cs.issue(nx.cb, nx.U, reinterpret_cast<const u32x4 *>(nx.x), tid);
+        if (tid == 0) go_on = chain_barrier(sync, p, gridDim.x, limit) ? 1u : 0u;
+        __syncthreads();
+        if (!go_on) return;
+        u32x4 xv[kXPerThread];
+        x_stage_load<NT, kCoherent>(xv, nx.x, nx.P, tid);
+        cs.store(cbl, nx.U, tid);
+        x_stage_store<NT>(xl, xv, nx.P, tid);
+        if (tid == 0) next_row = kGemvWaves;
+        lds_barrier();
+        cur = nx;
+    }
+}
+
+// Clears a chain's sync block before each run (a kernel, not a memset, so that graph capture
+// records an ordinary node).
+__global__ __launch_bounds__(64) void k_chain_reset(ChainSync *s) {
+    reinterpret_cast<uint32_t *>(s)[threadIdx.x] = 0u;
 }
 
 // ------------------------------------------------------------------------- fast skinny GEMM
@@ -1190,6 +1403,34 @@ struct DecodeRun {
     }
 };
 
+// A group of tensors that share x over a grid of `grid` workgroups (grid >= count): workgroups
+// per tensor in proportion to its rows, at least one each, and the row claims (dyn).
+void split_group(const cbk_tensor *ts, float *const *ys, uint32_t count, uint32_t grid, GemvGroup &grp) {
+    const uint64_t P = ts[0].cols / 64;
+    uint64_t rows = 0;
+    for (uint32_t i = 0; i < count; ++i) rows += ts[i].rows;
+    grp.count = count;
+    grp.P = static_cast<uint32_t>(P);
+    grp.S = static_cast<uint32_t>((P + 63) / 64);
+    // Rows claimed dynamically inside each workgroup from 8 rows per wave on: measured 4-7 %
+    // faster on 28672 x 8192 (14 rows per wave), even at 4 rows per wave and 3 % slower at 2.
+    grp.dyn = rows >= uint64_t(8) * grid * kGemvWaves ? 1u : 0u;
+    uint32_t first = 0;
+    uint64_t rows_before = 0;
+    for (uint32_t i = 0; i < count; ++i) {
+        const cbk_tensor &t = ts[i];
+        const uint32_t end = (i + 1 == count)
+            ? grid
+            : std::max<uint32_t>(first + 1, static_cast<uint32_t>(((rows_before + t.rows) * grid + rows / 2) / rows));
+        grp.t[i] = GemvTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, ys[i], static_cast<uint32_t>(t.rows),
+                              t.U};
+        grp.first_block[i] = first;
+        rows_before += t.rows;
+        first = std::min(end, grid - (count - 1 - i));
+    }
+    grp.first_block[count] = grid;
+}
+
 struct GemvArgs {
     const cbk_tensor *ts; uint32_t count; const uint16_t *x; float *const *ys; hipStream_t s; cbk_status st;
 };
@@ -1223,27 +1464,7 @@ struct GemvRun {
             a.count, std::min<uint64_t>(cu_count(), (rows + kGemvWaves - 1) / kGemvWaves)));
 
         GemvGroup grp{};
-        grp.count = a.count;
-        grp.P = static_cast<uint32_t>(P);
-        grp.S = static_cast<uint32_t>((P + 63) / 64);
-        // Rows claimed dynamically inside each workgroup from 8 rows per wave on: measured 4-7 %
-        // faster on 28672 x 8192 (14 rows per wave), even at 4 rows per wave and 3 % slower at 2.
-        grp.dyn = rows >= uint64_t(8) * grid * kGemvWaves ? 1u : 0u;
-        // Workgroups per tensor in proportion to its rows, at least one each.
-        uint32_t first = 0;
-        uint64_t rows_before = 0;
-        for (uint32_t i = 0; i < a.count; ++i) {
-            const cbk_tensor &t = a.ts[i];
-            const uint32_t end = (i + 1 == a.count)
-                ? grid
-                : std::max<uint32_t>(first + 1, static_cast<uint32_t>(((rows_before + t.rows) * grid + rows / 2) / rows));
-            grp.t[i] = GemvTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.ys[i],
-                                  static_cast<uint32_t>(t.rows), t.U};
-            grp.first_block[i] = first;
-            rows_before += t.rows;
-            first = std::min(end, grid - (a.count - 1 - i));
-        }
-        grp.first_block[a.count] = grid;
+        split_group(a.ts, a.ys, a.count, grid, grp);
         if (group) {
             hipLaunchKernelGGL(k_gemv_rows_group<B>, dim3(grid), dim3(64 * kGemvWaves), static_cast<uint32_t>(lds),
                                a.s, grp, a.x);
@@ -1454,6 +1675,102 @@ cbk_status launch_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_
 cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s) {
     float *ys[1] = {y};
     return launch_gemv_group(&t, 1, x, ys, s);
+}
+
+// ------------------------------------------------------------------ chained GEMV, host side
+namespace {
+
+using ChainB = std::integer_sequence<int, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15>;
+
+struct ChainBuildArgs {
+    const cbk_gemv_phase *phases; uint32_t count; void *buffer; cbk_gemv_chain *chain; cbk_status st;
+};
+
+// Plans every phase over one workgroup per CU (the grid that a cooperative launch keeps resident)
+// and uploads the plan after the zeroed sync block.
+template <int B>
+struct ChainBuild {
+    static bool run(ChainBuildArgs &a) {
+        using G = U64<B>;
+        uint64_t pmax = 0;
+        for (uint32_t p = 0; p < a.count; ++p) pmax = std::max<uint64_t>(pmax, a.phases[p].ts[0].cols / 64);
+        const uint64_t xbytes = pmax * (2 * 64 + 16);
+        const uint64_t lds = xbytes + uint64_t(kGemvWaves) * G::STAGE_CHUNKS * 16;
+        int dev = 0, coop = 0, occ = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return a.st = CBK_E_HIP, true;
+        if (lds + uint64_t(Table<B>::SIZE) * 2 + 16 > kLdsLimit || !allow_lds(k_gemv_chain<B>, static_cast<uint32_t>(lds)))
+            return a.st = CBK_E_UNSUPPORTED, true;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv_chain<B>, 64 * kGemvWaves,
+                                                         static_cast<size_t>(lds)) != hipSuccess)
+            return a.st = CBK_E_HIP, true;
+        if (!coop || occ < 1) return a.st = CBK_E_UNSUPPORTED, true;
+        const uint32_t grid = static_cast<uint32_t>(cu_count());
+        std::vector<unsigned char> host(gemv_chain_bytes(a.count), 0);
+        for (uint32_t p = 0; p < a.count; ++p) {
+            ChainPhase c{};
+            split_group(a.phases[p].ts, a.phases[p].ys, a.phases[p].count, grid, c.g);
+            c.x = a.phases[p].x;
+            std::memcpy(host.data() + sizeof(ChainSync) + size_t(p) * sizeof(ChainPhase), &c, sizeof(c));
+        }
+        if (hipMemcpy(a.buffer, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess)
+            return a.st = CBK_E_HIP, true;
+        *a.chain = cbk_gemv_chain{a.buffer, a.count, static_cast<uint32_t>(B), grid, static_cast<uint32_t>(lds),
+                                  static_cast<uint32_t>(xbytes), static_cast<uint32_t>(dev)};
+        a.st = CBK_OK;
+        return true;
+    }
+};
+
+struct ChainRunArgs {
+    const cbk_gemv_chain *chain; uint64_t limit; hipStream_t s; cbk_status st;
+};
+
+template <int B>
+struct ChainLaunch {
+    static bool run(ChainRunArgs &a) {
+        const cbk_gemv_chain &c = *a.chain;
+        ChainSync *sync = static_cast<ChainSync *>(c.buffer);
+        const ChainPhase *ph = reinterpret_cast<const ChainPhase *>(static_cast<unsigned char *>(c.buffer) + sizeof(ChainSync));
+        hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(64), 0, a.s, sync);
+        if (hipGetLastError() != hipSuccess) return a.st = CBK_E_HIP, true;
+        uint32_t nph = c.phases, xbytes = c.x_bytes;
+        uint64_t limit = a.limit;
+        void *args[] = {&ph, &nph, &xbytes, &sync, &limit};
+        const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(k_gemv_chain<B>), dim3(c.grid),
+                                                        dim3(64 * kGemvWaves), args, c.lds_bytes, a.s);
+        a.st = e == hipSuccess ? CBK_OK : (e == hipErrorCooperativeLaunchTooLarge ? CBK_E_UNSUPPORTED : CBK_E_HIP);
+        return true;
+    }
+};
+
+}  // namespace
+
+size_t gemv_chain_bytes(uint32_t phases) { return sizeof(ChainSync) + size_t(phases) * sizeof(ChainPhase); }
+
+cbk_status build_gemv_chain(const cbk_gemv_phase *phases, uint32_t count, void *buffer, cbk_gemv_chain *chain) {
+    ChainBuildArgs a{phases, count, buffer, chain, CBK_OK};
+    if (!dispatch_b<ChainBuild>(static_cast<int>(phases[0].ts[0].b), a, ChainB{})) return CBK_E_UNSUPPORTED;
+    return a.st;
+}
+
+cbk_status launch_gemv_chain(const cbk_gemv_chain &chain, uint32_t timeout_us, hipStream_t s) {
+    int dev = -1, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CBK_E_HIP;
+    if (static_cast<uint32_t>(dev) != chain.device) return CBK_E_INVALID;
+    // wall-clock ticks of the barrier waits' limit (the counter runs at hipDeviceAttributeWallClockRate kHz)
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) return CBK_E_HIP;
+    ChainRunArgs a{&chain, uint64_t(timeout_us) * uint64_t(khz) / 1000u, s, CBK_OK};
+    if (!dispatch_b<ChainLaunch>(static_cast<int>(chain.b), a, ChainB{})) return CBK_E_INVALID;
+    return a.st;
+}
+
+cbk_status gemv_chain_check(const cbk_gemv_chain &chain) {
+    uint32_t failed = 0;
+    if (hipMemcpy(&failed, static_cast<unsigned char *>(chain.buffer) + offsetof(ChainSync, failed), sizeof(failed),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return CBK_E_HIP;
+    return failed ? CBK_E_TIMEOUT : CBK_OK;
 }
 
 }  // namespace cbk

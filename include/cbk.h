@@ -25,8 +25,9 @@
  *    in host memory), enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  *    return without waiting.  Buffers must stay alive until that work completes.
  *  - The caller owns every buffer.  The library allocates no memory and keeps no per-call state,
- *    so calls are safe from several host threads and streams at once.  The one exception is
- *    cbk_encode_gpu_noalloc, which uses a static device array of the library (see there).
+ *    so calls are safe from several host threads and streams at once.  The exceptions are
+ *    cbk_encode_gpu_noalloc, which uses a static device array of the library, and a GEMV chain,
+ *    whose caller-owned buffer holds the state of its runs (see each).
  *  - Outputs must not alias inputs.
  *  - An index >= U in a (corrupt) stream never causes an out-of-bounds access; the weight it
  *    names reads as 0x7FC0 (a quiet NaN).
@@ -47,7 +48,8 @@ typedef enum {
     CBK_E_CAPACITY = 2,     /* cbk_encode: output word buffer too small (see words_needed)  */
     CBK_E_ALIGN = 3,        /* a device pointer or leading dimension breaks an alignment rule */
     CBK_E_UNSUPPORTED = 4,  /* shape beyond what the kernels accept (see each call)          */
-    CBK_E_HIP = 5           /* the HIP runtime reported an error at launch                   */
+    CBK_E_HIP = 5,          /* the HIP runtime reported an error at launch                   */
+    CBK_E_TIMEOUT = 6       /* a chained launch gave up waiting (cbk_gemv_chain_check)        */
 } cbk_status;
 
 /* A compressed tensor as the GPU calls see it.  Host struct, device pointers. */
@@ -187,6 +189,66 @@ cbk_status cbk_gemv(const cbk_tensor *t, const uint16_t *x, float *y, void *stre
  */
 cbk_status cbk_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x, float *const *ys,
                           void *stream);
+
+/*
+ * GEMV chain -- GPU.  A sequence of dependent grouped GEMVs ("phases", each as cbk_gemv_group)
+ * run by one persistent launch: phase p + 1 reads its x only after every output of phase p is
+ * written, as when x is computed from phase p's outputs (a decode step's [q, k, v] -> [o] ->
+ * [gate, up] -> [down] over its layers).  Each phase's outputs are the cbk_gemv_group results,
+ * bit for bit.
+ * Passage: the DFloat11 page ("No more compromises! DFloat11 ...", section "How it works in
+ * practice"): decompressing a transformer block's matrices together keeps the GPU busy and hides
+ * latency.  The chain carries that across the block's dependent phases: while the last rows of a
+ * phase are decoded, the first weights of the next one are already being read (the weights do not
+ * depend on x), and no launch boundary separates the phases.
+ *
+ * One workgroup per compute unit runs every phase, and the grid meets at a barrier between two
+ * phases.  The launch is cooperative (the runtime places the whole grid before it starts), and
+ * every wait at a barrier is bounded: past timeout_us microseconds of waiting a workgroup records
+ * the failure and stops, the others stop at their next wait, and cbk_gemv_chain_check reports
+ * CBK_E_TIMEOUT (the outputs are then incomplete).  So a run always ends.
+ *
+ * cbk_gemv_chain_bytes(phases) -- device bytes of a chain of that many phases (256 of state plus
+ *   the phase descriptors).
+ * cbk_gemv_chain_init -- host, synchronous.  Validates the phases, plans each over the chain's
+ *   grid and copies the plan into `buffer` (hipMemcpy to the current device).
+ *   phases   host array of count phases.  Every tensor of every phase has the same b (1..15);
+ *            within a phase every tensor has the same cols; cols % 64 == 0, cols <= 32768,
+ *            rows >= 1; codebooks and every x 16-byte aligned; ys[i] 4-byte aligned.
+ *   count    1..65536 phases.
+ *   buffer   device, caller-owned, >= cbk_gemv_chain_bytes(count) bytes, 256-byte aligned; it
+ *            must outlive every run, and holds the chain's barrier state: runs of one chain must
+ *            not overlap (order them on one stream).
+ *   chain    out (host): the handle the other calls take.  The tensors, x and ys are recorded by
+ *            address: they must stay allocated, and their contents are read at each run.
+ *   Errors: CBK_E_INVALID (null pointer, count or a phase's count out of range, differing cols
+ *   within a phase, rows == 0), CBK_E_CAPACITY (buffer too small), CBK_E_ALIGN,
+ *   CBK_E_UNSUPPORTED (differing b across phases, b outside 1..15, cols outside the limits,
+ *   rows * cols / 64 >= 2^32, no cooperative launch on this device or not enough LDS), CBK_E_HIP.
+ * cbk_gemv_chain_run -- GPU.  Enqueues one run of every phase on `stream` (a small kernel that
+ *   clears the barrier state, then the chained kernel), on the device the chain was built on.
+ *   timeout_us bounds each barrier wait (0: give up at once when a wait is needed; a
+ *   million is a safe value for any shape).
+ * cbk_gemv_chain_check -- host, synchronous.  After a run has completed (its stream
+ *   synchronized): CBK_OK if it finished every phase, CBK_E_TIMEOUT if a wait gave up.
+ */
+typedef struct {
+    const cbk_tensor *ts;  /* host array of count tensors (device pointers inside)          */
+    uint32_t count;        /* 1..8                                                          */
+    const uint16_t *x;     /* device, cols BF16 patterns                                    */
+    float *const *ys;      /* host array of count device pointers, ys[i]: ts[i].rows fp32   */
+} cbk_gemv_phase;
+
+typedef struct {           /* filled by cbk_gemv_chain_init; the caller only passes it on   */
+    void *buffer;          /* the caller's device buffer                                    */
+    uint32_t phases, b, grid, lds_bytes, x_bytes, device;
+} cbk_gemv_chain;
+
+size_t cbk_gemv_chain_bytes(uint32_t phases);
+cbk_status cbk_gemv_chain_init(const cbk_gemv_phase *phases, uint32_t count, void *buffer, size_t bytes,
+                               cbk_gemv_chain *chain);
+cbk_status cbk_gemv_chain_run(const cbk_gemv_chain *chain, uint32_t timeout_us, void *stream);
+cbk_status cbk_gemv_chain_check(const cbk_gemv_chain *chain);
 
 /*
  * cbk_gemm_small -- GPU.  Fused decode + skinny GEMM: Y[j][r] = sum_k W[r][k] * X[j][k] for

@@ -107,6 +107,29 @@ static int check_record(const std::vector<uint16_t> &w, uint32_t K, uint64_t rec
         return fail("gemv with a wrong b", rec);
     if (cbk_encode_gpu_noalloc(nullptr, n + 1, nullptr, nullptr, 0, nullptr, nullptr) != CBK_E_INVALID)
         return fail("noalloc encode without pointers", rec);
+    // a GEMV chain of two phases of this tensor (a 64-column row shape when it has any): a buffer
+    // one byte short, a misaligned x, then a phase with a second tensor of other cols
+    if (n && b >= 1 && b <= 15) {
+        t.b = b;
+        cbk_tensor two[2] = {t, t};
+        two[0].rows = 1;
+        two[0].cols = 64;
+        two[1] = two[0];
+        float *ys[2] = {reinterpret_cast<float *>(0x4000), reinterpret_cast<float *>(0x5000)};
+        cbk_gemv_phase ph[2] = {{two, 1, reinterpret_cast<const uint16_t *>(0x3000), ys},
+                                {two, 2, reinterpret_cast<const uint16_t *>(0x3000), ys}};
+        cbk_gemv_chain chain;
+        void *buf = reinterpret_cast<void *>(0x100000);
+        const size_t need = cbk_gemv_chain_bytes(2);
+        if (U > 0 && cbk_gemv_chain_init(ph, 2, buf, need - 1, &chain) != CBK_E_CAPACITY)
+            return fail("chain buffer one byte short", rec);
+        ph[1].x = reinterpret_cast<const uint16_t *>(0x3008);
+        if (U > 0 && cbk_gemv_chain_init(ph, 2, buf, need, &chain) != CBK_E_ALIGN) return fail("chain x misaligned", rec);
+        two[1].cols = 128;
+        ph[1].x = reinterpret_cast<const uint16_t *>(0x3000);
+        if (U > 0 && cbk_gemv_chain_init(ph, 2, buf, need, &chain) != CBK_E_INVALID)
+            return fail("chain phase with differing cols", rec);
+    }
     return 0;
 }
 

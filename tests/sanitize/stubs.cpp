@@ -24,6 +24,10 @@ cbk_status launch_gemm_group(const cbk_tensor *, uint32_t, const uint16_t *, uin
                              const uint64_t *, hipStream_t) {
     reached("gemm_group");
 }
+size_t gemv_chain_bytes(uint32_t phases) { return 256 + size_t(phases) * 320; }
+cbk_status build_gemv_chain(const cbk_gemv_phase *, uint32_t, void *, cbk_gemv_chain *) { reached("gemv_chain"); }
+cbk_status launch_gemv_chain(const cbk_gemv_chain &, uint32_t, hipStream_t) { reached("gemv_chain_run"); }
+cbk_status gemv_chain_check(const cbk_gemv_chain &) { reached("gemv_chain_check"); }
 size_t encode_gpu_workspace_bytes() { return 65536; }
 cbk_status launch_encode_gpu(const uint16_t *, uint64_t, void *, uint16_t *, uint32_t *, uint32_t *, hipStream_t) {
     reached("encode_gpu");

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
               "cbk_words_for", "cbk_compressed_bytes", "cbk_status_str", "cbk_encode_gpu",
               "cbk_encode_gpu_workspace_bytes", "cbk_ec_plan", "cbk_ec_encode", "cbk_ec_decode_bf16",
               "cbk_ec_spans", "cbk_ec_stream_words", "cbk_ec_gap_words", "cbk_ec_blocks",
-              "cbk_ec_stored_bytes", "cbk_cap_patterns", "cbk_ec_gemv", "cbk_encode_gpu_noalloc"]:
+              "cbk_ec_stored_bytes", "cbk_cap_patterns", "cbk_ec_gemv", "cbk_encode_gpu_noalloc",
+              "cbk_gemv_chain_bytes", "cbk_gemv_chain_init", "cbk_gemv_chain_run", "cbk_gemv_chain_check"]:
         assert n in names
 
 
@@ -211,3 +212,44 @@ def test_gpu_encoder_noalloc_validates_before_any_hip_call(cbk):
     assert f(W, 1000, ctypes.c_void_p(0x30001), WD, cap, M, None) == 3   # codebook not 2 B aligned
     assert f(W, 1000, CB, WD, cap - 1, M, None) == 2                    # words_cap too small
     assert f(W, 1 << 40, CB, WD, 1 << 62, M, None) == 4                 # n beyond the limit
+
+
+def test_gemv_chain_validates_before_any_hip_call(cbk):
+    """cbk_gemv_chain_init rejects bad phases and buffers on the host, and the run and check calls
+    reject a missing chain, before any HIP call (no device is present here)."""
+    lib = cbk.load_library()
+    assert lib.cbk_gemv_chain_bytes(0) == 256
+    per = lib.cbk_gemv_chain_bytes(1) - 256
+    assert per > 0 and lib.cbk_gemv_chain_bytes(128) == 256 + 128 * per
+    X, BUF = ctypes.c_void_p(0x4000), ctypes.c_void_p(0x100000)
+    need = lib.cbk_gemv_chain_bytes(2)
+
+    def phase(tensors, x=X, ys=None):
+        arr = (cbk._Tensor * len(tensors))(*tensors)
+        ys = ys or (ctypes.c_void_p * len(tensors))(*[0x8000 + 0x1000 * i for i in range(len(tensors))])
+        return cbk._GemvPhase(arr, len(tensors), x, ys), (arr, ys)
+
+    def init(phs, buf=BUF, nbytes=need):
+        arr = (cbk._GemvPhase * len(phs))(*[p for p, _ in phs])
+        return lib.cbk_gemv_chain_init(arr, len(phs), buf, nbytes, ctypes.byref(cbk._GemvChain()))
+
+    good = lambda rows=4, cols=64, U=5000, b=13: _tensor(cbk, rows, cols, U, b)
+    assert init([phase([good()]), phase([good()])], buf=None) == 1                      # null buffer
+    assert lib.cbk_gemv_chain_init(None, 1, BUF, need, ctypes.byref(cbk._GemvChain())) == 1
+    assert init([]) == 1                                                                # no phases
+    assert init([phase([good()]), phase([good()], x=None)]) == 1                        # null x
+    assert init([phase([good()]), phase([good(cols=64), good(cols=128)])]) == 1         # differing cols
+    assert init([phase([good()]), phase([good(rows=0)])]) == 1                          # empty tensor
+    assert init([phase([good()]), phase([good()] * 9)]) == 1                            # more than 8
+    assert init([phase([good()]), phase([good(U=200, b=8)])]) == 4                      # b differs
+    assert init([phase([good(U=40000, b=16)])]) == 4                                    # b = 16
+    assert init([phase([good(cols=96)])]) == 4                                          # cols % 64
+    assert init([phase([good(cols=32768 + 64)])]) == 4                                  # cols too large
+    assert init([phase([good()]), phase([good()], x=ctypes.c_void_p(0x4008))]) == 3     # x not 16 B
+    assert init([phase([good()], ys=(ctypes.c_void_p * 1)(0x8002))]) == 3               # y not 4 B
+    assert init([phase([good()]), phase([good()])], buf=ctypes.c_void_p(0x100080)) == 3  # buffer not 256 B
+    assert init([phase([good()]), phase([good()])], nbytes=need - 1) == 2               # buffer too small
+    assert lib.cbk_gemv_chain_run(None, 1000, None) == 1
+    assert lib.cbk_gemv_chain_run(ctypes.byref(cbk._GemvChain()), 1000, None) == 1      # never initialised
+    assert lib.cbk_gemv_chain_check(None) == 1
+    assert lib.cbk_status_str(6) == b"a chained launch gave up waiting"
