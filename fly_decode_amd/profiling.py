@@ -176,7 +176,8 @@ def summarize_timed_trace(trace_dir: str, line: dict, out_md: str, title: str, c
               f"| HIP events in the same run (the JSON line) | {float(line['ms_per_step']) * 1e3:.2f} us | "
               f"{line['roofline']['frac']:.4f} |", "",
               f"Algorithmic bytes per step: {int(step_bytes)} ({cfg['workload']}, {cfg['tensors']} tensors)."]
-    pattern = cfg.get("phase_pattern")
+    # (a chained run is one launch per step: no per-phase dispatches to tabulate)
+    pattern = cfg.get("phase_pattern") if cfg.get("launch", "phases") == "phases" else None
     if pattern:
         per = len(pattern)
         lines += ["", "Per launch of a layer (position in the repeating pattern):", "",
