@@ -10,6 +10,8 @@ persistent cooperative launch, through the C ABI.
   CBK_E_TIMEOUT, and the next run with a normal limit completes with the full results.
 * One layer of the 7B- and 70B-shaped steps as bench.py builds them: the chain equals the
   per-phase launches bit for bit.
+* Other index widths (b = 1, 4, 8, 15) on a three-phase chain: bit-equal to the single launches,
+  within tolerance of the oracle.
 
 The oracle's inputs are the same host patterns, encoded by the oracle itself.
 """
@@ -145,3 +147,35 @@ def test_chain_step_layer_equals_phase_launches(env, workload):
     assert work.chain.check() == 0
     for i, y in enumerate(work.ys):
         assert np.array_equal(y.cpu().numpy(), want[i]), f"{work.specs[i][2].name}: chain differs"
+
+
+@pytest.mark.parametrize("distinct", [2, 9, 200, 20000])  # b = 1, 4, 8, 15
+def test_chain_other_widths(env, oracle_mod, distinct):
+    """A three-phase chain (K = 1024, 4096 and 5120: one, one and two wave steps per row) at other
+    index widths: equal to cbk_gemv_group bit for bit and to the oracle within tolerance."""
+    torch, cbk = env
+    shapes = [[(700, 1024), (64, 1024)], [(300, 4096)], [(257, 5120)]]
+    phases, host = [], []
+    for p, group in enumerate(shapes):
+        ws = [synth.with_distinct_count(r * c, distinct, [43, distinct, p, i],
+                                        exponents=synth.finite_exponents(distinct)).reshape(r, c)
+              for i, (r, c) in enumerate(group)]
+        x = synth.activation_bf16(group[0][1], [44, p])
+        ds = [cbk.encode(w).to("cuda") for w in ws]
+        xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+        ys = [torch.full((d.rows,), float("nan"), dtype=torch.float32, device="cuda") for d in ds]
+        phases.append((ds, xd, ys))
+        host.append((ws, x))
+    print(f"chain at b = {phases[0][0][0].b}", flush=True)
+    chain = cbk.GemvChain(phases)
+    chain.run()
+    got = _outputs(torch, phases)
+    assert chain.check() == 0
+    for p, ((ds, xd, _), (ws, x)) in enumerate(zip(phases, host)):
+        single = cbk.gemv_group(ds, xd)
+        torch.cuda.synchronize()
+        for i, (d, s, w) in enumerate(zip(ds, single, ws)):
+            assert np.array_equal(got[p][i], s.cpu().numpy()), f"phase {p} tensor {i}: differs from cbk_gemv_group"
+            rows = np.unique([0, d.rows // 2, d.rows - 1])
+            ref, absb = oracle_mod.gemv(oracle_mod.encode(w[rows]), x)
+            assert np.all(np.abs(got[p][i][rows] - ref) <= TOL * absb)
