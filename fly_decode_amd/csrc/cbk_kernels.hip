@@ -342,11 +342,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *
 
 // -------------------------------------------------------------------------------- fast GEMV
 // Rows are dealt round-robin to the waves of the tensor's workgroups (row gw, gw + NW, ...; see
-// gemv_rows for the dynamic variant), so at any moment the grid reads one contiguous window of the
-// stream, front to back.  A row of P units
-// is S = ceil(P / 64) wave steps; lane l of step j decodes unit 64j + l of the row (the last step
-// is partial when P % 64 != 0), accumulates in registers across the row's steps, and one wave
-// reduction per row produces y.
+// gemv_rows_loop for the dynamic variant), so at any moment the grid reads one contiguous window
+// of the stream, front to back.  A row of P units is S = ceil(P / 64) wave steps; lane l of step j
+// decodes unit 64j + l of the row (the last step is partial when P % 64 != 0), accumulates in
+// registers across the row's steps, and one wave reduction per row produces y.
 //
 // Up to kMaxGroup tensors that share x (same cols and width b) run in one launch: workgroups
 // [first_block[t], first_block[t + 1]) belong to tensor t, so the launch's ramp-up and tail are
@@ -1691,20 +1690,24 @@ struct ChainBuildArgs {
 template <int B>
 struct ChainBuild {
     static bool run(ChainBuildArgs &a) {
+        a.st = build(a);
+        return true;
+    }
+    static cbk_status build(const ChainBuildArgs &a) {
         using G = U64<B>;
         uint64_t pmax = 0;
         for (uint32_t p = 0; p < a.count; ++p) pmax = std::max<uint64_t>(pmax, a.phases[p].ts[0].cols / 64);
         const uint64_t xbytes = pmax * (2 * 64 + 16);
         const uint64_t lds = xbytes + uint64_t(kGemvWaves) * G::STAGE_CHUNKS * 16;
         int dev = 0, coop = 0, occ = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return a.st = CBK_E_HIP, true;
+        if (hipGetDevice(&dev) != hipSuccess) return CBK_E_HIP;
         if (lds + uint64_t(Table<B>::SIZE) * 2 + 16 > kLdsLimit || !allow_lds(k_gemv_chain<B>, static_cast<uint32_t>(lds)))
-            return a.st = CBK_E_UNSUPPORTED, true;
+            return CBK_E_UNSUPPORTED;
         if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv_chain<B>, 64 * kGemvWaves,
                                                          static_cast<size_t>(lds)) != hipSuccess)
-            return a.st = CBK_E_HIP, true;
-        if (!coop || occ < 1) return a.st = CBK_E_UNSUPPORTED, true;
+            return CBK_E_HIP;
+        if (!coop || occ < 1) return CBK_E_UNSUPPORTED;
         const uint32_t grid = static_cast<uint32_t>(cu_count());
         std::vector<unsigned char> host(gemv_chain_bytes(a.count), 0);
         for (uint32_t p = 0; p < a.count; ++p) {
@@ -1713,12 +1716,10 @@ struct ChainBuild {
             c.x = a.phases[p].x;
             std::memcpy(host.data() + sizeof(ChainSync) + size_t(p) * sizeof(ChainPhase), &c, sizeof(c));
         }
-        if (hipMemcpy(a.buffer, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess)
-            return a.st = CBK_E_HIP, true;
+        if (hipMemcpy(a.buffer, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) return CBK_E_HIP;
         *a.chain = cbk_gemv_chain{a.buffer, a.count, static_cast<uint32_t>(B), grid, static_cast<uint32_t>(lds),
                                   static_cast<uint32_t>(xbytes), static_cast<uint32_t>(dev)};
-        a.st = CBK_OK;
-        return true;
+        return CBK_OK;
     }
 };
 
@@ -1733,7 +1734,10 @@ struct ChainLaunch {
         ChainSync *sync = static_cast<ChainSync *>(c.buffer);
         const ChainPhase *ph = reinterpret_cast<const ChainPhase *>(static_cast<unsigned char *>(c.buffer) + sizeof(ChainSync));
         hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(64), 0, a.s, sync);
-        if (hipGetLastError() != hipSuccess) return a.st = CBK_E_HIP, true;
+        if (hipGetLastError() != hipSuccess) {
+            a.st = CBK_E_HIP;
+            return true;
+        }
         uint32_t nph = c.phases, xbytes = c.x_bytes;
         uint64_t limit = a.limit;
         void *args[] = {&ph, &nph, &xbytes, &sync, &limit};
