@@ -486,6 +486,66 @@ __device__ __forceinline__ void gemv_rows_loop(u32x4 (&nxt)[U64<B>::LPL], u32x4 
         return;
     }
 
+    if (!dyn) {
+        // Rows of three or more steps, dealt statically (gw, gw + NW, ...): taken step-major in
+        // groups of up to four rows, so each step's x unit is read from LDS once per group rather
+        // than once per row.  On the 70B down projection (K = 28672, four rows per wave) this took
+        // the launch from 64.1 to 61.6 us.
+        constexpr uint32_t RG = 4;
+        for (uint32_t r0 = gw; r0 < M;) {
+            const uint32_t nr = min(RG, (M - r0 + NW - 1) / NW);  // rows in this group (uniform)
+            float acc[RG][4];
+#pragma unroll
+            for (uint32_t k = 0; k < RG; ++k) acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0.f;
+            for (uint32_t j = 0; j < S; ++j) {
+                const uint32_t cu = 64 * j + lane;  // this lane's unit within the row
+                u32x4 xq[8];
+                if (cu < P) {
+                    const u32x4 *xb = reinterpret_cast<const u32x4 *>(xl + cu * XU);
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) xq[g] = xb[g];
+                }
+#pragma unroll
+                for (uint32_t k = 0; k < RG; ++k) {
+                    if (k < nr) {
+                        const uint32_t r = r0 + k * NW;
+                        uint32_t d[G::UD];
+                        transpose_step<B>(d, nxt, stage, r * P + 64 * j, lane);
+                        // next step of this wave: the group's next row at this step, then its
+                        // first row at the next step, then the next group's first row
+                        uint32_t rn, jn;
+                        if (k + 1 < nr) {
+                            rn = r + NW;
+                            jn = j;
+                        } else if (j + 1 < S) {
+                            rn = r0;
+                            jn = j + 1;
+                        } else {
+                            rn = r0 + nr * NW;
+                            jn = 0;
+                        }
+                        if (rn < M) load_step<B>(nxt, w4, rn * P + 64 * jn, min(64u, P - 64 * jn), ~uint64_t(0), true, lane);
+                        else tail();
+                        if (cu < P) gemv_unit<B>(d, cbl, xq, acc[k]);
+                    }
+                }
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < RG; ++k) {
+                if (k < nr) {
+                    a[0] = acc[k][0];
+                    a[1] = acc[k][1];
+                    a[2] = acc[k][2];
+                    a[3] = acc[k][3];
+                    reduce_row(r0 + k * NW);
+                }
+            }
+            r0 += nr * NW;
+        }
+        return;
+    }
+
+    // rows claimed dynamically: one row at a time
     uint32_t r = gw, j = 0;
     while (true) {
         const uint32_t us = r * P + 64 * j;
