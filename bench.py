@@ -173,7 +173,7 @@ class Workload:
     """A workload's tensors, inputs and outputs on the GPU, and its step (one pass of every phase's
     launch, in order), built exactly as the benchmark times it."""
 
-    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None):
+    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False):
         import torch
         import synth
         import fly_decode_amd as cbk
@@ -210,6 +210,8 @@ class Workload:
             self.enc_meta = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in self.raws]
         else:
             self.tensors = prepare(self.specs, threads, cap=cap)
+        # the span index of the entropy-coded tensors (load-time work, outside the timed step)
+        self.ec_index = [cbk.ec_build_index(t) for t in self.tensors] if (self.ecfmt and ec_index) else None
         self.setup_s = time.perf_counter() - t0
 
         self.xs = {}
@@ -236,9 +238,11 @@ class Workload:
                 i = ph[0]
                 cbk.encode_gpu_launch(self.raws[i], self.ws, self.enc_cb[i], self.enc_words[i], self.enc_meta[i])
             elif self.ecgemv:
-                cbk.ec_gemv(T[ph[0]], xs[T[ph[0]].cols], y=ys[ph[0]])
+                ix = self.ec_index[ph[0]] if self.ec_index else None
+                cbk.ec_gemv(T[ph[0]], xs[T[ph[0]].cols], y=ys[ph[0]], index=ix)
             elif self.ecfmt:
-                cbk.ec_decode_bf16(T[ph[0]], out=ys[ph[0]])
+                ix = self.ec_index[ph[0]] if self.ec_index else None
+                cbk.ec_decode_bf16(T[ph[0]], out=ys[ph[0]], index=ix)
             elif self.batch == 0:
                 cbk.decode_bf16(T[ph[0]], out=ys[ph[0]])
             elif self.batch > 1 and len(ph) == 1:
@@ -288,10 +292,12 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Bytes the method must move per step (the roofline's numerator)."""
         T, b = self.tensors, self.batch
+        # with the span index, its byte per 64-bit span is read too
+        ix = [((d.total_bits + 63) // 64) if self.ec_index else 0 for d in T] if self.ecfmt else None
         if self.ecgemv:  # the stored entropy-coded form + x read, y written
-            return sum(d.stored_bytes + 2 * d.cols + 4 * d.rows for d in T)
+            return sum(d.stored_bytes + k + 2 * d.cols + 4 * d.rows for d, k in zip(T, ix))
         if self.ecfmt:  # the stored entropy-coded form read + the BF16 written
-            return sum(d.stored_bytes + 2 * d.n for d in T)
+            return sum(d.stored_bytes + k + 2 * d.n for d, k in zip(T, ix))
         if b == 0:  # decode: compressed reads + the BF16 written; encode: the reverse
             return sum(d.compressed_bytes + 2 * d.n for d in T)
         # packed indices + codebook + Y for every tensor, X once per launch
@@ -305,7 +311,7 @@ class Workload:
         if self.encode:
             return "k_enc", "cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
         if self.ecfmt:
-            k = "k_ec_gemv" if self.ecgemv else "k_ec_decode"
+            k = ("k_ec_gemv" if self.ecgemv else "k_ec_decode") + ("_ix" if self.ec_index else "")
             return k, k
         if self.batch == 0:
             k = "k_decode_fast"
@@ -525,6 +531,36 @@ def check_encoded(work: Workload, which):
             raise SystemExit(f"GPU encoding of tensor {i} differs from the host encoder")
 
 
+def check_ec(work: Workload, which):
+    """The entropy-coded outputs of the last timed step for tensors `which`: the decode against
+    the host weights (exact); the fused GEMV on 8 sampled rows (first and last included) against the
+    C oracle's GEMV of the same weights, within the tolerance.  Returns the record for the line."""
+    import torch
+    import oracle
+    import synth
+    oracle.build(force=False)
+    worst = 0.0
+    for i in which:
+        cfg, layer, t = work.specs[i]
+        if not work.ecgemv:
+            got = work.ys[i].view(torch.int16).cpu().numpy().view(np.uint16).reshape(t.rows, t.cols)
+            if not np.array_equal(got, synth.workload_tensor(cfg, layer, t)):
+                raise SystemExit(f"entropy-coded decode of tensor {i} is not bit-exact")
+            continue
+        rows = sample_rows(t.rows, 8, [cfg, layer, t.tensor_id, 99])
+        x = synth.workload_x(cfg, t.cols)[0]
+        ref, absb = oracle.gemv(oracle.encode(synth.workload_rows(cfg, layer, t, rows)), x)
+        got = work.ys[i].cpu().numpy().astype(np.float64)[rows]
+        ratio = np.abs(got - ref) / np.maximum(TOL * absb, 1e-300)
+        worst = max(worst, float(ratio.max()))
+        if not np.all(np.abs(got - ref) <= TOL * absb):
+            raise SystemExit(f"entropy-coded GEMV of tensor {i} is outside the tolerance")
+    if work.ecgemv:
+        return {"tensors": len(which), "rows_per_tensor": 8, "worst_err_over_bound": round(worst, 6),
+                "tolerance": "1e-3 * sum_k |W x|"}
+    return {"tensors": len(which), "bit_exact": True}
+
+
 # ------------------------------------------------------------------------- profile summaries
 
 def summarize_trace_main(args):
@@ -574,6 +610,8 @@ def main():
     ap.add_argument("--cap", type=int, default=0, metavar="K",
                     help="lossy: cap every codebook at K entries (cbk_cap_patterns) before encoding")
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
+    ap.add_argument("--ec-index", action="store_true",
+                    help="entropy-coded workloads: build the span index at setup and decode with one walk per span")
     ap.add_argument("--launch", choices=("phases", "chain"), default="phases",
                     help="batch 1: one launch per phase (graph-replayed), or the whole step as one GEMV "
                          "chain (a persistent cooperative launch)")
@@ -626,7 +664,8 @@ def main():
     cbk.load_library()
     threads = host_threads()
     log(f"workload {args.workload}; host threads {threads} of {os.cpu_count()} CPUs")
-    work = Workload(args.workload, count=args.tensors, layers=args.layers, threads=threads, cap=args.cap or None)
+    work = Workload(args.workload, count=args.tensors, layers=args.layers, threads=threads, cap=args.cap or None,
+                    ec_index=args.ec_index)
     if args.no_group:
         work.phases = [[i] for ph in work.phases for i in ph]
     log(f"setup {work.setup_s:.1f} s: {len(work.tensors)} tensors, {len(work.phases)} launches per step, "
@@ -672,6 +711,10 @@ def main():
     if work.encode:
         check_encoded(work, sorted({0, len(work.raws) - 1}))
         log("device encodings of the first and last tensor equal the host encoder's")
+    ec_check = None
+    if work.ecfmt:
+        ec_check = check_ec(work, sorted({0, len(work.tensors) - 1}))
+        log(f"entropy-coded outputs of the first and last tensor checked: {ec_check}")
 
     copy_gbps = copy_bandwidth(args.copy_bytes)
     log(f"device-to-device copy of {args.copy_bytes} B: {copy_gbps:.1f} GB/s (read + write)")
@@ -726,6 +769,7 @@ def main():
             "raw_bf16_bytes_per_step": 2 * n_total,
             "graph_replay": graph is not None,
             "launch": args.launch if work.batch == 1 and not work.ecfmt else "phases",
+            "ec_span_index": bool(work.ec_index) if work.ecfmt else None,
             "launches_per_step": 2 if chain else 3 * launches if work.encode else 2 * launches if work.ecgemv else launches,
             "codebook_cap": args.cap or None,
             "warmup_seconds_min": args.warmup_seconds,
@@ -764,6 +808,8 @@ def main():
     if work.batch > 1:
         result["effective_TFLOPs"] = round(2.0 * work.batch * n_total / step_s / 1e12, 3)
 
+    if ec_check is not None:
+        result["check"] = ec_check
     if not args.no_cpu_baseline and work.batch >= 1 and not work.ecgemv:
         log("CPU baseline (oracle on sampled rows of every tensor) and output check ...")
         result["cpu_baseline"], result["check"] = cpu_baseline(work, args.cpu_rows, args.cpu_seconds, threads)

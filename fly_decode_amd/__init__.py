@@ -18,7 +18,8 @@ import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
            "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
-           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "cap_patterns", "GemvChain"]
+           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "ec_build_index", "cap_patterns",
+           "GemvChain"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # CBK_LIBRARY names another build of the same library (for side-by-side comparisons)
@@ -134,6 +135,16 @@ def load_library():
         lib.cbk_ec_gemv.restype = ctypes.c_int
         lib.cbk_ec_gemv.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_ec_index_bytes.restype = ctypes.c_uint64
+        lib.cbk_ec_index_bytes.argtypes = [ctypes.c_uint64]
+        lib.cbk_ec_build_index.restype = ctypes.c_int
+        lib.cbk_ec_build_index.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_ec_decode_bf16_indexed.restype = ctypes.c_int
+        lib.cbk_ec_decode_bf16_indexed.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p]
+        lib.cbk_ec_gemv_indexed.restype = ctypes.c_int
+        lib.cbk_ec_gemv_indexed.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_uint64,
+                                            ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -487,25 +498,48 @@ def ec_encode(w, rows: int | None = None, cols: int | None = None) -> ECTensor:
     return ECTensor(rows, cols, h.total_bits, list(h.lengths), sm, stream, gaps, bases, lut)
 
 
-def ec_decode_bf16(t: ECTensor, out=None, stream=None):
-    """GPU decode of an ECTensor on the device into a [rows][cols] torch.bfloat16 tensor."""
+def ec_build_index(t: ECTensor, stream=None):
+    """cbk_ec_build_index: the span index of a device ECTensor (a uint8 device tensor, one count per
+    64-bit span of the code stream), for the one-walk ``ec_decode_bf16`` and ``ec_gemv``."""
+    import torch
+    lib = load_library()
+    index = torch.zeros(max(16, int(lib.cbk_ec_index_bytes(t.total_bits))), dtype=torch.uint8, device=t.sm.device)
+    st = t._struct()
+    _check(lib.cbk_ec_build_index(ctypes.byref(st), ctypes.c_void_p(index.data_ptr()), _stream(stream)),
+           "cbk_ec_build_index")
+    return index
+
+
+def ec_decode_bf16(t: ECTensor, out=None, stream=None, index=None):
+    """GPU decode of an ECTensor on the device into a [rows][cols] torch.bfloat16 tensor; with the
+    span index from ``ec_build_index``, one walk per span (cbk_ec_decode_bf16_indexed)."""
     import torch
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device=t.sm.device)
     st = t._struct()
-    _check(load_library().cbk_ec_decode_bf16(ctypes.byref(st), ctypes.c_void_p(out.data_ptr() if out.numel() else None),
-                                             _stream(stream)), "cbk_ec_decode_bf16")
+    outp = ctypes.c_void_p(out.data_ptr() if out.numel() else None)
+    lib = load_library()
+    if index is None:
+        _check(lib.cbk_ec_decode_bf16(ctypes.byref(st), outp, _stream(stream)), "cbk_ec_decode_bf16")
+    else:
+        _check(lib.cbk_ec_decode_bf16_indexed(ctypes.byref(st), ctypes.c_void_p(index.data_ptr()), outp,
+                                              _stream(stream)), "cbk_ec_decode_bf16_indexed")
     return out
 
 
-def ec_gemv(t: ECTensor, x, y=None, stream=None):
-    """Fused decode + GEMV for an ECTensor on the device: x bfloat16[cols] -> float32[rows]."""
+def ec_gemv(t: ECTensor, x, y=None, stream=None, index=None):
+    """Fused decode + GEMV for an ECTensor on the device: x bfloat16[cols] -> float32[rows]; with the
+    span index, one walk per span (cbk_ec_gemv_indexed)."""
     import torch
     if y is None:
         y = torch.empty(t.rows, dtype=torch.float32, device=t.sm.device)
     st = t._struct()
-    _check(load_library().cbk_ec_gemv(ctypes.byref(st), t.rows, t.cols,
-                                      ctypes.c_void_p(x.data_ptr() if x.numel() else None),
-                                      ctypes.c_void_p(y.data_ptr() if y.numel() else None), _stream(stream)),
-           "cbk_ec_gemv")
+    xp = ctypes.c_void_p(x.data_ptr() if x.numel() else None)
+    yp = ctypes.c_void_p(y.data_ptr() if y.numel() else None)
+    lib = load_library()
+    if index is None:
+        _check(lib.cbk_ec_gemv(ctypes.byref(st), t.rows, t.cols, xp, yp, _stream(stream)), "cbk_ec_gemv")
+    else:
+        _check(lib.cbk_ec_gemv_indexed(ctypes.byref(st), ctypes.c_void_p(index.data_ptr()), t.rows, t.cols, xp, yp,
+                                       _stream(stream)), "cbk_ec_gemv_indexed")
     return y

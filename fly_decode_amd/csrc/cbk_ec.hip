@@ -114,14 +114,51 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
                                            false);
 }
 
+// The two-code table, built in LDS by every workgroup from the format's 4,096-entry one-code table
+// (exponent | length << 8 per 12-bit window): entry = first exponent | second exponent << 8 |
+// first length << 16 | both lengths << 20 | count << 24, count 2 when the second code also lies in
+// the 12 bits.  `stage` is 8 KB of LDS for the one-code table, free again on return.  Lengths are
+// clamped to 1..12, so every walk advances (a corrupt table cannot stall it).  All threads of the
+// workgroup call it (two barriers).
+__device__ __forceinline__ void build_multi(const uint16_t *__restrict__ lut, uint32_t *multi, u32x4 *stage,
+                                            uint32_t t) {
+    const uint16_t *single = reinterpret_cast<const uint16_t *>(stage);
+    for (uint32_t i = t; i < kLutEntries / 8; i += kSpansPerBlock) stage[i] = reinterpret_cast<const u32x4 *>(lut)[i];
+    __syncthreads();
+    for (uint32_t v = t; v < kLutEntries; v += kSpansPerBlock) {
+        const uint32_t e1 = single[v], l1 = std::min(std::max(e1 >> 8, 1u), 12u);
+        const uint32_t e2 = single[v >> l1], l2 = std::min(std::max(e2 >> 8, 1u), 12u);
+        const bool two = l1 + l2 <= CBK_EC_MAX_LEN;
+        multi[v] = (e1 & 0xFFu) | (two ? (e2 & 0xFFu) << 8 : 0u) | (l1 << 16) | ((two ? l1 + l2 : l1) << 20) |
+                   ((two ? 2u : 1u) << 24);
+    }
+    __syncthreads();
+}
+
+// The number of codes that start in a span: the walk from its gap to its end (end <= 64 bits).
+// While the whole 12-bit window lies before the span's end, both codes of a lookup start inside
+// the span; the last few bits go one code at a time.  Every step advances at least one bit per
+// code, so no span yields more than 64 codes.
+__device__ __forceinline__ uint32_t count_span(const uint32_t *multi, uint32_t w0, uint32_t w1, uint32_t w2,
+                                               uint32_t gap, uint32_t end) {
+    uint32_t cnt = 0, pos = gap;
+    for (; pos + CBK_EC_MAX_LEN <= end;) {
+        const uint32_t m = multi[window12(w0, w1, w2, pos)];
+        cnt += m >> 24;
+        pos += (m >> 20) & 15u;
+    }
+    for (; pos < end; ++cnt) pos += (multi[window12(w0, w1, w2, pos)] >> 16) & 15u;
+    return cnt;
+}
+
 // GEMV == false: decode to BF16 in out.  GEMV == true: y[r] += sum of W[r][k] x[k] over the
 // block's weights, per row in LDS first, then one global atomic add per row the block touches.
-template <bool GEMV>
+template <bool GEMV, bool IX>
 __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const uint32_t *__restrict__ stream,
                                           const uint32_t *__restrict__ gaps, const uint32_t *__restrict__ bases,
-                                          const uint16_t *__restrict__ lut, uint16_t *__restrict__ out,
-                                          EcGemvOut gv, uint64_t n, uint64_t total_bits, uint32_t spans,
-                                          uint32_t blocks) {
+                                          const uint16_t *__restrict__ lut, const uint8_t *__restrict__ index,
+                                          uint16_t *__restrict__ out, EcGemvOut gv, uint64_t n, uint64_t total_bits,
+                                          uint32_t spans, uint32_t blocks) {
     // two codes per lookup: entry = first exponent | second exponent << 8 | first length << 16 |
     // both lengths << 20 | count << 24, count 2 when the second code also lies in the 12 bits
     __shared__ uint32_t multi[kLutEntries];
@@ -135,21 +172,9 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
 
     // the format's one-code table goes through the (still unused) exponent array
     static_assert(sizeof(exps8) >= kLutEntries * 2, "table staging fits the exponent array");
-    const uint16_t *single = reinterpret_cast<const uint16_t *>(exps8);
-    for (uint32_t i = t; i < kLutEntries / 8; i += kSpansPerBlock)
-        reinterpret_cast<u32x4 *>(exps8)[i] = reinterpret_cast<const u32x4 *>(lut)[i];
     if constexpr (GEMV)
         for (uint32_t i = t; i < kGemvBlockRows; i += kSpansPerBlock) row_sum[i] = 0.f;
-    __syncthreads();
-    // lengths are clamped to 1..12, so every walk below advances (a corrupt table cannot stall it)
-    for (uint32_t v = t; v < kLutEntries; v += kSpansPerBlock) {
-        const uint32_t e1 = single[v], l1 = std::min(std::max(e1 >> 8, 1u), 12u);
-        const uint32_t e2 = single[v >> l1], l2 = std::min(std::max(e2 >> 8, 1u), 12u);
-        const bool two = l1 + l2 <= CBK_EC_MAX_LEN;
-        multi[v] = (e1 & 0xFFu) | (two ? (e2 & 0xFFu) << 8 : 0u) | (l1 << 16) | ((two ? l1 + l2 : l1) << 20) |
-                   ((two ? 2u : 1u) << 24);
-    }
-    __syncthreads();
+    build_multi(lut, multi, reinterpret_cast<u32x4 *>(exps8), t);
 
     const uint64_t stream_bytes = 8 * static_cast<uint64_t>(spans);
     const uint64_t gap_bytes = 4 * ((static_cast<uint64_t>(spans) + 7) / 8);
@@ -161,6 +186,7 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
     struct BlockIn {
         u32x2 ab;
         uint32_t c, gword;
+        uint32_t cnt;  // IX: the span's code count from the index
         uint64_t base;
         u32x2 smp[kJoinAhead];  // sm bytes of the block's first kJoinAhead segments per thread
         // GEMV: x under those segments and their rows
@@ -181,6 +207,13 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
         const __amdgpu_buffer_rsrc_t rg = rsrc(reinterpret_cast<const uint8_t *>(gaps) + (live ? gw0 : 0),
                                                live ? std::min<uint64_t>(gap_bytes - gw0, kSpansPerBlock / 2) : 0);
         in.gword = __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>((t / 8) * 4), 0, 0);
+        in.cnt = 0;
+        if constexpr (IX) {
+            const uint64_t i0 = static_cast<uint64_t>(k) * kSpansPerBlock;
+            const __amdgpu_buffer_rsrc_t ri = rsrc(index + (live ? i0 : 0),
+                                                   live ? std::min<uint64_t>(spans - i0, kSpansPerBlock) : 0);
+            in.cnt = __builtin_amdgcn_raw_buffer_load_b8(ri, static_cast<int>(t), 0, kStreamOnce);
+        }
         in.base = base;
         const uint64_t m0 = (base / 8) * 8;
         const uint64_t m1 = std::min<uint64_t>((std::min(limit, n) + 7) / 8 * 8, sm_bytes);
@@ -220,17 +253,14 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
         }
         const uint32_t w0 = cur.ab.x, w1 = cur.ab.y, w2 = cur.c;
 
-        // phase 1: how many codes start in this span.  While the whole 12-bit window lies before
-        // the span's end, both codes of a lookup start inside the span; the last few bits go one
-        // code at a time.  Every step advances at least one bit per code, so no span yields more
-        // than 64 codes.
-        uint32_t cnt = 0, pos = gap;
-        for (; pos + CBK_EC_MAX_LEN <= end;) {
-            const uint32_t m = multi[window12(w0, w1, w2, pos)];
-            cnt += m >> 24;
-            pos += (m >> 20) & 15u;
-        }
-        for (; pos < end; ++cnt) pos += (multi[window12(w0, w1, w2, pos)] >> 16) & 15u;
+        // phase 1: how many codes start in this span, walked, or read from the index (a count
+        // above 64 can only come from a wrong index; clamped, every write below stays in the
+        // exponent array and the block's range)
+        uint32_t cnt;
+        if constexpr (IX)
+            cnt = j < spans ? std::min(cur.cnt, static_cast<uint32_t>(kMaxPerSpan)) : 0u;
+        else
+            cnt = count_span(multi, w0, w1, w2, gap, end);
 
         // prefix sum of the counts over the workgroup
         const uint32_t incl = wave_scan(cnt);
@@ -244,8 +274,8 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
         }
         uint32_t at = static_cast<uint32_t>(base & 7) + before + incl - cnt;
 
-        // phase 2: the same walk again, exponents to their places
-        pos = gap;
+        // phase 2: the walk again (the only one with the index), exponents to their places
+        uint32_t pos = gap;
         for (; pos + CBK_EC_MAX_LEN <= end;) {
             const uint32_t m = multi[window12(w0, w1, w2, pos)];
             exps[at] = static_cast<uint8_t>(m);
@@ -369,24 +399,45 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
     }
 }
 
-__global__ __launch_bounds__(kSpansPerBlock) void k_ec_decode(const uint8_t *__restrict__ sm,
-                                                              const uint32_t *__restrict__ stream,
-                                                              const uint32_t *__restrict__ gaps,
-                                                              const uint32_t *__restrict__ bases,
-                                                              const uint16_t *__restrict__ lut,
-                                                              uint16_t *__restrict__ out, EcGemvOut gv, uint64_t n,
-                                                              uint64_t total_bits, uint32_t spans, uint32_t blocks) {
-    ec_blocks<false>(sm, stream, gaps, bases, lut, out, gv, n, total_bits, spans, blocks);
-}
+#define CBK_EC_KERNEL(NAME, GEMV, IX)                                                                           \
+    __global__ __launch_bounds__(kSpansPerBlock) void NAME(                                                     \
+        const uint8_t *__restrict__ sm, const uint32_t *__restrict__ stream, const uint32_t *__restrict__ gaps, \
+        const uint32_t *__restrict__ bases, const uint16_t *__restrict__ lut, uint16_t *__restrict__ out,       \
+        EcGemvOut gv, uint64_t n, uint64_t total_bits, uint32_t spans, uint32_t blocks,                         \
+        const uint8_t *__restrict__ index) {                                                                    \
+        ec_blocks<GEMV, IX>(sm, stream, gaps, bases, lut, index, out, gv, n, total_bits, spans, blocks);       \
+    }
+// decode to BF16 and the fused GEMV, each with two walks per span or one walk and the span index
+CBK_EC_KERNEL(k_ec_decode, false, false)
+CBK_EC_KERNEL(k_ec_gemv, true, false)
+CBK_EC_KERNEL(k_ec_decode_ix, false, true)
+CBK_EC_KERNEL(k_ec_gemv_ix, true, true)
+#undef CBK_EC_KERNEL
 
-__global__ __launch_bounds__(kSpansPerBlock) void k_ec_gemv(const uint8_t *__restrict__ sm,
-                                                            const uint32_t *__restrict__ stream,
-                                                            const uint32_t *__restrict__ gaps,
-                                                            const uint32_t *__restrict__ bases,
-                                                            const uint16_t *__restrict__ lut,
-                                                            uint16_t *__restrict__ out, EcGemvOut gv, uint64_t n,
-                                                            uint64_t total_bits, uint32_t spans, uint32_t blocks) {
-    ec_blocks<true>(sm, stream, gaps, bases, lut, out, gv, n, total_bits, spans, blocks);
+// The span index: the table walk of phase 1 over every span, its count stored as a byte.
+__global__ __launch_bounds__(kSpansPerBlock) void k_ec_index(const uint32_t *__restrict__ stream,
+                                                             const uint32_t *__restrict__ gaps,
+                                                             const uint16_t *__restrict__ lut, uint8_t *__restrict__ index,
+                                                             uint64_t total_bits, uint32_t spans, uint32_t blocks) {
+    __shared__ uint32_t multi[kLutEntries];
+    __shared__ u32x4 stage[kLutEntries / 8];
+    const uint32_t t = threadIdx.x;
+    build_multi(lut, multi, stage, t);
+    const uint64_t stream_bytes = 8 * static_cast<uint64_t>(spans);
+    for (uint32_t k = blockIdx.x; k < blocks; k += gridDim.x) {
+        const uint64_t j = static_cast<uint64_t>(k) * kSpansPerBlock + t;
+        const uint64_t sw0 = static_cast<uint64_t>(k) * kSpansPerBlock * 8;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(reinterpret_cast<const uint8_t *>(stream) + sw0,
+                                               std::min<uint64_t>(stream_bytes - sw0, kSpansPerBlock * 8 + 4));
+        const u32x2 ab = __builtin_amdgcn_raw_buffer_load_b64(rs, static_cast<int>(t * 8), 0, kStreamOnce);
+        const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(t * 8 + 8), 0, kStreamOnce);
+        if (j < spans) {
+            const uint32_t gap = (gaps[j / 8] >> (4 * (j % 8))) & 15u;
+            const uint64_t rem = total_bits - j * CBK_EC_SPAN_BITS;
+            const uint32_t end = rem < CBK_EC_SPAN_BITS ? static_cast<uint32_t>(rem) : CBK_EC_SPAN_BITS;
+            index[j] = static_cast<uint8_t>(count_span(multi, ab.x, ab.y, c, gap, end));
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_ec_zero(float *__restrict__ y, uint64_t rows) {
@@ -395,45 +446,62 @@ __global__ __launch_bounds__(256) void k_ec_zero(float *__restrict__ y, uint64_t
         y[i] = 0.f;
 }
 
-template <bool GEMV>
-cbk_status launch_ec(const cbk_ec_tensor *t, uint16_t *out, EcGemvOut gv, hipStream_t s) {
-    const uint64_t spans = (t->total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
-    const uint64_t blocks = (spans + kSpansPerBlock - 1) / kSpansPerBlock;
+// As many workgroups as fit the CUs at once (LDS bound); they loop over the blocks, so the tables
+// are built once per workgroup and the next block's loads overlap the current block's output.
+template <typename K>
+cbk_status resident_grid(K kernel, uint64_t blocks, std::atomic<int> (&per_cu)[64], uint32_t &grid) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return CBK_E_HIP;
-    // as many workgroups as fit the CUs at once (LDS bound); they loop over the blocks, so the
-    // tables are built once per workgroup and the next block's loads overlap the current block's
-    // output
     // (the per-device count is queried once; concurrent first calls store the same value)
-    static std::atomic<int> per_cu[64];
     if (dev < 0 || dev >= 64) return CBK_E_HIP;
     int occ = per_cu[dev].load(std::memory_order_relaxed);
     if (occ <= 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, GEMV ? k_ec_gemv : k_ec_decode, kSpansPerBlock, 0) !=
-                hipSuccess ||
-            occ <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kSpansPerBlock, 0) != hipSuccess || occ <= 0)
             return CBK_E_HIP;
         per_cu[dev].store(occ, std::memory_order_relaxed);
     }
-    const uint32_t grid = static_cast<uint32_t>(
-        std::max<uint64_t>(1, std::min<uint64_t>(blocks, static_cast<uint64_t>(occ) * cus)));
-    hipLaunchKernelGGL(GEMV ? k_ec_gemv : k_ec_decode, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream,
-                       t->gaps, t->bases,
-                       t->lut, out, gv, t->n, t->total_bits, static_cast<uint32_t>(spans),
-                       static_cast<uint32_t>(blocks));
+    grid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(blocks, static_cast<uint64_t>(occ) * cus)));
+    return CBK_OK;
+}
+
+template <bool GEMV, bool IX>
+cbk_status launch_ec(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, EcGemvOut gv, hipStream_t s) {
+    const uint64_t spans = (t->total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
+    const uint64_t blocks = (spans + kSpansPerBlock - 1) / kSpansPerBlock;
+    auto kernel = GEMV ? (IX ? k_ec_gemv_ix : k_ec_gemv) : (IX ? k_ec_decode_ix : k_ec_decode);
+    static std::atomic<int> per_cu[64];
+    uint32_t grid = 0;
+    const cbk_status st = resident_grid(kernel, blocks, per_cu, grid);
+    if (st != CBK_OK) return st;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream, t->gaps, t->bases, t->lut,
+                       out, gv, t->n, t->total_bits, static_cast<uint32_t>(spans), static_cast<uint32_t>(blocks),
+                       index);
     return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
 }
 
 }  // namespace
 
-cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s) {
-    return launch_ec<false>(t, out, EcGemvOut{nullptr, nullptr, 1, 1, 0, 0}, s);
+cbk_status launch_ec_decode(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, hipStream_t s) {
+    const EcGemvOut none{nullptr, nullptr, 1, 1, 0, 0};
+    return index ? launch_ec<false, true>(t, index, out, none, s) : launch_ec<false, false>(t, nullptr, out, none, s);
 }
 
-cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
-                          hipStream_t s) {
+cbk_status launch_ec_index(const cbk_ec_tensor *t, uint8_t *index, hipStream_t s) {
+    const uint64_t spans = (t->total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
+    const uint64_t blocks = (spans + kSpansPerBlock - 1) / kSpansPerBlock;
+    static std::atomic<int> per_cu[64];
+    uint32_t grid = 0;
+    const cbk_status st = resident_grid(k_ec_index, blocks, per_cu, grid);
+    if (st != CBK_OK) return st;
+    hipLaunchKernelGGL(k_ec_index, dim3(grid), dim3(kSpansPerBlock), 0, s, t->stream, t->gaps, t->lut, index,
+                       t->total_bits, static_cast<uint32_t>(spans), static_cast<uint32_t>(blocks));
+    return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
+}
+
+cbk_status launch_ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
+                          const uint16_t *x, float *y, hipStream_t s) {
     // y is accumulated with atomics, so it starts from zeros (a fill kernel, which graph capture
     // records as an ordinary node)
     const uint32_t zgrid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>((rows + 255) / 256, 1024)));
@@ -444,10 +512,8 @@ cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, 
     uint32_t l = 0;
     while ((uint64_t(1) << l) < cols) ++l;
     const uint32_t magic = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << l) - cols)) / cols + 1);
-    return launch_ec<true>(t, nullptr,
-                           EcGemvOut{x, y, static_cast<uint32_t>(cols), magic, std::min<uint32_t>(l, 1),
-                                     l > 0 ? l - 1 : 0},
-                           s);
+    const EcGemvOut gv{x, y, static_cast<uint32_t>(cols), magic, std::min<uint32_t>(l, 1), l > 0 ? l - 1 : 0};
+    return index ? launch_ec<true, true>(t, index, nullptr, gv, s) : launch_ec<true, false>(t, nullptr, nullptr, gv, s);
 }
 
 }  // namespace cbk

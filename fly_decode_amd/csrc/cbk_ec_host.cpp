@@ -188,21 +188,33 @@ cbk_status cbk_ec_encode(const uint16_t *w, const cbk_ec_header *h, uint8_t *sm,
     return CBK_OK;
 }
 
-cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *stream) {
+// Validation shared by the GPU calls of a tensor with n > 0 weights (stream, gaps, bases, table and
+// sign-mantissa bytes present, aligned and consistent with n).
+static cbk_status check_ec_arrays(const cbk_ec_tensor *t) {
+    const uint64_t n = t->n;
+    if (!t->sm || !t->stream || !t->gaps || !t->bases || !t->lut) return CBK_E_INVALID;
+    if (t->total_bits < n || t->total_bits > uint64_t(CBK_EC_MAX_LEN) * n) return CBK_E_INVALID;
+    if (!aligned16(t->sm) || !aligned16(t->stream) || !aligned16(t->gaps) || !aligned16(t->bases) ||
+        !aligned16(t->lut))
+        return CBK_E_ALIGN;
+    return CBK_OK;
+}
+
+static cbk_status ec_decode(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint16_t *out,
+                            void *stream) {
     if (!t) return CBK_E_INVALID;
     const uint64_t n = t->n;
     if (n >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
     if (n == 0) return CBK_OK;
-    if (!out || !t->sm || !t->stream || !t->gaps || !t->bases || !t->lut) return CBK_E_INVALID;
-    if (t->total_bits < n || t->total_bits > uint64_t(CBK_EC_MAX_LEN) * n) return CBK_E_INVALID;
-    if (!aligned16(out) || !aligned16(t->sm) || !aligned16(t->stream) || !aligned16(t->gaps) ||
-        !aligned16(t->bases) || !aligned16(t->lut))
-        return CBK_E_ALIGN;
-    return cbk::launch_ec_decode(t, out, static_cast<hipStream_t>(stream));
+    if (!out || (indexed && !index)) return CBK_E_INVALID;
+    const cbk_status st = check_ec_arrays(t);
+    if (st != CBK_OK) return st;
+    if (!aligned16(out) || (indexed && !aligned16(index))) return CBK_E_ALIGN;
+    return cbk::launch_ec_decode(t, indexed ? index : nullptr, out, static_cast<hipStream_t>(stream));
 }
 
-cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
-                       void *stream) {
+static cbk_status ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint64_t rows, uint64_t cols,
+                          const uint16_t *x, float *y, void *stream) {
     if (!t) return CBK_E_INVALID;
     const uint64_t n = t->n;
     if (n >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
@@ -213,13 +225,47 @@ cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, con
     if ((reinterpret_cast<uintptr_t>(y) & 3u) != 0) return CBK_E_ALIGN;
     if (n > 0) {
         if (cols % 8 != 0 || cols < 64) return CBK_E_UNSUPPORTED;
-        if (!t->sm || !t->stream || !t->gaps || !t->bases || !t->lut) return CBK_E_INVALID;
-        if (t->total_bits < n || t->total_bits > uint64_t(CBK_EC_MAX_LEN) * n) return CBK_E_INVALID;
-        if (!aligned16(x) || !aligned16(t->sm) || !aligned16(t->stream) || !aligned16(t->gaps) ||
-            !aligned16(t->bases) || !aligned16(t->lut))
-            return CBK_E_ALIGN;
+        if (indexed && !index) return CBK_E_INVALID;
+        const cbk_status st = check_ec_arrays(t);
+        if (st != CBK_OK) return st;
+        if (!aligned16(x) || (indexed && !aligned16(index))) return CBK_E_ALIGN;
     }
-    return cbk::launch_ec_gemv(t, rows, cols, x, y, static_cast<hipStream_t>(stream));
+    return cbk::launch_ec_gemv(t, indexed ? index : nullptr, rows, cols, x, y, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *stream) {
+    return ec_decode(t, nullptr, false, out, stream);
+}
+
+cbk_status cbk_ec_decode_bf16_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, void *stream) {
+    return ec_decode(t, index, true, out, stream);
+}
+
+cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
+                       void *stream) {
+    return ec_gemv(t, nullptr, false, rows, cols, x, y, stream);
+}
+
+cbk_status cbk_ec_gemv_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
+                               const uint16_t *x, float *y, void *stream) {
+    return ec_gemv(t, index, true, rows, cols, x, y, stream);
+}
+
+uint64_t cbk_ec_index_bytes(uint64_t total_bits) {
+    const uint64_t spans = (total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
+    return (spans + 15) / 16 * 16;
+}
+
+cbk_status cbk_ec_build_index(const cbk_ec_tensor *t, uint8_t *index, void *stream) {
+    if (!t) return CBK_E_INVALID;
+    const uint64_t n = t->n;
+    if (n >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
+    if (n == 0) return CBK_OK;
+    if (!index) return CBK_E_INVALID;
+    const cbk_status st = check_ec_arrays(t);
+    if (st != CBK_OK) return st;
+    if (!aligned16(index)) return CBK_E_ALIGN;
+    return cbk::launch_ec_index(t, index, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

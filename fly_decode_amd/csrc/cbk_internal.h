@@ -33,8 +33,10 @@ cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uin
 cbk_status encode_gpu_scratch(void **ws);
 
 // Exponent entropy-coded format (cbk_ec.hip).
-cbk_status launch_ec_decode(const cbk_ec_tensor *t, uint16_t *out, hipStream_t s);
-cbk_status launch_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
-                          hipStream_t s);
+// index: the span index (cbk_ec_build_index), or null for the two-walk decode.
+cbk_status launch_ec_decode(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, hipStream_t s);
+cbk_status launch_ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
+                          const uint16_t *x, float *y, hipStream_t s);
+cbk_status launch_ec_index(const cbk_ec_tensor *t, uint8_t *index, hipStream_t s);
 
 }  // namespace cbk

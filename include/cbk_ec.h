@@ -118,6 +118,28 @@ cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *strea
 cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, const uint16_t *x, float *y,
                        void *stream);
 
+/*
+ * Span index -- a derived structure built once at load time, not part of the stored format.
+ * Byte j is the number of codes that start in span j (0..64): what the decoder's first walk over
+ * the span counts.  The per-block output positions (bases) come from the same kind of count; the
+ * index carries it down to each span, so the decode and the fused GEMV below walk each span once
+ * instead of twice, for one more byte per 64 stream bits read.
+ *
+ * cbk_ec_index_bytes(total_bits) -- bytes of a tensor's index: its spans, rounded up to 16.
+ * cbk_ec_build_index -- GPU.  Writes the index of t (one walk over every span with the table).
+ *   index   out, device, cbk_ec_index_bytes(t->total_bits) bytes, 16-byte aligned, caller-owned.
+ *   Errors: as cbk_ec_decode_bf16 (NULL index with n > 0 gives CBK_E_INVALID).
+ * cbk_ec_decode_bf16_indexed, cbk_ec_gemv_indexed -- GPU.  As cbk_ec_decode_bf16 and cbk_ec_gemv,
+ *   bit for bit, with the index that cbk_ec_build_index wrote for t (device, 16-byte aligned).  An
+ *   index that does not match the stream gives wrong values but no access outside the arrays:
+ *   counts above 64 are read as 64, and each block writes only weights below n.
+ */
+uint64_t cbk_ec_index_bytes(uint64_t total_bits);
+cbk_status cbk_ec_build_index(const cbk_ec_tensor *t, uint8_t *index, void *stream);
+cbk_status cbk_ec_decode_bf16_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, void *stream);
+cbk_status cbk_ec_gemv_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
+                               const uint16_t *x, float *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

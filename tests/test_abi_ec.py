@@ -134,3 +134,31 @@ def test_gemv_validates_before_any_hip_call(cbk):
     assert call(x=A + 2) == 3 and call(y=A + 2) == 3
     assert call(n=0, rows=0, cols=64, x=0, y=0) == 0  # nothing to do
     assert call(n=0, rows=8, cols=0, x=0, y=0) == 1   # rows to write need y, even with no columns
+
+
+def test_span_index_calls_validate_before_any_hip_call(cbk):
+    """cbk_ec_build_index and the indexed decode and GEMV reject bad arguments on the host, with the
+    same codes as the calls without the index plus a missing or misaligned index."""
+    lib = cbk.load_library()
+    T = cbk._ECTensor
+    A = 0x10000   # 16-byte aligned stand-ins; nothing is dereferenced on these paths
+    for bits in [0, 1, 64, 65, 64 * 16, 64 * 16 + 1]:
+        spans = (bits + 63) // 64
+        assert lib.cbk_ec_index_bytes(bits) == (spans + 15) // 16 * 16
+    t = T(n=1000, total_bits=3000, sm=A, stream=A, gaps=A, bases=A, lut=A)
+    v = ctypes.c_void_p
+    assert lib.cbk_ec_build_index(None, v(A), None) == 1
+    assert lib.cbk_ec_build_index(ctypes.byref(t), None, None) == 1
+    assert lib.cbk_ec_build_index(ctypes.byref(t), v(A + 1), None) == 3
+    assert lib.cbk_ec_build_index(ctypes.byref(T(n=1000, total_bits=999, sm=A, stream=A, gaps=A, bases=A, lut=A)),
+                                  v(A), None) == 1
+    assert lib.cbk_ec_build_index(ctypes.byref(T(n=0, total_bits=0)), None, None) == 0   # empty: no-op
+    assert lib.cbk_ec_decode_bf16_indexed(ctypes.byref(t), None, v(A), None) == 1
+    assert lib.cbk_ec_decode_bf16_indexed(ctypes.byref(t), v(A + 8), v(A), None) == 3
+    assert lib.cbk_ec_decode_bf16_indexed(ctypes.byref(t), v(A), None, None) == 1
+    assert lib.cbk_ec_decode_bf16_indexed(ctypes.byref(t), v(A), v(A + 2), None) == 3
+    g = T(n=6400, total_bits=3 * 6400, sm=A, stream=A, gaps=A, bases=A, lut=A)
+    assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), None, 100, 64, v(A), v(A), None) == 1
+    assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), v(A + 4), 100, 64, v(A), v(A), None) == 3
+    assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), v(A), 99, 64, v(A), v(A), None) == 1
+    assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), v(A), 200, 32, v(A), v(A), None) == 4

@@ -212,3 +212,86 @@ def test_ec_decode_empty_tensor(env):
     out = cbk.ec_decode_bf16(d)
     torch.cuda.synchronize()
     assert out.numel() == 0
+
+
+# ---------------------------------------------------------------- span index (one walk per span)
+def _oracle_span_counts(t_host, w):
+    """Codes that start in each span, from the oracle's span decoder on its own encoding."""
+    o = ec.encode_with_lengths(w, t_host.lengths)
+    return np.array([len(ec.decode_span(o, j)) for j in range(o.spans)], dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["gaussian_300x777", "t2_heavy_tail", "constant", "two_exponents", "specials", "one"])
+def test_ec_index_counts_equal_the_oracle(env, name):
+    torch, cbk = env
+    w = _cases()[name]
+    t = cbk.ec_encode(w)
+    d = t.to("cuda")
+    index = cbk.ec_build_index(d)
+    torch.cuda.synchronize()
+    want = _oracle_span_counts(t, w)
+    got = index.cpu().numpy()[: want.size].astype(np.int64)
+    assert np.array_equal(got, want)
+    assert int(got.sum()) == w.size  # every code starts in exactly one span
+
+
+@pytest.mark.parametrize("name", list(_cases()))
+def test_ec_indexed_decode_bit_exact(env, name):
+    torch, cbk = env
+    w = _cases()[name]
+    print(f"ec indexed decode {name}", flush=True)
+    d = cbk.ec_encode(w).to("cuda")
+    out = cbk.ec_decode_bf16(d, index=cbk.ec_build_index(d))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape), w)
+
+
+@pytest.mark.parametrize("n", [7, 64, 65, 16384, 16385, 64 * 256 * 3 + 11])
+def test_ec_indexed_decode_ragged_lengths_and_guard(env, n):
+    torch, cbk = env
+    w = synth.gaussian_bf16((1, n), 0.02, seed=[57, n])
+    d = cbk.ec_encode(w).to("cuda")
+    index = cbk.ec_build_index(d)
+    buf = torch.full((n + 64,), -7, dtype=torch.int16, device="cuda")
+    cbk.ec_decode_bf16(d, out=buf[:n].view(torch.bfloat16).view(1, n), index=index)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:n].view(np.uint16), w.reshape(-1))
+    assert bool((got[n:] == -7).all())
+
+
+def test_ec_indexed_decode_workload_tensor(env):
+    torch, cbk = env
+    w = synth.workload_tensor(2, 0, synth.WORKLOADS[2][0][0])
+    d = cbk.ec_encode(w).to("cuda")
+    out = cbk.ec_decode_bf16(d, index=cbk.ec_build_index(d))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape), w)
+
+
+@pytest.mark.parametrize("name", list(_gemv_cases()))
+def test_ec_indexed_gemv_matches_oracle(env, name):
+    torch, cbk = env
+    w = _gemv_cases()[name]
+    x = synth.activation_bf16(w.shape[1], seed=[55, w.shape[1]])
+    d = cbk.ec_encode(w).to("cuda")
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+    y = cbk.ec_gemv(d, xd, index=cbk.ec_build_index(d))
+    torch.cuda.synchronize()
+    ref, absb = ec.gemv(ec.encode(w), w.shape[0], w.shape[1], x)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= TOL * absb), f"max err/bound {np.max(err / np.maximum(absb, 1e-300))}"
+
+
+def test_ec_wrong_index_stays_in_bounds(env):
+    """An index whose counts do not match the stream (every count 255, read as 64): the values are
+    undefined, but nothing is written outside the output."""
+    torch, cbk = env
+    n = 64 * 256 * 2 + 100
+    w = synth.gaussian_bf16((1, n), 0.02, seed=[58])
+    d = cbk.ec_encode(w).to("cuda")
+    index = torch.full_like(cbk.ec_build_index(d), 255)
+    buf = torch.full((n + 64,), -7, dtype=torch.int16, device="cuda")
+    cbk.ec_decode_bf16(d, out=buf[:n].view(torch.bfloat16).view(1, n), index=index)
+    torch.cuda.synchronize()
+    assert bool((buf[n:].cpu() == -7).all())
