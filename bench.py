@@ -20,7 +20,9 @@ each tensor with its own codebook):
   attn4096   24 distinct 4096x4096 attention projections, N(0, 0.02), one cbk_gemv launch each.
   decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors.
   ecdecode4096 / ecgemv4096  the attn4096 tensors in the exponent entropy-coded format, decoded to
-             HBM (cbk_ec_decode_bf16) or decoded inside the batch-1 GEMV (cbk_ec_gemv).
+             HBM (cbk_ec_decode_group, four tensors per launch, a layer's [q, k, v, o]) or decoded
+             inside the batch-1 GEMV (cbk_ec_gemv_group, three per launch, a layer's [q, k, v]);
+             --ec-group 1 launches each tensor alone, --ec-index adds the span index.
   encode4096 cbk_encode_gpu of the attn4096 tensors from raw BF16 in HBM (three launches each).
 
 The step workloads (l70b_*, llama7b) draw their weights on the GPU with the counter-based
@@ -173,7 +175,7 @@ class Workload:
     """A workload's tensors, inputs and outputs on the GPU, and its step (one pass of every phase's
     launch, in order), built exactly as the benchmark times it."""
 
-    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False):
+    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False, ec_group=0):
         import torch
         import synth
         import fly_decode_amd as cbk
@@ -183,6 +185,11 @@ class Workload:
         self.encode = name == "encode4096"
         self.ecfmt = name in ("ecdecode4096", "ecgemv4096")
         self.ecgemv = name == "ecgemv4096"
+        if self.ecfmt:
+            # a layer's matrices decoded together: [q, k, v, o] for the decode, the [q, k, v] that
+            # share x for the fused GEMV
+            g = ec_group or (3 if self.ecgemv else 4)
+            self.phases = [list(range(i, min(i + g, len(self.specs)))) for i in range(0, len(self.specs), g)]
         threads = threads or host_threads()
         t0 = time.perf_counter()
         if tensors is not None:
@@ -238,11 +245,17 @@ class Workload:
                 i = ph[0]
                 cbk.encode_gpu_launch(self.raws[i], self.ws, self.enc_cb[i], self.enc_words[i], self.enc_meta[i])
             elif self.ecgemv:
-                ix = self.ec_index[ph[0]] if self.ec_index else None
-                cbk.ec_gemv(T[ph[0]], xs[T[ph[0]].cols], y=ys[ph[0]], index=ix)
+                ix = [self.ec_index[i] for i in ph] if self.ec_index else None
+                if len(ph) == 1:
+                    cbk.ec_gemv(T[ph[0]], xs[T[ph[0]].cols], y=ys[ph[0]], index=ix and ix[0])
+                else:
+                    cbk.ec_gemv_group([T[i] for i in ph], xs[T[ph[0]].cols], ys=[ys[i] for i in ph], indexes=ix)
             elif self.ecfmt:
-                ix = self.ec_index[ph[0]] if self.ec_index else None
-                cbk.ec_decode_bf16(T[ph[0]], out=ys[ph[0]], index=ix)
+                ix = [self.ec_index[i] for i in ph] if self.ec_index else None
+                if len(ph) == 1:
+                    cbk.ec_decode_bf16(T[ph[0]], out=ys[ph[0]], index=ix and ix[0])
+                else:
+                    cbk.ec_decode_group([T[i] for i in ph], outs=[ys[i] for i in ph], indexes=ix)
             elif self.batch == 0:
                 cbk.decode_bf16(T[ph[0]], out=ys[ph[0]])
             elif self.batch > 1 and len(ph) == 1:
@@ -612,6 +625,9 @@ def main():
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
     ap.add_argument("--ec-index", action="store_true",
                     help="entropy-coded workloads: build the span index at setup and decode with one walk per span")
+    ap.add_argument("--ec-group", type=int, default=0, metavar="G",
+                    help="entropy-coded workloads: tensors per grouped launch (default 4 for the decode, 3 for "
+                         "the fused GEMV; 1: one launch per tensor)")
     ap.add_argument("--launch", choices=("phases", "chain"), default="phases",
                     help="batch 1: one launch per phase (graph-replayed), or the whole step as one GEMV "
                          "chain (a persistent cooperative launch)")
@@ -665,7 +681,7 @@ def main():
     threads = host_threads()
     log(f"workload {args.workload}; host threads {threads} of {os.cpu_count()} CPUs")
     work = Workload(args.workload, count=args.tensors, layers=args.layers, threads=threads, cap=args.cap or None,
-                    ec_index=args.ec_index)
+                    ec_index=args.ec_index, ec_group=args.ec_group)
     if args.no_group:
         work.phases = [[i] for ph in work.phases for i in ph]
     log(f"setup {work.setup_s:.1f} s: {len(work.tensors)} tensors, {len(work.phases)} launches per step, "
@@ -732,7 +748,11 @@ def main():
     algo_per_launch = comp_total / launches
     achieved = algo_per_launch / avg_launch_s / 1e9
     kernel_key, kernel_desc = work.kernel_name()
-    traffic = profiling.traffic_for(kernel_key, args.workload)
+    # traffic records are per launch, taken on each workload's default launch grouping
+    traffic_key = args.workload
+    if work.ecfmt and work.phases and len(work.phases[0]) != (3 if work.ecgemv else 4):
+        traffic_key += f"_g{len(work.phases[0])}"
+    traffic = profiling.traffic_for(kernel_key, traffic_key)
     bits = sorted({d.b for d in work.tensors}) if not work.ecfmt else [max(max(d.lengths) for d in work.tensors)]
 
     metric = ("GPU codebook encode of BF16 weights resident in HBM, raw-weight GB/s; % of HBM peak"
@@ -770,6 +790,7 @@ def main():
             "graph_replay": graph is not None,
             "launch": args.launch if work.batch == 1 and not work.ecfmt else "phases",
             "ec_span_index": bool(work.ec_index) if work.ecfmt else None,
+            "ec_tensors_per_launch": max(len(ph) for ph in work.phases) if work.ecfmt else None,
             "launches_per_step": 2 if chain else 3 * launches if work.encode else 2 * launches if work.ecgemv else launches,
             "codebook_cap": args.cap or None,
             "warmup_seconds_min": args.warmup_seconds,
@@ -797,7 +818,7 @@ def main():
             "bytes_per_launch": int(algo_per_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
             "launches_per_unit": 3 if work.encode else 2 if work.ecgemv else 1,
-            "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, args.workload), ROOT) if traffic else None,
+            "traffic_source": os.path.relpath(profiling.traffic_path(kernel_key, traffic_key), ROOT) if traffic else None,
         },
     }
     if args.workload in STEP_WORKLOADS:

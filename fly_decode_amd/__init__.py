@@ -18,7 +18,8 @@ import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
            "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
-           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "ec_build_index", "cap_patterns",
+           "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "ec_build_index",
+           "ec_decode_group", "ec_gemv_group", "cap_patterns",
            "GemvChain"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -145,6 +146,13 @@ def load_library():
         lib.cbk_ec_gemv_indexed.restype = ctypes.c_int
         lib.cbk_ec_gemv_indexed.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_uint64,
                                             ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_ec_decode_group.restype = ctypes.c_int
+        lib.cbk_ec_decode_group.argtypes = [ctypes.POINTER(_ECTensor), ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]
+        lib.cbk_ec_gemv_group.restype = ctypes.c_int
+        lib.cbk_ec_gemv_group.argtypes = [ctypes.POINTER(_ECTensor), ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                          ctypes.POINTER(ctypes.c_uint64), ctypes.c_uint64, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -543,3 +551,35 @@ def ec_gemv(t: ECTensor, x, y=None, stream=None, index=None):
         _check(lib.cbk_ec_gemv_indexed(ctypes.byref(st), ctypes.c_void_p(index.data_ptr()), t.rows, t.cols, xp, yp,
                                        _stream(stream)), "cbk_ec_gemv_indexed")
     return y
+
+
+def _ptrs(items):
+    """A ctypes array of device pointers (None for empty tensors)."""
+    return (ctypes.c_void_p * len(items))(*[a.data_ptr() if a.numel() else None for a in items])
+
+
+def ec_decode_group(ts, outs=None, stream=None, indexes=None):
+    """cbk_ec_decode_group: several device ECTensors decoded by one launch per run of up to 8 (each
+    output bit-identical to ``ec_decode_bf16``); ``indexes``: their span indexes, or None."""
+    import torch
+    if outs is None:
+        outs = [torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device=t.sm.device) for t in ts]
+    arr = (_ECTensor * len(ts))(*[t._struct() for t in ts])
+    ix = _ptrs(indexes) if indexes is not None else None
+    _check(load_library().cbk_ec_decode_group(arr, ix, len(ts), _ptrs(outs), _stream(stream)), "cbk_ec_decode_group")
+    return outs
+
+
+def ec_gemv_group(ts, x, ys=None, stream=None, indexes=None):
+    """cbk_ec_gemv_group: fused decode + GEMV of several device ECTensors of equal cols that share
+    x, one launch per run of up to 8; ``indexes``: their span indexes, or None."""
+    import torch
+    if ys is None:
+        ys = [torch.empty(t.rows, dtype=torch.float32, device=t.sm.device) for t in ts]
+    arr = (_ECTensor * len(ts))(*[t._struct() for t in ts])
+    rows = (ctypes.c_uint64 * len(ts))(*[t.rows for t in ts])
+    ix = _ptrs(indexes) if indexes is not None else None
+    xp = ctypes.c_void_p(x.data_ptr() if x.numel() else None)
+    _check(load_library().cbk_ec_gemv_group(arr, ix, len(ts), rows, ts[0].cols if ts else 0, xp, _ptrs(ys),
+                                            _stream(stream)), "cbk_ec_gemv_group")
+    return ys

@@ -153,12 +153,13 @@ __device__ __forceinline__ uint32_t count_span(const uint32_t *multi, uint32_t w
 
 // GEMV == false: decode to BF16 in out.  GEMV == true: y[r] += sum of W[r][k] x[k] over the
 // block's weights, per row in LDS first, then one global atomic add per row the block touches.
+// The workgroup takes blocks k_first, k_first + stride, ... of its tensor.
 template <bool GEMV, bool IX>
 __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const uint32_t *__restrict__ stream,
                                           const uint32_t *__restrict__ gaps, const uint32_t *__restrict__ bases,
                                           const uint16_t *__restrict__ lut, const uint8_t *__restrict__ index,
                                           uint16_t *__restrict__ out, EcGemvOut gv, uint64_t n, uint64_t total_bits,
-                                          uint32_t spans, uint32_t blocks) {
+                                          uint32_t spans, uint32_t blocks, uint32_t k_first, uint32_t stride) {
     // two codes per lookup: entry = first exponent | second exponent << 8 | first length << 16 |
     // both lengths << 20 | count << 24, count 2 when the second code also lies in the 12 bits
     __shared__ uint32_t multi[kLutEntries];
@@ -240,11 +241,11 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
     };
 
     auto base_of = [&](uint32_t k) { return k < blocks ? static_cast<uint64_t>(bases[k]) : n; };
-    BlockIn cur = fetch(blockIdx.x, base_of(blockIdx.x), base_of(blockIdx.x + 1));
-    for (uint32_t k = blockIdx.x; k < blocks; k += gridDim.x) {
+    BlockIn cur = fetch(k_first, base_of(k_first), base_of(k_first + 1));
+    for (uint32_t k = k_first; k < blocks; k += stride) {
         const uint64_t j = static_cast<uint64_t>(k) * kSpansPerBlock + t;
         const uint64_t base = cur.base;
-        const uint64_t base_after = base_of(k + gridDim.x), limit_after = base_of(k + gridDim.x + 1);
+        const uint64_t base_after = base_of(k + stride), limit_after = base_of(k + stride + 1);
         const uint32_t gap = (cur.gword >> (4 * (t % 8))) & 15u;
         uint32_t end = 0;
         if (j < spans) {
@@ -289,7 +290,7 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
             pos += (m >> 16) & 15u;
         }
         __syncthreads();
-        const BlockIn nxt = fetch(k + gridDim.x, base_after, limit_after);  // in flight during the join
+        const BlockIn nxt = fetch(k + stride, base_after, limit_after);  // in flight during the join
 
         // join with the sign-mantissa bytes: weights [base, base + total), clipped to n, in
         // 8-weight segments s0 .. s1 (segment s0 + t + i * 256 for the thread's i-th)
@@ -399,13 +400,37 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
     }
 }
 
-#define CBK_EC_KERNEL(NAME, GEMV, IX)                                                                           \
-    __global__ __launch_bounds__(kSpansPerBlock) void NAME(                                                     \
-        const uint8_t *__restrict__ sm, const uint32_t *__restrict__ stream, const uint32_t *__restrict__ gaps, \
-        const uint32_t *__restrict__ bases, const uint16_t *__restrict__ lut, uint16_t *__restrict__ out,       \
-        EcGemvOut gv, uint64_t n, uint64_t total_bits, uint32_t spans, uint32_t blocks,                         \
-        const uint8_t *__restrict__ index) {                                                                    \
-        ec_blocks<GEMV, IX>(sm, stream, gaps, bases, lut, index, out, gv, n, total_bits, spans, blocks);       \
+// One launch decodes up to kMaxEcGroup tensors (a transformer block's matrices together, as in the
+// DFloat11 page's block-level decompression): workgroups [first_wg[i], first_wg[i + 1]) take the
+// blocks of tensor i, and a single tensor is a group of one.
+constexpr uint32_t kMaxEcGroup = 8;
+struct EcArgs {
+    const uint8_t *sm;
+    const uint32_t *stream, *gaps, *bases;
+    const uint16_t *lut;
+    const uint8_t *index;  // span index (the `_ix` kernels only)
+    void *out;             // decode: BF16 patterns; fused GEMV: y (fp32)
+    uint64_t n, total_bits;
+    uint32_t spans, blocks;
+};
+struct EcGroup {
+    uint32_t first_wg[kMaxEcGroup + 1];  // first_wg[count] = grid size
+    uint32_t count;
+    uint32_t cols, magic, sh1, sh2;  // fused GEMV: the shared row length and row_of's constants
+    const uint16_t *x;
+    EcArgs t[kMaxEcGroup];
+};
+
+#define CBK_EC_KERNEL(NAME, GEMV, IX)                                                                          \
+    __global__ __launch_bounds__(kSpansPerBlock) void NAME(const EcGroup grp) {                                \
+        uint32_t k = 0;                                                                                        \
+        _Pragma("unroll") for (uint32_t j = 1; j < kMaxEcGroup; ++j) k +=                                      \
+            (j < grp.count && blockIdx.x >= grp.first_wg[j]) ? 1u : 0u;                                        \
+        const EcArgs &T = grp.t[k];                                                                            \
+        const uint32_t w0 = grp.first_wg[k];                                                                   \
+        const EcGemvOut gv{grp.x, static_cast<float *>(T.out), grp.cols, grp.magic, grp.sh1, grp.sh2};         \
+        ec_blocks<GEMV, IX>(T.sm, T.stream, T.gaps, T.bases, T.lut, T.index, static_cast<uint16_t *>(T.out), gv, \
+                            T.n, T.total_bits, T.spans, T.blocks, blockIdx.x - w0, grp.first_wg[k + 1] - w0);   \
     }
 // decode to BF16 and the fused GEMV, each with two walks per span or one walk and the span index
 CBK_EC_KERNEL(k_ec_decode, false, false)
@@ -440,10 +465,17 @@ __global__ __launch_bounds__(kSpansPerBlock) void k_ec_index(const uint32_t *__r
     }
 }
 
-__global__ __launch_bounds__(256) void k_ec_zero(float *__restrict__ y, uint64_t rows) {
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < rows;
-         i += static_cast<uint64_t>(gridDim.x) * 256)
-        y[i] = 0.f;
+// Zero-fill of the fused GEMV's outputs (a group's in one launch).
+struct EcZero {
+    float *y[kMaxEcGroup];
+    uint64_t rows[kMaxEcGroup];
+    uint32_t count;
+};
+__global__ __launch_bounds__(256) void k_ec_zero(const EcZero z) {
+    for (uint32_t g = 0; g < z.count; ++g)
+        for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; i < z.rows[g];
+             i += static_cast<uint64_t>(gridDim.x) * 256)
+            z.y[g][i] = 0.f;
 }
 
 // As many workgroups as fit the CUs at once (LDS bound); they loop over the blocks, so the tables
@@ -466,26 +498,61 @@ cbk_status resident_grid(K kernel, uint64_t blocks, std::atomic<int> (&per_cu)[6
     return CBK_OK;
 }
 
+// One launch for up to kMaxEcGroup tensors with n > 0: the resident grid split over them in
+// proportion to their blocks, at least one workgroup each.
 template <bool GEMV, bool IX>
-cbk_status launch_ec(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, EcGemvOut gv, hipStream_t s) {
-    const uint64_t spans = (t->total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
-    const uint64_t blocks = (spans + kSpansPerBlock - 1) / kSpansPerBlock;
+cbk_status launch_ec_run(EcGroup &g, hipStream_t s) {
     auto kernel = GEMV ? (IX ? k_ec_gemv_ix : k_ec_gemv) : (IX ? k_ec_decode_ix : k_ec_decode);
     static std::atomic<int> per_cu[64];
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < g.count; ++i) total += g.t[i].blocks;
     uint32_t grid = 0;
-    const cbk_status st = resident_grid(kernel, blocks, per_cu, grid);
+    const cbk_status st = resident_grid(kernel, total, per_cu, grid);
     if (st != CBK_OK) return st;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSpansPerBlock), 0, s, t->sm, t->stream, t->gaps, t->bases, t->lut,
-                       out, gv, t->n, t->total_bits, static_cast<uint32_t>(spans), static_cast<uint32_t>(blocks),
-                       index);
+    uint32_t at = 0;
+    for (uint32_t i = 0; i < g.count; ++i) {
+        g.first_wg[i] = at;
+        const uint64_t share = (static_cast<uint64_t>(grid) * g.t[i].blocks + total / 2) / total;
+        at += static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(share, g.t[i].blocks)));
+    }
+    for (uint32_t i = g.count; i <= kMaxEcGroup; ++i) g.first_wg[i] = at;
+    hipLaunchKernelGGL(kernel, dim3(at), dim3(kSpansPerBlock), 0, s, g);
     return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
+}
+
+// The tensors with n > 0, in runs of up to kMaxEcGroup per launch.  outs[i]: BF16 output or y.
+template <bool GEMV>
+cbk_status launch_ec_all(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count, void *const *outs,
+                         EcGroup g, hipStream_t s) {
+    g.count = 0;
+    auto flush = [&]() -> cbk_status {
+        if (g.count == 0) return CBK_OK;
+        const cbk_status st = indexes ? launch_ec_run<GEMV, true>(g, s) : launch_ec_run<GEMV, false>(g, s);
+        g.count = 0;
+        return st;
+    };
+    for (uint32_t i = 0; i < count; ++i) {
+        const cbk_ec_tensor &t = ts[i];
+        if (t.n == 0) continue;
+        const uint64_t spans = (t.total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
+        EcArgs &a = g.t[g.count++];
+        a = EcArgs{t.sm, t.stream, t.gaps, t.bases, t.lut, indexes ? indexes[i] : nullptr, outs[i], t.n, t.total_bits,
+                   static_cast<uint32_t>(spans), static_cast<uint32_t>((spans + kSpansPerBlock - 1) / kSpansPerBlock)};
+        if (g.count == kMaxEcGroup) {
+            const cbk_status st = flush();
+            if (st != CBK_OK) return st;
+        }
+    }
+    return flush();
 }
 
 }  // namespace
 
-cbk_status launch_ec_decode(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, hipStream_t s) {
-    const EcGemvOut none{nullptr, nullptr, 1, 1, 0, 0};
-    return index ? launch_ec<false, true>(t, index, out, none, s) : launch_ec<false, false>(t, nullptr, out, none, s);
+cbk_status launch_ec_decode(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                            uint16_t *const *outs, hipStream_t s) {
+    EcGroup g{};
+    g.cols = g.magic = 1;
+    return launch_ec_all<false>(ts, indexes, count, reinterpret_cast<void *const *>(outs), g, s);
 }
 
 cbk_status launch_ec_index(const cbk_ec_tensor *t, uint8_t *index, hipStream_t s) {
@@ -500,20 +567,35 @@ cbk_status launch_ec_index(const cbk_ec_tensor *t, uint8_t *index, hipStream_t s
     return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
 }
 
-cbk_status launch_ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
-                          const uint16_t *x, float *y, hipStream_t s) {
-    // y is accumulated with atomics, so it starts from zeros (a fill kernel, which graph capture
-    // records as an ordinary node)
-    const uint32_t zgrid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>((rows + 255) / 256, 1024)));
-    hipLaunchKernelGGL(k_ec_zero, dim3(zgrid), dim3(256), 0, s, y, rows);
-    if (hipGetLastError() != hipSuccess) return CBK_E_HIP;
-    if (t->n == 0) return CBK_OK;
+cbk_status launch_ec_gemv(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                          const uint64_t *rows, uint64_t cols, const uint16_t *x, float *const *ys, hipStream_t s) {
+    // y is accumulated with atomics, so it starts from zeros: one fill kernel per run of up to
+    // kMaxEcGroup outputs (graph capture records it as an ordinary node)
+    for (uint32_t i0 = 0; i0 < count; i0 += kMaxEcGroup) {
+        EcZero z{};
+        uint64_t most = 0;
+        for (uint32_t i = i0; i < count && i < i0 + kMaxEcGroup; ++i) {
+            if (rows[i] == 0) continue;
+            z.y[z.count] = ys[i];
+            z.rows[z.count++] = rows[i];
+            most = std::max(most, rows[i]);
+        }
+        if (z.count == 0) continue;
+        const uint32_t zgrid = static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>((most + 255) / 256, 1024)));
+        hipLaunchKernelGGL(k_ec_zero, dim3(zgrid), dim3(256), 0, s, z);
+        if (hipGetLastError() != hipSuccess) return CBK_E_HIP;
+    }
+    if (cols == 0) return CBK_OK;
     // the divisor constants of row_of (cols < 2^32 here, so the product fits 64 bits)
     uint32_t l = 0;
     while ((uint64_t(1) << l) < cols) ++l;
-    const uint32_t magic = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << l) - cols)) / cols + 1);
-    const EcGemvOut gv{x, y, static_cast<uint32_t>(cols), magic, std::min<uint32_t>(l, 1), l > 0 ? l - 1 : 0};
-    return index ? launch_ec<true, true>(t, index, nullptr, gv, s) : launch_ec<true, false>(t, nullptr, nullptr, gv, s);
+    EcGroup g{};
+    g.cols = static_cast<uint32_t>(cols);
+    g.magic = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << l) - cols)) / cols + 1);
+    g.sh1 = std::min<uint32_t>(l, 1);
+    g.sh2 = l > 0 ? l - 1 : 0;
+    g.x = x;
+    return launch_ec_all<true>(ts, indexes, count, reinterpret_cast<void *const *>(ys), g, s);
 }
 
 }  // namespace cbk

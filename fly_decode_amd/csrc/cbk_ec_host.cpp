@@ -200,8 +200,8 @@ static cbk_status check_ec_arrays(const cbk_ec_tensor *t) {
     return CBK_OK;
 }
 
-static cbk_status ec_decode(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint16_t *out,
-                            void *stream) {
+// The single call's checks for one tensor of a decode; ok: launch it (n > 0).
+static cbk_status check_decode(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, const uint16_t *out) {
     if (!t) return CBK_E_INVALID;
     const uint64_t n = t->n;
     if (n >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
@@ -210,11 +210,12 @@ static cbk_status ec_decode(const cbk_ec_tensor *t, const uint8_t *index, bool i
     const cbk_status st = check_ec_arrays(t);
     if (st != CBK_OK) return st;
     if (!aligned16(out) || (indexed && !aligned16(index))) return CBK_E_ALIGN;
-    return cbk::launch_ec_decode(t, indexed ? index : nullptr, out, static_cast<hipStream_t>(stream));
+    return CBK_OK;
 }
 
-static cbk_status ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint64_t rows, uint64_t cols,
-                          const uint16_t *x, float *y, void *stream) {
+// The single call's checks for one tensor of a fused GEMV.
+static cbk_status check_gemv(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint64_t rows, uint64_t cols,
+                             const uint16_t *x, const float *y) {
     if (!t) return CBK_E_INVALID;
     const uint64_t n = t->n;
     if (n >= (uint64_t(1) << 32)) return CBK_E_UNSUPPORTED;
@@ -230,7 +231,21 @@ static cbk_status ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, bool ind
         if (st != CBK_OK) return st;
         if (!aligned16(x) || (indexed && !aligned16(index))) return CBK_E_ALIGN;
     }
-    return cbk::launch_ec_gemv(t, indexed ? index : nullptr, rows, cols, x, y, static_cast<hipStream_t>(stream));
+    return CBK_OK;
+}
+
+static cbk_status ec_decode(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint16_t *out,
+                            void *stream) {
+    const cbk_status st = check_decode(t, index, indexed, out);
+    if (st != CBK_OK || t->n == 0) return st;
+    return cbk::launch_ec_decode(t, indexed ? &index : nullptr, 1, &out, static_cast<hipStream_t>(stream));
+}
+
+static cbk_status ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, bool indexed, uint64_t rows, uint64_t cols,
+                          const uint16_t *x, float *y, void *stream) {
+    const cbk_status st = check_gemv(t, index, indexed, rows, cols, x, y);
+    if (st != CBK_OK || rows == 0) return st;
+    return cbk::launch_ec_gemv(t, indexed ? &index : nullptr, 1, &rows, cols, x, &y, static_cast<hipStream_t>(stream));
 }
 
 cbk_status cbk_ec_decode_bf16(const cbk_ec_tensor *t, uint16_t *out, void *stream) {
@@ -249,6 +264,27 @@ cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, con
 cbk_status cbk_ec_gemv_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
                                const uint16_t *x, float *y, void *stream) {
     return ec_gemv(t, index, true, rows, cols, x, y, stream);
+}
+
+cbk_status cbk_ec_decode_group(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                               uint16_t *const *outs, void *stream) {
+    if (!ts || !outs || count == 0) return CBK_E_INVALID;
+    for (uint32_t i = 0; i < count; ++i) {
+        const cbk_status st = check_decode(&ts[i], indexes ? indexes[i] : nullptr, indexes != nullptr, outs[i]);
+        if (st != CBK_OK) return st;
+    }
+    return cbk::launch_ec_decode(ts, indexes, count, outs, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_ec_gemv_group(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                             const uint64_t *rows, uint64_t cols, const uint16_t *x, float *const *ys, void *stream) {
+    if (!ts || !rows || !ys || count == 0) return CBK_E_INVALID;
+    for (uint32_t i = 0; i < count; ++i) {
+        const cbk_status st =
+            check_gemv(&ts[i], indexes ? indexes[i] : nullptr, indexes != nullptr, rows[i], cols, x, ys[i]);
+        if (st != CBK_OK) return st;
+    }
+    return cbk::launch_ec_gemv(ts, indexes, count, rows, cols, x, ys, static_cast<hipStream_t>(stream));
 }
 
 uint64_t cbk_ec_index_bytes(uint64_t total_bits) {

@@ -32,11 +32,13 @@ cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uin
 // encode_gpu_workspace_bytes() bytes); looked up on the device's first call.
 cbk_status encode_gpu_scratch(void **ws);
 
-// Exponent entropy-coded format (cbk_ec.hip).
-// index: the span index (cbk_ec_build_index), or null for the two-walk decode.
-cbk_status launch_ec_decode(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, hipStream_t s);
-cbk_status launch_ec_gemv(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
-                          const uint16_t *x, float *y, hipStream_t s);
+// Exponent entropy-coded format (cbk_ec.hip), count tensors in launches of up to 8.
+// indexes: each tensor's span index (cbk_ec_build_index), or null for the two-walk decode.
+cbk_status launch_ec_decode(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                            uint16_t *const *outs, hipStream_t s);
+// rows[i] * cols = ts[i].n; every y is zero-filled first (rows[i] > 0), x is read when cols > 0.
+cbk_status launch_ec_gemv(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                          const uint64_t *rows, uint64_t cols, const uint16_t *x, float *const *ys, hipStream_t s);
 cbk_status launch_ec_index(const cbk_ec_tensor *t, uint8_t *index, hipStream_t s);
 
 }  // namespace cbk

@@ -129,16 +129,44 @@ cbk_status cbk_ec_gemv(const cbk_ec_tensor *t, uint64_t rows, uint64_t cols, con
  * cbk_ec_build_index -- GPU.  Writes the index of t (one walk over every span with the table).
  *   index   out, device, cbk_ec_index_bytes(t->total_bits) bytes, 16-byte aligned, caller-owned.
  *   Errors: as cbk_ec_decode_bf16 (NULL index with n > 0 gives CBK_E_INVALID).
- * cbk_ec_decode_bf16_indexed, cbk_ec_gemv_indexed -- GPU.  As cbk_ec_decode_bf16 and cbk_ec_gemv,
- *   bit for bit, with the index that cbk_ec_build_index wrote for t (device, 16-byte aligned).  An
- *   index that does not match the stream gives wrong values but no access outside the arrays:
- *   counts above 64 are read as 64, and each block writes only weights below n.
+ * cbk_ec_decode_bf16_indexed, cbk_ec_gemv_indexed -- GPU.  As cbk_ec_decode_bf16 (bit for bit) and
+ *   cbk_ec_gemv (the same products, summed in an order that varies between calls), with the index
+ *   that cbk_ec_build_index wrote for t (device, 16-byte aligned).  An index that does not match
+ *   the stream gives wrong values but no access outside the arrays: counts above 64 are read as
+ *   64, and each block writes only weights below n.
  */
 uint64_t cbk_ec_index_bytes(uint64_t total_bits);
 cbk_status cbk_ec_build_index(const cbk_ec_tensor *t, uint8_t *index, void *stream);
 cbk_status cbk_ec_decode_bf16_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint16_t *out, void *stream);
 cbk_status cbk_ec_gemv_indexed(const cbk_ec_tensor *t, const uint8_t *index, uint64_t rows, uint64_t cols,
                                const uint16_t *x, float *y, void *stream);
+
+/*
+ * Grouped calls -- the matrices of a transformer block decoded together, following the DFloat11
+ * page's block-level decompression ("How it works in practice"): one launch takes up to 8 tensors
+ * (more are split into runs of 8), its workgroups divided among them in proportion to their
+ * blocks, so the launch's start-up and tail are paid once per run instead of once per tensor.
+ *
+ * cbk_ec_decode_group -- GPU.  outs[i] = the patterns of ts[i], bit for bit as cbk_ec_decode_bf16.
+ *   ts       host array of count tensors (device arrays inside, as for cbk_ec_decode_bf16).
+ *   indexes  NULL (two walks per span), or a host array of count device pointers, indexes[i] the
+ *            span index of ts[i] (every one non-NULL where ts[i].n > 0, 16-byte aligned).
+ *   outs     host array of count device pointers, outs[i] holds ts[i].n BF16 patterns, 16-byte
+ *            aligned; outputs must not overlap.
+ * cbk_ec_gemv_group -- GPU.  ys[i] = W_i x for tensors of rows[i] x cols weights that share x, as
+ *   cbk_ec_gemv (within the same bound; summation order varies); every ys[i] with rows[i] > 0 is
+ *   zero-filled first, by one kernel per run.
+ *   rows     host array of count row counts, rows[i] * cols == ts[i].n.
+ *   x        device, cols BF16 patterns, 16-byte aligned (read when cols > 0).
+ *   ys       host array of count device pointers, ys[i] holds rows[i] fp32, 4-byte aligned.
+ * Errors: count == 0 or a NULL ts, outs, rows or ys array: CBK_E_INVALID.  Every tensor is checked
+ * as by the single call before anything is launched, and the first failure's status is returned
+ * with nothing enqueued.
+ */
+cbk_status cbk_ec_decode_group(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                               uint16_t *const *outs, void *stream);
+cbk_status cbk_ec_gemv_group(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
+                             const uint64_t *rows, uint64_t cols, const uint16_t *x, float *const *ys, void *stream);
 
 #ifdef __cplusplus
 }

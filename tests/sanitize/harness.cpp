@@ -89,6 +89,35 @@ static int check_record(const std::vector<uint16_t> &w, uint32_t K, uint64_t rec
         if (cbk_ec_encode(wp, &h, sm.data(), stream.data(), gaps.data(), bases.data(), lut.data()) != CBK_OK)
             return fail("ec_encode", rec);
         if (n && cbk_ec_stored_bytes(&h) < n) return fail("ec stored bytes", rec);
+        // grouped calls with bad arguments (device addresses stand in; nothing is dereferenced)
+        if (n) {
+            const cbk_ec_tensor et = {n, h.total_bits, reinterpret_cast<const uint8_t *>(0x10000),
+                                      reinterpret_cast<const uint32_t *>(0x20000),
+                                      reinterpret_cast<const uint32_t *>(0x30000),
+                                      reinterpret_cast<const uint32_t *>(0x40000),
+                                      reinterpret_cast<const uint16_t *>(0x50000)};
+            cbk_ec_tensor two[2] = {et, et};
+            uint16_t *outs[2] = {reinterpret_cast<uint16_t *>(0x60000), nullptr};
+            if (cbk_ec_decode_group(two, nullptr, 2, outs, nullptr) != CBK_E_INVALID)
+                return fail("ec group decode without its second output", rec);
+            outs[1] = reinterpret_cast<uint16_t *>(0x70008);
+            if (cbk_ec_decode_group(two, nullptr, 2, outs, nullptr) != CBK_E_ALIGN)
+                return fail("ec group decode with a misaligned output", rec);
+            const uint8_t *ix[2] = {reinterpret_cast<const uint8_t *>(0x80000), nullptr};
+            outs[1] = reinterpret_cast<uint16_t *>(0x70000);
+            if (cbk_ec_decode_group(two, ix, 2, outs, nullptr) != CBK_E_INVALID)
+                return fail("ec group decode with a missing index", rec);
+            if (cbk_ec_decode_group(two, nullptr, 0, outs, nullptr) != CBK_E_INVALID)
+                return fail("ec group decode of no tensors", rec);
+            // an empty first tensor, then one whose rows do not match its n
+            two[0].n = 0;
+            two[0].total_bits = 0;
+            const uint64_t rows[2] = {0, n + 1};
+            float *ys[2] = {reinterpret_cast<float *>(0x90000), reinterpret_cast<float *>(0xA0000)};
+            if (cbk_ec_gemv_group(two, nullptr, 2, rows, 1, reinterpret_cast<const uint16_t *>(0xB0000), ys,
+                                  nullptr) != CBK_E_INVALID)
+                return fail("ec group gemv with rows * cols != n", rec);
+        }
     }
 
     // GPU entry points with bad arguments: validation returns before any launch (the launchers of

@@ -33,9 +33,11 @@ cbk_status launch_encode_gpu(const uint16_t *, uint64_t, void *, uint16_t *, uin
     reached("encode_gpu");
 }
 cbk_status encode_gpu_scratch(void **) { reached("encode_gpu_scratch"); }
-cbk_status launch_ec_decode(const cbk_ec_tensor *, const uint8_t *, uint16_t *, hipStream_t) { reached("ec_decode"); }
-cbk_status launch_ec_gemv(const cbk_ec_tensor *, const uint8_t *, uint64_t, uint64_t, const uint16_t *, float *,
-                          hipStream_t) {
+cbk_status launch_ec_decode(const cbk_ec_tensor *, const uint8_t *const *, uint32_t, uint16_t *const *, hipStream_t) {
+    reached("ec_decode");
+}
+cbk_status launch_ec_gemv(const cbk_ec_tensor *, const uint8_t *const *, uint32_t, const uint64_t *, uint64_t,
+                          const uint16_t *, float *const *, hipStream_t) {
     reached("ec_gemv");
 }
 cbk_status launch_ec_index(const cbk_ec_tensor *, uint8_t *, hipStream_t) { reached("ec_index"); }

@@ -162,3 +162,42 @@ def test_span_index_calls_validate_before_any_hip_call(cbk):
     assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), v(A + 4), 100, 64, v(A), v(A), None) == 3
     assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), v(A), 99, 64, v(A), v(A), None) == 1
     assert lib.cbk_ec_gemv_indexed(ctypes.byref(g), v(A), 200, 32, v(A), v(A), None) == 4
+
+
+def test_group_calls_validate_before_any_hip_call(cbk):
+    """cbk_ec_decode_group and cbk_ec_gemv_group check every tensor as the single calls do, plus
+    the arrays and the count, before anything is launched (a failure in the last tensor returns
+    its code with nothing enqueued; no device is present here)."""
+    lib = cbk.load_library()
+    T = cbk._ECTensor
+    A = 0x10000   # 16-byte aligned stand-ins; nothing is dereferenced on these paths
+    P = ctypes.c_void_p
+    good = dict(n=1000, total_bits=3000, sm=A, stream=A, gaps=A, bases=A, lut=A)
+
+    def arr(*ds):
+        return (T * len(ds))(*[T(**d) for d in ds])
+
+    def ptrs(*vs):
+        return (P * len(vs))(*vs)
+    ts = arr(good, good, dict(good, lut=None))
+    assert lib.cbk_ec_decode_group(ts, None, 3, ptrs(A, A, A), None) == 1          # last tensor without its table
+    assert lib.cbk_ec_decode_group(arr(good, good), None, 2, ptrs(A, A + 2), None) == 3   # misaligned output
+    assert lib.cbk_ec_decode_group(arr(good, good), ptrs(A, None), 2, ptrs(A, A), None) == 1  # an index missing
+    assert lib.cbk_ec_decode_group(arr(good, good), ptrs(A, A + 8), 2, ptrs(A, A), None) == 3  # misaligned index
+    assert lib.cbk_ec_decode_group(arr(good), None, 0, ptrs(A), None) == 1          # no tensors
+    assert lib.cbk_ec_decode_group(None, None, 1, ptrs(A), None) == 1
+    assert lib.cbk_ec_decode_group(arr(good), None, 1, None, None) == 1
+    assert lib.cbk_ec_decode_group(arr(dict(n=0, total_bits=0)), None, 1, ptrs(None), None) == 0  # empty: no-op
+    assert lib.cbk_ec_decode_group(arr(good, dict(good, n=1 << 32, total_bits=1 << 33)), None, 2, ptrs(A, A), None) == 4
+
+    g = dict(n=6400, total_bits=3 * 6400, sm=A, stream=A, gaps=A, bases=A, lut=A)
+    R = ctypes.c_uint64 * 2
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 99), 64, P(A), ptrs(A, A), None) == 1   # rows * cols != n
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, P(A), ptrs(A, A + 2), None) == 3  # misaligned y
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, P(A + 8), ptrs(A, A), None) == 3  # misaligned x
+    assert lib.cbk_ec_gemv_group(arr(g, g), ptrs(A, None), 2, R(100, 100), 64, P(A), ptrs(A, A), None) == 1
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(200, 200), 32, P(A), ptrs(A, A), None) == 4   # cols < 64
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, None, 64, P(A), ptrs(A, A), None) == 1
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, P(A), None, None) == 1
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 0, R(100, 100), 64, P(A), ptrs(A, A), None) == 1
+    assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, None, ptrs(A, A), None) == 1  # no x

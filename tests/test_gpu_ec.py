@@ -295,3 +295,91 @@ def test_ec_wrong_index_stays_in_bounds(env):
     cbk.ec_decode_bf16(d, out=buf[:n].view(torch.bfloat16).view(1, n), index=index)
     torch.cuda.synchronize()
     assert bool((buf[n:].cpu() == -7).all())
+
+
+# ------------------------------------------------- grouped calls (a block's matrices together)
+def _group_weights():
+    """Eleven tensors (two launches: a run of eight, then three): shapes from one weight to several
+    blocks, heavy tails, one-bit codes, a ragged length and an empty tensor in the middle."""
+    cases = _cases()
+    ws = [synth.gaussian_bf16((257, 1000), 0.02, seed=[70]), cases["t2_heavy_tail"], cases["constant"],
+          np.zeros((0, 64), dtype=np.uint16), cases["one"], synth.gaussian_bf16((1, 64 * 256 * 3 + 11), 0.02, seed=[71]),
+          cases["specials"], cases["two_exponents"], synth.student_t_bf16((64, 4096), 4.0, 0.02, seed=[72]),
+          cases["every_pattern"], synth.gaussian_bf16((3, 7), 0.02, seed=[73])]
+    return ws
+
+
+@pytest.mark.parametrize("indexed", [False, True])
+def test_ec_decode_group_bit_exact(env, indexed):
+    """cbk_ec_decode_group: every output equals the input patterns (and so the single call), with
+    and without the span indexes."""
+    torch, cbk = env
+    ws = _group_weights()
+    print(f"ec decode group of {len(ws)} tensors, indexed={indexed}", flush=True)
+    ds = [cbk.ec_encode(w).to("cuda") for w in ws]
+    ix = [cbk.ec_build_index(d) for d in ds] if indexed else None
+    outs = [torch.full((d.rows, d.cols), float("nan"), dtype=torch.bfloat16, device="cuda") for d in ds]
+    cbk.ec_decode_group(ds, outs=outs, indexes=ix)
+    torch.cuda.synchronize()
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        got = o.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape)
+        assert np.array_equal(got, w), f"tensor {i} {w.shape}"
+
+
+def test_ec_decode_group_workload_layer(env):
+    """Four 4096^2 attention-workload tensors, the bench's grouped launch: every weight exact."""
+    torch, cbk = env
+    t = synth.WORKLOADS[2][0][0]
+    ws = [synth.workload_tensor(2, layer, t) for layer in range(4)]
+    ds = [cbk.ec_encode(w).to("cuda") for w in ws]
+    ix = [cbk.ec_build_index(d) for d in ds]
+    outs = cbk.ec_decode_group(ds, indexes=ix)
+    torch.cuda.synchronize()
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        assert np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), w), f"tensor {i}"
+
+
+@pytest.mark.parametrize("indexed", [False, True])
+def test_ec_gemv_group_matches_oracle(env, indexed):
+    """cbk_ec_gemv_group over nine tensors of 1,000 columns and different rows (a run of eight,
+    then one; one tensor has no rows): every y within the tolerance of the oracle's decode and
+    float64 product, and every y overwritten."""
+    torch, cbk = env
+    cols = 1000
+    shapes = [(300, cols), (1, cols), (0, cols), (77, cols), (1100, cols), (17, cols), (64, cols), (5, cols), (129, cols)]
+    ws = [synth.student_t_bf16(s, 4.0, 0.02, seed=[74, i]) if i % 2 else synth.gaussian_bf16(s, 0.02, seed=[74, i])
+          for i, s in enumerate(shapes)]
+    x = synth.activation_bf16(cols, seed=[75])
+    print(f"ec gemv group of {len(ws)} tensors, indexed={indexed}", flush=True)
+    ds = [cbk.ec_encode(w).to("cuda") for w in ws]
+    ix = [cbk.ec_build_index(d) for d in ds] if indexed else None
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ys = [torch.full((d.rows,), 1e30, dtype=torch.float32, device="cuda") for d in ds]
+    cbk.ec_gemv_group(ds, xd, ys=ys, indexes=ix)
+    torch.cuda.synchronize()
+    for i, (w, y) in enumerate(zip(ws, ys)):
+        if w.shape[0] == 0:
+            continue
+        ref, absb = ec.gemv(ec.encode(w), w.shape[0], cols, x)
+        err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= TOL * absb), f"tensor {i}: max err/bound {np.max(err / np.maximum(absb, 1e-300))}"
+
+
+def test_ec_gemv_group_workload_rows(env):
+    """Three 4096^2 attention-workload tensors sharing x, as the bench groups them: sampled rows
+    (first and last included) within the tolerance of the oracle."""
+    torch, cbk = env
+    t = synth.WORKLOADS[2][0][0]
+    ws = [synth.workload_tensor(2, layer, t) for layer in range(3)]
+    x = synth.workload_x(2, 4096)[0]
+    ds = [cbk.ec_encode(w).to("cuda") for w in ws]
+    ix = [cbk.ec_build_index(d) for d in ds]
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ys = cbk.ec_gemv_group(ds, xd, indexes=ix)
+    torch.cuda.synchronize()
+    rows = np.concatenate([[0, 4095], np.random.default_rng(76).choice(np.arange(1, 4095), 30, replace=False)])
+    for i, (w, y) in enumerate(zip(ws, ys)):
+        sub = np.ascontiguousarray(w[rows])
+        ref, absb = ec.gemv(ec.encode(sub), len(rows), 4096, x)
+        err = np.abs(y.cpu().numpy().astype(np.float64)[rows] - ref)
+        assert np.all(err <= TOL * absb), f"tensor {i}"
