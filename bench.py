@@ -325,6 +325,9 @@ class Workload:
             return "k_enc", "cbk_encode_gpu per tensor (k_enc_clear, k_enc_presence, k_enc_pack)"
         if self.ecfmt:
             k = ("k_ec_gemv" if self.ecgemv else "k_ec_decode") + ("_ix" if self.ec_index else "")
+            # the decode's fitted kernel when every block holds at most 8,185 codes
+            if not self.ecgemv and all(0 < d.max_block_codes <= 8185 for d in self.tensors):
+                k += "_fit"
             return k, k
         if self.batch == 0:
             k = "k_decode_fast"

@@ -61,7 +61,7 @@ class _ECHeader(ctypes.Structure):
 class _ECTensor(ctypes.Structure):
     _fields_ = [("n", ctypes.c_uint64), ("total_bits", ctypes.c_uint64), ("sm", ctypes.c_void_p),
                 ("stream", ctypes.c_void_p), ("gaps", ctypes.c_void_p), ("bases", ctypes.c_void_p),
-                ("lut", ctypes.c_void_p)]
+                ("lut", ctypes.c_void_p), ("max_block_codes", ctypes.c_uint32)]
 
 
 def library_path() -> str:
@@ -146,6 +146,8 @@ def load_library():
         lib.cbk_ec_gemv_indexed.restype = ctypes.c_int
         lib.cbk_ec_gemv_indexed.argtypes = [ctypes.POINTER(_ECTensor), ctypes.c_void_p, ctypes.c_uint64,
                                             ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_ec_max_block_codes.restype = ctypes.c_uint32
+        lib.cbk_ec_max_block_codes.argtypes = [hp, ctypes.c_void_p]
         lib.cbk_ec_decode_group.restype = ctypes.c_int
         lib.cbk_ec_decode_group.argtypes = [ctypes.POINTER(_ECTensor), ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
                                             ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]
@@ -436,12 +438,14 @@ class GemvChain:
 class ECTensor:
     """A tensor in the exponent entropy-coded format: code lengths, stream length and the arrays
     sm (uint8[n]), stream (uint32), gaps (uint32), bases (uint32) and lut (uint16[4096]).  Host
-    numpy arrays after ``ec_encode``; ``to(device)`` gives torch tensors on the device."""
+    numpy arrays after ``ec_encode``; ``to(device)`` gives torch tensors on the device.
+    ``max_block_codes``: the most codes in one block (cbk_ec_max_block_codes), 0 if unknown."""
 
-    def __init__(self, rows, cols, total_bits, lengths, sm, stream, gaps, bases, lut):
+    def __init__(self, rows, cols, total_bits, lengths, sm, stream, gaps, bases, lut, max_block_codes=0):
         self.rows, self.cols, self.total_bits = int(rows), int(cols), int(total_bits)
         self.lengths = list(lengths)
         self.sm, self.stream, self.gaps, self.bases, self.lut = sm, stream, gaps, bases, lut
+        self.max_block_codes = int(max_block_codes)
 
     @property
     def n(self) -> int:
@@ -468,13 +472,13 @@ class ECTensor:
             return torch.from_numpy(a.view(view)).to(device)
         return ECTensor(self.rows, self.cols, self.total_bits, self.lengths, put(self.sm, np.uint8, True),
                         put(self.stream, np.int32), put(self.gaps, np.int32), put(self.bases, np.int32),
-                        put(self.lut, np.int16))
+                        put(self.lut, np.int16), self.max_block_codes)
 
     def _struct(self) -> _ECTensor:
         def ptr(a):
             return a.data_ptr() if a.numel() else None
         return _ECTensor(self.n, self.total_bits, ptr(self.sm), ptr(self.stream), ptr(self.gaps),
-                         ptr(self.bases), ptr(self.lut))
+                         ptr(self.bases), ptr(self.lut), self.max_block_codes)
 
 
 def ec_encode(w, rows: int | None = None, cols: int | None = None) -> ECTensor:
@@ -503,7 +507,8 @@ def ec_encode(w, rows: int | None = None, cols: int | None = None) -> ECTensor:
     def p(a):
         return a.ctypes.data if a.size else None
     _check(lib.cbk_ec_encode(src, hp, p(sm), p(stream), p(gaps), p(bases), p(lut)), "cbk_ec_encode")
-    return ECTensor(rows, cols, h.total_bits, list(h.lengths), sm, stream, gaps, bases, lut)
+    most = int(lib.cbk_ec_max_block_codes(hp, p(bases)))
+    return ECTensor(rows, cols, h.total_bits, list(h.lengths), sm, stream, gaps, bases, lut, most)
 
 
 def ec_build_index(t: ECTensor, stream=None):

@@ -17,6 +17,12 @@
 //   4. the block's values, bases[k] .. bases[k] + total, are joined with their sign-mantissa bytes
 //      (coalesced 8-byte loads, issued with the block's stream loads) and written as 16-byte
 //      non-temporal stores (element stores at the two ragged ends of the block's range).
+// With a span index (one byte per span: the codes that start in it, written once by k_ec_index
+// with the same walk), the `_ix` kernels read each span's count with its stream words and skip
+// the counting walk of step 2.  A launch takes up to eight tensors, its workgroups divided among
+// them (a transformer block's matrices decoded together).  The `_fit` decode kernels keep half a
+// block's worst case of exponents in LDS, for tensors whose blocks all hold at most kFitCodes
+// codes, and so run six workgroups per CU instead of four.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,6 +43,10 @@ constexpr int kMaxPerSpan = CBK_EC_SPAN_BITS;       // codes are at least one bi
 constexpr int kLutEntries = CBK_EC_LUT_ENTRIES;
 constexpr int kStreamOnce = 2;                      // non-temporal: data touched once
 constexpr int kJoinAhead = 4;                       // join segments per thread loaded in advance
+// The fitted decode holds the exponents of blocks of at most kFitCodes codes (a block's first
+// weight can sit up to 7 places into the array's first 8-byte word): half the worst case, so that
+// six workgroups fit a CU instead of four.
+constexpr uint32_t kFitCodes = kSpansPerBlock * kMaxPerSpan / 2 - 7;
 
 static_assert(kSpansPerBlock == 256, "one thread per span, 256 spans per block");
 
@@ -153,8 +163,10 @@ __device__ __forceinline__ uint32_t count_span(const uint32_t *multi, uint32_t w
 
 // GEMV == false: decode to BF16 in out.  GEMV == true: y[r] += sum of W[r][k] x[k] over the
 // block's weights, per row in LDS first, then one global atomic add per row the block touches.
+// FIT: the exponent array holds kFitCodes values; a block with more (possible only when the
+// caller's bound on the codes per block was wrong) is skipped, its outputs left as they were.
 // The workgroup takes blocks k_first, k_first + stride, ... of its tensor.
-template <bool GEMV, bool IX>
+template <bool GEMV, bool IX, bool FIT>
 __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const uint32_t *__restrict__ stream,
                                           const uint32_t *__restrict__ gaps, const uint32_t *__restrict__ bases,
                                           const uint16_t *__restrict__ lut, const uint8_t *__restrict__ index,
@@ -164,8 +176,9 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
     // both lengths << 20 | count << 24, count 2 when the second code also lies in the 12 bits
     __shared__ uint32_t multi[kLutEntries];
     // exponents of one block, placed so that index i holds the value of weight (base & ~7) + i;
-    // 16 spare bytes cover the 8-byte reads at the end of the range
-    __shared__ uint64_t exps8[(kSpansPerBlock * kMaxPerSpan + 16) / 8];
+    // 16 spare bytes cover the 8-byte reads at the end of the range (FIT: and 64 the codes a
+    // thread can write past its count when an index is wrong)
+    __shared__ uint64_t exps8[FIT ? (kFitCodes + 7 + 16 + kMaxPerSpan) / 8 : (kSpansPerBlock * kMaxPerSpan + 16) / 8];
     __shared__ uint32_t wave_sum[kSpansPerBlock / 64];
     __shared__ float row_sum[GEMV ? kGemvBlockRows : 1];
     uint8_t *exps = reinterpret_cast<uint8_t *>(exps8);
@@ -274,9 +287,11 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
             total += wave_sum[i];
         }
         uint32_t at = static_cast<uint32_t>(base & 7) + before + incl - cnt;
+        // FIT: the block's exponents fit the array (the same in every lane)
+        const bool fits = !FIT || __builtin_amdgcn_readfirstlane(total) <= kFitCodes;
 
         // phase 2: the walk again (the only one with the index), exponents to their places
-        uint32_t pos = gap;
+        uint32_t pos = fits ? gap : end;
         for (; pos + CBK_EC_MAX_LEN <= end;) {
             const uint32_t m = multi[window12(w0, w1, w2, pos)];
             exps[at] = static_cast<uint8_t>(m);
@@ -295,7 +310,7 @@ __device__ __forceinline__ void ec_blocks(const uint8_t *__restrict__ sm, const 
         // join with the sign-mantissa bytes: weights [base, base + total), clipped to n, in
         // 8-weight segments s0 .. s1 (segment s0 + t + i * 256 for the thread's i-th)
         const uint64_t stop = std::min<uint64_t>(base + total, n);
-        if (base < stop) {
+        if (fits && base < stop) {
             const uint64_t s0 = base / 8, s1 = (stop + 7) / 8;
             // GEMV: one wave-wide call (every lane, `valid` false past s1) can reduce the wave's
             // partial sums in registers when they all belong to one row, the common case
@@ -421,7 +436,7 @@ struct EcGroup {
     EcArgs t[kMaxEcGroup];
 };
 
-#define CBK_EC_KERNEL(NAME, GEMV, IX)                                                                          \
+#define CBK_EC_KERNEL(NAME, GEMV, IX, FIT)                                                                     \
     __global__ __launch_bounds__(kSpansPerBlock) void NAME(const EcGroup grp) {                                \
         uint32_t k = 0;                                                                                        \
         _Pragma("unroll") for (uint32_t j = 1; j < kMaxEcGroup; ++j) k +=                                      \
@@ -429,14 +444,19 @@ struct EcGroup {
         const EcArgs &T = grp.t[k];                                                                            \
         const uint32_t w0 = grp.first_wg[k];                                                                   \
         const EcGemvOut gv{grp.x, static_cast<float *>(T.out), grp.cols, grp.magic, grp.sh1, grp.sh2};         \
-        ec_blocks<GEMV, IX>(T.sm, T.stream, T.gaps, T.bases, T.lut, T.index, static_cast<uint16_t *>(T.out), gv, \
+        ec_blocks<GEMV, IX, FIT>(T.sm, T.stream, T.gaps, T.bases, T.lut, T.index, static_cast<uint16_t *>(T.out),  \
+                                 gv,                                                                              \
                             T.n, T.total_bits, T.spans, T.blocks, blockIdx.x - w0, grp.first_wg[k + 1] - w0);   \
     }
-// decode to BF16 and the fused GEMV, each with two walks per span or one walk and the span index
-CBK_EC_KERNEL(k_ec_decode, false, false)
-CBK_EC_KERNEL(k_ec_gemv, true, false)
-CBK_EC_KERNEL(k_ec_decode_ix, false, true)
-CBK_EC_KERNEL(k_ec_gemv_ix, true, true)
+// decode to BF16 and the fused GEMV, each with two walks per span or one walk and the span index;
+// the decode also for blocks of at most kFitCodes codes (the fused GEMV keeps four workgroups per
+// CU, its registers allowing no more than five, which measured slower)
+CBK_EC_KERNEL(k_ec_decode, false, false, false)
+CBK_EC_KERNEL(k_ec_gemv, true, false, false)
+CBK_EC_KERNEL(k_ec_decode_ix, false, true, false)
+CBK_EC_KERNEL(k_ec_gemv_ix, true, true, false)
+CBK_EC_KERNEL(k_ec_decode_fit, false, false, true)
+CBK_EC_KERNEL(k_ec_decode_ix_fit, false, true, true)
 #undef CBK_EC_KERNEL
 
 // The span index: the table walk of phase 1 over every span, its count stored as a byte.
@@ -500,9 +520,10 @@ cbk_status resident_grid(K kernel, uint64_t blocks, std::atomic<int> (&per_cu)[6
 
 // One launch for up to kMaxEcGroup tensors with n > 0: the resident grid split over them in
 // proportion to their blocks, at least one workgroup each.
-template <bool GEMV, bool IX>
+template <bool GEMV, bool IX, bool FIT>
 cbk_status launch_ec_run(EcGroup &g, hipStream_t s) {
-    auto kernel = GEMV ? (IX ? k_ec_gemv_ix : k_ec_gemv) : (IX ? k_ec_decode_ix : k_ec_decode);
+    auto kernel = GEMV ? (IX ? k_ec_gemv_ix : k_ec_gemv)
+                       : FIT ? (IX ? k_ec_decode_ix_fit : k_ec_decode_fit) : (IX ? k_ec_decode_ix : k_ec_decode);
     static std::atomic<int> per_cu[64];
     uint64_t total = 0;
     for (uint32_t i = 0; i < g.count; ++i) total += g.t[i].blocks;
@@ -525,16 +546,23 @@ template <bool GEMV>
 cbk_status launch_ec_all(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count, void *const *outs,
                          EcGroup g, hipStream_t s) {
     g.count = 0;
+    bool fit = true;  // every tensor of the run has a known bound of at most kFitCodes per block
     auto flush = [&]() -> cbk_status {
         if (g.count == 0) return CBK_OK;
-        const cbk_status st = indexes ? launch_ec_run<GEMV, true>(g, s) : launch_ec_run<GEMV, false>(g, s);
+        cbk_status st;
+        if (!GEMV && fit)
+            st = indexes ? launch_ec_run<GEMV, true, true>(g, s) : launch_ec_run<GEMV, false, true>(g, s);
+        else
+            st = indexes ? launch_ec_run<GEMV, true, false>(g, s) : launch_ec_run<GEMV, false, false>(g, s);
         g.count = 0;
+        fit = true;
         return st;
     };
     for (uint32_t i = 0; i < count; ++i) {
         const cbk_ec_tensor &t = ts[i];
         if (t.n == 0) continue;
         const uint64_t spans = (t.total_bits + CBK_EC_SPAN_BITS - 1) / CBK_EC_SPAN_BITS;
+        fit = fit && t.max_block_codes > 0 && t.max_block_codes <= kFitCodes;
         EcArgs &a = g.t[g.count++];
         a = EcArgs{t.sm, t.stream, t.gaps, t.bases, t.lut, indexes ? indexes[i] : nullptr, outs[i], t.n, t.total_bits,
                    static_cast<uint32_t>(spans), static_cast<uint32_t>((spans + kSpansPerBlock - 1) / kSpansPerBlock)};

@@ -111,6 +111,17 @@ uint64_t cbk_ec_gap_words(const cbk_ec_header *h) { return (cbk_ec_spans(h) + 7)
 uint64_t cbk_ec_blocks(const cbk_ec_header *h) {
     return (cbk_ec_spans(h) + CBK_EC_BLOCK_SPANS - 1) / CBK_EC_BLOCK_SPANS;
 }
+uint32_t cbk_ec_max_block_codes(const cbk_ec_header *h, const uint32_t *bases) {
+    if (!h || !bases || h->n == 0) return 0;
+    const uint64_t blocks = cbk_ec_blocks(h);
+    uint64_t most = 0;
+    for (uint64_t k = 0; k < blocks; ++k) {
+        const uint64_t next = k + 1 < blocks ? bases[k + 1] : h->n;
+        if (next > bases[k]) most = std::max<uint64_t>(most, next - bases[k]);
+    }
+    return static_cast<uint32_t>(std::min<uint64_t>(most, uint64_t(CBK_EC_BLOCK_SPANS) * CBK_EC_SPAN_BITS));
+}
+
 uint64_t cbk_ec_stored_bytes(const cbk_ec_header *h) {
     if (!h) return 0;
     return h->n + 4 * (cbk_ec_stream_words(h) + cbk_ec_gap_words(h) + cbk_ec_blocks(h)) + 2 * CBK_EC_LUT_ENTRIES + 256;
@@ -193,6 +204,7 @@ cbk_status cbk_ec_encode(const uint16_t *w, const cbk_ec_header *h, uint8_t *sm,
 static cbk_status check_ec_arrays(const cbk_ec_tensor *t) {
     const uint64_t n = t->n;
     if (!t->sm || !t->stream || !t->gaps || !t->bases || !t->lut) return CBK_E_INVALID;
+    if (t->max_block_codes > uint32_t(CBK_EC_BLOCK_SPANS) * CBK_EC_SPAN_BITS) return CBK_E_INVALID;
     if (t->total_bits < n || t->total_bits > uint64_t(CBK_EC_MAX_LEN) * n) return CBK_E_INVALID;
     if (!aligned16(t->sm) || !aligned16(t->stream) || !aligned16(t->gaps) || !aligned16(t->bases) ||
         !aligned16(t->lut))

@@ -87,7 +87,19 @@ typedef struct {
     const uint32_t *gaps;    /* cbk_ec_gap_words words        */
     const uint32_t *bases;   /* cbk_ec_blocks words           */
     const uint16_t *lut;     /* 4096 entries                  */
+    uint32_t max_block_codes;  /* cbk_ec_max_block_codes of the host arrays, or 0 if unknown */
 } cbk_ec_tensor;
+
+/*
+ * cbk_ec_max_block_codes -- host.  The most codes that start in one block of 256 spans
+ * (bases[k + 1] - bases[k], n - bases[last] for the last block), 0 for n == 0; h and bases as
+ * cbk_ec_encode wrote them (NULL bases or h: 0).  Carried in cbk_ec_tensor.max_block_codes: at
+ * most 8185 (every block of codes averaging about two bits or more, as weights' exponents do)
+ * lets the GPU decode hold half a block's worst case of exponents in LDS and run more workgroups
+ * per CU.  A nonzero value below a block's true count gives unspecified values for that block's
+ * weights (never an access outside the arrays); values above 16384 are rejected (CBK_E_INVALID).
+ */
+uint32_t cbk_ec_max_block_codes(const cbk_ec_header *h, const uint32_t *bases);
 
 /*
  * cbk_ec_decode_bf16 -- GPU.  out[i] = the original pattern of weight i, for i < n.  One

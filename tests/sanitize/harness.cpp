@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "cbk.h"
@@ -89,6 +90,11 @@ static int check_record(const std::vector<uint16_t> &w, uint32_t K, uint64_t rec
         if (cbk_ec_encode(wp, &h, sm.data(), stream.data(), gaps.data(), bases.data(), lut.data()) != CBK_OK)
             return fail("ec_encode", rec);
         if (n && cbk_ec_stored_bytes(&h) < n) return fail("ec stored bytes", rec);
+        // the largest per-block code count, from bases
+        uint64_t most = 0;
+        for (uint64_t k = 0; n && k < cbk_ec_blocks(&h); ++k)
+            most = std::max<uint64_t>(most, (k + 1 < cbk_ec_blocks(&h) ? bases[k + 1] : n) - bases[k]);
+        if (cbk_ec_max_block_codes(&h, bases.data()) != most) return fail("ec max block codes", rec);
         // grouped calls with bad arguments (device addresses stand in; nothing is dereferenced)
         if (n) {
             const cbk_ec_tensor et = {n, h.total_bits, reinterpret_cast<const uint8_t *>(0x10000),

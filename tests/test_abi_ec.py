@@ -201,3 +201,27 @@ def test_group_calls_validate_before_any_hip_call(cbk):
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, P(A), None, None) == 1
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 0, R(100, 100), 64, P(A), ptrs(A, A), None) == 1
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, None, ptrs(A, A), None) == 1  # no x
+
+
+def test_max_block_codes_and_its_check(cbk):
+    """cbk_ec_max_block_codes is the largest per-block code count that bases gives (the last block
+    counted up to n), 0 for an empty tensor; a tensor claiming more than a block can hold (16,384)
+    is rejected before any HIP call."""
+    import synth
+    lib = cbk.load_library()
+    rng = np.random.default_rng(9)
+    cases = [synth.gaussian_bf16((300, 777), 0.02, seed=[91]),
+             rng.choice(np.array([0x3F80, 0x4012], dtype=np.uint16), (1, 64 * 256 * 3 + 11)),
+             np.full((10, 1000), 0x3F80, dtype=np.uint16), np.array([[0x3F80]], dtype=np.uint16)]
+    for w in cases:
+        t = cbk.ec_encode(w)
+        want = int(np.diff(np.append(t.bases.astype(np.int64), w.size)).max())
+        assert t.max_block_codes == want, (w.shape, t.max_block_codes, want)
+    assert cbk.ec_encode(np.zeros((0, 8), dtype=np.uint16)).max_block_codes == 0
+    assert lib.cbk_ec_max_block_codes(None, None) == 0
+    T = cbk._ECTensor
+    A = 0x10000
+    bad = T(n=1000, total_bits=3000, sm=A, stream=A, gaps=A, bases=A, lut=A, max_block_codes=16385)
+    assert lib.cbk_ec_decode_bf16(ctypes.byref(bad), ctypes.c_void_p(A), None) == 1
+    ok = T(n=1000, total_bits=3000, sm=A, stream=A, gaps=A, bases=A, lut=A, max_block_codes=16384)
+    assert lib.cbk_ec_decode_bf16_indexed(ctypes.byref(ok), None, ctypes.c_void_p(A), None) == 1  # (no index)

@@ -35,6 +35,16 @@ def _check(env, w, oracle_too=False):
     return t
 
 
+def _mixed_short_codes(shape, seed):
+    """A leading run of 60 % of the weights shares one exponent (random mantissas), so that exponent
+    gets a one-bit code: the blocks of the run hold more codes than the decoder's exponent array
+    and are placed and joined in two halves, the blocks after it in one pass."""
+    w = synth.gaussian_bf16(shape, 0.02, seed=seed).reshape(-1).copy()
+    k = int(0.6 * w.size)
+    w[:k] = (0x3C00 | np.random.default_rng(seed).integers(0, 128, k)).astype(np.uint16)
+    return w.reshape(shape)
+
+
 def _cases():
     rng = np.random.default_rng(21)
     return {
@@ -46,6 +56,9 @@ def _cases():
         "every_pattern": rng.permutation(np.arange(65536, dtype=np.uint32)).astype(np.uint16).reshape(256, 256),
         "specials": rng.choice(np.array([0x7F80, 0xFF80, 0x7FC1, 0x0000, 0x8000, 0x0001, 0x807F], dtype=np.uint16), (9, 111)),
         "one": np.array([[0xC2F7]], dtype=np.uint16),
+        # one-bit codes over several blocks and a ragged end: every block in two halves
+        "one_bit_codes_multi_block": rng.choice(np.array([0x3F80, 0x4012], dtype=np.uint16), (1, 64 * 256 * 3 + 11)),
+        "mixed_short_codes": _mixed_short_codes((200, 1000), [45]),
     }
 
 
@@ -57,6 +70,10 @@ def test_ec_decode_bit_exact(env, name):
         assert t.total_bits == w.size   # 64 one-bit codes in every span
     if name == "t2_heavy_tail":
         assert max(t.lengths) >= 10     # long codes, spans that start inside a code
+    if name == "mixed_short_codes":
+        # blocks of both kinds: more codes than the decoder places at once (8,192) and fewer
+        per_block = np.diff(np.append(t.bases.astype(np.int64), w.size))
+        assert per_block.max() > 8192 and per_block[:-1].min() < 8185, per_block
 
 
 @pytest.mark.parametrize("n", [7, 8, 9, 63, 64, 65, 1000, 16383, 16384, 16385, 64 * 256 * 3 + 11])
@@ -158,6 +175,9 @@ def _gemv_cases():
         "cols_72_500x72": synth.gaussian_bf16((500, 72), 0.02, seed=[61]),
         "specials_free_mix_37x128": rng.choice(np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4000, 0x3C00],
                                                         dtype=np.uint16), (37, 128)),
+        # blocks placed in two halves (one-bit codes), rows crossing the halves and the blocks
+        "one_bit_codes_60x1000": rng.choice(np.array([0x3F80, 0xBF80], dtype=np.uint16), (60, 1000)),
+        "mixed_short_codes_200x1024": _mixed_short_codes((200, 1024), [62]),
     }
 
 
@@ -221,7 +241,8 @@ def _oracle_span_counts(t_host, w):
     return np.array([len(ec.decode_span(o, j)) for j in range(o.spans)], dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["gaussian_300x777", "t2_heavy_tail", "constant", "two_exponents", "specials", "one"])
+@pytest.mark.parametrize("name", ["gaussian_300x777", "t2_heavy_tail", "constant", "two_exponents", "specials", "one",
+                                  "mixed_short_codes"])
 def test_ec_index_counts_equal_the_oracle(env, name):
     torch, cbk = env
     w = _cases()[name]
@@ -383,3 +404,32 @@ def test_ec_gemv_group_workload_rows(env):
         ref, absb = ec.gemv(ec.encode(sub), len(rows), 4096, x)
         err = np.abs(y.cpu().numpy().astype(np.float64)[rows] - ref)
         assert np.all(err <= TOL * absb), f"tensor {i}"
+
+
+def test_ec_decode_fitted_kernel_and_a_wrong_bound(env):
+    """Blocks of at most 8,185 codes take the decode that holds half a block's exponents; a tensor
+    whose stated bound is below its true block counts (one-bit codes: 16,384 per block) gets
+    unspecified values for those blocks but no write outside the output, with and without the
+    index; with its true bound it decodes exactly."""
+    torch, cbk = env
+    n = 64 * 256 * 3 + 11
+    w = np.random.default_rng(77).choice(np.array([0x3F80, 0x4012], dtype=np.uint16), (1, n))
+    d = cbk.ec_encode(w).to("cuda")
+    assert d.max_block_codes == 16384
+    ix = cbk.ec_build_index(d)
+    for index in (None, ix):
+        d.max_block_codes = 8000   # wrong: the fitted kernel runs and skips the full blocks
+        buf = torch.full((n + 64,), -7, dtype=torch.int16, device="cuda")
+        cbk.ec_decode_bf16(d, out=buf[:n].view(torch.bfloat16).view(1, n), index=index)
+        torch.cuda.synchronize()
+        assert bool((buf[n:].cpu() == -7).all())
+        d.max_block_codes = 16384  # true bound: the general kernel, exact
+        out = cbk.ec_decode_bf16(d, index=index)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), w)
+    g = synth.gaussian_bf16((300, 1000), 0.02, seed=[78])
+    dg = cbk.ec_encode(g).to("cuda")
+    assert 0 < dg.max_block_codes <= 8185   # the fitted kernel
+    out = cbk.ec_decode_bf16(dg)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), g)
