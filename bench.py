@@ -23,7 +23,8 @@ each tensor with its own codebook):
              HBM (cbk_ec_decode_group, four tensors per launch, a layer's [q, k, v, o]) or decoded
              inside the batch-1 GEMV (cbk_ec_gemv_group, three per launch, a layer's [q, k, v]);
              --ec-group 1 launches each tensor alone, --ec-index adds the span index.
-  encode4096 cbk_encode_gpu of the attn4096 tensors from raw BF16 in HBM (three launches each).
+  encode4096 cbk_encode_gpu_group of the attn4096 tensors from raw BF16 in HBM, four per call
+             (three launches per call; --enc-group 1: cbk_encode_gpu per tensor).
 
 The step workloads (l70b_*, llama7b) draw their weights on the GPU with the counter-based
 generator of ``synth.counter`` and compress them there with cbk_encode_gpu, one tensor at a time,
@@ -175,7 +176,8 @@ class Workload:
     """A workload's tensors, inputs and outputs on the GPU, and its step (one pass of every phase's
     launch, in order), built exactly as the benchmark times it."""
 
-    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False, ec_group=0):
+    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False, ec_group=0,
+                 enc_group=0):
         import torch
         import synth
         import fly_decode_amd as cbk
@@ -189,6 +191,10 @@ class Workload:
             # a layer's matrices decoded together: [q, k, v, o] for the decode, the [q, k, v] that
             # share x for the fused GEMV
             g = ec_group or (3 if self.ecgemv else 4)
+            self.phases = [list(range(i, min(i + g, len(self.specs)))) for i in range(0, len(self.specs), g)]
+        if self.encode:
+            # a layer's [q, k, v, o] encoded together
+            g = enc_group or 4
             self.phases = [list(range(i, min(i + g, len(self.specs)))) for i in range(0, len(self.specs), g)]
         threads = threads or host_threads()
         t0 = time.perf_counter()
@@ -210,7 +216,8 @@ class Workload:
             self.raws = [torch.from_numpy(w.reshape(-1).view(np.int16)).to("cuda") for w, _ in pairs]
             # the host encodings: sizes for the byte count, and the check after timing
             self.tensors = [c for _, c in pairs]
-            self.ws = torch.empty(cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
+            # one workspace per tensor of a run of up to 8
+            self.ws = torch.empty(8 * cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
             self.enc_cb = [torch.empty(65536, dtype=torch.int16, device="cuda") for _ in self.raws]
             self.enc_words = [torch.empty(cbk.words_for(r.numel(), 16), dtype=torch.int32, device="cuda")
                               for r in self.raws]
@@ -241,9 +248,12 @@ class Workload:
         import fly_decode_amd as cbk
         T, xs, ys = self.tensors, self.xs, self.ys
         for ph in self.phases:
-            if self.encode:
+            if self.encode and len(ph) == 1:
                 i = ph[0]
                 cbk.encode_gpu_launch(self.raws[i], self.ws, self.enc_cb[i], self.enc_words[i], self.enc_meta[i])
+            elif self.encode:
+                cbk.encode_gpu_group_launch([self.raws[i] for i in ph], self.ws, [self.enc_cb[i] for i in ph],
+                                            [self.enc_words[i] for i in ph], [self.enc_meta[i] for i in ph])
             elif self.ecgemv:
                 ix = [self.ec_index[i] for i in ph] if self.ec_index else None
                 if len(ph) == 1:
@@ -631,6 +641,9 @@ def main():
     ap.add_argument("--ec-group", type=int, default=0, metavar="G",
                     help="entropy-coded workloads: tensors per grouped launch (default 4 for the decode, 3 for "
                          "the fused GEMV; 1: one launch per tensor)")
+    ap.add_argument("--enc-group", type=int, default=0, metavar="G",
+                    help="encode4096: tensors per grouped encode (cbk_encode_gpu_group; default 4, 1: "
+                         "cbk_encode_gpu per tensor)")
     ap.add_argument("--launch", choices=("phases", "chain"), default="phases",
                     help="batch 1: one launch per phase (graph-replayed), or the whole step as one GEMV "
                          "chain (a persistent cooperative launch)")
@@ -684,7 +697,7 @@ def main():
     threads = host_threads()
     log(f"workload {args.workload}; host threads {threads} of {os.cpu_count()} CPUs")
     work = Workload(args.workload, count=args.tensors, layers=args.layers, threads=threads, cap=args.cap or None,
-                    ec_index=args.ec_index, ec_group=args.ec_group)
+                    ec_index=args.ec_index, ec_group=args.ec_group, enc_group=args.enc_group)
     if args.no_group:
         work.phases = [[i] for ph in work.phases for i in ph]
     log(f"setup {work.setup_s:.1f} s: {len(work.tensors)} tensors, {len(work.phases)} launches per step, "
@@ -753,7 +766,7 @@ def main():
     kernel_key, kernel_desc = work.kernel_name()
     # traffic records are per launch, taken on each workload's default launch grouping
     traffic_key = args.workload
-    if work.ecfmt and work.phases and len(work.phases[0]) != (3 if work.ecgemv else 4):
+    if (work.ecfmt or work.encode) and work.phases and len(work.phases[0]) != (3 if work.ecgemv else 4):
         traffic_key += f"_g{len(work.phases[0])}"
     traffic = profiling.traffic_for(kernel_key, traffic_key)
     bits = sorted({d.b for d in work.tensors}) if not work.ecfmt else [max(max(d.lengths) for d in work.tensors)]
@@ -793,7 +806,7 @@ def main():
             "graph_replay": graph is not None,
             "launch": args.launch if work.batch == 1 and not work.ecfmt else "phases",
             "ec_span_index": bool(work.ec_index) if work.ecfmt else None,
-            "ec_tensors_per_launch": max(len(ph) for ph in work.phases) if work.ecfmt else None,
+            "tensors_per_launch": max(len(ph) for ph in work.phases),
             "launches_per_step": 2 if chain else 3 * launches if work.encode else 2 * launches if work.ecgemv else launches,
             "codebook_cap": args.cap or None,
             "warmup_seconds_min": args.warmup_seconds,

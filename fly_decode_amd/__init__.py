@@ -43,6 +43,11 @@ class _Tensor(ctypes.Structure):
                 ("b", ctypes.c_uint32), ("codebook", ctypes.c_void_p), ("words", ctypes.c_void_p)]
 
 
+class _EncodeJob(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("n", ctypes.c_uint64), ("codebook", ctypes.c_void_p),
+                ("words", ctypes.c_void_p), ("words_cap", ctypes.c_uint64), ("meta", ctypes.c_void_p)]
+
+
 class _GemvPhase(ctypes.Structure):
     _fields_ = [("ts", ctypes.POINTER(_Tensor)), ("count", ctypes.c_uint32), ("x", ctypes.c_void_p),
                 ("ys", ctypes.POINTER(ctypes.c_void_p))]
@@ -106,6 +111,9 @@ def load_library():
         lib.cbk_encode_gpu.restype = ctypes.c_int
         lib.cbk_encode_gpu.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_encode_gpu_group.restype = ctypes.c_int
+        lib.cbk_encode_gpu_group.argtypes = [ctypes.POINTER(_EncodeJob), ctypes.c_uint32, ctypes.c_void_p,
+                                             ctypes.c_void_p]
         lib.cbk_encode_gpu_noalloc.restype = ctypes.c_int
         lib.cbk_encode_gpu_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
@@ -265,6 +273,18 @@ def encode_gpu_launch(w, workspace, codebook, words, meta, stream=None) -> None:
         ctypes.c_void_p(codebook.data_ptr()), ctypes.c_void_p(words.data_ptr()),
         words.numel() * words.element_size() // 4, ctypes.c_void_p(meta.data_ptr()), _stream(stream)),
         "cbk_encode_gpu")
+
+
+def encode_gpu_group_launch(ws, workspace, codebooks, words, metas, stream=None) -> None:
+    """Enqueue cbk_encode_gpu_group: tensors ws[i] encoded into codebooks[i], words[i], metas[i] (as
+    ``encode_gpu_launch``), one run of three launches per 8 tensors; workspace holds
+    min(len(ws), 8) * encode_gpu_workspace_bytes() bytes."""
+    jobs = (_EncodeJob * len(ws))(*[
+        _EncodeJob(w.data_ptr() if w.numel() else None, w.numel(), cb.data_ptr(), wd.data_ptr(),
+                   wd.numel() * wd.element_size() // 4, m.data_ptr())
+        for w, cb, wd, m in zip(ws, codebooks, words, metas)])
+    _check(load_library().cbk_encode_gpu_group(jobs, len(ws), ctypes.c_void_p(workspace.data_ptr()),
+                                               _stream(stream)), "cbk_encode_gpu_group")
 
 
 def encode_gpu_noalloc_launch(w, codebook, words, meta, stream=None) -> None:

@@ -221,28 +221,45 @@ cbk_status cbk_cap_patterns(const uint16_t *w, uint64_t n, uint32_t K, uint16_t 
 
 size_t cbk_encode_gpu_workspace_bytes(void) { return cbk::encode_gpu_workspace_bytes(); }
 
+// The checks of one GPU encode job (the workspace is checked by the caller).
+static cbk_status check_encode_job(const cbk_encode_job &j) {
+    if (!j.codebook || !j.meta || (j.n > 0 && (!j.w || !j.words))) return CBK_E_INVALID;
+    if (j.n >= (uint64_t(1) << 40)) return CBK_E_UNSUPPORTED;
+    if (!aligned(j.codebook, 2) || !aligned(j.meta, 4) || (j.n > 0 && (!aligned(j.w, 16) || !aligned(j.words, 16))))
+        return CBK_E_ALIGN;
+    if (j.words_cap < cbk_words_for(j.n, 16)) return CBK_E_CAPACITY;
+    return CBK_OK;
+}
+
 cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook, uint32_t *words,
                           uint64_t words_cap, uint32_t *meta, void *stream) {
-    if (!workspace || !codebook || !meta || (n > 0 && (!w || !words))) return CBK_E_INVALID;
-    if (n >= (uint64_t(1) << 40)) return CBK_E_UNSUPPORTED;
-    if (!aligned(workspace, 16) || !aligned(codebook, 2) || !aligned(meta, 4) ||
-        (n > 0 && (!aligned(w, 16) || !aligned(words, 16))))
-        return CBK_E_ALIGN;
-    if (words_cap < cbk_words_for(n, 16)) return CBK_E_CAPACITY;
-    return cbk::launch_encode_gpu(w, n, workspace, codebook, words, meta, static_cast<hipStream_t>(stream));
+    if (!workspace) return CBK_E_INVALID;
+    const cbk_encode_job job{w, n, codebook, words, words_cap, meta};
+    cbk_status st = check_encode_job(job);
+    if (st != CBK_OK) return st;
+    if (!aligned(workspace, 16)) return CBK_E_ALIGN;
+    return cbk::launch_encode_gpu(&job, 1, workspace, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_encode_gpu_group(const cbk_encode_job *jobs, uint32_t count, void *workspace, void *stream) {
+    if (!jobs || !workspace || count == 0) return CBK_E_INVALID;
+    for (uint32_t i = 0; i < count; ++i) {
+        const cbk_status st = check_encode_job(jobs[i]);
+        if (st != CBK_OK) return st;
+    }
+    if (!aligned(workspace, 16)) return CBK_E_ALIGN;
+    return cbk::launch_encode_gpu(jobs, count, workspace, static_cast<hipStream_t>(stream));
 }
 
 cbk_status cbk_encode_gpu_noalloc(const uint16_t *w, uint64_t n, uint16_t *codebook, uint32_t *words,
                                   uint64_t words_cap, uint32_t *meta, void *stream) {
-    if (!codebook || !meta || (n > 0 && (!w || !words))) return CBK_E_INVALID;
-    if (n >= (uint64_t(1) << 40)) return CBK_E_UNSUPPORTED;
-    if (!aligned(codebook, 2) || !aligned(meta, 4) || (n > 0 && (!aligned(w, 16) || !aligned(words, 16))))
-        return CBK_E_ALIGN;
-    if (words_cap < cbk_words_for(n, 16)) return CBK_E_CAPACITY;
-    void *ws = nullptr;
-    const cbk_status st = cbk::encode_gpu_scratch(&ws);
+    const cbk_encode_job job{w, n, codebook, words, words_cap, meta};
+    cbk_status st = check_encode_job(job);
     if (st != CBK_OK) return st;
-    return cbk::launch_encode_gpu(w, n, ws, codebook, words, meta, static_cast<hipStream_t>(stream));
+    void *ws = nullptr;
+    st = cbk::encode_gpu_scratch(&ws);
+    if (st != CBK_OK) return st;
+    return cbk::launch_encode_gpu(&job, 1, ws, static_cast<hipStream_t>(stream));
 }
 
 cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream) {

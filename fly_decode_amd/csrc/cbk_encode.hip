@@ -57,8 +57,39 @@ constexpr int kStreamOnce = 2;
 // Workspace: kCopies global presence bitmaps.
 constexpr size_t kWsMapBytes = kCopies * kMapWords * 4;
 
-__global__ __launch_bounds__(256) void k_enc_clear(uint32_t *__restrict__ map) {
-    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < kCopies * kMapWords; i += gridDim.x * 256) map[i] = 0;
+// A launch takes up to kMaxEncGroup tensors (a transformer block's matrices encoded together), each
+// with its own kCopies bitmaps: workgroups [first_wg[i], first_wg[i + 1]) of a launch work on
+// tensor i.  A single tensor is a group of one.
+constexpr uint32_t kMaxEncGroup = 8;
+struct EncJob {
+    const uint16_t *w;
+    uint64_t n;
+    uint32_t *map;  // its kCopies global bitmaps
+    uint16_t *codebook;
+    uint32_t *meta;
+    uint32_t *words;
+};
+struct EncGroup {
+    uint32_t first_wg[kMaxEncGroup + 1];
+    uint32_t count;
+    EncJob j[kMaxEncGroup];
+};
+
+// The member of the group that workgroup blockIdx.x works on, with the workgroup's index among
+// that member's workgroups and their number (all uniform).
+struct EncMember {
+    uint32_t k, wg, nwg;
+};
+__device__ __forceinline__ EncMember enc_member(const EncGroup &g) {
+    uint32_t k = 0;
+#pragma unroll
+    for (uint32_t i = 1; i < kMaxEncGroup; ++i) k += (i < g.count && blockIdx.x >= g.first_wg[i]) ? 1u : 0u;
+    return EncMember{k, blockIdx.x - g.first_wg[k], g.first_wg[k + 1] - g.first_wg[k]};
+}
+
+// Zero `words` words of bitmaps (the group's, contiguous in the workspace).
+__global__ __launch_bounds__(256) void k_enc_clear(uint32_t *__restrict__ map, uint32_t words) {
+    for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < words; i += gridDim.x * 256) map[i] = 0;
 }
 
 __device__ __forceinline__ void mark(uint32_t *bm, uint32_t v) {
@@ -86,18 +117,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pass_rsrc(const u32x4 *w4, uin
                                              static_cast<int>(bytes), 0x00020000);
 }
 
-__global__ __launch_bounds__(kPresThreads) void k_enc_presence(const uint16_t *__restrict__ w, uint64_t n,
-                                                               uint32_t *__restrict__ map) {
+__global__ __launch_bounds__(kPresThreads) void k_enc_presence(const EncGroup grp) {
     __shared__ uint32_t bm[kMapWords];
+    const EncMember me = enc_member(grp);
+    const EncJob &J = grp.j[me.k];
+    const uint16_t *__restrict__ w = J.w;
+    const uint64_t n = J.n;
+    uint32_t *__restrict__ map = J.map;
     const uint32_t t = threadIdx.x;
     for (uint32_t i = t; i < kMapWords; i += kPresThreads) bm[i] = 0;
     __syncthreads();
     const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w);
     const uint64_t chunks = n / 8;
-    const uint32_t stride = gridDim.x * kPresThreads;      // chunks between a thread's loads
+    const uint32_t stride = me.nwg * kPresThreads;         // chunks between a thread's loads
     const uint64_t span = static_cast<uint64_t>(stride) * kPresUnroll;  // chunks per pass
     const uint64_t passes = (chunks + span - 1) / span;
-    const uint32_t mine = blockIdx.x * kPresThreads + t;   // chunk of this thread's first load
+    const uint32_t mine = me.wg * kPresThreads + t;        // chunk of this thread's first load
     u32x4 a[kPresUnroll], b[kPresUnroll];
     auto load = [&](u32x4 (&v)[kPresUnroll], uint64_t pass) {
         const __amdgpu_buffer_rsrc_t rs = pass_rsrc(w4, chunks, pass, span);
@@ -118,9 +153,9 @@ __global__ __launch_bounds__(kPresThreads) void k_enc_presence(const uint16_t *_
         load(a, p + 2);
         mark_pass(b, p + 1);
     }
-    if (blockIdx.x == 0 && t < n % 8) mark(bm, w[chunks * 8 + t]);
+    if (me.wg == 0 && t < n % 8) mark(bm, w[chunks * 8 + t]);
     __syncthreads();
-    uint32_t *copy = map + (blockIdx.x % kCopies) * kMapWords;
+    uint32_t *copy = map + (me.wg % kCopies) * kMapWords;
     for (uint32_t i = t; i < kMapWords; i += kPresThreads)
         if (bm[i]) atomicOr(&copy[i], bm[i]);
 }
@@ -150,16 +185,17 @@ __device__ __forceinline__ uint32_t index_of(const uint2 *rt, uint32_t v) {
     return e.y + __popc(e.x & ((1u << (v & 31)) - 1u));
 }
 
+// Workgroup wg of the nwg that pack this tensor.
 template <int B>
 __device__ void pack_blocks(const uint16_t *__restrict__ w, uint64_t n, const uint2 *rt,
                             uint32_t *__restrict__ words, uint16_t *sidx, uint32_t *sout,
-                            const u32x4 (&pre)[4]) {
+                            const u32x4 (&pre)[4], uint32_t wg, uint32_t nwg) {
     const uint64_t words_total = ((n * B + 31) / 32 + 3) / 4 * 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t blocks = (n + kPackFields - 1) / kPackFields;
-    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kPackWaves + wave;
+    const uint64_t first = static_cast<uint64_t>(wg) * kPackWaves + wave;
     u32x4 *words4 = reinterpret_cast<u32x4 *>(words);
-    for (uint64_t blk = first; blk < blocks; blk += static_cast<uint64_t>(gridDim.x) * kPackWaves) {
+    for (uint64_t blk = first; blk < blocks; blk += static_cast<uint64_t>(nwg) * kPackWaves) {
         const uint64_t f0 = blk * kPackFields;
         // coalesced: load q covers fields [q*512 + lane*8, +8) of the block
         if (f0 + kPackFields <= n) {
@@ -219,11 +255,15 @@ __device__ void pack_blocks(const uint16_t *__restrict__ w, uint64_t n, const ui
 // table), so no separate rank launch is needed; workgroups share out the codebook writes and
 // workgroup 0 writes U and b.  Each wave's first block is loaded before the ranking so that the
 // stream is already in flight while the table is built.
-__global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__restrict__ w, uint64_t n,
-                                                              const uint32_t *__restrict__ map,
-                                                              uint16_t *__restrict__ codebook,
-                                                              uint32_t *__restrict__ meta,
-                                                              uint32_t *__restrict__ words) {
+__global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const EncGroup grp) {
+    const EncMember me = enc_member(grp);
+    const EncJob &J = grp.j[me.k];
+    const uint16_t *__restrict__ w = J.w;
+    const uint64_t n = J.n;
+    const uint32_t *__restrict__ map = J.map;
+    uint16_t *__restrict__ codebook = J.codebook;
+    uint32_t *__restrict__ meta = J.meta;
+    uint32_t *__restrict__ words = J.words;
     // one 4 KB stage per wave: first the block's 2,048 indices, then (after every lane has read its
     // 32) the block's 64 b packed words
     __shared__ u32x4 stage[kPackWaves][256];
@@ -247,7 +287,7 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__
     // unconditional buffer loads through a wave-uniform resource clipped to the tensor: bytes past
     // its end read as zero without a memory access (a partial block's values go unused)
     u32x4 pre[4];
-    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kPackWaves + wave_u;
+    const uint64_t first = static_cast<uint64_t>(me.wg) * kPackWaves + wave_u;
     const uint64_t f_first = std::min<uint64_t>(first * kPackFields, n);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(w + f_first), static_cast<short>(0),
@@ -282,13 +322,13 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__
     uint32_t b = 0;
     while ((1u << b) < U) ++b;
     b = __builtin_amdgcn_readfirstlane(b);
-    if (blockIdx.x == 0 && t == 0) {
+    if (me.wg == 0 && t == 0) {
         meta[0] = U;
         meta[1] = b;
     }
     __syncthreads();
-    // the codebook: word i (handled by workgroup i % grid) holds entries [its prefix, ...) in order
-    for (uint32_t i = blockIdx.x + t * gridDim.x; i < kMapWords; i += gridDim.x * (64 * kPackWaves)) {
+    // the codebook: word i (handled by workgroup i % nwg) holds entries [its prefix, ...) in order
+    for (uint32_t i = me.wg + t * me.nwg; i < kMapWords; i += me.nwg * (64 * kPackWaves)) {
         const uint2 e = rt[i];
         uint32_t bits = e.x, r = e.y;
         while (bits) {
@@ -300,22 +340,22 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_enc_pack(const uint16_t *__
     uint16_t *si = reinterpret_cast<uint16_t *>(stage[wave]);
     uint32_t *so = reinterpret_cast<uint32_t *>(stage[wave]);
     switch (b) {
-    case 1: pack_blocks<1>(w, n, rt, words, si, so, pre); break;
-    case 2: pack_blocks<2>(w, n, rt, words, si, so, pre); break;
-    case 3: pack_blocks<3>(w, n, rt, words, si, so, pre); break;
-    case 4: pack_blocks<4>(w, n, rt, words, si, so, pre); break;
-    case 5: pack_blocks<5>(w, n, rt, words, si, so, pre); break;
-    case 6: pack_blocks<6>(w, n, rt, words, si, so, pre); break;
-    case 7: pack_blocks<7>(w, n, rt, words, si, so, pre); break;
-    case 8: pack_blocks<8>(w, n, rt, words, si, so, pre); break;
-    case 9: pack_blocks<9>(w, n, rt, words, si, so, pre); break;
-    case 10: pack_blocks<10>(w, n, rt, words, si, so, pre); break;
-    case 11: pack_blocks<11>(w, n, rt, words, si, so, pre); break;
-    case 12: pack_blocks<12>(w, n, rt, words, si, so, pre); break;
-    case 13: pack_blocks<13>(w, n, rt, words, si, so, pre); break;
-    case 14: pack_blocks<14>(w, n, rt, words, si, so, pre); break;
-    case 15: pack_blocks<15>(w, n, rt, words, si, so, pre); break;
-    case 16: pack_blocks<16>(w, n, rt, words, si, so, pre); break;
+    case 1: pack_blocks<1>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 2: pack_blocks<2>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 3: pack_blocks<3>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 4: pack_blocks<4>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 5: pack_blocks<5>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 6: pack_blocks<6>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 7: pack_blocks<7>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 8: pack_blocks<8>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 9: pack_blocks<9>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 10: pack_blocks<10>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 11: pack_blocks<11>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 12: pack_blocks<12>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 13: pack_blocks<13>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 14: pack_blocks<14>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 15: pack_blocks<15>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
+    case 16: pack_blocks<16>(w, n, rt, words, si, so, pre, me.wg, me.nwg); break;
     default: break;  // b == 0: no words
     }
 }
@@ -346,27 +386,62 @@ cbk_status encode_gpu_scratch(void **ws) {
     return CBK_OK;
 }
 
-cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
-                             uint32_t *words, uint32_t *meta, hipStream_t s) {
+// Workgroups for each of a group's tensors: `need` each (at least one), scaled down in proportion
+// when they add up to more than `grid`.
+static uint32_t split_enc(EncGroup &g, const uint64_t *need, uint64_t grid) {
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < g.count; ++i) total += std::max<uint64_t>(1, need[i]);
+    uint32_t at = 0;
+    for (uint32_t i = 0; i < g.count; ++i) {
+        g.first_wg[i] = at;
+        const uint64_t want = std::max<uint64_t>(1, need[i]);
+        const uint64_t share = total <= grid ? want : std::max<uint64_t>(1, (grid * want + total / 2) / total);
+        at += static_cast<uint32_t>(share);
+    }
+    for (uint32_t i = g.count; i <= kMaxEncGroup; ++i) g.first_wg[i] = at;
+    return at;
+}
+
+// One run of up to kMaxEncGroup jobs: clear their bitmaps, mark presence, rank and pack.
+static cbk_status launch_encode_run(const cbk_encode_job *jobs, uint32_t count, uint32_t *maps, int cus,
+                                    hipStream_t s) {
+    EncGroup g{};
+    g.count = count;
+    for (uint32_t i = 0; i < count; ++i)
+        g.j[i] = EncJob{jobs[i].w, jobs[i].n, maps + static_cast<size_t>(i) * kCopies * kMapWords, jobs[i].codebook,
+                        jobs[i].meta, jobs[i].words};
+    const uint32_t map_words = count * kCopies * kMapWords;
+    hipLaunchKernelGGL(k_enc_clear, dim3(std::min<uint32_t>(map_words / 256, 1024)), dim3(256), 0, s, maps, map_words);
+    // presence: two 1,024-thread workgroups per CU, each taking kPresUnroll 16-byte chunks per
+    // thread per pass
+    uint64_t need[kMaxEncGroup];
+    const uint64_t per_block = static_cast<uint64_t>(kPresThreads) * kPresUnroll;
+    for (uint32_t i = 0; i < count; ++i) need[i] = (jobs[i].n / 8 + per_block - 1) / per_block;
+    const uint32_t pgrid = split_enc(g, need, static_cast<uint64_t>(cus) * 2);
+    hipLaunchKernelGGL(k_enc_presence, dim3(pgrid), dim3(kPresThreads), 0, s, g);
+    // pack: two 8-wave workgroups per CU (48 KB of LDS each: the stages and the rank table), which
+    // measured 6 % faster than one of 16 waves; at least one workgroup per tensor, so that U, b
+    // and the codebook are written even for n == 0
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint64_t blocks = (jobs[i].n + kPackFields - 1) / kPackFields;
+        need[i] = (blocks + kPackWaves - 1) / kPackWaves;
+    }
+    const uint32_t kgrid = split_enc(g, need, static_cast<uint64_t>(cus) * 2);
+    hipLaunchKernelGGL(k_enc_pack, dim3(kgrid), dim3(64 * kPackWaves), 0, s, g);
+    return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
+}
+
+cbk_status launch_encode_gpu(const cbk_encode_job *jobs, uint32_t count, void *workspace, hipStream_t s) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return CBK_E_HIP;
-    uint32_t *map = static_cast<uint32_t *>(workspace);
-    hipLaunchKernelGGL(k_enc_clear, dim3(kCopies * kMapWords / 256), dim3(256), 0, s, map);
-    const uint64_t per_block = static_cast<uint64_t>(kPresThreads) * kPresUnroll;
-    const uint64_t chunk_blocks = (n / 8 + per_block - 1) / per_block;
-    const uint32_t pgrid = static_cast<uint32_t>(
-        std::max<uint64_t>(1, std::min<uint64_t>(static_cast<uint64_t>(cus) * 2, chunk_blocks)));
-    hipLaunchKernelGGL(k_enc_presence, dim3(pgrid), dim3(kPresThreads), 0, s, w, n, map);
-    // two 8-wave workgroups per CU (48 KB of LDS each: the stages and the rank table), which
-    // measured 6 % faster than one of 16 waves; at least one workgroup, so that U, b and the
-    // codebook are written even for n == 0
-    const uint64_t blocks = (n + kPackFields - 1) / kPackFields;
-    const uint32_t kgrid = static_cast<uint32_t>(std::max<uint64_t>(
-        1, std::min<uint64_t>(static_cast<uint64_t>(cus) * 2, (blocks + kPackWaves - 1) / kPackWaves)));
-    hipLaunchKernelGGL(k_enc_pack, dim3(kgrid), dim3(64 * kPackWaves), 0, s, w, n, map, codebook, meta, words);
-    return hipGetLastError() == hipSuccess ? CBK_OK : CBK_E_HIP;
+    uint32_t *maps = static_cast<uint32_t *>(workspace);
+    for (uint32_t i = 0; i < count; i += kMaxEncGroup) {
+        const cbk_status st = launch_encode_run(jobs + i, std::min(kMaxEncGroup, count - i), maps, cus, s);
+        if (st != CBK_OK) return st;
+    }
+    return CBK_OK;
 }
 
 }  // namespace cbk

@@ -26,8 +26,9 @@ cbk_status launch_gemm_group(const cbk_tensor *ts, uint32_t count, const uint16_
 
 // GPU encoder (cbk_encode.hip).
 size_t encode_gpu_workspace_bytes();
-cbk_status launch_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16_t *codebook,
-                             uint32_t *words, uint32_t *meta, hipStream_t s);
+// count jobs, in runs of up to 8 (each run uses the first min(count, 8) workspaces of
+// encode_gpu_workspace_bytes() bytes).
+cbk_status launch_encode_gpu(const cbk_encode_job *jobs, uint32_t count, void *workspace, hipStream_t s);
 // Device address of the library's static encoder scratch on the current device (a workspace of
 // encode_gpu_workspace_bytes() bytes); looked up on the device's first call.
 cbk_status encode_gpu_scratch(void **ws);

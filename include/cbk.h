@@ -134,6 +134,30 @@ cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16
                           uint64_t words_cap, uint32_t *meta, void *stream);
 
 /*
+ * cbk_encode_gpu_group -- GPU.  cbk_encode_gpu for several tensors, such as a transformer block's
+ * matrices, with one clear, one presence and one pack launch per run of up to 8 tensors (more are
+ * split into runs of 8) instead of three launches each: the launches' start-up and tail are paid
+ * once per run, as the DFloat11 page does for a block's matrices ("How it works in practice",
+ * block-level decompression).  Each job's result is bit-identical to cbk_encode_gpu on it.
+ *   jobs       host array of count jobs; each job's fields mean what the same-named arguments of
+ *              cbk_encode_gpu mean, with the same alignment rules.
+ *   workspace  device scratch of min(count, 8) * cbk_encode_gpu_workspace_bytes() bytes, 16-byte
+ *              aligned, owned by the caller; its contents on entry do not matter.
+ * Errors: CBK_E_INVALID (NULL jobs or workspace, count == 0, or a job with a null pointer); then
+ * each job's checks as in cbk_encode_gpu, in order; the first failure is returned and nothing is
+ * enqueued.
+ */
+typedef struct {
+    const uint16_t *w;   /* in, device, n patterns                                   */
+    uint64_t n;
+    uint16_t *codebook;  /* out, device, capacity 65536 entries                       */
+    uint32_t *words;     /* out, device, capacity words_cap >= cbk_words_for(n, 16)   */
+    uint64_t words_cap;
+    uint32_t *meta;      /* out, device, meta[0] = U, meta[1] = b                     */
+} cbk_encode_job;
+cbk_status cbk_encode_gpu_group(const cbk_encode_job *jobs, uint32_t count, void *workspace, void *stream);
+
+/*
  * cbk_encode_gpu_noalloc -- GPU.  For callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same encoding as
  * cbk_encode_gpu (arguments, result, alignment and errors as there), without the workspace

@@ -29,7 +29,7 @@ cbk_status build_gemv_chain(const cbk_gemv_phase *, uint32_t, void *, cbk_gemv_c
 cbk_status launch_gemv_chain(const cbk_gemv_chain &, uint32_t, hipStream_t) { reached("gemv_chain_run"); }
 cbk_status gemv_chain_check(const cbk_gemv_chain &) { reached("gemv_chain_check"); }
 size_t encode_gpu_workspace_bytes() { return 65536; }
-cbk_status launch_encode_gpu(const uint16_t *, uint64_t, void *, uint16_t *, uint32_t *, uint32_t *, hipStream_t) {
+cbk_status launch_encode_gpu(const cbk_encode_job *, uint32_t, void *, hipStream_t) {
     reached("encode_gpu");
 }
 cbk_status encode_gpu_scratch(void **) { reached("encode_gpu_scratch"); }

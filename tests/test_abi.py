@@ -196,6 +196,27 @@ def test_gpu_encoder_validates_before_any_hip_call(cbk):
     assert lib.cbk_encode_gpu(W, 1 << 40, WS, CB, WD, 1 << 62, M, None) == 4      # n beyond the limit
 
 
+def test_gpu_encoder_group_validates_before_any_hip_call(cbk):
+    """cbk_encode_gpu_group checks the array, the count and the workspace, then every job as
+    cbk_encode_gpu does, before anything is launched (a failure in the last job is found)."""
+    lib = cbk.load_library()
+    J = cbk._EncodeJob
+    cap = cbk.words_for(1000, 16)
+    good = dict(w=0x10000, n=1000, codebook=0x30000, words=0x40000, words_cap=cap, meta=0x50000)
+
+    def jobs(*ds):
+        return (J * len(ds))(*[J(**d) for d in ds])
+    WS = ctypes.c_void_p(0x20000)
+    assert lib.cbk_encode_gpu_group(None, 1, WS, None) == 1
+    assert lib.cbk_encode_gpu_group(jobs(good), 0, WS, None) == 1
+    assert lib.cbk_encode_gpu_group(jobs(good), 1, None, None) == 1
+    assert lib.cbk_encode_gpu_group(jobs(good, dict(good, meta=None)), 2, WS, None) == 1
+    assert lib.cbk_encode_gpu_group(jobs(good, dict(good, w=0x10008)), 2, WS, None) == 3
+    assert lib.cbk_encode_gpu_group(jobs(good, dict(good, words_cap=cap - 1)), 2, WS, None) == 2
+    assert lib.cbk_encode_gpu_group(jobs(good, dict(good, n=1 << 40, words_cap=1 << 62)), 2, WS, None) == 4
+    assert lib.cbk_encode_gpu_group(jobs(good, good), 2, ctypes.c_void_p(0x20004), None) == 3
+
+
 def test_gpu_encoder_noalloc_validates_before_any_hip_call(cbk):
     """cbk_encode_gpu_noalloc rejects bad arguments on the host, before it looks up its static
     scratch or launches anything (no device is present here)."""

@@ -496,6 +496,30 @@ def test_encode_gpu_workload_tensor_and_oracle(env, oracle_mod):
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape), w)
 
 
+def test_encode_gpu_group_matches_host(env):
+    """cbk_encode_gpu_group over eleven tensors (a run of eight, then three reusing the first
+    workspaces): empty and ragged lengths, widths from 0 to 16 (every 16-bit pattern) and a
+    workload tensor; each job's codebook, U, b and words equal the host encoder's."""
+    torch, cbk = env
+    ws = [synth.gaussian_bf16((n,), 0.02, seed=[97, n]) for n in (0, 1, 7, 2049, 100003)]
+    ws += [synth.with_distinct_count(max(U, 50000), U, seed=[98, U]) for U in (1, 2, 257, 32769, 65536)]
+    ws.append(synth.workload_tensor(1, 0, synth.WORKLOADS[1][0][0]).reshape(-1))
+    print(f"encode group of {len(ws)} tensors", flush=True)
+    devs = [torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to("cuda") for w in ws]
+    cbs = [torch.empty(65536, dtype=torch.int16, device="cuda") for _ in ws]
+    words = [torch.full((max(cbk.words_for(w.size, 16), 4),), -1, dtype=torch.int32, device="cuda") for w in ws]
+    metas = [torch.full((2,), -1, dtype=torch.int32, device="cuda") for _ in ws]
+    space = torch.empty(8 * cbk.encode_gpu_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    cbk.encode_gpu_group_launch(devs, space, cbs, words, metas)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        host = cbk.encode(w.reshape(1, -1))
+        U, b = (int(v) for v in metas[i].cpu().tolist())
+        assert (U, b) == (host.U, host.b), (i, w.size)
+        assert np.array_equal(cbs[i][:U].cpu().numpy().view(np.uint16), host.codebook), i
+        assert np.array_equal(words[i][:cbk.words_for(w.size, b)].cpu().numpy().view(np.uint32), host.words), i
+
+
 @pytest.mark.parametrize("rows,K,U", [([1, 4097, 33], 1024, 600), ([8193, 1, 2, 1023], 640, 600),
                                       ([300, 7], 4160, 4500), ([2049, 1025, 513, 3], 8192, 4500),
                                       ([100, 31, 7, 1], 12288, 4500)])
