@@ -18,13 +18,16 @@ each tensor with its own codebook):
              per layer [gate, up] one grouped launch, then down.
   mlp_b8     the same tensors at batch 8 (VALU skinny GEMM).
   attn4096   24 distinct 4096x4096 attention projections, N(0, 0.02), one cbk_gemv launch each.
-  decode4096 standalone decode to BF16 in HBM (cbk_decode_bf16) of the attn4096 tensors.
+  decode4096 standalone decode to BF16 in HBM of the attn4096 tensors, four per call
+             (cbk_decode_group, a layer's [q, k, v, o]).
   ecdecode4096 / ecgemv4096  the attn4096 tensors in the exponent entropy-coded format, decoded to
              HBM (cbk_ec_decode_group, four tensors per launch, a layer's [q, k, v, o]) or decoded
              inside the batch-1 GEMV (cbk_ec_gemv_group, three per launch, a layer's [q, k, v]);
-             --ec-group 1 launches each tensor alone, --ec-index adds the span index.
+             --ec-index adds the span index.
   encode4096 cbk_encode_gpu_group of the attn4096 tensors from raw BF16 in HBM, four per call
-             (three launches per call; --enc-group 1: cbk_encode_gpu per tensor).
+             (three launches per call).
+  --tensors-per-call G sets the tensors per call of these five (1: one call per tensor, as
+  attn4096 always does by default).
 
 The step workloads (l70b_*, llama7b) draw their weights on the GPU with the counter-based
 generator of ``synth.counter`` and compress them there with cbk_encode_gpu, one tensor at a time,
@@ -66,6 +69,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 TOL = 1e-3  # |y - y_ref| <= TOL * sum_k |W x| per element
+# tensors per call of the 4096x4096 workloads (--tensors-per-call overrides)
+PER_CALL_DEFAULT = {"attn4096": 1, "decode4096": 4, "encode4096": 4, "ecdecode4096": 4, "ecgemv4096": 3}
 STEP_WORKLOADS = ("l70b_b1", "l70b_b16", "llama7b")
 ALL_WORKLOADS = ["l70b_b1", "l70b_b16", "llama7b", "mlp_b1", "mlp_b8", "attn4096", "decode4096",
                  "encode4096", "ecdecode4096", "ecgemv4096"]
@@ -176,8 +181,7 @@ class Workload:
     """A workload's tensors, inputs and outputs on the GPU, and its step (one pass of every phase's
     launch, in order), built exactly as the benchmark times it."""
 
-    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False, ec_group=0,
-                 enc_group=0):
+    def __init__(self, name, count=24, layers=0, threads=None, cap=None, tensors=None, ec_index=False, per_call=0):
         import torch
         import synth
         import fly_decode_amd as cbk
@@ -187,14 +191,10 @@ class Workload:
         self.encode = name == "encode4096"
         self.ecfmt = name in ("ecdecode4096", "ecgemv4096")
         self.ecgemv = name == "ecgemv4096"
-        if self.ecfmt:
-            # a layer's matrices decoded together: [q, k, v, o] for the decode, the [q, k, v] that
-            # share x for the fused GEMV
-            g = ec_group or (3 if self.ecgemv else 4)
-            self.phases = [list(range(i, min(i + g, len(self.specs)))) for i in range(0, len(self.specs), g)]
-        if self.encode:
-            # a layer's [q, k, v, o] encoded together
-            g = enc_group or 4
+        if name in PER_CALL_DEFAULT:
+            # tensors per call: a layer's [q, k, v, o] decoded or encoded together, the [q, k, v]
+            # that share x in the entropy-coded fused GEMV; attn4096 is the single-tensor GEMV
+            g = per_call or PER_CALL_DEFAULT[name]
             self.phases = [list(range(i, min(i + g, len(self.specs)))) for i in range(0, len(self.specs), g)]
         threads = threads or host_threads()
         t0 = time.perf_counter()
@@ -266,8 +266,10 @@ class Workload:
                     cbk.ec_decode_bf16(T[ph[0]], out=ys[ph[0]], index=ix and ix[0])
                 else:
                     cbk.ec_decode_group([T[i] for i in ph], outs=[ys[i] for i in ph], indexes=ix)
-            elif self.batch == 0:
+            elif self.batch == 0 and len(ph) == 1:
                 cbk.decode_bf16(T[ph[0]], out=ys[ph[0]])
+            elif self.batch == 0:
+                cbk.decode_group([T[i] for i in ph], outs=[ys[i] for i in ph])
             elif self.batch > 1 and len(ph) == 1:
                 cbk.gemm_small(T[ph[0]], xs[T[ph[0]].cols], Y=ys[ph[0]])
             elif self.batch > 1:
@@ -638,12 +640,9 @@ def main():
     ap.add_argument("--no-group", action="store_true", help="one launch per tensor (no grouped phases)")
     ap.add_argument("--ec-index", action="store_true",
                     help="entropy-coded workloads: build the span index at setup and decode with one walk per span")
-    ap.add_argument("--ec-group", type=int, default=0, metavar="G",
-                    help="entropy-coded workloads: tensors per grouped launch (default 4 for the decode, 3 for "
-                         "the fused GEMV; 1: one launch per tensor)")
-    ap.add_argument("--enc-group", type=int, default=0, metavar="G",
-                    help="encode4096: tensors per grouped encode (cbk_encode_gpu_group; default 4, 1: "
-                         "cbk_encode_gpu per tensor)")
+    ap.add_argument("--tensors-per-call", type=int, default=0, metavar="G",
+                    help="the 4096x4096 workloads: tensors per grouped call (default: 4 for decode4096, "
+                         "encode4096 and ecdecode4096, 3 for ecgemv4096, 1 for attn4096; 1: one call per tensor)")
     ap.add_argument("--launch", choices=("phases", "chain"), default="phases",
                     help="batch 1: one launch per phase (graph-replayed), or the whole step as one GEMV "
                          "chain (a persistent cooperative launch)")
@@ -697,7 +696,7 @@ def main():
     threads = host_threads()
     log(f"workload {args.workload}; host threads {threads} of {os.cpu_count()} CPUs")
     work = Workload(args.workload, count=args.tensors, layers=args.layers, threads=threads, cap=args.cap or None,
-                    ec_index=args.ec_index, ec_group=args.ec_group, enc_group=args.enc_group)
+                    ec_index=args.ec_index, per_call=args.tensors_per_call)
     if args.no_group:
         work.phases = [[i] for ph in work.phases for i in ph]
     log(f"setup {work.setup_s:.1f} s: {len(work.tensors)} tensors, {len(work.phases)} launches per step, "
@@ -766,7 +765,7 @@ def main():
     kernel_key, kernel_desc = work.kernel_name()
     # traffic records are per launch, taken on each workload's default launch grouping
     traffic_key = args.workload
-    if (work.ecfmt or work.encode) and work.phases and len(work.phases[0]) != (3 if work.ecgemv else 4):
+    if args.workload in PER_CALL_DEFAULT and work.phases and len(work.phases[0]) != PER_CALL_DEFAULT[args.workload]:
         traffic_key += f"_g{len(work.phases[0])}"
     traffic = profiling.traffic_for(kernel_key, traffic_key)
     bits = sorted({d.b for d in work.tensors}) if not work.ecfmt else [max(max(d.lengths) for d in work.tensors)]

@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = ["CBK_OK", "CbkError", "bits_for", "words_for", "compressed_bytes", "encode",
-           "Compressed", "decode_bf16", "gemv", "gemv_group", "gemm_small", "library_path",
+           "Compressed", "decode_bf16", "decode_group", "gemv", "gemv_group", "gemm_small", "library_path",
            "load_library", "ECTensor", "ec_encode", "ec_decode_bf16", "ec_gemv", "ec_build_index",
            "ec_decode_group", "ec_gemv_group", "cap_patterns",
            "GemvChain"]
@@ -111,6 +111,8 @@ def load_library():
         lib.cbk_encode_gpu.restype = ctypes.c_int
         lib.cbk_encode_gpu.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.cbk_decode_group.restype = ctypes.c_int
+        lib.cbk_decode_group.argtypes = [tp, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]
         lib.cbk_encode_gpu_group.restype = ctypes.c_int
         lib.cbk_encode_gpu_group.argtypes = [ctypes.POINTER(_EncodeJob), ctypes.c_uint32, ctypes.c_void_p,
                                              ctypes.c_void_p]
@@ -339,6 +341,18 @@ def decode_bf16(t: Compressed, out=None, stream=None):
     _check(load_library().cbk_decode_bf16(ctypes.byref(ts), ctypes.c_void_p(out.data_ptr() or None),
                                           _stream(stream)), "cbk_decode_bf16")
     return out
+
+
+def decode_group(ts, outs=None, stream=None):
+    """cbk_decode_group: several tensors decoded into [rows][cols] torch.bfloat16 tensors, one launch
+    per run of up to 8 of one width (each output bit-identical to ``decode_bf16``)."""
+    import torch
+    if outs is None:
+        outs = [torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device=t.words.device) for t in ts]
+    arr = (_Tensor * len(ts))(*[t._struct() for t in ts])
+    ptrs = (ctypes.c_void_p * len(outs))(*[o.data_ptr() or None for o in outs])
+    _check(load_library().cbk_decode_group(arr, len(ts), ptrs, _stream(stream)), "cbk_decode_group")
+    return outs
 
 
 def gemv(t: Compressed, x, y=None, stream=None):

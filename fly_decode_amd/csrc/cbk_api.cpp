@@ -242,7 +242,8 @@ cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16
 }
 
 cbk_status cbk_encode_gpu_group(const cbk_encode_job *jobs, uint32_t count, void *workspace, void *stream) {
-    if (!jobs || !workspace || count == 0) return CBK_E_INVALID;
+    if (count == 0) return CBK_OK;
+    if (!jobs || !workspace) return CBK_E_INVALID;
     for (uint32_t i = 0; i < count; ++i) {
         const cbk_status st = check_encode_job(jobs[i]);
         if (st != CBK_OK) return st;
@@ -262,14 +263,30 @@ cbk_status cbk_encode_gpu_noalloc(const uint16_t *w, uint64_t n, uint16_t *codeb
     return cbk::launch_encode_gpu(&job, 1, ws, static_cast<hipStream_t>(stream));
 }
 
-cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream) {
+// The checks of one decode (n == 0 passes: nothing to do).
+static cbk_status check_decode(const cbk_tensor *t, const uint16_t *out) {
     cbk_status st = check_tensor(t);
     if (st != CBK_OK) return st;
-    const uint64_t n = t->rows * t->cols;
-    if (n == 0) return CBK_OK;
+    if (t->rows * t->cols == 0) return CBK_OK;
     if (!out) return CBK_E_INVALID;
     if (!aligned(out, 2)) return CBK_E_ALIGN;
+    return CBK_OK;
+}
+
+cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream) {
+    const cbk_status st = check_decode(t, out);
+    if (st != CBK_OK || t->rows * t->cols == 0) return st;
     return cbk::launch_decode(*t, out, static_cast<hipStream_t>(stream));
+}
+
+cbk_status cbk_decode_group(const cbk_tensor *ts, uint32_t count, uint16_t *const *outs, void *stream) {
+    if (count == 0) return CBK_OK;
+    if (!ts || !outs) return CBK_E_INVALID;
+    for (uint32_t i = 0; i < count; ++i) {
+        const cbk_status st = check_decode(&ts[i], outs[i]);
+        if (st != CBK_OK) return st;
+    }
+    return cbk::launch_decode_group(ts, count, outs, static_cast<hipStream_t>(stream));
 }
 
 cbk_status cbk_gemv(const cbk_tensor *t, const uint16_t *x, float *y, void *stream) {

@@ -280,7 +280,8 @@ cbk_status cbk_ec_gemv_indexed(const cbk_ec_tensor *t, const uint8_t *index, uin
 
 cbk_status cbk_ec_decode_group(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
                                uint16_t *const *outs, void *stream) {
-    if (!ts || !outs || count == 0) return CBK_E_INVALID;
+    if (count == 0) return CBK_OK;
+    if (!ts || !outs) return CBK_E_INVALID;
     for (uint32_t i = 0; i < count; ++i) {
         const cbk_status st = check_decode(&ts[i], indexes ? indexes[i] : nullptr, indexes != nullptr, outs[i]);
         if (st != CBK_OK) return st;
@@ -290,7 +291,8 @@ cbk_status cbk_ec_decode_group(const cbk_ec_tensor *ts, const uint8_t *const *in
 
 cbk_status cbk_ec_gemv_group(const cbk_ec_tensor *ts, const uint8_t *const *indexes, uint32_t count,
                              const uint64_t *rows, uint64_t cols, const uint16_t *x, float *const *ys, void *stream) {
-    if (!ts || !rows || !ys || count == 0) return CBK_E_INVALID;
+    if (count == 0) return CBK_OK;
+    if (!ts || !rows || !ys) return CBK_E_INVALID;
     for (uint32_t i = 0; i < count; ++i) {
         const cbk_status st =
             check_gemv(&ts[i], indexes ? indexes[i] : nullptr, indexes != nullptr, rows[i], cols, x, ys[i]);

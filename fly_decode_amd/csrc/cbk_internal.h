@@ -11,6 +11,7 @@
 namespace cbk {
 
 cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s);
+cbk_status launch_decode_group(const cbk_tensor *ts, uint32_t count, uint16_t *const *outs, hipStream_t s);
 cbk_status launch_gemv(const cbk_tensor &t, const uint16_t *x, float *y, hipStream_t s);
 cbk_status launch_gemv_group(const cbk_tensor *ts, uint32_t count, const uint16_t *x,
                              float *const *ys, hipStream_t s);

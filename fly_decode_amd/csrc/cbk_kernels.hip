@@ -274,19 +274,42 @@ constexpr uint32_t decode_stage_bytes() {
     return U64<B>::STAGE_CHUNKS * 16 > 64 * kOutUnit ? U64<B>::STAGE_CHUNKS * 16 : 64 * kOutUnit;
 }
 
+// A launch decodes up to kMaxGroup tensors of one width (a transformer block's matrices together):
+// workgroups [first_wg[i], first_wg[i + 1]) take tensor i.  A single tensor is a group of one.
+struct DecodeTensor {
+    const u32x4 *w4;
+    const uint16_t *cb;
+    uint16_t *out;
+    uint64_t n;
+    uint32_t nchunks, U, T;
+};
+constexpr int kMaxDecodeGroup = 8;
+struct DecodeGroup {
+    uint32_t first_wg[kMaxDecodeGroup + 1];
+    uint32_t count;
+    DecodeTensor t[kMaxDecodeGroup];
+};
+
 template <int B>
-__global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const u32x4 *__restrict__ w4,
-                                                                   const uint16_t *__restrict__ cb,
-                                                                   uint16_t *__restrict__ out, uint64_t n,
-                                                                   uint32_t nchunks, uint32_t U, uint32_t T) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void k_decode_fast(const DecodeGroup grp) {
     using G = U64<B>;
     constexpr int NT = 64 * kDecodeWaves;
     __shared__ __attribute__((aligned(16))) uint16_t cbl[Table<B>::SIZE];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint32_t k = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxDecodeGroup; ++i) k += (i < static_cast<int>(grp.count) && blockIdx.x >= grp.first_wg[i]) ? 1u : 0u;
+    const DecodeTensor &Tn = grp.t[k];
+    const u32x4 *__restrict__ w4 = Tn.w4;
+    const uint16_t *__restrict__ cb = Tn.cb;
+    uint16_t *__restrict__ out = Tn.out;
+    const uint64_t n = Tn.n;
+    const uint32_t nchunks = Tn.nchunks, U = Tn.U, T = Tn.T;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     unsigned char *stb = smem + wave * decode_stage_bytes<B>();
     u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
-    const uint32_t NW = gridDim.x * kDecodeWaves, gw = blockIdx.x * kDecodeWaves + wave;
+    const uint32_t NW = (grp.first_wg[k + 1] - grp.first_wg[k]) * kDecodeWaves,
+                   gw = (blockIdx.x - grp.first_wg[k]) * kDecodeWaves + wave;
     const uint32_t steps = (T + 63) / 64;
 
     CbStage<B, NT> cs;
@@ -1435,28 +1458,44 @@ bool dispatch_b(int b, Args &args, std::integer_sequence<int, Bs...>) {
 }
 using AllB = std::integer_sequence<int, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>;
 
+// A run of up to kMaxDecodeGroup tensors of width B with n > 0 and 16-byte aligned outputs.
 struct DecodeArgs {
-    const cbk_tensor &t; uint16_t *out; hipStream_t s; cbk_status st;
+    const cbk_tensor *ts; uint32_t count; uint16_t *const *outs; hipStream_t s; cbk_status st;
 };
 
 template <int B>
 struct DecodeRun {
     static bool run(DecodeArgs &a) {
-        const cbk_tensor &t = a.t;
-        const uint64_t n = t.rows * t.cols;
-        const uint64_t T64 = (n + 63) / 64;
-        const uint64_t nchunks = cbk_words_for(n, B) / 4;
-        if (T64 * U64<B>::UD / 4 + 64 * U64<B>::LPL >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32)) return false;
-        if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
         const uint32_t lds = kDecodeWaves * decode_stage_bytes<B>();
         if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
         if (!allow_lds(k_decode_fast<B>, lds)) return false;
-        const uint64_t steps = (T64 + 63) / 64;
-        const uint32_t grid = static_cast<uint32_t>(
-            std::max<uint64_t>(1, std::min<uint64_t>(2 * cu_count(), (steps + kDecodeWaves - 1) / kDecodeWaves)));
-        hipLaunchKernelGGL(k_decode_fast<B>, dim3(grid), dim3(64 * kDecodeWaves), lds, a.s,
-                           reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.out, n,
-                           static_cast<uint32_t>(nchunks), t.U, static_cast<uint32_t>(T64));
+        DecodeGroup grp{};
+        grp.count = a.count;
+        uint64_t need[kMaxDecodeGroup], total = 0;
+        for (uint32_t i = 0; i < a.count; ++i) {
+            const cbk_tensor &t = a.ts[i];
+            const uint64_t n = t.rows * t.cols;
+            const uint64_t T64 = (n + 63) / 64;
+            const uint64_t nchunks = cbk_words_for(n, B) / 4;
+            if (T64 * U64<B>::UD / 4 + 64 * U64<B>::LPL >= (uint64_t(1) << 32) || nchunks >= (uint64_t(1) << 32))
+                return false;
+            if (reinterpret_cast<uintptr_t>(t.codebook) & 15) return false;
+            grp.t[i] = DecodeTensor{reinterpret_cast<const u32x4 *>(t.words), t.codebook, a.outs[i], n,
+                                    static_cast<uint32_t>(nchunks), t.U, static_cast<uint32_t>(T64)};
+            need[i] = std::max<uint64_t>(1, ((T64 + 63) / 64 + kDecodeWaves - 1) / kDecodeWaves);
+            total += need[i];
+        }
+        // two workgroups per CU in all, divided in proportion to the tensors' wave steps, at
+        // least one each
+        const uint64_t grid = std::max<uint64_t>(a.count, std::min<uint64_t>(2 * cu_count(), total));
+        uint32_t at = 0;
+        for (uint32_t i = 0; i < a.count; ++i) {
+            grp.first_wg[i] = at;
+            at += static_cast<uint32_t>(
+                std::max<uint64_t>(1, std::min<uint64_t>(need[i], (grid * need[i] + total / 2) / total)));
+        }
+        for (uint32_t i = a.count; i <= static_cast<uint32_t>(kMaxDecodeGroup); ++i) grp.first_wg[i] = at;
+        hipLaunchKernelGGL(k_decode_fast<B>, dim3(at), dim3(64 * kDecodeWaves), lds, a.s, grp);
         a.st = launched();
         return true;
     }
@@ -1633,16 +1672,52 @@ struct GemmRun {
 
 }  // namespace
 
-cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s) {
+static cbk_status launch_decode_generic(const cbk_tensor &t, uint16_t *out, hipStream_t s) {
     const uint64_t n = t.rows * t.cols;
-    if (t.b > 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-        DecodeArgs a{t, out, s, CBK_OK};
-        if (dispatch_b<DecodeRun>(static_cast<int>(t.b), a, AllB{})) return a.st;
-    }
     const uint32_t grid = static_cast<uint32_t>(std::min<uint64_t>((n + 255) / 256, 65536));
     hipLaunchKernelGGL(k_decode_generic, dim3(grid), dim3(256), 0, s, t.words, t.b, t.codebook, t.U,
                        out, n);
     return launched();
+}
+
+cbk_status launch_decode_group(const cbk_tensor *ts, uint32_t count, uint16_t *const *outs, hipStream_t s) {
+    // Runs of up to kMaxDecodeGroup consecutive nonempty tensors of one width b > 0 with 16-byte
+    // aligned outputs take one fast launch each; the rest, and any run the fast kernel declines,
+    // take the generic kernel one tensor at a time.
+    auto fast = [&](uint32_t k) {
+        return ts[k].b > 0 && ts[k].rows * ts[k].cols > 0 && (reinterpret_cast<uintptr_t>(outs[k]) & 15) == 0;
+    };
+    uint32_t i = 0;
+    while (i < count) {
+        if (ts[i].rows * ts[i].cols == 0) {
+            ++i;
+            continue;
+        }
+        uint32_t j = i + 1;
+        if (fast(i))
+            while (j < count && j - i < static_cast<uint32_t>(kMaxDecodeGroup) && fast(j) && ts[j].b == ts[i].b) ++j;
+        bool done = false;
+        if (fast(i)) {
+            DecodeArgs a{ts + i, j - i, outs + i, s, CBK_OK};
+            if (dispatch_b<DecodeRun>(static_cast<int>(ts[i].b), a, AllB{})) {
+                if (a.st != CBK_OK) return a.st;
+                done = true;
+            }
+        }
+        if (!done) {
+            for (uint32_t k = i; k < j; ++k) {
+                const cbk_status st = launch_decode_generic(ts[k], outs[k], s);
+                if (st != CBK_OK) return st;
+            }
+        }
+        i = j;
+    }
+    return CBK_OK;
+}
+
+cbk_status launch_decode(const cbk_tensor &t, uint16_t *out, hipStream_t s) {
+    uint16_t *outs[1] = {out};
+    return launch_decode_group(&t, 1, outs, s);
 }
 
 cbk_status launch_gemm_generic(const cbk_tensor &t, const uint16_t *X, uint64_t ldx, uint32_t batch,

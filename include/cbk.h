@@ -143,9 +143,9 @@ cbk_status cbk_encode_gpu(const uint16_t *w, uint64_t n, void *workspace, uint16
  *              cbk_encode_gpu mean, with the same alignment rules.
  *   workspace  device scratch of min(count, 8) * cbk_encode_gpu_workspace_bytes() bytes, 16-byte
  *              aligned, owned by the caller; its contents on entry do not matter.
- * Errors: CBK_E_INVALID (NULL jobs or workspace, count == 0, or a job with a null pointer); then
- * each job's checks as in cbk_encode_gpu, in order; the first failure is returned and nothing is
- * enqueued.
+ * count == 0 is a no-op.  Errors: CBK_E_INVALID (NULL jobs or workspace, or a job with a null
+ * pointer); then each job's checks as in cbk_encode_gpu, in order; the first failure is returned
+ * and nothing is enqueued.
  */
 typedef struct {
     const uint16_t *w;   /* in, device, n patterns                                   */
@@ -185,6 +185,20 @@ cbk_status cbk_encode_gpu_noalloc(const uint16_t *w, uint64_t n, uint16_t *codeb
  *   out   device, rows*cols uint16, 2-byte aligned.
  */
 cbk_status cbk_decode_bf16(const cbk_tensor *t, uint16_t *out, void *stream);
+
+/*
+ * cbk_decode_group -- GPU.  cbk_decode_bf16 for count tensors: consecutive tensors of one width
+ * (up to 8) are decoded by one launch whose workgroups are divided among them, so a transformer
+ * block's matrices pay one launch's start-up and tail (the DFloat11 page, "How it works in
+ * practice": a block's matrices decompressed together).  Each output is bit-identical to
+ * cbk_decode_bf16 on its tensor.
+ *   ts    host array of count tensors (device arrays inside).
+ *   outs  host array of count device pointers, outs[i] holds rows*cols uint16 of ts[i], 2-byte
+ *         aligned (16-byte aligned outputs take the fast kernel); outputs must not overlap.
+ * count == 0 is a no-op.  Errors: CBK_E_INVALID for a NULL array; every tensor is checked as by
+ * cbk_decode_bf16 before anything is launched, and the first failure's status is returned.
+ */
+cbk_status cbk_decode_group(const cbk_tensor *ts, uint32_t count, uint16_t *const *outs, void *stream);
 
 /*
  * cbk_gemv -- GPU.  Fused decode + GEMV at batch 1: y[r] = sum_k W[r][k] * x[k], products and

@@ -171,7 +171,7 @@ cbk_status cbk_ec_gemv_indexed(const cbk_ec_tensor *t, const uint8_t *index, uin
  *   rows     host array of count row counts, rows[i] * cols == ts[i].n.
  *   x        device, cols BF16 patterns, 16-byte aligned (read when cols > 0).
  *   ys       host array of count device pointers, ys[i] holds rows[i] fp32, 4-byte aligned.
- * Errors: count == 0 or a NULL ts, outs, rows or ys array: CBK_E_INVALID.  Every tensor is checked
+ * count == 0 is a no-op.  Errors: a NULL ts, outs, rows or ys array: CBK_E_INVALID.  Every tensor is checked
  * as by the single call before anything is launched, and the first failure's status is returned
  * with nothing enqueued.
  */

@@ -13,6 +13,7 @@ namespace {
 }
 }  // namespace
 cbk_status launch_decode(const cbk_tensor &, uint16_t *, hipStream_t) { reached("decode"); }
+cbk_status launch_decode_group(const cbk_tensor *, uint32_t, uint16_t *const *, hipStream_t) { reached("decode_group"); }
 cbk_status launch_gemv(const cbk_tensor &, const uint16_t *, float *, hipStream_t) { reached("gemv"); }
 cbk_status launch_gemv_group(const cbk_tensor *, uint32_t, const uint16_t *, float *const *, hipStream_t) {
     reached("gemv_group");

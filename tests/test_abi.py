@@ -172,6 +172,13 @@ def test_gpu_calls_validate_before_any_hip_call(cbk):
     assert lib.cbk_gemm_group(pair, 2, X, 8, 2, ys_bad, ld, None) == 3            # Y not 4-byte aligned
     assert lib.cbk_gemm_group((cbk._Tensor * 2)(_tensor(cbk, 4, 8, 5, 3), _tensor(cbk, 4, 8, 5, 2)),
                               2, X, 8, 2, ys, ld, None) == 1                      # bad b
+    # grouped decode: each tensor checked as by cbk_decode_bf16; count 0 is a no-op
+    outs = (ctypes.c_void_p * 2)(0x8000, 0x9000)
+    assert lib.cbk_decode_group(None, 0, None, None) == 0
+    assert lib.cbk_decode_group(None, 2, outs, None) == 1
+    assert lib.cbk_decode_group(arr2, 2, outs, None) == 1                        # bad b in the second tensor
+    assert lib.cbk_decode_group(arr, 2, (ctypes.c_void_p * 2)(0x8000, None), None) == 1
+    assert lib.cbk_decode_group(arr, 2, (ctypes.c_void_p * 2)(0x8000, 0x9001), None) == 3
     # zero-size tensors are accepted without work (no HIP call either)
     assert lib.cbk_gemv(T(rows=0, cols=0, U=0, b=0, cb=0, words=0), None, None, None) == 0
     assert lib.cbk_decode_bf16(T(rows=0, cols=9, U=0, b=0, cb=0, words=0), None, None) == 0
@@ -208,7 +215,7 @@ def test_gpu_encoder_group_validates_before_any_hip_call(cbk):
         return (J * len(ds))(*[J(**d) for d in ds])
     WS = ctypes.c_void_p(0x20000)
     assert lib.cbk_encode_gpu_group(None, 1, WS, None) == 1
-    assert lib.cbk_encode_gpu_group(jobs(good), 0, WS, None) == 1
+    assert lib.cbk_encode_gpu_group(None, 0, None, None) == 0      # no jobs: no-op
     assert lib.cbk_encode_gpu_group(jobs(good), 1, None, None) == 1
     assert lib.cbk_encode_gpu_group(jobs(good, dict(good, meta=None)), 2, WS, None) == 1
     assert lib.cbk_encode_gpu_group(jobs(good, dict(good, w=0x10008)), 2, WS, None) == 3

@@ -184,7 +184,7 @@ def test_group_calls_validate_before_any_hip_call(cbk):
     assert lib.cbk_ec_decode_group(arr(good, good), None, 2, ptrs(A, A + 2), None) == 3   # misaligned output
     assert lib.cbk_ec_decode_group(arr(good, good), ptrs(A, None), 2, ptrs(A, A), None) == 1  # an index missing
     assert lib.cbk_ec_decode_group(arr(good, good), ptrs(A, A + 8), 2, ptrs(A, A), None) == 3  # misaligned index
-    assert lib.cbk_ec_decode_group(arr(good), None, 0, ptrs(A), None) == 1          # no tensors
+    assert lib.cbk_ec_decode_group(None, None, 0, None, None) == 0                  # no tensors: no-op
     assert lib.cbk_ec_decode_group(None, None, 1, ptrs(A), None) == 1
     assert lib.cbk_ec_decode_group(arr(good), None, 1, None, None) == 1
     assert lib.cbk_ec_decode_group(arr(dict(n=0, total_bits=0)), None, 1, ptrs(None), None) == 0  # empty: no-op
@@ -199,7 +199,7 @@ def test_group_calls_validate_before_any_hip_call(cbk):
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(200, 200), 32, P(A), ptrs(A, A), None) == 4   # cols < 64
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, None, 64, P(A), ptrs(A, A), None) == 1
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, P(A), None, None) == 1
-    assert lib.cbk_ec_gemv_group(arr(g, g), None, 0, R(100, 100), 64, P(A), ptrs(A, A), None) == 1
+    assert lib.cbk_ec_gemv_group(None, None, 0, None, 64, None, None, None) == 0  # no tensors: no-op
     assert lib.cbk_ec_gemv_group(arr(g, g), None, 2, R(100, 100), 64, None, ptrs(A, A), None) == 1  # no x
 
 

@@ -496,6 +496,32 @@ def test_encode_gpu_workload_tensor_and_oracle(env, oracle_mod):
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(w.shape), w)
 
 
+def test_decode_group_bit_exact(env):
+    """cbk_decode_group over sixteen tensors: runs of one width split by a width change, a run of
+    nine (eight, then one), an empty tensor, b = 0, a misaligned output (the generic kernel) and
+    ragged lengths; every output equals the input patterns, as the single-tensor call's does."""
+    torch, cbk = env
+    shapes = [(300, 1000, 5000), (1, 7, 3), (4096, 64, 5000), (0, 64, 1), (17, 333, 1), (9, 1000, 5000),
+              (70, 130, 2), (257, 512, 2), (100, 100, 2), (33, 65, 2), (64, 64, 2), (5, 999, 2),
+              (3, 64, 2), (40, 72, 2), (2, 8, 2), (11, 1024, 2)]
+    ws, ds = [], []
+    for i, (r, c, U) in enumerate(shapes):
+        n = r * c
+        w = (synth.with_distinct_count(n, min(U, n), seed=[110, i]) if n else np.zeros(0, np.uint16)).reshape(r, c)
+        ws.append(w)
+        ds.append(cbk.encode(w).to("cuda"))
+    print(f"decode group of {len(ws)} tensors, widths {[d.b for d in ds]}", flush=True)
+    outs = [torch.full((d.rows, d.cols), float("nan"), dtype=torch.bfloat16, device="cuda") for d in ds]
+    # tensor 6's output starts 2 bytes into its buffer: not 16-byte aligned
+    spare = torch.full((ds[6].rows * ds[6].cols + 8,), -1, dtype=torch.int16, device="cuda")
+    outs[6] = spare[1:1 + ds[6].rows * ds[6].cols].view(torch.bfloat16).view(ds[6].rows, ds[6].cols)
+    cbk.decode_group(ds, outs=outs)
+    torch.cuda.synchronize()
+    for i, (w, o) in enumerate(zip(ws, outs)):
+        assert np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), w), (i, w.shape)
+    assert int(spare[0]) == -1 and bool((spare[1 + ws[6].size:].cpu() == -1).all())
+
+
 def test_encode_gpu_group_matches_host(env):
     """cbk_encode_gpu_group over eleven tensors (a run of eight, then three reusing the first
     workspaces): empty and ragged lengths, widths from 0 to 16 (every 16-bit pattern) and a
