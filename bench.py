@@ -512,6 +512,44 @@ def cpu_baseline_encode(work: Workload, seconds: float):
     }
 
 
+def cpu_baseline_decode(work: Workload, seconds: float):
+    """The oracle's decoder (plain C, one host thread) on one whole tensor of the workload, encoded
+    by the oracle beforehand (not timed)."""
+    import oracle
+    import synth
+
+    oracle.build(force=False)
+    cfg, layer, t = work.specs[0]
+    e = oracle.encode(synth.workload_tensor(cfg, layer, t))
+    t_total, used = 0.0, 0
+    while t_total < seconds and used < 4096:
+        t0 = time.perf_counter()
+        oracle.decode(e)
+        t_total += time.perf_counter() - t0
+        used += 1
+    return {
+        "value": round(2.0 * used * t.rows * t.cols / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": f"{used} full decodes of one {t.rows}x{t.cols} tensor of the workload with the "
+                  f"oracle's decoder (one host thread), {t_total:.1f} s",
+    }
+
+
+def check_decoded(work: Workload, which):
+    """The decoded BF16 of tensors `which` after the timed steps against the host weights (exact)."""
+    import torch
+    import synth
+    for i in which:
+        cfg, layer, t = work.specs[i]
+        got = work.ys[i].view(torch.int16).cpu().numpy().view(np.uint16).reshape(t.rows, t.cols)
+        if not np.array_equal(got, synth.workload_tensor(cfg, layer, t)):
+            raise SystemExit(f"decode of tensor {i} is not bit-exact")
+    return {"tensors": len(which), "bit_exact": True}
+
+
 def cpu_baseline_ec(work: Workload, seconds: float):
     """The oracle's bit-by-bit decoder of the entropy-coded format (pure Python, one thread) on
     leading rows of one tensor of the workload, growing the sample until about `seconds` pass.
@@ -557,6 +595,7 @@ def check_encoded(work: Workload, which):
             np.array_equal(work.enc_words[i][:nw].cpu().numpy().view(np.uint32), h.words)
         if not ok:
             raise SystemExit(f"GPU encoding of tensor {i} differs from the host encoder")
+    return {"tensors": len(which), "equal_to_host_encoder": True}
 
 
 def check_ec(work: Workload, which):
@@ -739,13 +778,18 @@ def main():
         if st != 0:
             print(f"the GEMV chain gave up waiting (status {st})", file=sys.stderr)
             sys.exit(1)
+    # outputs of the last timed step, first and last tensor (the GEMV and GEMM workloads are checked
+    # on sampled rows of every tensor with the CPU baseline below)
+    out_check = None
     if work.encode:
-        check_encoded(work, sorted({0, len(work.raws) - 1}))
+        out_check = check_encoded(work, sorted({0, len(work.raws) - 1}))
         log("device encodings of the first and last tensor equal the host encoder's")
-    ec_check = None
-    if work.ecfmt:
-        ec_check = check_ec(work, sorted({0, len(work.tensors) - 1}))
-        log(f"entropy-coded outputs of the first and last tensor checked: {ec_check}")
+    elif work.ecfmt:
+        out_check = check_ec(work, sorted({0, len(work.tensors) - 1}))
+        log(f"entropy-coded outputs of the first and last tensor checked: {out_check}")
+    elif work.batch == 0:
+        out_check = check_decoded(work, sorted({0, len(work.tensors) - 1}))
+        log(f"decoded outputs of the first and last tensor checked: {out_check}")
 
     copy_gbps = copy_bandwidth(args.copy_bytes)
     log(f"device-to-device copy of {args.copy_bytes} B: {copy_gbps:.1f} GB/s (read + write)")
@@ -844,8 +888,8 @@ def main():
     if work.batch > 1:
         result["effective_TFLOPs"] = round(2.0 * work.batch * n_total / step_s / 1e12, 3)
 
-    if ec_check is not None:
-        result["check"] = ec_check
+    if out_check is not None:
+        result["check"] = out_check
     if not args.no_cpu_baseline and work.batch >= 1 and not work.ecgemv:
         log("CPU baseline (oracle on sampled rows of every tensor) and output check ...")
         result["cpu_baseline"], result["check"] = cpu_baseline(work, args.cpu_rows, args.cpu_seconds, threads)
@@ -856,6 +900,9 @@ def main():
     elif not args.no_cpu_baseline and work.encode:
         log("CPU baseline (oracle encoder) ...")
         result["cpu_baseline"] = cpu_baseline_encode(work, args.cpu_seconds)
+    elif not args.no_cpu_baseline and work.batch == 0:
+        log("CPU baseline (oracle decoder) ...")
+        result["cpu_baseline"] = cpu_baseline_decode(work, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
