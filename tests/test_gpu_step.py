@@ -9,6 +9,10 @@
 * One layer of each step workload captured in a HIP graph exactly as bench.py builds and times it,
   replayed twice with the outputs clobbered in between: every tensor's output, on sampled rows, is
   within tolerance of the oracle after each replay.
+* The grouped calls of the 4096^2 workloads (decode, GPU encode, entropy-coded decode and fused
+  GEMV) captured and replayed three times the same way: the first and last tensor of every call
+  equal the host weights or the host encoder (the fused GEMV: sampled rows within tolerance of the
+  oracle) after each replay.
 
 The oracle's inputs are the host draws of the same rows (synth.workload_rows), encoded by the
 oracle itself; nothing the GPU computes is used as an expected value.
@@ -111,3 +115,34 @@ def test_layer_step_graph_replay(env, oracle_mod, workload):
             pick = (lambda r: yh[r]) if work.batch == 1 else (lambda r: yh[:, r])
             _check_rows(oracle_mod, cfg, layer, t, pick, X[t.cols], rows)
             assert not np.isnan(yh).any(), f"{t.name}: replay {rep} left outputs unwritten"
+
+
+@pytest.mark.parametrize("workload,ec_index", [("decode4096", False), ("encode4096", False), ("ecdecode4096", False),
+                                               ("ecdecode4096", True), ("ecgemv4096", True)])
+def test_grouped_calls_graph_replay(env, workload, ec_index):
+    """The grouped calls of the 4096^2 workloads (cbk_decode_group, cbk_encode_gpu_group,
+    cbk_ec_decode_group, cbk_ec_gemv_group; four or three tensors per call, the last call ragged)
+    captured in a HIP graph as bench.py builds it and replayed three times, every output clobbered
+    before each replay: the first and last tensor of every call are checked after each replay
+    (bit-exact, or within the tolerance for the fused GEMV)."""
+    torch, cbk = env
+    import bench
+    print(f"graph replay of {workload} (index {ec_index})", flush=True)
+    work = bench.Workload(workload, count=10, ec_index=ec_index)
+    graph = work.capture()
+    which = sorted({i for ph in work.phases for i in (ph[0], ph[-1])})
+    for rep in range(3):
+        if work.encode:
+            for t in work.enc_words + work.enc_meta + work.enc_cb:
+                t.fill_(-1)
+        else:
+            for y in work.ys:
+                y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        if work.encode:
+            bench.check_encoded(work, which)
+        elif work.ecfmt:
+            bench.check_ec(work, which)
+        else:
+            bench.check_decoded(work, which)
