@@ -7,12 +7,14 @@ and distinct counts up to 65,536.
 * The size helpers agree with the definitions: b = bits_for(U), 2U + ceil(n b / 8) bytes, and the
   word count rounded up to 16 bytes.
 * The capped codebook (cbk_cap_patterns) equals its oracle on random tensors and caps.
+* The exponent entropy-coded encoder equals its oracle on random exponent distributions (one
+  exponent to a skew the 12-bit cap binds), and its largest per-block code count matches the bases.
 
 The derandomized profile keeps the cases fixed from run to run.
 """
 import numpy as np
 import pytest
-from hypothesis import HealthCheck, given, settings
+from hypothesis import HealthCheck, example, given, settings
 from hypothesis import strategies as st
 
 import synth
@@ -97,3 +99,63 @@ def test_capped_codebook_equals_oracle(cbk, K, distinct, seed):
     ref = capped.cap(w, K)
     assert np.array_equal(got, ref)
     assert U == len(np.unique(ref)) == min(distinct, K)
+
+
+@st.composite
+def ec_tensors(draw, max_n=30000):
+    """BF16 patterns whose exponents take k distinct values with geometric frequencies (ratio r),
+    random signs and mantissas: from one exponent (one-bit codes) to heavy skew and long codes."""
+    k = draw(st.integers(1, 40))
+    r = draw(st.floats(0.3, 1.0))
+    n = draw(st.integers(0, max_n))
+    seed = draw(st.integers(0, 2 ** 31))
+    rng = np.random.default_rng(seed)
+    exps = rng.choice(np.arange(256), size=k, replace=False)
+    p = r ** np.arange(k)
+    e = exps[rng.choice(k, size=n, p=p / p.sum())].astype(np.uint16)
+    sm = rng.integers(0, 256, size=n).astype(np.uint16)
+    w = ((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)
+    return w.astype(np.uint16).reshape(1, n)
+
+
+def _ec_example(n, k, r, seed):
+    rng = np.random.default_rng(seed)
+    exps = rng.choice(np.arange(256), size=k, replace=False)
+    p = r ** np.arange(k)
+    e = exps[rng.choice(k, size=n, p=p / p.sum())].astype(np.uint16)
+    sm = rng.integers(0, 256, size=n).astype(np.uint16)
+    return (((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)).astype(np.uint16).reshape(1, n)
+
+
+def _ec_capped(k, seed):
+    """k exponents with counts 2^(k-1), ..., 2, 1 (shuffled): an uncapped Huffman code would reach
+    k - 1 bits, so the 12-bit cap binds."""
+    rng = np.random.default_rng(seed)
+    exps = rng.choice(np.arange(256), size=k, replace=False)
+    e = rng.permutation(np.repeat(exps, 2 ** np.arange(k - 1, -1, -1))).astype(np.uint16)
+    sm = rng.integers(0, 256, size=e.size).astype(np.uint16)
+    return (((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)).astype(np.uint16).reshape(1, e.size)
+
+
+@settings(max_examples=40, **SETTINGS)
+@given(ec_tensors())
+@example(_ec_example(50000, 1, 1.0, 1))      # one exponent: one-bit codes, 16,384 per full block
+@example(_ec_capped(16, 2))                  # a skew that the 12-bit cap binds (65,535 weights)
+@example(_ec_example(40000, 12, 0.8, 3))     # weights-like spread over several blocks
+def test_entropy_encoder_equals_oracle(cbk, w):
+    """The library's exponent entropy-coded encoder on random exponent distributions: the oracle's
+    optimal stream length under the 12-bit cap, a prefix code (Kraft sum at most 1), every array
+    byte-identical to the oracle's encoding with the same lengths, and the largest per-block code
+    count (cbk_ec_max_block_codes) equal to the one the bases give."""
+    from oracle import entropy as ec
+    t = cbk.ec_encode(w)
+    n = w.size
+    assert t.total_bits == ec.encode(w).total_bits
+    present = [l for l in t.lengths if l]
+    assert all(1 <= l <= ec.L_MAX for l in present)
+    assert sum(2.0 ** -l for l in present) <= 1.0 + 1e-12
+    o = ec.encode_with_lengths(w, t.lengths)
+    for a in ("sm", "stream", "gaps", "bases", "lut"):
+        assert np.array_equal(getattr(t, a), getattr(o, a)), a
+    want = int(np.diff(np.append(t.bases.astype(np.int64), n)).max()) if n else 0
+    assert t.max_block_codes == want
