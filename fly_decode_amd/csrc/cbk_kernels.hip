@@ -1114,7 +1114,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_mfma(const GemmGroup g
 // every v_dot2c reads its X operand from the owning lane with a row_newbcast DPP broadcast.  For
 // group f the owners are lanes 2f and 2f + 1.  The broadcasts are written as inline asm because
 // the compiler does not fold a DPP move into v_dot2c; each block starts with s_nop 1, the wait a
-// DPP read of a VGPR needs after a VALU write to it.
+// DPP read of a VGPR needs after a VALU write to it, and ends with s_nop 2: on this chip another
+// VALU instruction that reads a register a dot instruction has just written needs three wait
+// states, and the compiler, which does not see inside the asm, would not insert them.
 template <int NB>
 struct DppDot;
 
@@ -1128,6 +1130,7 @@ struct DppDot<1> {
             "v_dot2c_f32_bf16_dpp %0, %2, %4 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %0, %1, %5 row_newbcast:%c8 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %0, %2, %6 row_newbcast:%c8 row_mask:0xf bank_mask:0xf\n"
+            "s_nop 2\n"
             : "+v"(a[0])
             : "v"(xr[0]), "v"(xr[1]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
     }
@@ -1147,6 +1150,7 @@ struct DppDot<2> {
             "v_dot2c_f32_bf16_dpp %1, %3, %7 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %1, %4, %8 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %1, %5, %9 row_newbcast:%c11 row_mask:0xf bank_mask:0xf\n"
+            "s_nop 2\n"
             : "+v"(a[0]), "+v"(a[1])
             : "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
     }
@@ -1174,6 +1178,7 @@ struct DppDot<4> {
             "v_dot2c_f32_bf16_dpp %3, %9, %13 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %3, %10, %14 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %3, %11, %15 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n"
+            "s_nop 2\n"
             : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
             : "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]), "v"(xr[7]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
     }
@@ -1217,21 +1222,26 @@ struct DppDot<8> {
             "v_dot2c_f32_bf16_dpp %7, %21, %25 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %7, %22, %26 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
             "v_dot2c_f32_bf16_dpp %7, %23, %27 row_newbcast:%c29 row_mask:0xf bank_mask:0xf\n"
+            "s_nop 2\n"
             : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
             : "v"(xr[0]), "v"(xr[1]), "v"(xr[2]), "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]), "v"(xr[7]), "v"(xr[8]), "v"(xr[9]), "v"(xr[10]), "v"(xr[11]), "v"(xr[12]), "v"(xr[13]), "v"(xr[14]), "v"(xr[15]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "i"(2 * F), "i"(2 * F + 1));
     }
 };
 
 // X registers of one step for lane (i, g): chunk q = f NB + n (16 bytes: fields 8f .. 8f + 7 of
-// batch row n, unit u) for q in [i NB / 2, (i + 1) NB / 2); for NB = 1, half of chunk i / 2.  Rows
-// >= batch and units past the wave's range read as zero.
+// batch row n, unit u) for q in [i NB / 2, (i + 1) NB / 2); for NB = 1, half of chunk i / 2.  The
+// loads go through a buffer resource over X's batch rows (`xs`, batch * ldx elements; the host
+// keeps that under 2^30 bytes).  Rows >= batch and units past the wave's range get an offset past
+// the resource and read zeros with no memory access, so there is neither a branch nor a zero fill.
+constexpr uint32_t kPastResource = 0x80000000u;
+
 template <int NB>
-__device__ __forceinline__ void gemm_load_xr(uint32_t (&v)[2 * NB], const uint16_t *__restrict__ X, uint32_t u,
+__device__ __forceinline__ void gemm_load_xr(uint32_t (&v)[2 * NB], __amdgpu_buffer_rsrc_t xs, uint32_t u,
                                              bool unit_ok, const GemmShape &s, int li) {
     if constexpr (NB == 1) {
         const uint32_t f = static_cast<uint32_t>(li) >> 1, c = (static_cast<uint32_t>(li) & 1u) * 2u;
-        u32x2 t = {0u, 0u};
-        if (unit_ok) t = *reinterpret_cast<const u32x2 *>(X + static_cast<uint64_t>(u) * 64 + 8 * f + 2 * c);
+        const uint32_t off = unit_ok ? (u * 64u + 8u * f + 2u * c) * 2u : kPastResource;
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(xs, static_cast<int>(off), 0, 0);
         v[0] = t.x;
         v[1] = t.y;
     } else {
@@ -1239,9 +1249,8 @@ __device__ __forceinline__ void gemm_load_xr(uint32_t (&v)[2 * NB], const uint16
         for (int h = 0; h < NB / 2; ++h) {
             const uint32_t q = static_cast<uint32_t>(li) * (NB / 2) + h;
             const uint32_t f = q / NB, n = q % NB;
-            u32x4 t = {0u, 0u, 0u, 0u};
-            if (unit_ok && n < s.batch)
-                t = *reinterpret_cast<const u32x4 *>(X + static_cast<uint64_t>(n) * s.ldx + static_cast<uint64_t>(u) * 64 + 8 * f);
+            const uint32_t off = (unit_ok && n < s.batch) ? (n * s.ldx + u * 64u + 8u * f) * 2u : kPastResource;
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xs, static_cast<int>(off), 0, 0);
             v[4 * h] = t.x; v[4 * h + 1] = t.y; v[4 * h + 2] = t.z; v[4 * h + 3] = t.w;
         }
     }
@@ -1251,6 +1260,78 @@ template <int NB, int... F>
 __device__ __forceinline__ void dpp_groups(float (&acc)[NB], const uint32_t (&xr)[2 * NB], const uint32_t (&wp)[8][4],
                                            std::integer_sequence<int, F...>) {
     (DppDot<NB>::template group<F>(acc, xr, wp[F]), ...);
+}
+
+// Decode the lane's unit (d, UD dwords read back from the stage) and accumulate its dot products
+// with the step's X registers.
+template <int B, int NB>
+__device__ __forceinline__ void valu_unit(float (&acc)[NB], const uint32_t (&d)[GemmGeo<B>::UD],
+                                          const uint16_t *cbl, const uint32_t (&xr)[2 * NB]) {
+    uint32_t wp[8][4];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = unit_gather<B>(cbl, d, 8 * f + i);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wp[f][c] = w[2 * c] | (w[2 * c + 1] << 16);
+    }
+    dpp_groups<NB>(acc, xr, wp, std::make_integer_sequence<int, 8>{});
+}
+
+// One wave step of k_gemm_valu: stage the step's weights (nw) and read back the lane's unit, issue
+// the next step's loads (weights into nw, X into xn), then decode and multiply with this step's X
+// (xc).  The caller alternates two X register sets, so no X register is copied.
+template <int B, int NB, bool LAST>
+__device__ __forceinline__ void valu_step(float (&acc)[NB], u32x4 (&nw)[GemmGeo<B>::LPL],
+                                          const uint32_t (&xc)[2 * NB], uint32_t (&xn)[2 * NB], u32x4 *stage,
+                                          const uint16_t *cbl, const u32x4 *__restrict__ w4, uint64_t nch,
+                                          __amdgpu_buffer_rsrc_t xs, const GemmShape &s, uint32_t row0,
+                                          uint32_t ku1, uint32_t u0, int lane) {
+    using G = GemmGeo<B>;
+    const int li = lane & 15, lg = lane >> 4;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < G::LPL; ++j) {
+        const uint32_t q = j * 64 + lane;
+        if (q < G::STEP_CH) {
+            const uint32_t i = q / G::RCH, c = q - i * G::RCH;
+            stage[i * G::SRC + c] = nw[j];
+        }
+    }
+    asm volatile("" ::: "memory");
+    const uint64_t rr = min(row0 + li, s.M - 1);
+    const uint32_t off = static_cast<uint32_t>(((rr * s.P + u0) * G::UD) & 3u);  // 0 or 2 dwords
+    const u32x2 *st2 = reinterpret_cast<const u32x2 *>(stage + li * G::SRC) + off / 2 + lg * B;
+    uint32_t d[G::UD];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const u32x2 t = st2[j];
+        d[2 * j] = t.x; d[2 * j + 1] = t.y;
+    }
+    asm volatile("" ::: "memory");
+    // The next step's loads (every step but the wave's last), ahead of the multiply, which hides
+    // their latency; the wait before the multiply then covers this step's X only.
+    if constexpr (!LAST) {
+        gemm_load_w<B, kGemmValuW>(nw, w4, nch, row0, u0 + 4, s, lane);
+        gemm_load_xr<NB>(xn, xs, u0 + 4 + lg, u0 + 4 + lg < ku1, s, li);
+        asm volatile("" ::: "memory");
+    }
+    // A step that runs past the wave's part of K (only the last one, LAST, when K / 64 is not a
+    // multiple of 4): the lanes of units past it keep their sums from before the step.  Their X is
+    // zero, but the stage there holds other data, whose table entries may be NaN (the padding).
+    // Lanes of rows past M need nothing: their sums stay in their own lanes and are never written.
+    const bool partial = LAST && u0 + 4 > ku1;  // wave-uniform
+    float kept[NB];
+    if (partial) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) kept[n] = acc[n];
+    }
+    valu_unit<B, NB>(acc, d, cbl, xc);
+    if (partial && u0 + lg >= ku1) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] = kept[n];
+    }
 }
 
 template <int B, int NB>
@@ -1296,9 +1377,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_valu(const GemmGroup g
     cs.issue(cb, U, reinterpret_cast<const u32x4 *>(X), tid);
     issue_barrier();
     u32x4 nw[G::LPL];
-    uint32_t nxr[2 * NB];
+    uint32_t xa[2 * NB], xb[2 * NB];
     gemm_load_w<B, kGemmValuW>(nw, w4, T.nch, row0, ku0, s, lane);
-    gemm_load_xr<NB>(nxr, X, ku0 + lg, ku0 + lg < ku1, s, li);
+    // X's batch rows as one buffer (the host keeps batch * ldx * 2 bytes under 2^30)
+    const auto xs = wave_rsrc(X, s.batch * s.ldx * 2u);
+    gemm_load_xr<NB>(xa, xs, ku0 + lg, ku0 + lg < ku1, s, li);
     cs.store(cbl, U, tid);
     lds_barrier();
 
@@ -1307,47 +1390,19 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_valu(const GemmGroup g
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[n] = 0.f;
 
-    for (uint32_t st = 0; st < nsteps; ++st) {
-        const uint32_t u0 = ku0 + 4 * st;
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < G::LPL; ++j) {
-            const uint32_t q = j * 64 + lane;
-            if (q < G::STEP_CH) {
-                const uint32_t i = q / G::RCH, c = q - i * G::RCH;
-                stage[i * G::SRC + c] = nw[j];
-            }
-        }
-        asm volatile("" ::: "memory");
-        const uint64_t rr = min(row0 + li, s.M - 1);
-        const uint32_t off = static_cast<uint32_t>(((rr * s.P + u0) * G::UD) & 3u);  // 0 or 2 dwords
-        const u32x2 *st2 = reinterpret_cast<const u32x2 *>(stage + li * G::SRC) + off / 2 + lg * B;
-        uint32_t d[G::UD];
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const u32x2 t = st2[j];
-            d[2 * j] = t.x; d[2 * j + 1] = t.y;
-        }
-        asm volatile("" ::: "memory");
-        uint32_t xr[2 * NB];
-#pragma unroll
-        for (int i = 0; i < 2 * NB; ++i) xr[i] = nxr[i];
-        if (st + 1 < nsteps) {
-            gemm_load_w<B, kGemmValuW>(nw, w4, T.nch, row0, u0 + 4, s, lane);
-            gemm_load_xr<NB>(nxr, X, u0 + 4 + lg, u0 + 4 + lg < ku1, s, li);
-        }
-
-        const bool valid = row_ok && u0 + lg < ku1;
-        uint32_t wp[8][4];
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = unit_gather<B>(cbl, d, 8 * f + i);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) wp[f][c] = valid ? (w[2 * c] | (w[2 * c + 1] << 16)) : 0u;
-        }
-        dpp_groups<NB>(acc, xr, wp, std::make_integer_sequence<int, 8>{});
+    // Two steps per trip: the first multiplies X set a and loads set b, the second the reverse.
+    // The trips leave the last one or two steps to the code after the loop, so every load inside
+    // the loop feeds a later step (the compiler then keeps it ahead of the multiply).
+    uint32_t st = 0;
+    for (; st + 2 < nsteps; st += 2) {
+        valu_step<B, NB, false>(acc, nw, xa, xb, stage, cbl, w4, T.nch, xs, s, row0, ku1, ku0 + 4 * st, lane);
+        valu_step<B, NB, false>(acc, nw, xb, xa, stage, cbl, w4, T.nch, xs, s, row0, ku1, ku0 + 4 * (st + 1), lane);
+    }
+    if (st + 1 < nsteps) {
+        valu_step<B, NB, false>(acc, nw, xa, xb, stage, cbl, w4, T.nch, xs, s, row0, ku1, ku0 + 4 * st, lane);
+        valu_step<B, NB, true>(acc, nw, xb, xa, stage, cbl, w4, T.nch, xs, s, row0, ku1, ku0 + 4 * (st + 1), lane);
+    } else if (st < nsteps) {
+        valu_step<B, NB, true>(acc, nw, xa, xb, stage, cbl, w4, T.nch, xs, s, row0, ku1, ku0 + 4 * st, lane);
     }
 
     // lanes with g = 0 hold row l % 16 of every column after summing the four k-groups
@@ -1595,6 +1650,8 @@ bool gemm_launch(GemmArgs &a) {
     const uint32_t stage = MFMA ? gemm_stage_bytes<B, NB>() : static_cast<uint32_t>(GemmGeo<B>::WSTAGE);
     const uint32_t lds = kGemmWaves * stage + kGemmWaves * 256 * 4;
     if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
+    // the VALU kernel reads X through one buffer resource with 32-bit offsets
+    if (!MFMA && uint64_t(a.batch) * a.ldx * 2 >= (uint64_t(1) << 30)) return false;
     // Tiles per workgroup TW (the other kGemmWaves / TW waves split K).  The LDS decides how many
     // workgroups run on a CU at once (two at b = 13), and the grid drains in ceil(blocks / slots)
     // rounds of workgroups that each take TW tiles by the whole of K: pick the TW with the fewest
