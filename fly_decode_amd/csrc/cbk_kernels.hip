@@ -1263,20 +1263,38 @@ __device__ __forceinline__ void dpp_groups(float (&acc)[NB], const uint32_t (&xr
 }
 
 // Decode the lane's unit (d, UD dwords read back from the stage) and accumulate its dot products
-// with the step's X registers.
+// with the step's X registers.  The gathers of 8-field group f + 1 are issued before the dot
+// products of group f (the empty asm keeps the compiler from hoisting every gather of the step
+// ahead of the first multiply), so each wave's LDS latency overlaps its own VALU work.
+template <int B, int NB, int F>
+__device__ __forceinline__ void valu_group(float (&acc)[NB], const uint32_t (&d)[GemmGeo<B>::UD],
+                                           const uint16_t *cbl, const uint32_t (&xr)[2 * NB],
+                                           uint32_t (&w)[2][8]) {
+    if constexpr (F + 1 < 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[(F + 1) & 1][i] = unit_gather<B>(cbl, d, 8 * (F + 1) + i);
+    }
+    asm volatile("" ::: "memory");
+    uint32_t wp[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wp[c] = w[F & 1][2 * c] | (w[F & 1][2 * c + 1] << 16);
+    DppDot<NB>::template group<F>(acc, xr, wp);
+}
+
+template <int B, int NB, int... F>
+__device__ __forceinline__ void valu_unit_groups(float (&acc)[NB], const uint32_t (&d)[GemmGeo<B>::UD],
+                                                 const uint16_t *cbl, const uint32_t (&xr)[2 * NB],
+                                                 std::integer_sequence<int, F...>) {
+    uint32_t w[2][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[0][i] = unit_gather<B>(cbl, d, i);
+    (valu_group<B, NB, F>(acc, d, cbl, xr, w), ...);
+}
+
 template <int B, int NB>
 __device__ __forceinline__ void valu_unit(float (&acc)[NB], const uint32_t (&d)[GemmGeo<B>::UD],
                                           const uint16_t *cbl, const uint32_t (&xr)[2 * NB]) {
-    uint32_t wp[8][4];
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = unit_gather<B>(cbl, d, 8 * f + i);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) wp[f][c] = w[2 * c] | (w[2 * c + 1] << 16);
-    }
-    dpp_groups<NB>(acc, xr, wp, std::make_integer_sequence<int, 8>{});
+    valu_unit_groups<B, NB>(acc, d, cbl, xr, std::make_integer_sequence<int, 8>{});
 }
 
 // One wave step of k_gemm_valu: stage the step's weights (nw) and read back the lane's unit, issue
