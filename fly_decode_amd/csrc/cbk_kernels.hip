@@ -1073,6 +1073,10 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_mfma(const GemmGroup g
             const uint32_t *w = wv[f & 1];
             u32x4 wp = {w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16)};
             if (!valid) wp = (u32x4){0u, 0u, 0u, 0u};
+            // Group f's operand passes through an empty asm that is ordered after group f + 1's
+            // LDS reads, so the multiply stays behind them: otherwise the compiler moves some
+            // multiplies ahead of the next group's reads and waits for every read before them.
+            asm volatile("" : "+v"(wp) :: "memory");
             // B operand: lane (n = l % 16, g) holds X[n][unit g, fields 8f .. 8f + 7]
             cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wp),
                                                          __builtin_bit_cast(bf16x8_t, xq[f & 1]), cm, 0, 0, 0);
