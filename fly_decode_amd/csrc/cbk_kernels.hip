@@ -873,6 +873,7 @@ struct GemmGeo {
     static constexpr int WSTAGE = 16 * SRC * 16;             // bytes of the weight stage
 };
 static_assert(GemmGeo<13>::SRC == 33 && GemmGeo<16>::SRC == 33 && GemmGeo<1>::SRC == 17, "stage stride");
+static_assert(GemmGeo<1>::WSTAGE >= 16 * 16 * 4, "a wave's stage holds its 16 x 16 partial tile");
 
 constexpr uint32_t kXUnit = 2 * 64 + 16;   // LDS bytes per 64-column unit of one X row (16 B padding)
 constexpr uint32_t kXRow = 4 * kXUnit + 16;  // LDS bytes per X row of one step
@@ -973,7 +974,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_mfma(const GemmGroup g
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     unsigned char *stb = smem + wave * SB;                    // this wave's stage (weights, then X)
     u32x4 *stage = reinterpret_cast<u32x4 *>(stb);
-    float *part = reinterpret_cast<float *>(smem + kGemmWaves * SB);  // [wave][16 rows][16 columns]
+    // Wave w's partial tile (16 x 16 floats) goes to the start of its own stage, which it no longer
+    // needs once its last step is read back; the other waves read it only after the barrier.
+    auto part_of = [&](uint32_t w) { return reinterpret_cast<float *>(smem + w * SB); };
 
     // This workgroup's tensor (uniform): count the group boundaries at or below blockIdx.x.
     uint32_t k = 0;
@@ -1095,7 +1098,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_mfma(const GemmGroup g
         }
         return;
     }
-    float *mine = part + wave * 256;
+    float *mine = part_of(wave);
 #pragma unroll
     for (int r = 0; r < 4; ++r) mine[(4 * lg + r) * 16 + li] = cm[r];
     lds_barrier();
@@ -1105,7 +1108,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_mfma(const GemmGroup g
     for (int k = 0; k < 4; ++k) {
         const uint32_t e = 4 * lane + k, row = e >> 4, n = e & 15;
         float v = 0.f;
-        for (uint32_t p = 0; p < s.KW; ++p) v += part[(p * s.TW + tw) * 256 + e];
+        for (uint32_t p = 0; p < s.KW; ++p) v += part_of(p * s.TW + tw)[e];
         if (n < s.batch && n < static_cast<uint32_t>(NB) && row0 + row < s.M) Y[static_cast<uint64_t>(n) * s.ldy + row0 + row] = v;
     }
 }
@@ -1366,7 +1369,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_valu(const GemmGroup g
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     u32x4 *stage = reinterpret_cast<u32x4 *>(smem + wave * SB);  // this wave's weight stage
-    float *part = reinterpret_cast<float *>(smem + kGemmWaves * SB);  // [wave][16 rows][16 columns]
+    // Wave w's partial tile (16 x 16 floats) goes to the start of its own stage, which it no longer
+    // needs once its last step is read back; the other waves read it only after the barrier.
+    auto part_of = [&](uint32_t w) { return reinterpret_cast<float *>(smem + w * SB); };
 
     uint32_t k = 0;
 #pragma unroll
@@ -1444,7 +1449,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_valu(const GemmGroup g
         }
         return;
     }
-    float *mine = part + wave * 256;
+    float *mine = part_of(wave);
     if (lg == 0) {
 #pragma unroll
         for (int n = 0; n < NB; ++n) mine[li * 16 + n] = acc[n];
@@ -1455,7 +1460,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_valu(const GemmGroup g
     for (int k2 = 0; k2 < 4; ++k2) {
         const uint32_t e = 4 * lane + k2, row = e >> 4, n = e & 15;
         float v = 0.f;
-        for (uint32_t p = 0; p < s.KW; ++p) v += part[(p * s.TW + tw) * 256 + e];
+        for (uint32_t p = 0; p < s.KW; ++p) v += part_of(p * s.TW + tw)[e];
         if (n < s.batch && n < static_cast<uint32_t>(NB) && row0 + row < s.M) Y[static_cast<uint64_t>(n) * s.ldy + row0 + row] = v;
     }
 }
@@ -1667,10 +1672,11 @@ bool gemm_launch(GemmArgs &a) {
     grp.P = static_cast<uint32_t>(P);
     grp.batch = a.batch;
     grp.ldx = static_cast<uint32_t>(a.ldx);
-    // LDS: the waves' stages (weights only for the VALU kernel, whose X stays in registers) and
-    // the partial tiles of the split K, plus the codebook table.
+    // LDS: the waves' stages (weights only for the VALU kernel, whose X stays in registers; each
+    // wave's partial tile of the split K goes into its own stage after its last step), plus the
+    // codebook table.
     const uint32_t stage = MFMA ? gemm_stage_bytes<B, NB>() : static_cast<uint32_t>(GemmGeo<B>::WSTAGE);
-    const uint32_t lds = kGemmWaves * stage + kGemmWaves * 256 * 4;
+    const uint32_t lds = kGemmWaves * stage;  // the partial tiles reuse the stages
     if (uint64_t(lds) + uint64_t(Table<B>::SIZE) * 2 > kLdsLimit) return false;
     // the VALU kernel reads X through one buffer resource with 32-bit offsets
     if (!MFMA && uint64_t(a.batch) * a.ldx * 2 >= (uint64_t(1) << 30)) return false;
