@@ -277,6 +277,30 @@ def test_gemm_batches(env, oracle_mod, batch):
             _gemm_check(env, oracle_mod, w, X)
 
 
+@pytest.mark.parametrize("batch", [2, 5, 8, 12, 16])
+@pytest.mark.parametrize("cols", [320, 640])
+def test_gemm_partial_step_ignores_next_row_nonfinite(env, oracle_mod, batch, cols):
+    """K / 64 is not a multiple of 4 here, so a wave's last step runs past its part of K and its
+    unused units hold the next row's first fields.  Every odd row starts with 192 infinite
+    weights: the even rows' outputs must still match the oracle (the fast kernels drop those
+    units' products instead of multiplying them by zero), and the odd rows are non-finite."""
+    torch, cbk = env
+    rows = 48
+    w = synth.gaussian_bf16((rows, cols), 0.02, seed=[57, batch, cols]).copy()
+    w[1::2, :192] = 0x7F80  # +inf
+    X = synth.activations_bf16(batch, cols, 58)
+    d = cbk.encode(w).to("cuda")
+    Y = cbk.gemm_small(d, _up(torch, X, torch.bfloat16))
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy().astype(np.float64)
+    even = list(range(0, rows, 2))
+    ref, absb = _oracle_rows(oracle_mod, w, even, lambda e: oracle_mod.gemm(e, X))
+    got = Y[:, even]
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= TOL * absb)
+    assert not np.any(np.isfinite(Y[:, 1::2]))
+
+
 def test_gemm_integer_exact_and_column_equals_gemv(env, oracle_mod):
     torch, cbk = env
     rng = np.random.default_rng(53)
