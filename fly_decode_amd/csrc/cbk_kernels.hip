@@ -1263,12 +1263,6 @@ __device__ __forceinline__ void gemm_load_xr(uint32_t (&v)[2 * NB], __amdgpu_buf
     }
 }
 
-template <int NB, int... F>
-__device__ __forceinline__ void dpp_groups(float (&acc)[NB], const uint32_t (&xr)[2 * NB], const uint32_t (&wp)[8][4],
-                                           std::integer_sequence<int, F...>) {
-    (DppDot<NB>::template group<F>(acc, xr, wp[F]), ...);
-}
-
 // Decode the lane's unit (d, UD dwords read back from the stage) and accumulate its dot products
 // with the step's X registers.  The gathers of 8-field group f + 1 are issued before the dot
 // products of group f (the empty asm keeps the compiler from hoisting every gather of the step
